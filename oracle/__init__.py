@@ -1,0 +1,25 @@
+"""Plain CPU oracle of Purlin's collectives.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product (the HIP library and its
+Python binding) imports, links or calls this package; only the tests, the
+smoke check and the benchmark's CPU-baseline leg do.  It shares no code with
+the GPU path: it is numpy and plain Python, written from the definitions in
+"Purlin: Separating Orchestration from the Datapath of Collectives"
+(arXiv 2609.36954): the abstract (a collective is a naming of an input and an
+output layout plus a copy or a reduction), Figure 4 (ReduceScatter,
+AllGather and AllToAll layouts), Figure 6 (AllReduce composed of both) and
+Table 2 / Figure 16 (variable-length variants).
+
+Every function is pinned by the oracle tests; the readings it takes where the
+pages are silent are documented in ``semantics.py``.
+"""
+from .bf16 import widen_bf16, round_bf16
+from .semantics import (NAMINGS, OPS, DTYPES, ELEM_BYTES, COLLECTIVES,
+                         name_count, partitions, collective, OracleError)
+from .brute import collective_brute
+
+__all__ = [
+    "widen_bf16", "round_bf16", "NAMINGS", "OPS", "DTYPES", "ELEM_BYTES",
+    "COLLECTIVES", "name_count", "partitions", "collective", "OracleError",
+    "collective_brute",
+]
