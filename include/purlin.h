@@ -1,0 +1,192 @@
+/*
+ * purlin.h - C ABI of the Purlin collective hot path on one gfx950 GPU.
+ *
+ * Source of the semantics: "Purlin: Separating Orchestration from the
+ * Datapath of Collectives" (arXiv 2609.36954).
+ *   - A collective is a naming of an input layout and an output layout plus a
+ *     copy or a reduction (abstract).
+ *   - Layouts: ReduceScatter combines partition k of every input into y_k at
+ *     rank k; AllGather places every y_k, in rank order, at every rank;
+ *     AllToAll gives rank j partition j of every source (Figure 4 caption).
+ *   - AllReduce is ReduceScatter and AllGather composed chunk by chunk
+ *     (Figure 6 caption).
+ *   - (V) variants have variable partition sizes (Table 2, Figure 16).
+ *   - Coordination is derived from the specification by the SNAC protocol
+ *     (Stage, Notify, And Consume; abstract), the bytes are moved by the Atom
+ *     copy and reduce primitives (abstract), and the zero-staging variant
+ *     (Purlin-ZS) omits the staging step (Figure 10 caption).
+ *
+ * The P "ranks" are P buffer sets in the memory of the one current HIP
+ * device: each launch performs the share of every rank.  All pointers in
+ * purlin_layout are device pointers owned by the caller; nothing here takes
+ * ownership of them, frees them or keeps them after the call returns.
+ *
+ * Thread safety: none; serialize calls from different host threads.
+ */
+#ifndef PURLIN_H_
+#define PURLIN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PURLIN_MAX_RANKS 8
+
+#ifndef PURLIN_API
+#define PURLIN_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+  PURLIN_OK = 0,
+  PURLIN_ERR_INVALID_ARG = 1, /* bad pointer, P, count, alignment, overlap */
+  PURLIN_ERR_UNSUPPORTED = 2, /* the (naming, naming, op) triple is not a collective */
+  PURLIN_ERR_NO_MEMORY = 3,   /* workspace allocation failed */
+  PURLIN_ERR_HIP = 4,         /* a HIP call or kernel launch failed */
+  PURLIN_ERR_TIMEOUT = 5      /* a bounded device wait expired (see purlin_check) */
+} purlin_status;
+
+typedef enum { PURLIN_OP_COPY = 0, PURLIN_OP_SUM = 1 } purlin_op;
+
+/* Element type.  SUM widens each element exactly to fp32, adds in fp32 in
+ * ascending source rank, and rounds once to the output type (bf16: round to
+ * nearest even).  COPY moves bytes and only uses the element size. */
+typedef enum { PURLIN_F32 = 0, PURLIN_BF16 = 1 } purlin_dtype;
+
+/* How a rank's buffer is split into partitions, and each partition's name
+ * (r = the buffer's rank, q = the partition index). */
+typedef enum {
+  PURLIN_NAME_WHOLE = 0,         /* 1 partition,  name ()     */
+  PURLIN_NAME_BY_RANK = 1,       /* 1 partition,  name (r)    */
+  PURLIN_NAME_BY_INDEX = 2,      /* P partitions, name (q)    */
+  PURLIN_NAME_BY_RANK_INDEX = 3, /* P partitions, name (r, q) */
+  PURLIN_NAME_BY_INDEX_RANK = 4  /* P partitions, name (q, r) */
+} purlin_naming;
+
+typedef struct {
+  purlin_naming naming;
+  void *const *bufs; /* P device pointers, one buffer per rank; caller-owned.
+                        A buffer holding no element of the collective may be NULL. */
+} purlin_layout;
+
+typedef enum {
+  PURLIN_STAGING_AUTO = 0,  /* policy table decides */
+  PURLIN_STAGING_ZS = 1,    /* zero staging: consumers read the inputs directly */
+  PURLIN_STAGING_STAGED = 2 /* producers stage chunks in a ring, notify, consumers consume */
+} purlin_staging;
+
+/* Execution policy ("codesign policies tune execution", Figure 1 caption).
+ * A zero field means "automatic".  It never changes a result, only speed. */
+typedef struct {
+  int64_t chunk_bytes;   /* bytes per work chunk / staging slot; multiple of 4096 */
+  int32_t depth;         /* staging slots per channel, 1..8 (staged only) */
+  int32_t wgs_per_rank;  /* workgroups per rank; grid = P * wgs_per_rank */
+  int32_t zero_staging;  /* purlin_staging */
+  int32_t sync;          /* entry/exit notify flags: 0 auto, 1 on, 2 off */
+  int64_t watchdog_ns;   /* bound of every device spin wait */
+  int32_t test_withhold; /* test only: k > 0 withholds the k-th ready notify
+                            of staging channel 0, to exercise the watchdog */
+  int32_t reserved;
+} purlin_policy;
+
+/* One (output partition, matching input partition) pair of a plan. */
+typedef struct {
+  int32_t src_rank, dst_rank;
+  int64_t src_off, dst_off, len; /* elements */
+} purlin_segment;
+
+/* What the most recent purlin_collective launched (measurement only). */
+typedef struct {
+  int32_t grid;          /* workgroups launched */
+  int32_t threads;       /* threads per workgroup */
+  int32_t zero_staging;  /* 1 if the ZS kernel ran, 0 if the staged one */
+  int32_t depth;         /* staging depth used (staged) */
+  int64_t chunk_bytes;   /* chunk size used */
+  int64_t tiles;         /* work chunks in the launch */
+  int64_t bytes_min;     /* compulsory HBM bytes: inputs read once + outputs written once */
+  int32_t njobs;
+  int32_t sync;
+} purlin_launch_info;
+
+/*
+ * Run one collective over P ranks, asynchronously on `stream`.
+ *
+ * Output partition (j, s) receives `op` applied to every input partition
+ * (i, q) whose name equals its own, in ascending i: COPY needs exactly one
+ * such partition, SUM at least one.  The seven collectives:
+ *
+ *   collective        in naming      out naming     op    counts
+ *   AllReduce         WHOLE          WHOLE          SUM   [N]
+ *   ReduceScatter(V)  BY_INDEX       BY_RANK        SUM   [c_0 .. c_{P-1}] (y_k has c_k)
+ *   AllGather(V)      BY_RANK        BY_INDEX       COPY  [c_0 .. c_{P-1}] (rank k sends c_k)
+ *   AllToAll(V)       BY_RANK_INDEX  BY_INDEX_RANK  COPY  [P*P], counts[i*P+j] = size of
+ *                                                          partition j of rank i = slot i of rank j
+ *
+ * counts: one element count per name (names (a, b) are numbered a*P + b);
+ *   so it holds 1 entry for WHOLE, P for BY_RANK / BY_INDEX and P*P for the
+ *   pair namings.  A collective is "V" exactly when its counts differ.
+ * displs: NULL for partitions packed in index order, or 2 * len(counts)
+ *   element offsets: the input offsets then the output offsets, each indexed
+ *   by name like counts, into the buffer of the rank holding that name
+ *   (BY_INDEX and WHOLE offsets are shared by every rank).  Output elements
+ *   outside every partition are never written.
+ *
+ * Requirements (else PURLIN_ERR_INVALID_ARG, checked before any HIP call):
+ *   1 <= P <= 8; non-NULL layouts and counts; counts and displs >= 0; every
+ *   buffer that holds an element non-NULL and aligned to the element size;
+ *   output partitions disjoint; no input byte overlaps an output byte.
+ * Other (naming, naming, op) triples return PURLIN_ERR_UNSUPPORTED.
+ *
+ * The call enqueues one kernel and returns; it never synchronizes.  Inputs
+ * must stay valid and outputs untouched until the stream reaches that point.
+ * A device-side watchdog expiry is reported by purlin_check.
+ */
+PURLIN_API purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *out,
+                                purlin_op op, purlin_dtype dtype, int P,
+                                const int64_t *counts, const int64_t *displs,
+                                hipStream_t stream);
+
+/* Synchronize `stream`, then read and clear the device status word of the
+ * current device: PURLIN_ERR_TIMEOUT if any wait expired since the last
+ * check, PURLIN_ERR_HIP if the synchronization failed, else PURLIN_OK. */
+PURLIN_API purlin_status purlin_check(hipStream_t stream);
+
+/* Replace the policy (NULL restores the defaults).  Environment variables
+ * PURLIN_CHUNK_BYTES, PURLIN_DEPTH, PURLIN_WGS_PER_RANK, PURLIN_ZS (0/1),
+ * PURLIN_SYNC (0/1) and PURLIN_WATCHDOG_NS override the defaults only.
+ * INVALID_ARG for out-of-range fields.  Takes effect on the next call. */
+PURLIN_API purlin_status purlin_set_policy(const purlin_policy *p);
+
+/* The policy in force (defaults, environment, then purlin_set_policy). */
+PURLIN_API purlin_status purlin_get_policy(purlin_policy *p);
+
+/* Test/debug: the plan of a collective without running it (no HIP call).
+ * Writes up to *n_segs segments to segs (which may be NULL) and sets *n_segs
+ * to the number the plan has.  Same argument rules as purlin_collective. */
+PURLIN_API purlin_status purlin_plan_describe(const purlin_layout *in, const purlin_layout *out,
+                                   purlin_op op, purlin_dtype dtype, int P,
+                                   const int64_t *counts, const int64_t *displs,
+                                   purlin_segment *segs, int64_t *n_segs);
+
+/* Measurement: the launch shape of the most recent successful call. */
+PURLIN_API purlin_status purlin_last_launch(purlin_launch_info *info);
+
+/* Measurement: a plain 128-bit streaming copy of `bytes` bytes (both
+ * pointers 16-byte aligned, bytes a multiple of 16), the calibration and
+ * ceiling kernel for HBM counters.  Asynchronous on `stream`. */
+PURLIN_API purlin_status purlin_stream_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+PURLIN_API const char *purlin_strerror(purlin_status s);
+
+/* Free the library-owned workspace (flags, staging ring) of every device.
+ * The next purlin_collective allocates it again. */
+PURLIN_API void purlin_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PURLIN_H_ */

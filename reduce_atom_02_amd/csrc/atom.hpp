@@ -1,0 +1,269 @@
+// Atom: the datapath primitives, copy and reduce, for gfx950.
+//
+// Purlin puts "how bytes move on a given GPU generation" in a layer of its
+// own with two primitives, copy and reduce (abstract; Figure 1 caption).
+// This is that layer for one CDNA4 GPU, where every byte moves through HBM:
+//
+//  * 16-byte global loads and stores (dwordx4), 64 lanes x 16 B = 1 KiB per
+//    wavefront instruction, 4 KiB per 256-thread workgroup pass, with kU
+//    independent units per lane in flight;
+//  * units are aligned to the *destination*, so every store is a full
+//    aligned 16-byte store; a source whose address differs from the
+//    destination's modulo 16 is read as two aligned 16-byte blocks and
+//    shifted into place in registers (v_alignbyte), never by unaligned or
+//    byte-wise memory accesses;
+//  * the reduce is a per-lane fold over the sources in ascending rank, in
+//    fp32 (bf16 widened exactly), with one final round to nearest even for
+//    a bf16 output; there is no cross-lane tree, so the summation order is
+//    the same for every element.
+//
+// Reading an aligned 16-byte block that contains at least one byte of a
+// buffer never touches an unmapped page (pages are 16-byte aligned), so the
+// realigning reads at the ends of a source stay inside mapped memory.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.hpp"
+
+namespace purlin {
+namespace atom {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool kNT>
+__device__ __forceinline__ u32x4 ld16(uint64_t addr) {
+  const u32x4 *p = reinterpret_cast<const u32x4 *>(addr);
+  if constexpr (kNT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool kNT>
+__device__ __forceinline__ void st16(uint64_t addr, u32x4 v) {
+  u32x4 *p = reinterpret_cast<u32x4 *>(addr);
+  if constexpr (kNT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// The 16 bytes that start `sh` bytes into the 32-byte pair (lo, hi);
+// sh in [0, 16) is the same for every lane.
+__device__ __forceinline__ u32x4 funnel(u32x4 lo, u32x4 hi, uint32_t sh) {
+  uint32_t w0 = lo.x, w1 = lo.y, w2 = lo.z, w3 = lo.w;
+  uint32_t w4 = hi.x, w5 = hi.y, w6 = hi.z, w7 = hi.w;
+  if (sh & 8) { w0 = w2; w1 = w3; w2 = w4; w3 = w5; w4 = w6; w5 = w7; }
+  if (sh & 4) { w0 = w1; w1 = w2; w2 = w3; w3 = w4; w4 = w5; }
+  const uint32_t r = sh & 3;  // bytes still to shift inside a dword
+  u32x4 o;
+  o.x = __builtin_amdgcn_alignbyte(w1, w0, r);
+  o.y = __builtin_amdgcn_alignbyte(w2, w1, r);
+  o.z = __builtin_amdgcn_alignbyte(w3, w2, r);
+  o.w = __builtin_amdgcn_alignbyte(w4, w3, r);
+  return o;
+}
+
+// 16 bytes at byte address `a` whose misalignment is sh = a & 15 (uniform).
+template <bool kNT>
+__device__ __forceinline__ u32x4 ld16_shifted(uint64_t a, uint32_t sh) {
+  const uint64_t base = a - sh;
+  const u32x4 lo = ld16<kNT>(base);
+  // With sh == 0 the second block is the first one again (no read past the
+  // unit); otherwise it holds the unit's last bytes.
+  const u32x4 hi = ld16<kNT>(base + (sh ? 16u : 0u));
+  return funnel(lo, hi, sh);
+}
+
+// ---- bf16 <-> fp32 -------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// IEEE round to nearest, ties to even, of fp32 to bf16.  Overflow carries
+// into the exponent and gives inf; a NaN keeps its sign and top payload bits
+// and gets the quiet bit, so it can never round to inf.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rounded;
+}
+
+// ---- element operations (head and tail of a tile, < 16 bytes) -------------
+
+// Copy moves 2-byte elements: every offset of an fp32 or bf16 buffer is a
+// multiple of 2.
+struct CopyOp {
+  static constexpr bool kSum = false;
+  static constexpr int kElem = 2;
+};
+struct SumF32 {
+  static constexpr bool kSum = true;
+  static constexpr int kElem = 4;
+};
+struct SumBf16 {
+  static constexpr bool kSum = true;
+  static constexpr int kElem = 2;
+};
+
+// Sources: byte x of the job lives at a[i] + x.  Entries past n repeat
+// source 0, so reads of them are harmless and need no branch.
+struct Srcs {
+  uint64_t a[kMaxRanks];
+  int n;
+};
+// Destinations: byte x of the job goes to b[d] + x; all congruent mod 16.
+struct Dsts {
+  uint64_t b[kMaxRanks + 1];
+  int n;
+};
+
+template <class Op>
+__device__ __forceinline__ void elements(const Srcs &s, const Dsts &d, int64_t y0, int64_t y1) {
+  const int64_t n = (y1 - y0) / Op::kElem;
+  if (threadIdx.x >= n) return;
+  const int64_t x = y0 + int64_t(threadIdx.x) * Op::kElem;
+  // Loops over sources and destinations are fully unrolled with a guard so
+  // that the pointer arrays stay in registers.
+  if constexpr (!Op::kSum) {
+    const uint16_t v = *reinterpret_cast<const uint16_t *>(s.a[0] + x);
+#pragma unroll
+    for (int k = 0; k < kMaxRanks + 1; ++k)
+      if (k < d.n) *reinterpret_cast<uint16_t *>(d.b[k] + x) = v;
+  } else if constexpr (Op::kElem == 4) {
+    float acc = *reinterpret_cast<const float *>(s.a[0] + x);
+#pragma unroll
+    for (int i = 1; i < kMaxRanks; ++i)
+      if (i < s.n) acc = acc + *reinterpret_cast<const float *>(s.a[i] + x);
+#pragma unroll
+    for (int k = 0; k < kMaxRanks + 1; ++k)
+      if (k < d.n) *reinterpret_cast<float *>(d.b[k] + x) = acc;
+  } else {
+    float acc = bf16_lo(*reinterpret_cast<const uint16_t *>(s.a[0] + x));
+#pragma unroll
+    for (int i = 1; i < kMaxRanks; ++i)
+      if (i < s.n) acc = acc + bf16_lo(*reinterpret_cast<const uint16_t *>(s.a[i] + x));
+    const uint16_t r = uint16_t(bf16_rne(acc));
+#pragma unroll
+    for (int k = 0; k < kMaxRanks + 1; ++k)
+      if (k < d.n) *reinterpret_cast<uint16_t *>(d.b[k] + x) = r;
+  }
+}
+
+// ---- 16-byte unit operations ----------------------------------------------
+
+// Fold of one unit over the sources, in ascending rank, fp32 accumulator.
+__device__ __forceinline__ u32x4 fold_f32(const u32x4 *x, int n) {
+  float a0 = __uint_as_float(x[0].x), a1 = __uint_as_float(x[0].y);
+  float a2 = __uint_as_float(x[0].z), a3 = __uint_as_float(x[0].w);
+#pragma unroll
+  for (int i = 1; i < kMaxRanks; ++i) {
+    if (i < n) {
+      a0 = a0 + __uint_as_float(x[i].x);
+      a1 = a1 + __uint_as_float(x[i].y);
+      a2 = a2 + __uint_as_float(x[i].z);
+      a3 = a3 + __uint_as_float(x[i].w);
+    }
+  }
+  u32x4 o;
+  o.x = __float_as_uint(a0); o.y = __float_as_uint(a1);
+  o.z = __float_as_uint(a2); o.w = __float_as_uint(a3);
+  return o;
+}
+
+__device__ __forceinline__ u32x4 fold_bf16(const u32x4 *x, int n) {
+  float a[8];
+  a[0] = bf16_lo(x[0].x); a[1] = bf16_hi(x[0].x);
+  a[2] = bf16_lo(x[0].y); a[3] = bf16_hi(x[0].y);
+  a[4] = bf16_lo(x[0].z); a[5] = bf16_hi(x[0].z);
+  a[6] = bf16_lo(x[0].w); a[7] = bf16_hi(x[0].w);
+#pragma unroll
+  for (int i = 1; i < kMaxRanks; ++i) {
+    if (i < n) {
+      a[0] = a[0] + bf16_lo(x[i].x); a[1] = a[1] + bf16_hi(x[i].x);
+      a[2] = a[2] + bf16_lo(x[i].y); a[3] = a[3] + bf16_hi(x[i].y);
+      a[4] = a[4] + bf16_lo(x[i].z); a[5] = a[5] + bf16_hi(x[i].z);
+      a[6] = a[6] + bf16_lo(x[i].w); a[7] = a[7] + bf16_hi(x[i].w);
+    }
+  }
+  u32x4 o;
+  o.x = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
+  o.y = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
+  o.z = bf16_rne(a[4]) | (bf16_rne(a[5]) << 16);
+  o.w = bf16_rne(a[6]) | (bf16_rne(a[7]) << 16);
+  return o;
+}
+
+// Body of a tile: units [0, nunits) of 16 bytes starting at job byte xa,
+// where every destination b[d] + xa is 16-byte aligned.  Each lane handles
+// units tid, tid + 256, ...; kU of them are loaded before any is stored.
+// Addresses are a uniform 64-bit base per buffer plus one 32-bit lane offset
+// shared by all buffers, so the loads and stores use the scalar-base form
+// and the sources cost no per-lane address registers.
+template <class Op, int kU, bool kAligned, bool kNTL, bool kNTS>
+__device__ __forceinline__ void body(const uint64_t *sa, int ns, const uint64_t *db, int nd,
+                                     uint32_t nunits, const uint32_t *sh) {
+  constexpr int kS = Op::kSum ? kMaxRanks : 1;
+  const uint32_t tid = threadIdx.x;
+  for (uint32_t u0 = 0; u0 < nunits; u0 += uint32_t(kThreads) * kU) {
+    u32x4 x[kU][kS];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const uint32_t u = u0 + uint32_t(k) * kThreads + tid;
+      if (u < nunits) {
+        const uint64_t o = uint64_t(u * 16u);
+#pragma unroll
+        for (int i = 0; i < kS; ++i) {
+          if constexpr (kAligned) x[k][i] = ld16<kNTL>(sa[i] + o);
+          else x[k][i] = ld16_shifted<kNTL>(sa[i] + o, sh[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const uint32_t u = u0 + uint32_t(k) * kThreads + tid;
+      if (u < nunits) {
+        u32x4 v;
+        if constexpr (!Op::kSum) v = x[k][0];
+        else if constexpr (Op::kElem == 4) v = fold_f32(x[k], ns);
+        else v = fold_bf16(x[k], ns);
+        const uint64_t o = uint64_t(u * 16u);
+#pragma unroll
+        for (int j = 0; j < kMaxRanks + 1; ++j)
+          if (j < nd) st16<kNTS>(db[j] + o, v);
+      }
+    }
+  }
+}
+
+// One tile: job bytes [x0, x1).  x0 is 0 or destination-aligned, x1 is the
+// job's end or destination-aligned; the unaligned head and tail (< 16 bytes
+// each) are done element by element.  A tile spans less than 4 GiB.
+template <class Op, int kU, bool kNTL, bool kNTS>
+__device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1) {
+  if (x1 <= x0) return;
+  const uint64_t b0 = d.b[0];
+  int64_t xa = x0 + int64_t((16u - uint32_t((b0 + uint64_t(x0)) & 15u)) & 15u);
+  if (xa > x1) xa = x1;
+  const uint32_t nunits = uint32_t((x1 - xa) >> 4);
+  const int64_t xb = xa + int64_t(nunits) * 16;
+  if (xa > x0) elements<Op>(s, d, x0, xa);
+  if (x1 > xb) elements<Op>(s, d, xb, x1);
+  if (nunits == 0) return;
+  uint64_t sa[kMaxRanks];
+  uint64_t db[kMaxRanks + 1];
+  uint32_t sh[kMaxRanks];
+  uint32_t any = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxRanks; ++i) {
+    sa[i] = s.a[i] + uint64_t(xa);
+    sh[i] = uint32_t(sa[i] & 15u);
+    any |= sh[i];
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(xa);
+  // The realigning path reads two blocks per unit, so it keeps half as many
+  // units in flight to stay within the same register budget.
+  if (any == 0) body<Op, kU, true, kNTL, kNTS>(sa, s.n, db, d.n, nunits, sh);
+  else body<Op, (kU > 1 ? kU / 2 : 1), false, kNTL, kNTS>(sa, s.n, db, d.n, nunits, sh);
+}
+
+}  // namespace atom
+}  // namespace purlin

@@ -1,0 +1,336 @@
+// The collective kernels: zero-staging (ZS) and staged SNAC pipelines built
+// from the Atom copy / reduce tiles, plus the plain streaming copy used to
+// calibrate HBM counters.
+#include <hip/hip_runtime.h>
+
+#include "atom.hpp"
+#include "kernels.hpp"
+#include "snac.hpp"
+
+namespace purlin {
+
+namespace {
+
+__device__ __forceinline__ void job_srcs(const LaunchPlan &p, const Job &jb, atom::Srcs &s) {
+  if (jb.src < 0) {
+    s.n = p.P;
+#pragma unroll
+    for (int i = 0; i < kMaxRanks; ++i)
+      s.a[i] = uint64_t(p.in[i < p.P ? i : 0]) + uint64_t(jb.src_off);
+  } else {
+    s.n = 1;
+    const uint64_t a = uint64_t(p.in[jb.src]) + uint64_t(jb.src_off);
+#pragma unroll
+    for (int i = 0; i < kMaxRanks; ++i) s.a[i] = a;
+  }
+}
+
+// Job byte range of tile tl (of ntl) of a job of n bytes whose first
+// destination byte is at address b0: tile 0 also takes the bytes before the
+// first 16-byte boundary, so every later tile starts on one.
+__device__ __forceinline__ void tile_bounds(uint64_t b0, int64_t n, int64_t C, int tl, int ntl,
+                                            int64_t &x0, int64_t &x1) {
+  int64_t h = int64_t((16u - uint32_t(b0 & 15u)) & 15u);
+  if (h > n) h = n;
+  x0 = tl == 0 ? 0 : h + int64_t(tl) * C;
+  x1 = tl == ntl - 1 ? n : h + int64_t(tl + 1) * C;
+  if (x0 > n) x0 = n;
+  if (x1 > n) x1 = n;
+}
+
+// ---- zero staging --------------------------------------------------------
+// Purlin-ZS omits staging (Figure 10 caption): every workgroup reads the
+// inputs of all ranks directly and writes each result unit straight from
+// registers to every destination (Figure 6: the reduced chunk of piece k
+// reaches all ranks without a second pass).  Tiles are dealt to a resident
+// grid in grid-stride order; the tile list holds the share of rank 0, then
+// rank 1, and so on.
+template <class Op, int kU, bool kNTL, bool kNTS>
+__global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
+  // A workgroup whose entry wait failed skips its tiles but still counts
+  // itself out, so the next launch's exit check is not poisoned.
+  const bool run = !p.sync || snac::entry(p);
+  int j = 0;
+  for (int t = run ? int(blockIdx.x) : p.total_tiles; t < p.total_tiles; t += gridDim.x) {
+    while (t >= p.tile_begin[j + 1]) ++j;
+    const Job jb = p.jobs[j];
+    atom::Srcs s;
+    job_srcs(p, jb, s);
+    atom::Dsts d;
+    if (jb.dst < 0) {
+      d.n = p.P;
+#pragma unroll
+      for (int k = 0; k < kMaxRanks; ++k)
+        d.b[k] = uint64_t(p.out[k < p.P ? k : 0]) + uint64_t(jb.dst_off);
+    } else {
+      d.n = 1;
+#pragma unroll
+      for (int k = 0; k < kMaxRanks; ++k) d.b[k] = uint64_t(p.out[jb.dst]) + uint64_t(jb.dst_off);
+    }
+    d.b[kMaxRanks] = d.b[0];
+    int64_t x0, x1;
+    tile_bounds(d.b[0], jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
+                p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
+    atom::tile<Op, kU, kNTL, kNTS>(s, d, x0, x1);
+  }
+  if (p.sync) snac::exit_notify(p);
+}
+
+// ---- staged SNAC pipeline --------------------------------------------------
+// Each job runs on `lanes` parallel pipelines; chunk c goes to lane c % lanes.
+// Per lane the job has three kinds of workgroup:
+//   owner    combines chunk c: its own rank's input read directly, every other
+//            source taken from that source's staging ring after its ready
+//            notify, in ascending rank; writes the owner's output and, when
+//            other ranks need the result, stages it in the scatter ring.
+//   stager   (one per source rank other than the owner) copies its rank's
+//            chunk into a ring slot, then notifies (Stage, Notify).
+//   scatter  (one per destination rank other than the owner) waits for the
+//            owner's notify and copies the slot into its rank's output
+//            (Consume), then returns a credit for the slot.
+// A ring has `depth` slots; a producer reuses a slot only after its consumers'
+// credits for the previous round arrived.  No workgroup touches another
+// rank's input or output buffer: cross-rank bytes travel through the rings.
+struct SlotRef {
+  uint64_t data;
+  uint64_t *ready;
+  uint64_t *credit;
+};
+
+__device__ __forceinline__ SlotRef slot_ref(const StagedPlan &sp, int ring, int slot) {
+  const int64_t g = int64_t(ring) * sp.depth + slot;
+  SlotRef r;
+  r.data = uint64_t(sp.ring) + uint64_t(g * sp.slot_stride);
+  r.ready = sp.slot_flags + g * 32;
+  r.credit = sp.slot_flags + g * 32 + 16;
+  return r;
+}
+
+// Base address such that job byte x of chunk [x0, x1) lands at base + x,
+// keeping the destination's alignment modulo 16 inside the slot.
+__device__ __forceinline__ uint64_t slot_base(uint64_t slot, uint64_t b0, int64_t x0) {
+  return slot + ((b0 + uint64_t(x0)) & 15u) - uint64_t(x0);
+}
+
+__device__ __forceinline__ uint64_t tag(uint32_t epoch, uint64_t v) {
+  return (uint64_t(epoch) << 32) | v;
+}
+
+template <class Op, int kU, bool kNTL, bool kNTS>
+__global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
+  const LaunchPlan &p = sp.base;
+  __shared__ int ok;
+  int j = 0;
+  while (j + 1 < p.njobs && int(blockIdx.x) >= sp.sj[j + 1].role_begin) ++j;
+  const StagedJob sj = sp.sj[j];
+  const Job jb = p.jobs[j];
+  const int L = sp.lanes;
+  const int r = int(blockIdx.x) - sj.role_begin;
+  const int lane = r % L;
+  const int kind = r / L;  // 0 owner, 1..n_stage stager, then scatter
+  const int owner = sj.owner;
+  const int rings_per_lane = sj.n_stage + (sj.n_scatter > 0 ? 1 : 0);
+  const int ring0 = sj.ring_begin + lane * rings_per_lane;
+  const int ntl = p.tile_begin[j + 1] - p.tile_begin[j];
+  const int D = sp.depth;
+  const uint32_t e = p.epoch;
+
+  // first destination address of the job (alignment reference for the slots)
+  const uint64_t b0 =
+      uint64_t(p.out[jb.dst < 0 ? 0 : jb.dst]) + uint64_t(jb.dst_off);
+  if (threadIdx.x == 0) ok = 1;
+  __syncthreads();
+
+  if (kind == 0) {
+    // ---------------- owner ----------------
+    int notified = 0;
+    for (int m = 0;; ++m) {
+      const int c = lane + L * m;
+      if (c >= ntl) break;
+      const int slot = m % D;
+      const uint64_t round = uint64_t(m / D);
+      int64_t x0, x1;
+      tile_bounds(b0, jb.nbytes, p.chunk_bytes, c, ntl, x0, x1);
+      // wait for every staged source chunk, and for the scatter slot's credits
+      if (threadIdx.x == 0) {
+        for (int k = 0; k < sj.n_stage && ok; ++k)
+          if (!snac::wait_geq<uint64_t>(slot_ref(sp, ring0 + k, slot).ready, tag(e, round + 1), p))
+            ok = 0;
+        if (sj.n_scatter > 0 && ok) {
+          const SlotRef o = slot_ref(sp, ring0 + sj.n_stage, slot);
+          if (round == 0) {
+            __hip_atomic_store(o.credit, tag(e, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else if (!snac::wait_geq<uint64_t>(o.credit, tag(e, round * sj.n_scatter), p)) {
+            ok = 0;
+          }
+        }
+      }
+      __syncthreads();
+      if (!ok) break;
+      atom::Srcs s;
+      if (jb.src < 0) {
+        s.n = p.P;
+        for (int i = 0; i < kMaxRanks; ++i) {
+          const int src = i < p.P ? i : 0;
+          if (src == owner) {
+            s.a[i] = uint64_t(p.in[owner]) + uint64_t(jb.src_off);
+          } else {
+            const int k = src < owner ? src : src - 1;
+            s.a[i] = slot_base(slot_ref(sp, ring0 + k, slot).data, b0, x0);
+          }
+        }
+      } else {
+        s.n = 1;
+        const uint64_t a = jb.src == owner
+                               ? uint64_t(p.in[owner]) + uint64_t(jb.src_off)
+                               : slot_base(slot_ref(sp, ring0, slot).data, b0, x0);
+        for (int i = 0; i < kMaxRanks; ++i) s.a[i] = a;
+      }
+      // destinations: the owner's output (when it is one) and the scatter slot
+      atom::Dsts d;
+      const bool to_own = jb.dst < 0 || jb.dst == owner;
+      const uint64_t own = uint64_t(p.out[owner]) + uint64_t(jb.dst_off);
+      const uint64_t scat =
+          sj.n_scatter > 0 ? slot_base(slot_ref(sp, ring0 + sj.n_stage, slot).data, b0, x0) : own;
+      d.n = (to_own ? 1 : 0) + (sj.n_scatter > 0 ? 1 : 0);
+      d.b[0] = to_own ? own : scat;
+#pragma unroll
+      for (int k = 1; k < kMaxRanks + 1; ++k) d.b[k] = scat;
+      atom::tile<Op, kU, kNTL, kNTS>(s, d, x0, x1);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        for (int k = 0; k < sj.n_stage; ++k)
+          snac::add_rel(slot_ref(sp, ring0 + k, slot).credit, uint64_t(1));
+        if (sj.n_scatter > 0)
+          snac::store_rel(slot_ref(sp, ring0 + sj.n_stage, slot).ready, tag(e, round + 1));
+      }
+      ++notified;
+    }
+    (void)notified;
+  } else if (kind <= sj.n_stage) {
+    // ---------------- stager ----------------
+    const int k = kind - 1;
+    const int src = jb.src >= 0 ? jb.src : (k < owner ? k : k + 1);
+    const int ring = ring0 + k;
+    for (int m = 0;; ++m) {
+      const int c = lane + L * m;
+      if (c >= ntl) break;
+      const int slot = m % D;
+      const uint64_t round = uint64_t(m / D);
+      const SlotRef o = slot_ref(sp, ring, slot);
+      if (threadIdx.x == 0) {
+        if (round == 0) {
+          __hip_atomic_store(o.credit, tag(e, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (!snac::wait_geq<uint64_t>(o.credit, tag(e, round), p)) {
+          ok = 0;
+        }
+      }
+      __syncthreads();
+      if (!ok) break;
+      int64_t x0, x1;
+      tile_bounds(b0, jb.nbytes, p.chunk_bytes, c, ntl, x0, x1);
+      atom::Srcs s;
+      s.n = 1;
+      const uint64_t a = uint64_t(p.in[src]) + uint64_t(jb.src_off);
+      for (int i = 0; i < kMaxRanks; ++i) s.a[i] = a;
+      atom::Dsts d;
+      d.n = 1;
+#pragma unroll
+      for (int q = 0; q < kMaxRanks + 1; ++q) d.b[q] = slot_base(o.data, b0, x0);
+      atom::tile<atom::CopyOp, kU, kNTL, false>(s, d, x0, x1);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const bool withhold = sp.withhold > 0 && ring == 0 && m + 1 == sp.withhold;
+        if (!withhold) snac::store_rel(o.ready, tag(e, round + 1));
+      }
+    }
+  } else {
+    // ---------------- scatter consumer ----------------
+    const int k = kind - 1 - sj.n_stage;
+    const int dst = k < owner ? k : k + 1;
+    const int ring = ring0 + sj.n_stage;
+    for (int m = 0;; ++m) {
+      const int c = lane + L * m;
+      if (c >= ntl) break;
+      const int slot = m % D;
+      const uint64_t round = uint64_t(m / D);
+      const SlotRef o = slot_ref(sp, ring, slot);
+      if (threadIdx.x == 0 && !snac::wait_geq<uint64_t>(o.ready, tag(e, round + 1), p)) ok = 0;
+      __syncthreads();
+      if (!ok) break;
+      int64_t x0, x1;
+      tile_bounds(b0, jb.nbytes, p.chunk_bytes, c, ntl, x0, x1);
+      atom::Srcs s;
+      s.n = 1;
+      const uint64_t a = slot_base(o.data, b0, x0);
+      for (int i = 0; i < kMaxRanks; ++i) s.a[i] = a;
+      atom::Dsts d;
+      d.n = 1;
+#pragma unroll
+      for (int q = 0; q < kMaxRanks + 1; ++q) d.b[q] = uint64_t(p.out[dst]) + uint64_t(jb.dst_off);
+      atom::tile<atom::CopyOp, kU, false, kNTS>(s, d, x0, x1);
+      __syncthreads();
+      if (threadIdx.x == 0) snac::add_rel(o.credit, uint64_t(1));
+    }
+  }
+}
+
+// ---- calibration copy ------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) stream_copy_kernel(atom::u32x4 *dst,
+                                                                const atom::u32x4 *src,
+                                                                int64_t n16) {
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
+}
+
+template <class Op, int kU, bool kNTL, bool kNTS>
+void *zs_fn() { return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNTL, kNTS>); }
+template <class Op, int kU, bool kNTL, bool kNTS>
+void *st_fn() { return reinterpret_cast<void *>(&staged_kernel<Op, kU, kNTL, kNTS>); }
+
+template <class Op, int kU>
+void *pick(bool staged, int nt) {
+  switch (nt & 3) {
+    case 0: return staged ? st_fn<Op, kU, false, false>() : zs_fn<Op, kU, false, false>();
+    case 1: return staged ? st_fn<Op, kU, true, false>() : zs_fn<Op, kU, true, false>();
+    case 2: return staged ? st_fn<Op, kU, false, true>() : zs_fn<Op, kU, false, true>();
+    default: return staged ? st_fn<Op, kU, true, true>() : zs_fn<Op, kU, true, true>();
+  }
+}
+
+}  // namespace
+
+void *kernel_fn(KernelKind kind, bool staged, int nt) {
+  switch (kind) {
+    case KernelKind::kCopy: return pick<atom::CopyOp, 4>(staged, nt);
+    case KernelKind::kSumF32: return pick<atom::SumF32, 2>(staged, nt);
+    default: return pick<atom::SumBf16, 2>(staged, nt);
+  }
+}
+
+hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, int nt, int grid, hipStream_t stream) {
+  void *args[] = {const_cast<LaunchPlan *>(&p)};
+  return hipLaunchKernel(kernel_fn(kind, false, nt), dim3(grid), dim3(kThreads), args, 0, stream);
+}
+
+hipError_t launch_staged(const StagedPlan &p, KernelKind kind, int nt, hipStream_t stream) {
+  void *args[] = {const_cast<StagedPlan *>(&p)};
+  return hipLaunchKernel(kernel_fn(kind, true, nt), dim3(p.total_roles), dim3(kThreads), args, 0,
+                         stream);
+}
+
+hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                     reinterpret_cast<atom::u32x4 *>(dst),
+                     reinterpret_cast<const atom::u32x4 *>(src), bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t max_resident_per_cu(KernelKind kind, bool staged, int nt, int *blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, kernel_fn(kind, staged, nt),
+                                                      kThreads, 0);
+}
+
+}  // namespace purlin

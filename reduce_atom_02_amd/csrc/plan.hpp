@@ -1,0 +1,82 @@
+// Launch plan shared by the host planner and the device kernels.
+//
+// A collective (Purlin, abstract: input naming, output naming, copy or sum)
+// is derived into at most P*P jobs.  A job produces `nbytes` bytes: byte x of
+// it is op(src_i[x] for each source i in ascending rank) written to every
+// destination.  Sources are one rank or every rank (a sum in rank order);
+// destinations are one rank or every rank (a broadcast).  Each job is cut
+// into chunks ("tiles") of chunk_bytes of destination bytes; chunk
+// boundaries sit on 16-byte boundaries of the destination so that every
+// chunk body is whole 16-byte units.
+#pragma once
+#include <stdint.h>
+
+namespace purlin {
+
+constexpr int kMaxRanks = 8;
+constexpr int kMaxJobs = kMaxRanks * kMaxRanks;
+constexpr int kThreads = 256;           // 4 wavefronts of 64
+constexpr int kFlagStride = 32;          // u32 words between flags (128 bytes)
+
+// Flag block layout (u32 words, each flag on its own 128-byte line).
+enum FlagWord : int {
+  kFlagEntry = 0,                              // kMaxRanks entry epochs
+  kFlagExit = kMaxRanks * kFlagStride,         // 2 exit counters (epoch parity)
+  kFlagStatus = (kMaxRanks + 2) * kFlagStride, // sticky device status bits
+  kFlagAbort = (kMaxRanks + 3) * kFlagStride,  // epoch of an aborted launch
+  kFlagWords = (kMaxRanks + 4) * kFlagStride,
+};
+constexpr uint32_t kStatusTimeout = 1u;
+
+struct Job {
+  int64_t src_off;  // byte offset into in[src] (into every in[i] when src < 0)
+  int64_t dst_off;  // byte offset into out[dst] (into every out[j] when dst < 0)
+  int64_t nbytes;
+  int32_t src;      // source rank, or -1: every rank, summed in ascending order
+  int32_t dst;      // destination rank, or -1: every rank
+};
+
+// Staged (SNAC) role layout: for each job, per lane, one owner workgroup,
+// one stager per source other than the owner, and one scatter consumer per
+// destination other than the owner.
+struct StagedJob {
+  int16_t owner;        // rank that combines the chunk (reducer / root)
+  int16_t n_stage;      // sources other than the owner (0 or P-1)
+  int16_t n_scatter;    // destinations other than the owner (0 or P-1)
+  int16_t pad;
+  int32_t role_begin;   // first workgroup of this job
+  int32_t ring_begin;   // first ring of this job
+};
+
+struct LaunchPlan {
+  const char *in[kMaxRanks];
+  char *out[kMaxRanks];
+  uint32_t *flags;          // kFlagWords u32 words
+  int32_t P;
+  int32_t njobs;
+  int32_t total_tiles;
+  uint32_t epoch;           // increases by one per launch on a device
+  int64_t chunk_bytes;      // bytes per tile (multiple of 4096)
+  uint64_t watchdog_ticks;  // bound of every spin wait, in wall-clock ticks
+  uint32_t exit_expect;     // exit-counter value of the previous launch (sync)
+  int32_t sync;             // 1: entry/exit notify flags on
+  int32_t tile_begin[kMaxJobs + 1];
+  Job jobs[kMaxJobs];
+};
+
+struct StagedPlan {
+  LaunchPlan base;
+  char *ring;               // staging rings
+  uint64_t *slot_flags;     // per slot: ready at [2*s*8], credit at [2*s*8 + 8] (u64)
+  int64_t slot_stride;      // bytes per slot (chunk_bytes + 256)
+  int32_t depth;            // slots per ring
+  int32_t lanes;            // parallel rings per (job, source)
+  int32_t total_roles;      // grid size
+  int32_t withhold;         // test only: > 0 withholds that ready notify of ring 0
+  StagedJob sj[kMaxJobs];
+};
+
+static_assert(sizeof(LaunchPlan) <= 3072, "launch plan must fit in kernel arguments");
+static_assert(sizeof(StagedPlan) <= 3840, "staged plan must fit in kernel arguments");
+
+}  // namespace purlin

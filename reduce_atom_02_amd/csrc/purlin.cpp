@@ -1,0 +1,419 @@
+// C ABI of the collective library: argument checks, policy, workspace and
+// launch.  Semantics are documented in include/purlin.h.
+#include "../../include/purlin.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kernels.hpp"
+#include "planner.hpp"
+
+namespace purlin {
+namespace {
+
+constexpr int64_t kDefaultWatchdogNs = 2000000000;  // 2 s
+constexpr int kMaxLanes = 32;
+
+struct DeviceState {
+  bool ready = false;
+  int cus = 0;
+  uint64_t wall_khz = 0;
+  uint32_t *flags = nullptr;
+  char *ring = nullptr;
+  int64_t ring_bytes = 0;
+  uint64_t *slot_flags = nullptr;
+  int64_t slot_flag_bytes = 0;
+  uint32_t epoch = 0;
+  uint32_t exit_total[2] = {0, 0};
+  int occ[3][2][4] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
+};
+
+std::vector<DeviceState> &devices() {
+  static std::vector<DeviceState> d;
+  return d;
+}
+
+purlin_policy &user_policy() {
+  static purlin_policy p{};
+  return p;
+}
+bool g_user_policy_set = false;
+purlin_launch_info g_last{};
+bool g_have_last = false;
+
+int64_t env_i64(const char *name, int64_t dflt) {
+  const char *v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  char *end = nullptr;
+  long long x = std::strtoll(v, &end, 0);
+  return (end && *end == 0) ? int64_t(x) : dflt;
+}
+
+bool policy_valid(const purlin_policy &p) {
+  if (p.chunk_bytes < 0 || (p.chunk_bytes % 4096) != 0 || p.chunk_bytes > (int64_t(64) << 20))
+    return false;
+  if (p.depth < 0 || p.depth > 8) return false;
+  if (p.wgs_per_rank < 0 || p.wgs_per_rank > 4096) return false;
+  if (p.zero_staging < 0 || p.zero_staging > 2) return false;
+  if (p.sync < 0 || p.sync > 2) return false;
+  if (p.watchdog_ns < 0 || p.test_withhold < 0) return false;
+  return true;
+}
+
+// Defaults, then environment overrides, then purlin_set_policy fields.
+purlin_policy effective_policy() {
+  purlin_policy p{};
+  p.chunk_bytes = env_i64("PURLIN_CHUNK_BYTES", 0);
+  p.depth = int32_t(env_i64("PURLIN_DEPTH", 0));
+  p.wgs_per_rank = int32_t(env_i64("PURLIN_WGS_PER_RANK", 0));
+  const int64_t zs = env_i64("PURLIN_ZS", -1);
+  p.zero_staging = zs < 0 ? PURLIN_STAGING_AUTO : (zs ? PURLIN_STAGING_ZS : PURLIN_STAGING_STAGED);
+  const int64_t sy = env_i64("PURLIN_SYNC", -1);
+  p.sync = sy < 0 ? 0 : (sy ? 1 : 2);
+  p.watchdog_ns = env_i64("PURLIN_WATCHDOG_NS", 0);
+  if (!policy_valid(p)) p = purlin_policy{};
+  if (g_user_policy_set) {
+    const purlin_policy &u = user_policy();
+    if (u.chunk_bytes) p.chunk_bytes = u.chunk_bytes;
+    if (u.depth) p.depth = u.depth;
+    if (u.wgs_per_rank) p.wgs_per_rank = u.wgs_per_rank;
+    if (u.zero_staging) p.zero_staging = u.zero_staging;
+    if (u.sync) p.sync = u.sync;
+    if (u.watchdog_ns) p.watchdog_ns = u.watchdog_ns;
+    p.test_withhold = u.test_withhold;
+  }
+  return p;
+}
+
+int nt_bits() { return int(env_i64("PURLIN_NT", 0)) & 3; }
+
+purlin_status device_state(DeviceState **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PURLIN_ERR_HIP;
+  auto &all = devices();
+  if (int(all.size()) <= dev) all.resize(dev + 1);
+  DeviceState &s = all[dev];
+  if (!s.ready) {
+    int cus = 0, khz = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+      return PURLIN_ERR_HIP;
+    s.cus = cus;
+    s.wall_khz = uint64_t(khz > 0 ? khz : 100000);
+    s.ready = true;
+  }
+  if (!s.flags) {
+    void *f = nullptr;
+    if (hipMalloc(&f, kFlagWords * sizeof(uint32_t)) != hipSuccess) return PURLIN_ERR_NO_MEMORY;
+    if (hipMemset(f, 0, kFlagWords * sizeof(uint32_t)) != hipSuccess) {
+      (void)hipFree(f);
+      return PURLIN_ERR_HIP;
+    }
+    s.flags = static_cast<uint32_t *>(f);
+    s.exit_total[0] = s.exit_total[1] = 0;
+  }
+  *out = &s;
+  return PURLIN_OK;
+}
+
+int occupancy(DeviceState &s, KernelKind kind, bool staged, int nt) {
+  int &o = s.occ[int(kind)][staged ? 1 : 0][nt & 3];
+  if (o == 0) {
+    int b = 0;
+    if (max_resident_per_cu(kind, staged, nt, &b) != hipSuccess || b < 1) b = 1;
+    o = b;
+  }
+  return o;
+}
+
+purlin_status ensure_staging(DeviceState &s, int64_t ring_bytes, int64_t flag_bytes) {
+  if (ring_bytes <= s.ring_bytes && flag_bytes <= s.slot_flag_bytes) return PURLIN_OK;
+  // A previous launch may still read the old ring: finish all work first.
+  if (hipDeviceSynchronize() != hipSuccess) return PURLIN_ERR_HIP;
+  if (ring_bytes > s.ring_bytes) {
+    if (s.ring) (void)hipFree(s.ring);
+    s.ring = nullptr;
+    s.ring_bytes = 0;
+    void *r = nullptr;
+    if (hipMalloc(&r, size_t(ring_bytes)) != hipSuccess) return PURLIN_ERR_NO_MEMORY;
+    s.ring = static_cast<char *>(r);
+    s.ring_bytes = ring_bytes;
+  }
+  if (flag_bytes > s.slot_flag_bytes) {
+    if (s.slot_flags) (void)hipFree(s.slot_flags);
+    s.slot_flags = nullptr;
+    s.slot_flag_bytes = 0;
+    void *f = nullptr;
+    if (hipMalloc(&f, size_t(flag_bytes)) != hipSuccess) return PURLIN_ERR_NO_MEMORY;
+    if (hipMemset(f, 0, size_t(flag_bytes)) != hipSuccess) {
+      (void)hipFree(f);
+      return PURLIN_ERR_HIP;
+    }
+    s.slot_flags = static_cast<uint64_t *>(f);
+    s.slot_flag_bytes = flag_bytes;
+  }
+  return PURLIN_OK;
+}
+
+KernelKind kind_of(purlin_op op, purlin_dtype dtype) {
+  if (op == PURLIN_OP_COPY) return KernelKind::kCopy;
+  return dtype == PURLIN_F32 ? KernelKind::kSumF32 : KernelKind::kSumBf16;
+}
+
+// Chunk size when the policy leaves it open: small chunks while the message
+// cannot fill the resident grid, growing so that large messages get about
+// 16 chunks per resident workgroup, never above 64 KiB.
+int64_t auto_chunk(int64_t out_bytes, int capacity) {
+  int64_t c = 4096;
+  while (c < (int64_t(64) << 10) && out_bytes / c > int64_t(capacity) * 16) c *= 2;
+  return c;
+}
+
+void fill_tiles(LaunchPlan &lp, const std::vector<Job> &jobs, int64_t chunk) {
+  lp.njobs = int32_t(jobs.size());
+  int64_t t = 0;
+  for (size_t k = 0; k < jobs.size(); ++k) {
+    lp.jobs[k] = jobs[k];
+    lp.tile_begin[k] = int32_t(t);
+    t += std::max<int64_t>(1, (jobs[k].nbytes + chunk - 1) / chunk);
+  }
+  lp.tile_begin[jobs.size()] = int32_t(t);
+  for (size_t k = jobs.size() + 1; k <= size_t(kMaxJobs); ++k) lp.tile_begin[k] = int32_t(t);
+  lp.total_tiles = int32_t(t);
+}
+
+}  // namespace
+}  // namespace purlin
+
+using namespace purlin;
+
+extern "C" {
+
+const char *purlin_strerror(purlin_status s) {
+  switch (s) {
+    case PURLIN_OK: return "ok";
+    case PURLIN_ERR_INVALID_ARG: return "invalid argument";
+    case PURLIN_ERR_UNSUPPORTED: return "unsupported collective";
+    case PURLIN_ERR_NO_MEMORY: return "out of device memory";
+    case PURLIN_ERR_HIP: return "HIP error";
+    case PURLIN_ERR_TIMEOUT: return "device wait timed out";
+  }
+  return "unknown status";
+}
+
+purlin_status purlin_set_policy(const purlin_policy *p) {
+  if (!p) {
+    g_user_policy_set = false;
+    user_policy() = purlin_policy{};
+    return PURLIN_OK;
+  }
+  if (!policy_valid(*p)) return PURLIN_ERR_INVALID_ARG;
+  user_policy() = *p;
+  g_user_policy_set = true;
+  return PURLIN_OK;
+}
+
+purlin_status purlin_get_policy(purlin_policy *p) {
+  if (!p) return PURLIN_ERR_INVALID_ARG;
+  *p = effective_policy();
+  return PURLIN_OK;
+}
+
+purlin_status purlin_plan_describe(const purlin_layout *in, const purlin_layout *out,
+                                   purlin_op op, purlin_dtype dtype, int P,
+                                   const int64_t *counts, const int64_t *displs,
+                                   purlin_segment *segs, int64_t *n_segs) {
+  if (!in || !out || !in->bufs || !out->bufs || !n_segs) return PURLIN_ERR_INVALID_ARG;
+  const Derived *d = nullptr;
+  purlin_status s = derive_cached(in->naming, out->naming, op, dtype, P, counts, displs, &d);
+  if (s != PURLIN_OK) return s;
+  s = check_pointers(*d, in->bufs, out->bufs);
+  if (s != PURLIN_OK) return s;
+  const int64_t n = int64_t(d->segs.size());
+  if (segs) {
+    const int64_t m = std::min<int64_t>(*n_segs, n);
+    for (int64_t k = 0; k < m; ++k) segs[k] = d->segs[size_t(k)];
+  }
+  *n_segs = n;
+  return PURLIN_OK;
+}
+
+purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *out,
+                                purlin_op op, purlin_dtype dtype, int P,
+                                const int64_t *counts, const int64_t *displs,
+                                hipStream_t stream) {
+  if (!in || !out || !in->bufs || !out->bufs) return PURLIN_ERR_INVALID_ARG;
+  const Derived *d = nullptr;
+  purlin_status st = derive_cached(in->naming, out->naming, op, dtype, P, counts, displs, &d);
+  if (st != PURLIN_OK) return st;
+  st = check_pointers(*d, in->bufs, out->bufs);
+  if (st != PURLIN_OK) return st;
+  if (d->jobs.empty()) return PURLIN_OK;  // every partition is empty
+
+  DeviceState *ds = nullptr;
+  st = device_state(&ds);
+  if (st != PURLIN_OK) return st;
+  const purlin_policy pol = effective_policy();
+  const int nt = nt_bits();
+  const KernelKind kind = kind_of(op, dtype);
+
+  std::vector<Job> jobs;
+  std::vector<int> owners;
+  launch_jobs(*d, reinterpret_cast<char *const *>(out->bufs), &jobs, &owners);
+
+  const bool staged = pol.zero_staging == PURLIN_STAGING_STAGED;
+  const int capacity = ds->cus * occupancy(*ds, kind, staged, nt);
+  int64_t out_bytes = 0;
+  for (const Job &jb : jobs) out_bytes += jb.nbytes * (jb.dst < 0 ? P : 1);
+
+  if (++ds->epoch == 0) ds->epoch = 1;  // epoch 0 would match freshly cleared flags
+  const int64_t wd_ns = pol.watchdog_ns ? pol.watchdog_ns : kDefaultWatchdogNs;
+
+  LaunchPlan lp{};
+  for (int r = 0; r < kMaxRanks; ++r) {
+    lp.in[r] = r < P ? static_cast<const char *>(in->bufs[r]) : nullptr;
+    lp.out[r] = r < P ? static_cast<char *>(out->bufs[r]) : nullptr;
+  }
+  lp.flags = ds->flags;
+  lp.P = P;
+  lp.epoch = ds->epoch;
+  lp.watchdog_ticks = uint64_t(wd_ns) * ds->wall_khz / 1000000u + 1;
+
+  purlin_launch_info info{};
+  info.threads = kThreads;
+  info.bytes_min = d->bytes_min;
+  info.njobs = int32_t(jobs.size());
+
+  hipError_t err;
+  if (!staged) {
+    const int64_t chunk = pol.chunk_bytes ? pol.chunk_bytes : auto_chunk(out_bytes, capacity);
+    lp.chunk_bytes = chunk;
+    fill_tiles(lp, jobs, chunk);
+    int grid = std::min<int64_t>(lp.total_tiles, capacity);
+    if (pol.wgs_per_rank) grid = std::min<int64_t>(grid, int64_t(P) * pol.wgs_per_rank);
+    grid = std::max(grid, 1);
+    lp.sync = pol.sync == 2 ? 0 : 1;
+    lp.exit_expect = ds->exit_total[(ds->epoch - 1u) & 1u];
+    err = launch_zs(lp, kind, nt, grid, stream);
+    if (err == hipSuccess && lp.sync) ds->exit_total[ds->epoch & 1u] += uint32_t(grid);
+    info.grid = grid;
+    info.zero_staging = 1;
+    info.chunk_bytes = chunk;
+    info.tiles = lp.total_tiles;
+    info.sync = lp.sync;
+  } else {
+    StagedPlan sp{};
+    sp.base = lp;
+    const int64_t chunk = pol.chunk_bytes ? pol.chunk_bytes : (int64_t(64) << 10);
+    sp.base.chunk_bytes = chunk;
+    fill_tiles(sp.base, jobs, chunk);
+    sp.depth = pol.depth ? pol.depth : 4;
+    sp.slot_stride = chunk + 256;
+    sp.withhold = pol.test_withhold;
+    // roles and rings per lane
+    int roles_per_lane = 0, max_tiles = 1;
+    std::vector<StagedJob> sj(jobs.size());
+    for (size_t k = 0; k < jobs.size(); ++k) {
+      const Job &jb = jobs[k];
+      const int owner = jb.dst >= 0 ? jb.dst : (jb.src >= 0 ? jb.src : owners[k]);
+      sj[k].owner = int16_t(owner);
+      sj[k].n_stage = int16_t(jb.src < 0 ? P - 1 : (jb.src != owner ? 1 : 0));
+      sj[k].n_scatter = int16_t(jb.dst < 0 ? P - 1 : 0);
+      roles_per_lane += 1 + sj[k].n_stage + sj[k].n_scatter;
+      max_tiles = std::max(max_tiles, sp.base.tile_begin[k + 1] - sp.base.tile_begin[k]);
+    }
+    int lanes = pol.wgs_per_rank ? pol.wgs_per_rank : capacity / std::max(1, roles_per_lane);
+    lanes = std::max(1, std::min({lanes, kMaxLanes, max_tiles}));
+    while (lanes > 1 && lanes * roles_per_lane > capacity) --lanes;
+    if (roles_per_lane > capacity) return PURLIN_ERR_UNSUPPORTED;  // cannot be co-resident
+    sp.lanes = lanes;
+    int role = 0, ring = 0;
+    for (size_t k = 0; k < jobs.size(); ++k) {
+      sj[k].role_begin = role;
+      sj[k].ring_begin = ring;
+      role += (1 + sj[k].n_stage + sj[k].n_scatter) * lanes;
+      ring += (sj[k].n_stage + (sj[k].n_scatter > 0 ? 1 : 0)) * lanes;
+      sp.sj[k] = sj[k];
+    }
+    for (size_t k = jobs.size(); k < size_t(kMaxJobs); ++k) sp.sj[k].role_begin = role;
+    sp.total_roles = role;
+    const int64_t ring_bytes = std::max<int64_t>(1, int64_t(ring) * sp.depth * sp.slot_stride);
+    const int64_t flag_bytes = std::max<int64_t>(256, int64_t(ring) * sp.depth * 256);
+    st = ensure_staging(*ds, ring_bytes, flag_bytes);
+    if (st != PURLIN_OK) return st;
+    sp.ring = ds->ring;
+    sp.slot_flags = ds->slot_flags;
+    sp.base.sync = 0;
+    err = launch_staged(sp, kind, nt, stream);
+    info.grid = sp.total_roles;
+    info.zero_staging = 0;
+    info.depth = sp.depth;
+    info.chunk_bytes = chunk;
+    info.tiles = sp.base.total_tiles;
+    info.sync = 0;
+  }
+  if (err != hipSuccess) return PURLIN_ERR_HIP;
+  g_last = info;
+  g_have_last = true;
+  return PURLIN_OK;
+}
+
+purlin_status purlin_check(hipStream_t stream) {
+  if (hipStreamSynchronize(stream) != hipSuccess) return PURLIN_ERR_HIP;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PURLIN_ERR_HIP;
+  auto &all = devices();
+  if (int(all.size()) <= dev || !all[dev].flags) return PURLIN_OK;
+  uint32_t status = 0;
+  uint32_t *word = all[dev].flags + kFlagStatus;
+  if (hipMemcpy(&status, word, sizeof(status), hipMemcpyDeviceToHost) != hipSuccess)
+    return PURLIN_ERR_HIP;
+  if (status == 0) return PURLIN_OK;
+  if (hipMemset(word, 0, sizeof(uint32_t)) != hipSuccess) return PURLIN_ERR_HIP;
+  return (status & kStatusTimeout) ? PURLIN_ERR_TIMEOUT : PURLIN_ERR_HIP;
+}
+
+purlin_status purlin_last_launch(purlin_launch_info *info) {
+  if (!info) return PURLIN_ERR_INVALID_ARG;
+  if (!g_have_last) return PURLIN_ERR_INVALID_ARG;
+  *info = g_last;
+  return PURLIN_OK;
+}
+
+purlin_status purlin_stream_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream) {
+  if (!dst || !src || bytes < 0 || (bytes & 15) || (uintptr_t(dst) & 15) || (uintptr_t(src) & 15))
+    return PURLIN_ERR_INVALID_ARG;
+  if (bytes == 0) return PURLIN_OK;
+  DeviceState *ds = nullptr;
+  purlin_status st = device_state(&ds);
+  if (st != PURLIN_OK) return st;
+  const int grid = ds->cus * 8;
+  return launch_stream_copy(dst, src, bytes, grid, stream) == hipSuccess ? PURLIN_OK
+                                                                           : PURLIN_ERR_HIP;
+}
+
+void purlin_release(void) {
+  auto &all = devices();
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (size_t dev = 0; dev < all.size(); ++dev) {
+    DeviceState &s = all[dev];
+    if (!s.flags && !s.ring && !s.slot_flags) continue;
+    if (hipSetDevice(int(dev)) != hipSuccess) continue;
+    (void)hipDeviceSynchronize();
+    if (s.flags) (void)hipFree(s.flags);
+    if (s.ring) (void)hipFree(s.ring);
+    if (s.slot_flags) (void)hipFree(s.slot_flags);
+    s.flags = nullptr;
+    s.ring = nullptr;
+    s.slot_flags = nullptr;
+    s.ring_bytes = s.slot_flag_bytes = 0;
+  }
+  if (have_cur) (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// SNAC device protocol: notify flags, credits and the watchdog.
+//
+// Purlin's middle layer is Stage, Notify, And Consume (abstract): a producer
+// stages a chunk, notifies, and a consumer consumes it.  Here every flag is
+// a word in HBM written with an agent-scope release store (or add) and read
+// with agent-scope acquire loads, so a chunk written by one workgroup is
+// visible to a workgroup on another XCD once the flag is seen.  Flag values
+// carry the launch epoch in their high bits, so a flag is never reset
+// between launches; a consumer waits for the exact value it expects.
+//
+// Every wait is bounded by a wall-clock watchdog.  On expiry the workgroup
+// sets the device status word and the launch's abort epoch; every other
+// wait of the same launch then gives up at once, so each wavefront exits
+// and the host reads PURLIN_ERR_TIMEOUT from purlin_check.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.hpp"
+
+namespace purlin {
+namespace snac {
+
+__device__ __forceinline__ uint32_t load_acq(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_acq(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_rel(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_rel(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void add_rel(uint32_t *p, uint32_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void add_rel(uint64_t *p, uint64_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool aborted(const LaunchPlan &p) {
+  return __hip_atomic_load(&p.flags[kFlagAbort], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+         p.epoch;
+}
+
+__device__ __forceinline__ void raise_timeout(const LaunchPlan &p) {
+  __hip_atomic_fetch_or(&p.flags[kFlagStatus], kStatusTimeout, __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&p.flags[kFlagAbort], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin until *f - target >= 0 (wrap-aware); false if the watchdog expired or
+// the launch was aborted.
+template <class W>
+__device__ bool wait_geq(const W *f, W target, const LaunchPlan &p) {
+  using S = typename std::conditional<sizeof(W) == 8, int64_t, int32_t>::type;
+  const uint64_t t0 = wall_clock64();
+  while (true) {
+    if (S(load_acq(f) - target) >= 0) return true;
+    if (aborted(p)) return false;
+    if (wall_clock64() - t0 > p.watchdog_ticks) {
+      raise_timeout(p);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Entry notify: rank r may let peers read its input and write its output
+// once every reader of the previous collective is done (exit counter), and
+// announces that with entry[r] = epoch.  Every workgroup then waits for the
+// entry flag of every rank before its first access.  Workgroup b announces
+// ranks b, b + grid, ...; all workgroups are resident at once (the grid
+// never exceeds what the device holds), so the announcements always happen.
+__device__ bool entry(const LaunchPlan &p) {
+  __shared__ int ok;
+  if (threadIdx.x == 0) ok = 1;
+  __syncthreads();
+  uint32_t *f = p.flags;
+  if (threadIdx.x == 0 && int(blockIdx.x) < p.P) {
+    const uint32_t prev = (p.epoch - 1u) & 1u;
+    if (!wait_geq<uint32_t>(&f[kFlagExit + prev * kFlagStride], p.exit_expect, p)) ok = 0;
+    for (int r = blockIdx.x; r < p.P; r += gridDim.x) store_rel(&f[kFlagEntry + r * kFlagStride], p.epoch);
+  }
+  __syncthreads();
+  if (int(threadIdx.x) < p.P && ok) {
+    if (!wait_geq<uint32_t>(&f[kFlagEntry + threadIdx.x * kFlagStride], p.epoch, p)) ok = 0;
+  }
+  __syncthreads();
+  return ok != 0;
+}
+
+// Exit notify: this workgroup has finished reading every input and writing
+// every output of this launch.
+__device__ void exit_notify(const LaunchPlan &p) {
+  __syncthreads();
+  if (threadIdx.x == 0) add_rel(&p.flags[kFlagExit + (p.epoch & 1u) * kFlagStride], 1u);
+}
+
+}  // namespace snac
+}  // namespace purlin

@@ -1,0 +1,280 @@
+"""Python binding of libpurlin: argument marshalling only.
+
+Every step of a collective runs in the HIP library; this module turns
+Python values (torch tensors or raw device addresses) into the C ABI's
+arguments and status codes into exceptions.  The library is loaded at import
+time and the import fails when it has not been built (``python -m
+reduce_atom_02_amd.build``): there is no other implementation to fall back to.
+
+Names follow include/purlin.h: namings ``whole``, ``by_rank``, ``by_index``,
+``by_rank_index``, ``by_index_rank``; ops ``copy`` and ``sum``; dtypes
+``f32`` and ``bf16``.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "LIB_PATH", "NAMINGS", "OPS", "DTYPES", "STATUS", "PurlinError", "collective",
+    "all_reduce", "reduce_scatter", "all_gather", "all_to_all", "check",
+    "set_policy", "get_policy", "plan_describe", "last_launch", "stream_copy",
+    "release", "exported_symbols",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpurlin.so")
+
+NAMINGS = {"whole": 0, "by_rank": 1, "by_index": 2, "by_rank_index": 3, "by_index_rank": 4}
+OPS = {"copy": 0, "sum": 1}
+DTYPES = {"f32": 0, "bf16": 1}
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "NO_MEMORY", 4: "HIP", 5: "TIMEOUT"}
+STAGING = {"auto": 0, "zs": 1, "staged": 2}
+
+COLLECTIVES = {
+    "allreduce": ("whole", "whole", "sum"),
+    "reducescatter": ("by_index", "by_rank", "sum"),
+    "allgather": ("by_rank", "by_index", "copy"),
+    "alltoall": ("by_rank_index", "by_index_rank", "copy"),
+}
+
+
+class PurlinError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = STATUS.get(status, str(status))
+        super().__init__("%s: %s (%s)" % (what, self.status, _lib.purlin_strerror(status).decode()))
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("naming", ctypes.c_int), ("bufs", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class Policy(ctypes.Structure):
+    _fields_ = [("chunk_bytes", ctypes.c_int64), ("depth", ctypes.c_int32),
+                ("wgs_per_rank", ctypes.c_int32), ("zero_staging", ctypes.c_int32),
+                ("sync", ctypes.c_int32), ("watchdog_ns", ctypes.c_int64),
+                ("test_withhold", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("src_rank", ctypes.c_int32), ("dst_rank", ctypes.c_int32),
+                ("src_off", ctypes.c_int64), ("dst_off", ctypes.c_int64),
+                ("len", ctypes.c_int64)]
+
+
+class LaunchInfo(ctypes.Structure):
+    _fields_ = [("grid", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("zero_staging", ctypes.c_int32), ("depth", ctypes.c_int32),
+                ("chunk_bytes", ctypes.c_int64), ("tiles", ctypes.c_int64),
+                ("bytes_min", ctypes.c_int64), ("njobs", ctypes.c_int32),
+                ("sync", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libpurlin.so is not built (%s); run: python -m reduce_atom_02_amd.build"
+                          % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P_LAYOUT = ctypes.POINTER(Layout)
+    P_I64 = ctypes.POINTER(ctypes.c_int64)
+    lib.purlin_collective.argtypes = [P_LAYOUT, P_LAYOUT, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      P_I64, P_I64, ctypes.c_void_p]
+    lib.purlin_collective.restype = ctypes.c_int
+    lib.purlin_check.argtypes = [ctypes.c_void_p]
+    lib.purlin_check.restype = ctypes.c_int
+    lib.purlin_set_policy.argtypes = [ctypes.POINTER(Policy)]
+    lib.purlin_set_policy.restype = ctypes.c_int
+    lib.purlin_get_policy.argtypes = [ctypes.POINTER(Policy)]
+    lib.purlin_get_policy.restype = ctypes.c_int
+    lib.purlin_plan_describe.argtypes = [P_LAYOUT, P_LAYOUT, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, P_I64, P_I64, ctypes.POINTER(Segment),
+                                         P_I64]
+    lib.purlin_plan_describe.restype = ctypes.c_int
+    lib.purlin_last_launch.argtypes = [ctypes.POINTER(LaunchInfo)]
+    lib.purlin_last_launch.restype = ctypes.c_int
+    lib.purlin_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_void_p]
+    lib.purlin_stream_copy.restype = ctypes.c_int
+    lib.purlin_strerror.argtypes = [ctypes.c_int]
+    lib.purlin_strerror.restype = ctypes.c_char_p
+    lib.purlin_release.argtypes = []
+    lib.purlin_release.restype = None
+    return lib
+
+
+_lib = _load()
+
+
+def exported_symbols():
+    """Names of the C ABI functions the loaded library resolves."""
+    names = ["purlin_collective", "purlin_check", "purlin_set_policy", "purlin_get_policy",
+             "purlin_plan_describe", "purlin_last_launch", "purlin_stream_copy",
+             "purlin_strerror", "purlin_release"]
+    return [n for n in names if hasattr(_lib, n)]
+
+
+def _raise(status, what):
+    if status != 0:
+        raise PurlinError(status, what)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()          # torch tensor
+
+
+def _dtype_of(bufs, dtype):
+    if dtype is not None:
+        return dtype
+    for b in bufs:
+        if b is not None and not isinstance(b, int):
+            name = str(b.dtype)
+            if name == "torch.float32":
+                return "f32"
+            if name == "torch.bfloat16":
+                return "bf16"
+            raise ValueError("unsupported tensor dtype %s" % name)
+    raise ValueError("dtype must be given for raw pointers")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _layout(naming, bufs):
+    arr = (ctypes.c_void_p * len(bufs))(*[_ptr(b) for b in bufs])
+    return Layout(NAMINGS[naming], arr), arr
+
+
+def _i64(values):
+    if values is None:
+        return None
+    vals = [int(v) for v in values]
+    return (ctypes.c_int64 * max(1, len(vals)))(*vals)
+
+
+def collective(ins, outs, in_naming, out_naming, op, counts, displs=None, dtype=None,
+               stream=None):
+    """Enqueue one collective on ``stream`` (torch's current stream by default).
+
+    ins, outs: P torch tensors or device addresses, one per rank.
+    counts: one element count per name (see include/purlin.h).
+    displs: None (packed) or input offsets then output offsets, by name.
+    """
+    P = len(ins)
+    if len(outs) != P:
+        raise ValueError("need as many output buffers as input buffers")
+    dt = _dtype_of(list(ins) + list(outs), dtype)
+    lin, keep_in = _layout(in_naming, ins)
+    lout, keep_out = _layout(out_naming, outs)
+    c = _i64(counts)
+    d = _i64(displs)
+    status = _lib.purlin_collective(ctypes.byref(lin), ctypes.byref(lout), OPS[op], DTYPES[dt], P,
+                                    c, d, ctypes.c_void_p(_stream(stream)))
+    _raise(status, "purlin_collective")
+
+
+def _numel(t):
+    return t if isinstance(t, int) else t.numel()
+
+
+def all_reduce(ins, outs, count=None, **kw):
+    n = count if count is not None else _numel(ins[0])
+    collective(ins, outs, "whole", "whole", "sum", [n], **kw)
+
+
+def reduce_scatter(ins, outs, counts=None, **kw):
+    if counts is None:
+        counts = [_numel(o) for o in outs]
+    collective(ins, outs, "by_index", "by_rank", "sum", counts, **kw)
+
+
+def all_gather(ins, outs, counts=None, **kw):
+    if counts is None:
+        counts = [_numel(i) for i in ins]
+    collective(ins, outs, "by_rank", "by_index", "copy", counts, **kw)
+
+
+def all_to_all(ins, outs, counts=None, **kw):
+    """counts: P*P (row-major [src * P + dst]), or P (every source sends c_j to rank j)."""
+    P = len(ins)
+    if counts is None:
+        n = _numel(ins[0])
+        if n % P:
+            raise ValueError("equal partitions need a size divisible by P")
+        counts = [n // P] * (P * P)
+    elif len(counts) == P:
+        counts = [counts[j] for _ in range(P) for j in range(P)]
+    collective(ins, outs, "by_rank_index", "by_index_rank", "copy", counts, **kw)
+
+
+def check(stream=None):
+    """Synchronize the stream; raise PurlinError on a device-side timeout."""
+    _raise(_lib.purlin_check(ctypes.c_void_p(_stream(stream))), "purlin_check")
+
+
+def set_policy(chunk_bytes=0, depth=0, wgs_per_rank=0, zero_staging="auto", sync=None,
+               watchdog_ns=0, test_withhold=0, reset=False):
+    if reset:
+        _raise(_lib.purlin_set_policy(None), "purlin_set_policy")
+        return
+    p = Policy(chunk_bytes, depth, wgs_per_rank, STAGING[zero_staging],
+               0 if sync is None else (1 if sync else 2), watchdog_ns, test_withhold, 0)
+    _raise(_lib.purlin_set_policy(ctypes.byref(p)), "purlin_set_policy")
+
+
+def get_policy():
+    p = Policy()
+    _raise(_lib.purlin_get_policy(ctypes.byref(p)), "purlin_get_policy")
+    return {f: getattr(p, f) for f, _ in Policy._fields_}
+
+
+def plan_describe(in_naming, out_naming, op, dtype, counts, in_bufs, out_bufs, displs=None):
+    """Segments (src_rank, dst_rank, src_off, dst_off, len) of a plan; runs no HIP call."""
+    P = len(in_bufs)
+    lin, keep_in = _layout(in_naming, in_bufs)
+    lout, keep_out = _layout(out_naming, out_bufs)
+    c = _i64(counts)
+    d = _i64(displs)
+    n = ctypes.c_int64(0)
+    _raise(_lib.purlin_plan_describe(ctypes.byref(lin), ctypes.byref(lout), OPS[op], DTYPES[dtype],
+                                     P, c, d, None, ctypes.byref(n)), "purlin_plan_describe")
+    segs = (Segment * max(1, n.value))()
+    _raise(_lib.purlin_plan_describe(ctypes.byref(lin), ctypes.byref(lout), OPS[op], DTYPES[dtype],
+                                     P, c, d, segs, ctypes.byref(n)), "purlin_plan_describe")
+    return [(s.src_rank, s.dst_rank, s.src_off, s.dst_off, s.len) for s in segs[:n.value]]
+
+
+def plan_status(in_naming, out_naming, op, dtype, counts, in_bufs, out_bufs, displs=None, P=None):
+    """Status name of planning a collective (no HIP call); 'OK' when it is valid."""
+    P = len(in_bufs) if P is None else P
+    lin, keep_in = _layout(in_naming, in_bufs)
+    lout, keep_out = _layout(out_naming, out_bufs)
+    n = ctypes.c_int64(0)
+    s = _lib.purlin_plan_describe(ctypes.byref(lin), ctypes.byref(lout),
+                                  OPS.get(op, op) if isinstance(op, str) else op,
+                                  DTYPES.get(dtype, dtype) if isinstance(dtype, str) else dtype,
+                                  P, _i64(counts), _i64(displs), None, ctypes.byref(n))
+    return STATUS[s]
+
+
+def last_launch():
+    info = LaunchInfo()
+    _raise(_lib.purlin_last_launch(ctypes.byref(info)), "purlin_last_launch")
+    return {f: getattr(info, f) for f, _ in LaunchInfo._fields_}
+
+
+def stream_copy(dst, src, nbytes, stream=None):
+    """The plain 128-bit streaming copy (calibration / ceiling kernel)."""
+    _raise(_lib.purlin_stream_copy(ctypes.c_void_p(_ptr(dst)), ctypes.c_void_p(_ptr(src)),
+                                   int(nbytes), ctypes.c_void_p(_stream(stream))),
+           "purlin_stream_copy")
+
+
+def release():
+    _lib.purlin_release()

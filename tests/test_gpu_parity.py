@@ -1,0 +1,161 @@
+"""Parity of the HIP path with the oracle, through the C ABI (needs a GPU).
+
+Element by element on seeded inputs at sizes the oracle finishes in seconds
+that still span several chunks and a ragged tail; copies and fp32 sums must
+match bit for bit, bf16 sums within 1 bf16 ulp (the kernel folds in the
+oracle's order, so the distance is expected to be 0 and is reported).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import pins
+import workloads
+from gpu_util import oracle_and_gpu, run_collective, compare, STORE
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["allreduce", "reducescatter", "allgather", "alltoall"]
+
+
+@pytest.fixture(scope="module")
+def purlin():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from reduce_atom_02_amd import purlin as p
+    return p
+
+
+@pytest.fixture(autouse=True)
+def _policy(purlin):
+    purlin.set_policy(reset=True)
+    yield
+    purlin.set_policy(reset=True)
+
+
+def _case(name, P, dtype, variant, rng, scale):
+    nparts = P * P if name == "alltoall" else P
+    if variant == "uniform":
+        sizes = [scale] * nparts
+    else:
+        sizes = [int(v) for v in rng.integers(0, 2 * scale + 1, nparts)]
+        sizes[int(rng.integers(0, nparts))] = 0           # an empty partition
+    counts = pins.counts_for(name, P, sizes)
+    displs = pins.gapped_displs(name, P, counts, rng) if variant == "gapped" else None
+    ins, outs = pins.make_case(name, P, counts, dtype, rng, displs, sentinel=0x5A5A)
+    return counts, displs, ins, outs
+
+
+@pytest.mark.parametrize("chunk", [4096, 0])
+@pytest.mark.parametrize("variant", ["uniform", "v", "gapped"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("P", [1, 2, 3, 8])
+def test_zs_matches_oracle(purlin, P, name, dtype, variant, chunk):
+    print("case zs", P, name, dtype, variant, chunk, flush=True)
+    rng = np.random.default_rng([P, NAMES.index(name), len(dtype), len(variant), chunk])
+    scale = 3000 if name != "alltoall" else 700
+    counts, displs, ins, outs = _case(name, P, dtype, variant, rng, scale)
+    purlin.set_policy(chunk_bytes=chunk, zero_staging="zs")
+    oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, displs)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", NAMES)
+def test_unaligned_buffers(purlin, name, dtype):
+    """Buffer bases at every element offset: sources realign in registers."""
+    P = 8
+    rng = np.random.default_rng([7, NAMES.index(name), len(dtype)])
+    counts, displs, ins, outs = _case(name, P, dtype, "v", rng, 2500)
+    esz = 4 if dtype == "f32" else 2
+    shifts = [int(v) for v in rng.integers(0, 16 // esz, P)]
+    # broadcast destinations must share their alignment for the one-pass
+    # write; give them different ones too, which splits the broadcast
+    out_shifts = [int(v) for v in rng.integers(0, 16 // esz, P)]
+    purlin.set_policy(chunk_bytes=4096, zero_staging="zs")
+    oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, displs, shifts, out_shifts)
+    out_same = [3 % (16 // esz)] * P
+    oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, displs, shifts, out_same)
+
+
+@pytest.mark.parametrize("depth", [1, 2, 3, 8])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", NAMES)
+def test_staged_matches_oracle(purlin, name, dtype, depth):
+    P = 8
+    print("case staged", name, dtype, depth, flush=True)
+    rng = np.random.default_rng([11, NAMES.index(name), len(dtype), depth])
+    counts, displs, ins, outs = _case(name, P, dtype, "v", rng, 9000 if name != "alltoall" else 2000)
+    purlin.set_policy(chunk_bytes=4096, depth=depth, zero_staging="staged", wgs_per_rank=2)
+    oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, displs)
+    info = purlin.last_launch()
+    assert info["zero_staging"] == 0 and info["depth"] == depth
+
+
+@pytest.mark.parametrize("P", [1, 3, 8])
+@pytest.mark.parametrize("name", NAMES)
+def test_staged_unaligned_and_gapped(purlin, name, P):
+    rng = np.random.default_rng([13, NAMES.index(name), P])
+    counts, displs, ins, outs = _case(name, P, "bf16", "gapped", rng, 3000)
+    shifts = [int(v) for v in rng.integers(0, 8, P)]
+    purlin.set_policy(chunk_bytes=4096, depth=2, zero_staging="staged")
+    oracle_and_gpu(purlin, name, P, counts, "bf16", ins, outs, displs, shifts, [5] * P)
+
+
+@pytest.mark.parametrize("sync", [True, False])
+def test_repeated_calls_and_sync_modes(purlin, sync):
+    """Many launches in a row (epochs advance, flags are never reset)."""
+    P = 8
+    purlin.set_policy(sync=sync, zero_staging="zs")
+    rng = np.random.default_rng(21)
+    for it in range(12):
+        name = NAMES[it % 4]
+        counts, displs, ins, outs = _case(name, P, "bf16", "v", rng, 500)
+        oracle_and_gpu(purlin, name, P, counts, "bf16", ins, outs, displs)
+    assert purlin.last_launch()["sync"] == (1 if sync else 0)
+
+
+def test_zero_counts_launch_nothing(purlin):
+    P = 8
+    ins = [np.zeros(4, np.uint16) for _ in range(P)]
+    outs = [np.full(4, 0x1234, np.uint16) for _ in range(P)]
+    got = run_collective(purlin, "by_index", "by_rank", "sum", "bf16", P, [0] * P, None, ins, outs)
+    for j in range(P):
+        assert np.all(got[j] == 0x1234)
+
+
+def test_special_values_sum(purlin):
+    """inf, -inf, NaN, subnormals and overflow follow the oracle's rules."""
+    P = 8
+    f = np.float32
+    vals = np.array([np.inf, -np.inf, np.nan, 2.0 ** -149, 3e38, -0.0, 1.0, 2.0 ** -130],
+                    dtype=f)
+    ins = [np.roll(vals, r).astype(f).view(np.uint32) for r in range(P)]
+    ins[3] = np.array([1.0, 2.0, 3e38, -0.0, 3e38, -0.0, 2.0 ** -149, 5.0], f).view(np.uint32)
+    outs = [np.zeros(8, np.uint32) for _ in range(P)]
+    oracle_and_gpu(purlin, "allreduce", P, [8], "f32", ins, outs)
+    ins16 = [oracle.round_bf16(x.view(np.float32)) for x in ins]
+    outs16 = [np.zeros(8, np.uint16) for _ in range(P)]
+    oracle_and_gpu(purlin, "allreduce", P, [8], "bf16", ins16, outs16)
+
+
+def test_other_derivable_specs(purlin):
+    """Namings outside the seven collectives run when the rule derives a plan."""
+    P = 4
+    rng = np.random.default_rng(5)
+    # by_index -> by_index sum: AllReduce of P named partitions
+    counts = [1000, 0, 37, 2048]
+    ins = [oracle.round_bf16(rng.standard_normal(sum(counts)).astype(np.float32)) for _ in range(P)]
+    outs = [np.zeros(sum(counts), np.uint16) for _ in range(P)]
+    want = oracle.collective("by_index", "by_index", "sum", "bf16", P, counts, None, ins, outs)
+    got = run_collective(purlin, "by_index", "by_index", "sum", "bf16", P, counts, None, ins, outs)
+    for j in range(P):
+        compare("by_index sum %d" % j, got[j], want[j], "bf16", "sum")
+    # by_rank -> by_rank copy: every rank copies its own buffer
+    counts = [5, 6000, 0, 77]
+    ins = [rng.integers(0, 65535, counts[r]).astype(np.uint16) for r in range(P)]
+    outs = [np.zeros(counts[r], np.uint16) for r in range(P)]
+    want = oracle.collective("by_rank", "by_rank", "copy", "bf16", P, counts, None, ins, outs)
+    got = run_collective(purlin, "by_rank", "by_rank", "copy", "bf16", P, counts, None, ins, outs)
+    for j in range(P):
+        compare("by_rank copy %d" % j, got[j], want[j], "bf16", "copy")
