@@ -1,0 +1,230 @@
+"""Benchmark of the collective hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--size BYTES] [--variant zs|staged]
+
+One step runs the seven collectives once each -- AllReduce, ReduceScatter,
+AllGather, AllToAll and the Zipf(s = 0.125) variable-length ReduceScatterV,
+AllGatherV, AllToAllV -- over P = 8 ranks emulated as 8 buffer sets in one
+GPU's HBM, bf16, at T bytes per rank (default 1 GiB, the top of the pages'
+1 MiB - 1 GiB bandwidth sweep).  T is the per-rank size of the partitioned
+side (AllReduce buffer, ReduceScatter input, AllGather output, AllToAll
+input; for the V variants the total of the Zipf partition).  Inputs are
+N(0,1) values drawn on the device from a seed and are resident in HBM
+before the timed region starts.
+
+Printed: one JSON line with the aggregate algorithm bandwidth
+(sum of T over the calls / elapsed time), the fraction of the HBM peak
+(8 TB/s) that the compulsory traffic B_min (every input byte read once,
+every output byte written once) reaches, per-collective kernel times from
+HIP events, the roofline of the dominant kernel, and the oracle's
+throughput on the host cores on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "algorithm GB/s + fraction of HBM peak; p50 latency, 1 KiB–1 GiB, P=8"
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+P = 8
+ESZ = 2                    # bf16
+
+# name -> (in naming, out naming, op)
+SPECS = {
+    "allreduce": ("whole", "whole", "sum"),
+    "reducescatter": ("by_index", "by_rank", "sum"),
+    "allgather": ("by_rank", "by_index", "copy"),
+    "alltoall": ("by_rank_index", "by_index_rank", "copy"),
+    "reducescatterv": ("by_index", "by_rank", "sum"),
+    "allgatherv": ("by_rank", "by_index", "copy"),
+    "alltoallv": ("by_rank_index", "by_index_rank", "copy"),
+}
+
+
+def collective_shapes(T):
+    """Per collective: counts (elements), input and output elements per rank,
+    compulsory bytes B_min and the algorithm size T (bytes)."""
+    import workloads
+    n = T // ESZ
+    z = workloads.zipf_counts(n, P)
+    shapes = {}
+    shapes["allreduce"] = dict(counts=[n], ins=[n] * P, outs=[n] * P)
+    shapes["reducescatter"] = dict(counts=[n // P] * P, ins=[n] * P, outs=[n // P] * P)
+    shapes["allgather"] = dict(counts=[n // P] * P, ins=[n // P] * P, outs=[n] * P)
+    shapes["alltoall"] = dict(counts=[n // P] * (P * P), ins=[n] * P, outs=[n] * P)
+    shapes["reducescatterv"] = dict(counts=z, ins=[n] * P, outs=list(z))
+    shapes["allgatherv"] = dict(counts=z, ins=list(z), outs=[n] * P)
+    shapes["alltoallv"] = dict(counts=[z[j] for _ in range(P) for j in range(P)], ins=[n] * P,
+                               outs=[P * z[j] for j in range(P)])
+    for name, s in shapes.items():
+        s["bmin"] = ESZ * (sum(s["ins"]) + sum(s["outs"]))
+        s["T"] = T
+    return shapes
+
+
+def kernel_of(name):
+    return "zs_kernel<SumBf16>" if SPECS[name][2] == "sum" else "zs_kernel<CopyOp>"
+
+
+def cpu_baseline(T_sample, names):
+    """The oracle, as it stands, on the host cores: seven collectives at
+    T_sample bytes per rank, same seeds; generation is not timed."""
+    import numpy as np
+    import oracle
+    import workloads
+    shapes = collective_shapes(T_sample)
+    n = T_sample // ESZ
+    ins = [workloads.host_values(n, "normal", "bf16", 3, r) for r in range(P)]
+    total_T, total_t = 0, 0.0
+    for name in names:
+        s = shapes[name]
+        in_n, out_n, op = SPECS[name]
+        xs = [ins[r][:s["ins"][r]] for r in range(P)]
+        ys = [np.zeros(s["outs"][r], np.uint16) for r in range(P)]
+        t0 = time.perf_counter()
+        oracle.collective(in_n, out_n, op, "bf16", P, s["counts"], None, xs, ys)
+        total_t += time.perf_counter() - t0
+        total_T += s["T"]
+    return {"value": round(total_T / total_t / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "the same seven collectives, bf16, P=8, at %d MiB per rank instead of "
+                      "%s; numpy oracle single-threaded; %.1f s of oracle time"
+                      % (T_sample >> 20, "the timed size", total_t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--size", type=int, default=1 << 30, help="T, bytes per rank")
+    ap.add_argument("--variant", choices=["zs", "staged"], default="zs")
+    ap.add_argument("--only", default="", help="comma-separated subset of collectives")
+    ap.add_argument("--cpu-sample", type=int, default=64 << 20,
+                    help="T of the oracle sample, bytes per rank (0 skips it)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the P ranks are emulated in one GPU's HBM and no "
+              "multi-GPU path exists in this build (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    if os.environ.get("WORLD_SIZE", "1") != "1":
+        print("bench.py runs as a single process", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from reduce_atom_02_amd import purlin
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    T = args.size
+    names = [n for n in SPECS if not args.only or n in args.only.split(",")]
+    shapes = collective_shapes(T)
+    purlin.set_policy(zero_staging=args.variant)
+
+    # one input set (N(0,1) bf16, drawn on the device) and one output set,
+    # shared by the collectives; each uses the prefix it needs
+    n = T // ESZ
+    ins = [workloads.device_values(n, "normal", "bf16", 3, r, dev) for r in range(P)]
+    out_len = max(max(s["outs"]) for s in shapes.values())
+    outs = [torch.empty(out_len, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def call(name):
+        s = shapes[name]
+        in_n, out_n, op = SPECS[name]
+        purlin.collective([ins[r][:s["ins"][r]] for r in range(P)],
+                          [outs[r][:s["outs"][r]] for r in range(P)],
+                          in_n, out_n, op, s["counts"], stream=stream)
+
+    for _ in range(args.warmup):
+        for name in names:
+            call(name)
+    purlin.check(stream)
+    launch = {}
+    for name in names:
+        call(name)
+        launch[name] = purlin.last_launch()
+        assert launch[name]["bytes_min"] == shapes[name]["bmin"], name
+    purlin.check(stream)
+
+    events = {name: [] for name in names}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for name in names:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call(name)
+            e1.record(stream)
+            events[name].append((e0, e1))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    purlin.check(stream)
+
+    per = {}
+    kern = {}
+    for name in names:
+        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in events[name])
+        mean = sum(ts) / len(ts)
+        p50 = ts[len(ts) // 2]
+        s = shapes[name]
+        per[name] = {"p50_us": round(p50 * 1e6, 2), "mean_us": round(mean * 1e6, 2),
+                     "algbw_GBps": round(s["T"] / p50 / 1e9, 1),
+                     "hbm_frac": round(s["bmin"] / p50 / HBM_PEAK, 4),
+                     "bmin_bytes": s["bmin"], "grid": launch[name]["grid"],
+                     "chunk_bytes": launch[name]["chunk_bytes"]}
+        k = kern.setdefault(kernel_of(name), {"bytes": 0, "time": 0.0, "launches": 0})
+        k["bytes"] += s["bmin"] * len(ts)
+        k["time"] += sum(ts)
+        k["launches"] += len(ts)
+
+    dom_name, dom = max(kern.items(), key=lambda kv: kv[1]["time"])
+    achieved = dom["bytes"] / dom["time"] / 1e9
+    total_T = sum(shapes[n_]["T"] for n_ in names) * args.steps
+    total_bmin = sum(shapes[n_]["bmin"] for n_ in names) * args.steps
+    value = total_T / elapsed / 1e9
+    cpu = cpu_baseline(min(args.cpu_sample, T), names) if args.cpu_sample else None
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "seven collectives (%s), P=8 virtual ranks in one HBM, bf16, "
+                               "T=%d MiB per rank, Zipf s=0.125 for the V variants, %s"
+                               % (",".join(names), T >> 20,
+                                  "zero staging" if args.variant == "zs" else "staged SNAC"),
+                   "P": P, "T_bytes_per_rank": T, "variant": args.variant},
+        "hbm_frac": round(total_bmin / elapsed / HBM_PEAK, 4),
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
+                     "launches": dom["launches"],
+                     "avg_launch_us": round(dom["time"] / dom["launches"] * 1e6, 2),
+                     "bytes_per_launch": dom["bytes"] // dom["launches"]},
+        "cpu_baseline": cpu,
+        "collectives": per,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

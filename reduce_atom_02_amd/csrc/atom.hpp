@@ -9,9 +9,10 @@
 //    independent units per lane in flight;
 //  * units are aligned to the *destination*, so every store is a full
 //    aligned 16-byte store; a source whose address differs from the
-//    destination's modulo 16 is read as two aligned 16-byte blocks and
-//    shifted into place in registers (v_alignbyte), never by unaligned or
-//    byte-wise memory accesses;
+//    destination's modulo 16 is read in aligned 16-byte blocks, and each
+//    lane shifts its block and its neighbour lane's block into place in
+//    registers (lane shuffle + v_alignbyte), never by unaligned or byte-wise
+//    memory accesses;
 //  * the reduce is a per-lane fold over the sources in ascending rank, in
 //    fp32 (bf16 widened exactly), with one final round to nearest even for
 //    a bf16 output; there is no cross-lane tree, so the summation order is
@@ -31,16 +32,27 @@ namespace atom {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Every access names the global address space explicitly, so the compiler
+// emits global_* instructions (scalar base + lane offset) instead of flat_*
+// ones, which would also occupy the counter that scalar loads wait on.
+template <class T>
+using gptr = __attribute__((address_space(1))) T *;
+
+template <class T>
+__device__ __forceinline__ gptr<T> gp(uint64_t addr) {
+  return reinterpret_cast<gptr<T>>(addr);
+}
+
 template <bool kNT>
 __device__ __forceinline__ u32x4 ld16(uint64_t addr) {
-  const u32x4 *p = reinterpret_cast<const u32x4 *>(addr);
+  gptr<const u32x4> p = gp<const u32x4>(addr);
   if constexpr (kNT) return __builtin_nontemporal_load(p);
   else return *p;
 }
 
 template <bool kNT>
 __device__ __forceinline__ void st16(uint64_t addr, u32x4 v) {
-  u32x4 *p = reinterpret_cast<u32x4 *>(addr);
+  gptr<u32x4> p = gp<u32x4>(addr);
   if constexpr (kNT) __builtin_nontemporal_store(v, p);
   else *p = v;
 }
@@ -59,17 +71,6 @@ __device__ __forceinline__ u32x4 funnel(u32x4 lo, u32x4 hi, uint32_t sh) {
   o.z = __builtin_amdgcn_alignbyte(w3, w2, r);
   o.w = __builtin_amdgcn_alignbyte(w4, w3, r);
   return o;
-}
-
-// 16 bytes at byte address `a` whose misalignment is sh = a & 15 (uniform).
-template <bool kNT>
-__device__ __forceinline__ u32x4 ld16_shifted(uint64_t a, uint32_t sh) {
-  const uint64_t base = a - sh;
-  const u32x4 lo = ld16<kNT>(base);
-  // With sh == 0 the second block is the first one again (no read past the
-  // unit); otherwise it holds the unit's last bytes.
-  const u32x4 hi = ld16<kNT>(base + (sh ? 16u : 0u));
-  return funnel(lo, hi, sh);
 }
 
 // ---- bf16 <-> fp32 -------------------------------------------------------
@@ -123,27 +124,27 @@ __device__ __forceinline__ void elements(const Srcs &s, const Dsts &d, int64_t y
   // Loops over sources and destinations are fully unrolled with a guard so
   // that the pointer arrays stay in registers.
   if constexpr (!Op::kSum) {
-    const uint16_t v = *reinterpret_cast<const uint16_t *>(s.a[0] + x);
+    const uint16_t v = *gp<const uint16_t>(s.a[0] + x);
 #pragma unroll
     for (int k = 0; k < kMaxRanks + 1; ++k)
-      if (k < d.n) *reinterpret_cast<uint16_t *>(d.b[k] + x) = v;
+      if (k < d.n) *gp<uint16_t>(d.b[k] + x) = v;
   } else if constexpr (Op::kElem == 4) {
-    float acc = *reinterpret_cast<const float *>(s.a[0] + x);
+    float acc = *gp<const float>(s.a[0] + x);
 #pragma unroll
     for (int i = 1; i < kMaxRanks; ++i)
-      if (i < s.n) acc = acc + *reinterpret_cast<const float *>(s.a[i] + x);
+      if (i < s.n) acc = acc + *gp<const float>(s.a[i] + x);
 #pragma unroll
     for (int k = 0; k < kMaxRanks + 1; ++k)
-      if (k < d.n) *reinterpret_cast<float *>(d.b[k] + x) = acc;
+      if (k < d.n) *gp<float>(d.b[k] + x) = acc;
   } else {
-    float acc = bf16_lo(*reinterpret_cast<const uint16_t *>(s.a[0] + x));
+    float acc = bf16_lo(*gp<const uint16_t>(s.a[0] + x));
 #pragma unroll
     for (int i = 1; i < kMaxRanks; ++i)
-      if (i < s.n) acc = acc + bf16_lo(*reinterpret_cast<const uint16_t *>(s.a[i] + x));
+      if (i < s.n) acc = acc + bf16_lo(*gp<const uint16_t>(s.a[i] + x));
     const uint16_t r = uint16_t(bf16_rne(acc));
 #pragma unroll
     for (int k = 0; k < kMaxRanks + 1; ++k)
-      if (k < d.n) *reinterpret_cast<uint16_t *>(d.b[k] + x) = r;
+      if (k < d.n) *gp<uint16_t>(d.b[k] + x) = r;
   }
 }
 
@@ -191,15 +192,16 @@ __device__ __forceinline__ u32x4 fold_bf16(const u32x4 *x, int n) {
   return o;
 }
 
-// Body of a tile: units [0, nunits) of 16 bytes starting at job byte xa,
-// where every destination b[d] + xa is 16-byte aligned.  Each lane handles
-// units tid, tid + 256, ...; kU of them are loaded before any is stored.
-// Addresses are a uniform 64-bit base per buffer plus one 32-bit lane offset
-// shared by all buffers, so the loads and stores use the scalar-base form
-// and the sources cost no per-lane address registers.
-template <class Op, int kU, bool kAligned, bool kNTL, bool kNTS>
-__device__ __forceinline__ void body(const uint64_t *sa, int ns, const uint64_t *db, int nd,
-                                     uint32_t nunits, const uint32_t *sh) {
+// Body of a tile, all sources aligned like the destinations: units
+// [0, nunits) of 16 bytes starting at job byte xa, where every destination
+// b[d] + xa is 16-byte aligned.  Each lane handles units tid, tid + 256, ...;
+// kU of them are loaded before any is stored.  Addresses are a uniform
+// 64-bit base per buffer plus one 32-bit lane offset shared by all buffers,
+// so the loads use the scalar-base form and the sources cost no per-lane
+// address registers.
+template <class Op, int kU, bool kNTL, bool kNTS>
+__device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const uint64_t *db,
+                                             int nd, uint32_t nunits) {
   constexpr int kS = Op::kSum ? kMaxRanks : 1;
   const uint32_t tid = threadIdx.x;
   for (uint32_t u0 = 0; u0 < nunits; u0 += uint32_t(kThreads) * kU) {
@@ -210,10 +212,7 @@ __device__ __forceinline__ void body(const uint64_t *sa, int ns, const uint64_t 
       if (u < nunits) {
         const uint64_t o = uint64_t(u * 16u);
 #pragma unroll
-        for (int i = 0; i < kS; ++i) {
-          if constexpr (kAligned) x[k][i] = ld16<kNTL>(sa[i] + o);
-          else x[k][i] = ld16_shifted<kNTL>(sa[i] + o, sh[i]);
-        }
+        for (int i = 0; i < kS; ++i) x[k][i] = ld16<kNTL>(sa[i] + o);
       }
     }
 #pragma unroll
@@ -224,6 +223,70 @@ __device__ __forceinline__ void body(const uint64_t *sa, int ns, const uint64_t 
         if constexpr (!Op::kSum) v = x[k][0];
         else if constexpr (Op::kElem == 4) v = fold_f32(x[k], ns);
         else v = fold_bf16(x[k], ns);
+        const uint64_t o = uint64_t(u * 16u);
+#pragma unroll
+        for (int j = 0; j < kMaxRanks + 1; ++j)
+          if (j < nd) st16<kNTS>(db[j] + o, v);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ u32x4 next_lane(u32x4 v) {
+  u32x4 o;
+  o.x = __shfl_down(v.x, 1);
+  o.y = __shfl_down(v.y, 1);
+  o.z = __shfl_down(v.z, 1);
+  o.w = __shfl_down(v.w, 1);
+  return o;
+}
+
+// Body of a tile when some source is not aligned like the destinations
+// (variable-length partitions at arbitrary element offsets).  A wavefront
+// row loads 64 consecutive aligned 16-byte blocks of each source, one per
+// lane, takes its right neighbour's block with a lane shuffle, and shifts
+// the pair into place, producing 63 destination units (the last lane only
+// supplies its block).  So every source byte is loaded once per row and the
+// units in flight match the aligned body.  Source i's blocks start at the
+// aligned address sa[i] - sh[i]; a source with sh[i] > 0 needs one block past
+// its last unit, which holds that unit's last bytes.
+template <class Op, int kU, bool kNTL, bool kNTS>
+__device__ __forceinline__ void body_shifted(const uint64_t *sa, int ns, const uint64_t *db,
+                                             int nd, uint32_t nunits, const uint32_t *sh) {
+  constexpr int kS = Op::kSum ? kMaxRanks : 1;
+  constexpr uint32_t kRow = 63;                        // units produced per wavefront row
+  constexpr uint32_t kPass = kRow * (kThreads / 64) * kU;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = threadIdx.x >> 6;
+  uint64_t base[kS];
+  uint32_t lim[kS];
+#pragma unroll
+  for (int i = 0; i < kS; ++i) {
+    base[i] = sa[i] - sh[i];
+    lim[i] = nunits + (sh[i] ? 1u : 0u);               // blocks this source may load
+  }
+  for (uint32_t u0 = 0; u0 < nunits; u0 += kPass) {
+    u32x4 x[kU][kS];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const uint32_t u = u0 + (uint32_t(k) * (kThreads / 64) + wave) * kRow + lane;
+#pragma unroll
+      for (int i = 0; i < kS; ++i) {
+        x[k][i] = u32x4{0u, 0u, 0u, 0u};
+        if (u < lim[i]) x[k][i] = ld16<kNTL>(base[i] + uint64_t(u * 16u));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const uint32_t u = u0 + (uint32_t(k) * (kThreads / 64) + wave) * kRow + lane;
+      u32x4 y[kS];
+#pragma unroll
+      for (int i = 0; i < kS; ++i) y[i] = funnel(x[k][i], next_lane(x[k][i]), sh[i]);
+      if (lane < kRow && u < nunits) {
+        u32x4 v;
+        if constexpr (!Op::kSum) v = y[0];
+        else if constexpr (Op::kElem == 4) v = fold_f32(y, ns);
+        else v = fold_bf16(y, ns);
         const uint64_t o = uint64_t(u * 16u);
 #pragma unroll
         for (int j = 0; j < kMaxRanks + 1; ++j)
@@ -259,10 +322,8 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
   }
 #pragma unroll
   for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(xa);
-  // The realigning path reads two blocks per unit, so it keeps half as many
-  // units in flight to stay within the same register budget.
-  if (any == 0) body<Op, kU, true, kNTL, kNTS>(sa, s.n, db, d.n, nunits, sh);
-  else body<Op, (kU > 1 ? kU / 2 : 1), false, kNTL, kNTS>(sa, s.n, db, d.n, nunits, sh);
+  if (any == 0) body_aligned<Op, kU, kNTL, kNTS>(sa, s.n, db, d.n, nunits);
+  else body_shifted<Op, kU, kNTL, kNTS>(sa, s.n, db, d.n, nunits, sh);
 }
 
 }  // namespace atom

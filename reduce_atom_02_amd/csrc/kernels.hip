@@ -170,6 +170,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       atom::Srcs s;
       if (jb.src < 0) {
         s.n = p.P;
+#pragma unroll
         for (int i = 0; i < kMaxRanks; ++i) {
           const int src = i < p.P ? i : 0;
           if (src == owner) {
@@ -184,6 +185,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
         const uint64_t a = jb.src == owner
                                ? uint64_t(p.in[owner]) + uint64_t(jb.src_off)
                                : slot_base(slot_ref(sp, ring0, slot).data, b0, x0);
+#pragma unroll
         for (int i = 0; i < kMaxRanks; ++i) s.a[i] = a;
       }
       // destinations: the owner's output (when it is one) and the scatter slot
@@ -197,10 +199,10 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
 #pragma unroll
       for (int k = 1; k < kMaxRanks + 1; ++k) d.b[k] = scat;
       atom::tile<Op, kU, kNTL, kNTS>(s, d, x0, x1);
-      __syncthreads();
+      snac::drain_workgroup();
       if (threadIdx.x == 0) {
         for (int k = 0; k < sj.n_stage; ++k)
-          snac::add_rel(slot_ref(sp, ring0 + k, slot).credit, uint64_t(1));
+          snac::add_rlx(slot_ref(sp, ring0 + k, slot).credit, uint64_t(1));
         if (sj.n_scatter > 0)
           snac::store_rel(slot_ref(sp, ring0 + sj.n_stage, slot).ready, tag(e, round + 1));
       }
@@ -232,6 +234,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       atom::Srcs s;
       s.n = 1;
       const uint64_t a = uint64_t(p.in[src]) + uint64_t(jb.src_off);
+#pragma unroll
       for (int i = 0; i < kMaxRanks; ++i) s.a[i] = a;
       atom::Dsts d;
       d.n = 1;
@@ -263,14 +266,15 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       atom::Srcs s;
       s.n = 1;
       const uint64_t a = slot_base(o.data, b0, x0);
+#pragma unroll
       for (int i = 0; i < kMaxRanks; ++i) s.a[i] = a;
       atom::Dsts d;
       d.n = 1;
 #pragma unroll
       for (int q = 0; q < kMaxRanks + 1; ++q) d.b[q] = uint64_t(p.out[dst]) + uint64_t(jb.dst_off);
       atom::tile<atom::CopyOp, kU, false, kNTS>(s, d, x0, x1);
-      __syncthreads();
-      if (threadIdx.x == 0) snac::add_rel(o.credit, uint64_t(1));
+      snac::drain_workgroup();
+      if (threadIdx.x == 0) snac::add_rlx(o.credit, uint64_t(1));
     }
   }
 }
@@ -284,40 +288,50 @@ __global__ void __launch_bounds__(kThreads) stream_copy_kernel(atom::u32x4 *dst,
     dst[i] = src[i];
 }
 
-template <class Op, int kU, bool kNTL, bool kNTS>
-void *zs_fn() { return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNTL, kNTS>); }
-template <class Op, int kU, bool kNTL, bool kNTS>
-void *st_fn() { return reinterpret_cast<void *>(&staged_kernel<Op, kU, kNTL, kNTS>); }
+template <class Op, int kU, bool kNT>
+void *zs_fn() { return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT>); }
+template <class Op, int kU, bool kNT>
+void *st_fn() { return reinterpret_cast<void *>(&staged_kernel<Op, kU, kNT, kNT>); }
 
-template <class Op, int kU>
-void *pick(bool staged, int nt) {
-  switch (nt & 3) {
-    case 0: return staged ? st_fn<Op, kU, false, false>() : zs_fn<Op, kU, false, false>();
-    case 1: return staged ? st_fn<Op, kU, true, false>() : zs_fn<Op, kU, true, false>();
-    case 2: return staged ? st_fn<Op, kU, false, true>() : zs_fn<Op, kU, false, true>();
-    default: return staged ? st_fn<Op, kU, true, true>() : zs_fn<Op, kU, true, true>();
+// Unroll depth: 16-byte units each lane keeps in flight per source.
+template <class Op, int kU0, int kU1, int kU2>
+void *pick(bool staged, bool nt, int unroll_sel) {
+  if (staged) return nt ? st_fn<Op, kU1, true>() : st_fn<Op, kU1, false>();
+  switch (unroll_sel) {
+    case 0: return nt ? zs_fn<Op, kU0, true>() : zs_fn<Op, kU0, false>();
+    case 2: return nt ? zs_fn<Op, kU2, true>() : zs_fn<Op, kU2, false>();
+    default: return nt ? zs_fn<Op, kU1, true>() : zs_fn<Op, kU1, false>();
   }
 }
 
 }  // namespace
 
-void *kernel_fn(KernelKind kind, bool staged, int nt) {
+int unroll_of(KernelKind kind, int unroll_sel) {
+  static const int copy_u[3] = {4, 8, 16};
+  static const int sum_u[3] = {1, 2, 4};
+  const int sel = unroll_sel < 0 || unroll_sel > 2 ? 1 : unroll_sel;
+  return kind == KernelKind::kCopy ? copy_u[sel] : sum_u[sel];
+}
+
+void *kernel_fn(KernelKind kind, bool staged, bool nt, int unroll_sel) {
   switch (kind) {
-    case KernelKind::kCopy: return pick<atom::CopyOp, 4>(staged, nt);
-    case KernelKind::kSumF32: return pick<atom::SumF32, 2>(staged, nt);
-    default: return pick<atom::SumBf16, 2>(staged, nt);
+    case KernelKind::kCopy: return pick<atom::CopyOp, 4, 8, 16>(staged, nt, unroll_sel);
+    case KernelKind::kSumF32: return pick<atom::SumF32, 1, 2, 4>(staged, nt, unroll_sel);
+    default: return pick<atom::SumBf16, 1, 2, 4>(staged, nt, unroll_sel);
   }
 }
 
-hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, int nt, int grid, hipStream_t stream) {
+hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, int grid,
+                     hipStream_t stream) {
   void *args[] = {const_cast<LaunchPlan *>(&p)};
-  return hipLaunchKernel(kernel_fn(kind, false, nt), dim3(grid), dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel), dim3(grid), dim3(kThreads), args,
+                         0, stream);
 }
 
-hipError_t launch_staged(const StagedPlan &p, KernelKind kind, int nt, hipStream_t stream) {
+hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStream_t stream) {
   void *args[] = {const_cast<StagedPlan *>(&p)};
-  return hipLaunchKernel(kernel_fn(kind, true, nt), dim3(p.total_roles), dim3(kThreads), args, 0,
-                         stream);
+  return hipLaunchKernel(kernel_fn(kind, true, nt, 1), dim3(p.total_roles), dim3(kThreads), args,
+                         0, stream);
 }
 
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,
@@ -328,9 +342,10 @@ hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int gri
   return hipGetLastError();
 }
 
-hipError_t max_resident_per_cu(KernelKind kind, bool staged, int nt, int *blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, kernel_fn(kind, staged, nt),
-                                                      kThreads, 0);
+hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel,
+                               int *blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks, kernel_fn(kind, staged, nt, staged ? 1 : unroll_sel), kThreads, 0);
 }
 
 }  // namespace purlin

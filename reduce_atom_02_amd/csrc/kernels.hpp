@@ -8,11 +8,15 @@ namespace purlin {
 
 enum class KernelKind { kCopy, kSumF32, kSumBf16 };
 
-// nt: bit 0 = nontemporal loads, bit 1 = nontemporal stores.
-hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, int nt, int grid, hipStream_t stream);
-hipError_t launch_staged(const StagedPlan &p, KernelKind kind, int nt, hipStream_t stream);
+// nt: nontemporal loads and stores.  unroll_sel picks one of three unroll
+// depths (units in flight per lane and source): copy 4 / 8 / 16, sum 1 / 2 / 4.
+hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, int grid,
+                     hipStream_t stream);
+hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStream_t stream);
+int unroll_of(KernelKind kind, int unroll_sel);
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,
                               hipStream_t stream);
-hipError_t max_resident_per_cu(KernelKind kind, bool staged, int nt, int *blocks);
+hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel,
+                               int *blocks);
 
 }  // namespace purlin

@@ -29,7 +29,7 @@ struct DeviceState {
   int64_t slot_flag_bytes = 0;
   uint32_t epoch = 0;
   uint32_t exit_total[2] = {0, 0};
-  int occ[3][2][4] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
+  int occ[3][2][2][3] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
 };
 
 std::vector<DeviceState> &devices() {
@@ -89,7 +89,11 @@ purlin_policy effective_policy() {
   return p;
 }
 
-int nt_bits() { return int(env_i64("PURLIN_NT", 0)) & 3; }
+bool nt_env(bool dflt) {
+  const int64_t v = env_i64("PURLIN_NT", -1);
+  return v < 0 ? dflt : v != 0;
+}
+int unroll_env() { return int(env_i64("PURLIN_UNROLL", -1)); }
 
 purlin_status device_state(DeviceState **out) {
   int dev = 0;
@@ -120,11 +124,11 @@ purlin_status device_state(DeviceState **out) {
   return PURLIN_OK;
 }
 
-int occupancy(DeviceState &s, KernelKind kind, bool staged, int nt) {
-  int &o = s.occ[int(kind)][staged ? 1 : 0][nt & 3];
+int occupancy(DeviceState &s, KernelKind kind, bool staged, bool nt, int unroll_sel) {
+  int &o = s.occ[int(kind)][staged ? 1 : 0][nt ? 1 : 0][unroll_sel];
   if (o == 0) {
     int b = 0;
-    if (max_resident_per_cu(kind, staged, nt, &b) != hipSuccess || b < 1) b = 1;
+    if (max_resident_per_cu(kind, staged, nt, unroll_sel, &b) != hipSuccess || b < 1) b = 1;
     o = b;
   }
   return o;
@@ -258,15 +262,17 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
   st = device_state(&ds);
   if (st != PURLIN_OK) return st;
   const purlin_policy pol = effective_policy();
-  const int nt = nt_bits();
   const KernelKind kind = kind_of(op, dtype);
+  const bool nt = nt_env(true);
+  int unroll_sel = unroll_env();
+  if (unroll_sel < 0 || unroll_sel > 2) unroll_sel = 1;
 
   std::vector<Job> jobs;
   std::vector<int> owners;
   launch_jobs(*d, reinterpret_cast<char *const *>(out->bufs), &jobs, &owners);
 
   const bool staged = pol.zero_staging == PURLIN_STAGING_STAGED;
-  const int capacity = ds->cus * occupancy(*ds, kind, staged, nt);
+  const int capacity = ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel);
   int64_t out_bytes = 0;
   for (const Job &jb : jobs) out_bytes += jb.nbytes * (jb.dst < 0 ? P : 1);
 
@@ -298,7 +304,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     grid = std::max(grid, 1);
     lp.sync = pol.sync == 2 ? 0 : 1;
     lp.exit_expect = ds->exit_total[(ds->epoch - 1u) & 1u];
-    err = launch_zs(lp, kind, nt, grid, stream);
+    err = launch_zs(lp, kind, nt, unroll_sel, grid, stream);
     if (err == hipSuccess && lp.sync) ds->exit_total[ds->epoch & 1u] += uint32_t(grid);
     info.grid = grid;
     info.zero_staging = 1;

@@ -2,11 +2,20 @@
 //
 // Purlin's middle layer is Stage, Notify, And Consume (abstract): a producer
 // stages a chunk, notifies, and a consumer consumes it.  Here every flag is
-// a word in HBM written with an agent-scope release store (or add) and read
-// with agent-scope acquire loads, so a chunk written by one workgroup is
-// visible to a workgroup on another XCD once the flag is seen.  Flag values
-// carry the launch epoch in their high bits, so a flag is never reset
-// between launches; a consumer waits for the exact value it expects.
+// a word in HBM.  Costs on a multi-XCD gfx950 shape the protocol:
+//  * an agent-scope acquire invalidates the XCD's L2 and an agent-scope
+//    release writes it back, so neither may sit inside a spin loop;
+//  * a wait therefore polls with relaxed agent-scope loads (which bypass the
+//    non-coherent caches) and issues one acquire fence once the value is
+//    seen;
+//  * a notify that publishes data ("ready") is a release store, so the
+//    chunk written by one workgroup is visible on every XCD;
+//  * a notify that only says "I have finished reading" (a credit, the exit
+//    count) is a relaxed add issued after every wavefront's loads have
+//    returned their data (s_waitcnt 0, then a barrier): once the data is in
+//    registers, the writer may overwrite the source.
+// Flag values carry the launch epoch in their high bits, so a flag is never
+// reset between launches; a consumer waits for the value it expects.
 //
 // Every wait is bounded by a wall-clock watchdog.  On expiry the workgroup
 // sets the device status word and the launch's abort epoch; every other
@@ -21,23 +30,32 @@
 namespace purlin {
 namespace snac {
 
-__device__ __forceinline__ uint32_t load_acq(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t load_rlx(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t load_acq(const uint64_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t load_rlx(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void acquire_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void store_rel(uint32_t *p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void store_rel(uint64_t *p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void add_rel(uint32_t *p, uint32_t v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void add_rlx(uint32_t *p, uint32_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void add_rel(uint64_t *p, uint64_t v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void add_rlx(uint64_t *p, uint64_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every wavefront of the workgroup has its loads back (and its stores
+// acknowledged); call from all threads.  After it, a relaxed notify may say
+// "done reading".
+__device__ __forceinline__ void drain_workgroup() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 __device__ __forceinline__ bool aborted(const LaunchPlan &p) {
@@ -51,14 +69,17 @@ __device__ __forceinline__ void raise_timeout(const LaunchPlan &p) {
   __hip_atomic_store(&p.flags[kFlagAbort], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Spin until *f - target >= 0 (wrap-aware); false if the watchdog expired or
-// the launch was aborted.
+// Spin until *f - target >= 0 (wrap-aware), then acquire; false if the
+// watchdog expired or the launch was aborted.
 template <class W>
-__device__ bool wait_geq(const W *f, W target, const LaunchPlan &p) {
+__device__ __forceinline__ bool wait_geq(const W *f, W target, const LaunchPlan &p) {
   using S = typename std::conditional<sizeof(W) == 8, int64_t, int32_t>::type;
   const uint64_t t0 = wall_clock64();
   while (true) {
-    if (S(load_acq(f) - target) >= 0) return true;
+    if (S(load_rlx(f) - target) >= 0) {
+      acquire_fence();
+      return true;
+    }
     if (aborted(p)) return false;
     if (wall_clock64() - t0 > p.watchdog_ticks) {
       raise_timeout(p);
@@ -74,7 +95,7 @@ __device__ bool wait_geq(const W *f, W target, const LaunchPlan &p) {
 // entry flag of every rank before its first access.  Workgroup b announces
 // ranks b, b + grid, ...; all workgroups are resident at once (the grid
 // never exceeds what the device holds), so the announcements always happen.
-__device__ bool entry(const LaunchPlan &p) {
+__device__ __forceinline__ bool entry(const LaunchPlan &p) {
   __shared__ int ok;
   if (threadIdx.x == 0) ok = 1;
   __syncthreads();
@@ -92,11 +113,12 @@ __device__ bool entry(const LaunchPlan &p) {
   return ok != 0;
 }
 
-// Exit notify: this workgroup has finished reading every input and writing
-// every output of this launch.
-__device__ void exit_notify(const LaunchPlan &p) {
-  __syncthreads();
-  if (threadIdx.x == 0) add_rel(&p.flags[kFlagExit + (p.epoch & 1u) * kFlagStride], 1u);
+// Exit notify: this workgroup has finished reading every input of this
+// launch.  (Its outputs reach the next launch through stream order; ranks on
+// separate GPUs would need a system-scope release here.)
+__device__ __forceinline__ void exit_notify(const LaunchPlan &p) {
+  drain_workgroup();
+  if (threadIdx.x == 0) add_rlx(&p.flags[kFlagExit + (p.epoch & 1u) * kFlagStride], 1u);
 }
 
 }  // namespace snac

@@ -159,3 +159,31 @@ def test_other_derivable_specs(purlin):
     got = run_collective(purlin, "by_rank", "by_rank", "copy", "bf16", P, counts, None, ins, outs)
     for j in range(P):
         compare("by_rank copy %d" % j, got[j], want[j], "bf16", "copy")
+
+
+@pytest.mark.parametrize("chunk", [4096, 65536, 1 << 20])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", NAMES)
+def test_large_unaligned_tiles(purlin, name, dtype, chunk):
+    """Partitions of ~100k elements at odd offsets: realigned rows, many passes per tile."""
+    P = 8
+    print("case large-unaligned", name, dtype, chunk, flush=True)
+    rng = np.random.default_rng([17, NAMES.index(name), len(dtype), chunk])
+    nparts = P * P if name == "alltoall" else P
+    hi = 60000 if name == "alltoall" else 150000
+    sizes = [int(v) | 1 for v in rng.integers(hi // 3, hi, nparts)]   # odd sizes
+    counts = pins.counts_for(name, P, sizes)
+    ins, outs = pins.make_case(name, P, counts, dtype, rng, None, sentinel=0x3C3C)
+    esz = 4 if dtype == "f32" else 2
+    shifts = [int(v) for v in rng.integers(0, 16 // esz, P)]
+    out_shift = [int(rng.integers(0, 16 // esz))] * P
+    for unroll in ("0", "1", "2"):
+        import os
+        os.environ["PURLIN_UNROLL"] = unroll
+        try:
+            purlin.set_policy(chunk_bytes=chunk, zero_staging="zs")
+            oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, None, shifts, out_shift)
+        finally:
+            os.environ.pop("PURLIN_UNROLL", None)
+    purlin.set_policy(chunk_bytes=chunk, zero_staging="staged", depth=2)
+    oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, None, shifts, out_shift)
