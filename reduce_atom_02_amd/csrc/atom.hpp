@@ -192,44 +192,55 @@ __device__ __forceinline__ u32x4 fold_bf16(const u32x4 *x, int n) {
   return o;
 }
 
+// One pass of the aligned body: kU units per lane, loaded before any is
+// stored.  kGuard = false for passes that lie wholly inside the tile: then
+// the pass is straight-line code, so the compiler keeps every load in
+// flight until its data is needed instead of draining at guard branches.
+template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard>
+__device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const uint64_t *db,
+                                             int nd, uint32_t nunits, uint32_t u0) {
+  constexpr int kS = Op::kSum ? kMaxRanks : 1;
+  const uint32_t tid = threadIdx.x;
+  u32x4 x[kU][kS];
+#pragma unroll
+  for (int k = 0; k < kU; ++k) {
+    const uint32_t u = u0 + uint32_t(k) * kThreads + tid;
+    if (!kGuard || u < nunits) {
+      const uint64_t o = uint64_t(u * 16u);
+#pragma unroll
+      for (int i = 0; i < kS; ++i) x[k][i] = ld16<kNTL>(sa[i] + o);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kU; ++k) {
+    const uint32_t u = u0 + uint32_t(k) * kThreads + tid;
+    if (!kGuard || u < nunits) {
+      u32x4 v;
+      if constexpr (!Op::kSum) v = x[k][0];
+      else if constexpr (Op::kElem == 4) v = fold_f32(x[k], ns);
+      else v = fold_bf16(x[k], ns);
+      const uint64_t o = uint64_t(u * 16u);
+#pragma unroll
+      for (int j = 0; j < kMaxRanks + 1; ++j)
+        if (j < nd) st16<kNTS>(db[j] + o, v);
+    }
+  }
+}
+
 // Body of a tile, all sources aligned like the destinations: units
-// [0, nunits) of 16 bytes starting at job byte xa, where every destination
-// b[d] + xa is 16-byte aligned.  Each lane handles units tid, tid + 256, ...;
-// kU of them are loaded before any is stored.  Addresses are a uniform
-// 64-bit base per buffer plus one 32-bit lane offset shared by all buffers,
-// so the loads use the scalar-base form and the sources cost no per-lane
-// address registers.
+// [0, nunits) of 16 bytes, where every destination db[d] is 16-byte
+// aligned.  Each lane handles units tid, tid + 256, ...  Addresses are a
+// uniform 64-bit base per buffer plus one 32-bit lane offset shared by all
+// buffers, so the loads use the scalar-base form and the sources cost no
+// per-lane address registers.
 template <class Op, int kU, bool kNTL, bool kNTS>
 __device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const uint64_t *db,
                                              int nd, uint32_t nunits) {
-  constexpr int kS = Op::kSum ? kMaxRanks : 1;
-  const uint32_t tid = threadIdx.x;
-  for (uint32_t u0 = 0; u0 < nunits; u0 += uint32_t(kThreads) * kU) {
-    u32x4 x[kU][kS];
-#pragma unroll
-    for (int k = 0; k < kU; ++k) {
-      const uint32_t u = u0 + uint32_t(k) * kThreads + tid;
-      if (u < nunits) {
-        const uint64_t o = uint64_t(u * 16u);
-#pragma unroll
-        for (int i = 0; i < kS; ++i) x[k][i] = ld16<kNTL>(sa[i] + o);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kU; ++k) {
-      const uint32_t u = u0 + uint32_t(k) * kThreads + tid;
-      if (u < nunits) {
-        u32x4 v;
-        if constexpr (!Op::kSum) v = x[k][0];
-        else if constexpr (Op::kElem == 4) v = fold_f32(x[k], ns);
-        else v = fold_bf16(x[k], ns);
-        const uint64_t o = uint64_t(u * 16u);
-#pragma unroll
-        for (int j = 0; j < kMaxRanks + 1; ++j)
-          if (j < nd) st16<kNTS>(db[j] + o, v);
-      }
-    }
-  }
+  constexpr uint32_t kPass = uint32_t(kThreads) * kU;
+  uint32_t u0 = 0;
+  for (; u0 + kPass <= nunits; u0 += kPass)
+    pass_aligned<Op, kU, kNTL, kNTS, false>(sa, ns, db, nd, nunits, u0);
+  if (u0 < nunits) pass_aligned<Op, kU, kNTL, kNTS, true>(sa, ns, db, nd, nunits, u0);
 }
 
 __device__ __forceinline__ u32x4 next_lane(u32x4 v) {
@@ -241,23 +252,66 @@ __device__ __forceinline__ u32x4 next_lane(u32x4 v) {
   return o;
 }
 
+constexpr uint32_t kRow = 56;  // units a wavefront row of the realigning body produces
+
+// One pass of the realigning body (see body_shifted).  kGuard = false for
+// passes whose every row, including the extra block each lane 56 reads, lies
+// inside the tile.
+template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard>
+__device__ __forceinline__ void pass_shifted(const uint64_t *base, const uint32_t *lim, int ns,
+                                             const uint64_t *db, int nd, uint32_t nunits,
+                                             const uint32_t *sh, uint32_t u0) {
+  constexpr int kS = Op::kSum ? kMaxRanks : 1;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = threadIdx.x >> 6;
+  u32x4 x[kU][kS];
+#pragma unroll
+  for (int k = 0; k < kU; ++k) {
+    const uint32_t u = u0 + (uint32_t(k) * (kThreads / 64) + wave) * kRow + lane;
+#pragma unroll
+    for (int i = 0; i < kS; ++i) {
+      if constexpr (kGuard) {
+        x[k][i] = u32x4{0u, 0u, 0u, 0u};
+        if (lane <= kRow && u < lim[i]) x[k][i] = ld16<kNTL>(base[i] + uint64_t(u * 16u));
+      } else {
+        // lanes past 56 read blocks of the next row, still inside the tile
+        x[k][i] = ld16<kNTL>(base[i] + uint64_t(u * 16u));
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kU; ++k) {
+    const uint32_t u = u0 + (uint32_t(k) * (kThreads / 64) + wave) * kRow + lane;
+    u32x4 y[kS];
+#pragma unroll
+    for (int i = 0; i < kS; ++i) y[i] = funnel(x[k][i], next_lane(x[k][i]), sh[i]);
+    if (lane < kRow && (!kGuard || u < nunits)) {
+      u32x4 v;
+      if constexpr (!Op::kSum) v = y[0];
+      else if constexpr (Op::kElem == 4) v = fold_f32(y, ns);
+      else v = fold_bf16(y, ns);
+      const uint64_t o = uint64_t(u * 16u);
+#pragma unroll
+      for (int j = 0; j < kMaxRanks + 1; ++j)
+        if (j < nd) st16<kNTS>(db[j] + o, v);
+    }
+  }
+}
+
 // Body of a tile when some source is not aligned like the destinations
 // (variable-length partitions at arbitrary element offsets).  A wavefront
-// row loads 64 consecutive aligned 16-byte blocks of each source, one per
+// row loads 57 consecutive aligned 16-byte blocks of each source, one per
 // lane, takes its right neighbour's block with a lane shuffle, and shifts
-// the pair into place, producing 63 destination units (the last lane only
-// supplies its block).  So every source byte is loaded once per row and the
-// units in flight match the aligned body.  Source i's blocks start at the
-// aligned address sa[i] - sh[i]; a source with sh[i] > 0 needs one block past
-// its last unit, which holds that unit's last bytes.
+// the pair into place, producing 56 destination units: 896 bytes, seven
+// whole 128-byte lines, so no store writes part of a line.  Every source
+// byte is loaded once per row.  Source i's blocks start at the aligned
+// address sa[i] - sh[i]; a source with sh[i] > 0 needs one block past its
+// last unit, which holds that unit's last bytes.
 template <class Op, int kU, bool kNTL, bool kNTS>
 __device__ __forceinline__ void body_shifted(const uint64_t *sa, int ns, const uint64_t *db,
                                              int nd, uint32_t nunits, const uint32_t *sh) {
   constexpr int kS = Op::kSum ? kMaxRanks : 1;
-  constexpr uint32_t kRow = 63;                        // units produced per wavefront row
   constexpr uint32_t kPass = kRow * (kThreads / 64) * kU;
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t wave = threadIdx.x >> 6;
   uint64_t base[kS];
   uint32_t lim[kS];
 #pragma unroll
@@ -265,65 +319,69 @@ __device__ __forceinline__ void body_shifted(const uint64_t *sa, int ns, const u
     base[i] = sa[i] - sh[i];
     lim[i] = nunits + (sh[i] ? 1u : 0u);               // blocks this source may load
   }
-  for (uint32_t u0 = 0; u0 < nunits; u0 += kPass) {
-    u32x4 x[kU][kS];
-#pragma unroll
-    for (int k = 0; k < kU; ++k) {
-      const uint32_t u = u0 + (uint32_t(k) * (kThreads / 64) + wave) * kRow + lane;
-#pragma unroll
-      for (int i = 0; i < kS; ++i) {
-        x[k][i] = u32x4{0u, 0u, 0u, 0u};
-        if (u < lim[i]) x[k][i] = ld16<kNTL>(base[i] + uint64_t(u * 16u));
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kU; ++k) {
-      const uint32_t u = u0 + (uint32_t(k) * (kThreads / 64) + wave) * kRow + lane;
-      u32x4 y[kS];
-#pragma unroll
-      for (int i = 0; i < kS; ++i) y[i] = funnel(x[k][i], next_lane(x[k][i]), sh[i]);
-      if (lane < kRow && u < nunits) {
-        u32x4 v;
-        if constexpr (!Op::kSum) v = y[0];
-        else if constexpr (Op::kElem == 4) v = fold_f32(y, ns);
-        else v = fold_bf16(y, ns);
-        const uint64_t o = uint64_t(u * 16u);
-#pragma unroll
-        for (int j = 0; j < kMaxRanks + 1; ++j)
-          if (j < nd) st16<kNTS>(db[j] + o, v);
-      }
-    }
-  }
+  uint32_t u0 = 0;
+  // an unguarded pass reads up to block u0 + kPass + 7 (lanes 57..63 of the
+  // last row), which must lie below every source's limit
+  for (; u0 + kPass + 8 <= nunits; u0 += kPass)
+    pass_shifted<Op, kU, kNTL, kNTS, false>(base, lim, ns, db, nd, nunits, sh, u0);
+  for (; u0 < nunits; u0 += kPass)
+    pass_shifted<Op, kU, kNTL, kNTS, true>(base, lim, ns, db, nd, nunits, sh, u0);
 }
 
-// One tile: job bytes [x0, x1).  x0 is 0 or destination-aligned, x1 is the
-// job's end or destination-aligned; the unaligned head and tail (< 16 bytes
-// each) are done element by element.  A tile spans less than 4 GiB.
 template <class Op, int kU, bool kNTL, bool kNTS>
+__device__ __forceinline__ void units(const uint64_t *sa, int ns, const uint64_t *db, int nd,
+                                      uint32_t n, const uint32_t *sh, bool aligned) {
+  if (aligned) body_aligned<Op, kU, kNTL, kNTS>(sa, ns, db, nd, n);
+  else body_shifted<Op, kU, kNTL, kNTS>(sa, ns, db, nd, n, sh);
+}
+
+// One tile: job bytes [x0, x1).  x0 is 0 or on a 128-byte boundary of the
+// destinations, x1 is the job's end or on such a boundary.  Layout:
+//   [x0, x16)    < 16 bytes before the first 16-byte boundary: element ops
+//   [x16, x128)  < 8 units before the first 128-byte boundary: plain stores
+//   [x128, xb)   the body: whole lines, nontemporal stores when kNT
+//   [xb, x1)     < 16 bytes of tail: element ops
+// Loads are nontemporal only when every source sits on the same 128-byte
+// phase as the destinations: a line shared by two wavefronts is then never
+// fetched twice, which the L2 would otherwise prevent.  A tile spans less
+// than 4 GiB.
+template <class Op, int kU, bool kNT>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1) {
   if (x1 <= x0) return;
   const uint64_t b0 = d.b[0];
-  int64_t xa = x0 + int64_t((16u - uint32_t((b0 + uint64_t(x0)) & 15u)) & 15u);
-  if (xa > x1) xa = x1;
-  const uint32_t nunits = uint32_t((x1 - xa) >> 4);
-  const int64_t xb = xa + int64_t(nunits) * 16;
-  if (xa > x0) elements<Op>(s, d, x0, xa);
+  int64_t x16 = x0 + int64_t((16u - uint32_t((b0 + uint64_t(x0)) & 15u)) & 15u);
+  if (x16 > x1) x16 = x1;
+  const uint32_t nall = uint32_t((x1 - x16) >> 4);
+  uint32_t nhead = ((128u - uint32_t((b0 + uint64_t(x16)) & 127u)) & 127u) >> 4;
+  if (nhead > nall) nhead = nall;
+  const uint32_t nbody = nall - nhead;
+  const int64_t x128 = x16 + int64_t(nhead) * 16;
+  const int64_t xb = x16 + int64_t(nall) * 16;
+  if (x16 > x0) elements<Op>(s, d, x0, x16);
   if (x1 > xb) elements<Op>(s, d, xb, x1);
-  if (nunits == 0) return;
+  if (nall == 0) return;
   uint64_t sa[kMaxRanks];
   uint64_t db[kMaxRanks + 1];
   uint32_t sh[kMaxRanks];
-  uint32_t any = 0;
+  uint32_t any = 0, phase = 0;
 #pragma unroll
   for (int i = 0; i < kMaxRanks; ++i) {
-    sa[i] = s.a[i] + uint64_t(xa);
+    sa[i] = s.a[i] + uint64_t(x16);
     sh[i] = uint32_t(sa[i] & 15u);
     any |= sh[i];
+    phase |= uint32_t((s.a[i] - b0) & 127u);
   }
 #pragma unroll
-  for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(xa);
-  if (any == 0) body_aligned<Op, kU, kNTL, kNTS>(sa, s.n, db, d.n, nunits);
-  else body_shifted<Op, kU, kNTL, kNTS>(sa, s.n, db, d.n, nunits, sh);
+  for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(x16);
+  const bool aligned = any == 0;
+  if (nhead) units<Op, kU, false, false>(sa, s.n, db, d.n, nhead, sh, aligned);
+  if (nbody == 0) return;
+#pragma unroll
+  for (int i = 0; i < kMaxRanks; ++i) sa[i] += uint64_t(nhead) * 16u;
+#pragma unroll
+  for (int j = 0; j < kMaxRanks + 1; ++j) db[j] += uint64_t(nhead) * 16u;
+  if (kNT && phase == 0) units<Op, kU, true, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
+  else units<Op, kU, false, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
 }
 
 }  // namespace atom

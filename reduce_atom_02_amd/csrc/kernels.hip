@@ -27,10 +27,10 @@ __device__ __forceinline__ void job_srcs(const LaunchPlan &p, const Job &jb, ato
 
 // Job byte range of tile tl (of ntl) of a job of n bytes whose first
 // destination byte is at address b0: tile 0 also takes the bytes before the
-// first 16-byte boundary, so every later tile starts on one.
+// first 128-byte boundary, so every later tile starts on a line.
 __device__ __forceinline__ void tile_bounds(uint64_t b0, int64_t n, int64_t C, int tl, int ntl,
                                             int64_t &x0, int64_t &x1) {
-  int64_t h = int64_t((16u - uint32_t(b0 & 15u)) & 15u);
+  int64_t h = int64_t((128u - uint32_t(b0 & 127u)) & 127u);
   if (h > n) h = n;
   x0 = tl == 0 ? 0 : h + int64_t(tl) * C;
   x1 = tl == ntl - 1 ? n : h + int64_t(tl + 1) * C;
@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     int64_t x0, x1;
     tile_bounds(d.b[0], jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
                 p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
-    atom::tile<Op, kU, kNTL, kNTS>(s, d, x0, x1);
+    atom::tile<Op, kU, kNTL>(s, d, x0, x1);
   }
   if (p.sync) snac::exit_notify(p);
 }
@@ -107,9 +107,9 @@ __device__ __forceinline__ SlotRef slot_ref(const StagedPlan &sp, int ring, int 
 }
 
 // Base address such that job byte x of chunk [x0, x1) lands at base + x,
-// keeping the destination's alignment modulo 16 inside the slot.
+// keeping the destination's phase modulo 128 inside the slot.
 __device__ __forceinline__ uint64_t slot_base(uint64_t slot, uint64_t b0, int64_t x0) {
-  return slot + ((b0 + uint64_t(x0)) & 15u) - uint64_t(x0);
+  return slot + ((b0 + uint64_t(x0)) & 127u) - uint64_t(x0);
 }
 
 __device__ __forceinline__ uint64_t tag(uint32_t epoch, uint64_t v) {
@@ -198,7 +198,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       d.b[0] = to_own ? own : scat;
 #pragma unroll
       for (int k = 1; k < kMaxRanks + 1; ++k) d.b[k] = scat;
-      atom::tile<Op, kU, kNTL, kNTS>(s, d, x0, x1);
+      atom::tile<Op, kU, kNTL>(s, d, x0, x1);
       snac::drain_workgroup();
       if (threadIdx.x == 0) {
         for (int k = 0; k < sj.n_stage; ++k)
@@ -240,7 +240,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       d.n = 1;
 #pragma unroll
       for (int q = 0; q < kMaxRanks + 1; ++q) d.b[q] = slot_base(o.data, b0, x0);
-      atom::tile<atom::CopyOp, kU, kNTL, false>(s, d, x0, x1);
+      atom::tile<atom::CopyOp, kU, kNTL>(s, d, x0, x1);
       __syncthreads();
       if (threadIdx.x == 0) {
         const bool withhold = sp.withhold > 0 && ring == 0 && m + 1 == sp.withhold;
@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       d.n = 1;
 #pragma unroll
       for (int q = 0; q < kMaxRanks + 1; ++q) d.b[q] = uint64_t(p.out[dst]) + uint64_t(jb.dst_off);
-      atom::tile<atom::CopyOp, kU, false, kNTS>(s, d, x0, x1);
+      atom::tile<atom::CopyOp, kU, kNTS>(s, d, x0, x1);
       snac::drain_workgroup();
       if (threadIdx.x == 0) snac::add_rlx(o.credit, uint64_t(1));
     }
