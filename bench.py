@@ -20,6 +20,8 @@ HIP events, the roofline of the dominant kernel, and the oracle's
 throughput on the host cores on a bounded sample.
 """
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -67,6 +69,35 @@ def collective_shapes(T):
     return shapes
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zs_kernels_seven_collectives_1GiB_hbm_counters.txt")
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: counters taken from other sources do not apply."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "reduce_atom_02_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, T, names, variant):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by a known-size copy), or
+    None when that summary was taken on other sources or another workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            line = next(l for l in f if l.startswith("traffic_json: "))
+        rec = json.loads(line[len("traffic_json: "):])
+    except (OSError, StopIteration, ValueError):
+        return None
+    if (rec.get("source_hash") != kernel_source_hash() or rec.get("T") != T
+            or rec.get("names") != list(names) or variant != "zs"):
+        return None
+    k = rec["kernels"].get(kernel)
+    return None if k is None else int(k["traffic_per_launch"])
+
+
 def kernel_of(name):
     return "zs_kernel<SumBf16>" if SPECS[name][2] == "sum" else "zs_kernel<CopyOp>"
 
@@ -97,6 +128,31 @@ def cpu_baseline(T_sample, names):
                       % (T_sample >> 20, "the timed size", total_t)}
 
 
+def calibrate_copy(purlin, T, steps, warmup, dev):
+    import torch
+    src = torch.empty(T // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        purlin.stream_copy(dst, src, T, stream=stream)
+    ev = []
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        purlin.stream_copy(dst, src, T, stream=stream)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+    p50 = ts[len(ts) // 2]
+    print(json.dumps({"calibration": "stream_copy_kernel", "bytes_read": T, "bytes_written": T,
+                      "launches": steps + warmup, "p50_us": round(p50 * 1e6, 2),
+                      "GBps_read_plus_write": round(2 * T / p50 / 1e9, 1),
+                      "hbm_frac": round(2 * T / p50 / HBM_PEAK, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,8 +161,11 @@ def main():
     ap.add_argument("--size", type=int, default=1 << 30, help="T, bytes per rank")
     ap.add_argument("--variant", choices=["zs", "staged"], default="zs")
     ap.add_argument("--only", default="", help="comma-separated subset of collectives")
-    ap.add_argument("--cpu-sample", type=int, default=64 << 20,
+    ap.add_argument("--cpu-sample", type=int, default=256 << 20,
                     help="T of the oracle sample, bytes per rank (0 skips it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="time only the plain 128-bit streaming copy of --size bytes "
+                         "(HBM counter calibration and copy ceiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the P ranks are emulated in one GPU's HBM and no "
@@ -125,6 +184,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     T = args.size
+    if args.calibrate_copy:
+        calibrate_copy(purlin, T, args.steps, args.warmup, dev)
+        return
     names = [n for n in SPECS if not args.only or n in args.only.split(",")]
     shapes = collective_shapes(T)
     purlin.set_policy(zero_staging=args.variant)
@@ -216,7 +278,8 @@ def main():
         "hbm_frac": round(total_bmin / elapsed / HBM_PEAK, 4),
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
+                     "frac": round(achieved * 1e9 / HBM_PEAK, 4),
+                     "traffic": measured_traffic(dom_name, T, names, args.variant),
                      "launches": dom["launches"],
                      "avg_launch_us": round(dom["time"] / dom["launches"] * 1e6, 2),
                      "bytes_per_launch": dom["bytes"] // dom["launches"]},

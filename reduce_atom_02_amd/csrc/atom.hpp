@@ -204,12 +204,13 @@ __device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const u
   u32x4 x[kU][kS];
 #pragma unroll
   for (int k = 0; k < kU; ++k) {
-    const uint32_t u = u0 + uint32_t(k) * kThreads + tid;
-    if (!kGuard || u < nunits) {
-      const uint64_t o = uint64_t(u * 16u);
+    uint32_t u = u0 + uint32_t(k) * kThreads + tid;
+    // The tail pass loads a clamped unit instead of branching around the
+    // load: a branch per load would make every load wait for the previous.
+    if (kGuard && u >= nunits) u = nunits - 1;
+    const uint64_t o = uint64_t(u * 16u);
 #pragma unroll
-      for (int i = 0; i < kS; ++i) x[k][i] = ld16<kNTL>(sa[i] + o);
-    }
+    for (int i = 0; i < kS; ++i) x[k][i] = ld16<kNTL>(sa[i] + o);
   }
 #pragma unroll
   for (int k = 0; k < kU; ++k) {
@@ -270,13 +271,11 @@ __device__ __forceinline__ void pass_shifted(const uint64_t *base, const uint32_
     const uint32_t u = u0 + (uint32_t(k) * (kThreads / 64) + wave) * kRow + lane;
 #pragma unroll
     for (int i = 0; i < kS; ++i) {
-      if constexpr (kGuard) {
-        x[k][i] = u32x4{0u, 0u, 0u, 0u};
-        if (lane <= kRow && u < lim[i]) x[k][i] = ld16<kNTL>(base[i] + uint64_t(u * 16u));
-      } else {
-        // lanes past 56 read blocks of the next row, still inside the tile
-        x[k][i] = ld16<kNTL>(base[i] + uint64_t(u * 16u));
-      }
+      // Unguarded passes: lanes past 56 read blocks of the next row, still
+      // inside the tile.  The tail pass clamps every lane to the source's
+      // last block instead of branching (see pass_aligned).
+      const uint32_t uc = (kGuard && u >= lim[i]) ? lim[i] - 1 : u;
+      x[k][i] = ld16<kNTL>(base[i] + uint64_t(uc * 16u));
     }
   }
 #pragma unroll
@@ -355,7 +354,6 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
   uint32_t nhead = ((128u - uint32_t((b0 + uint64_t(x16)) & 127u)) & 127u) >> 4;
   if (nhead > nall) nhead = nall;
   const uint32_t nbody = nall - nhead;
-  const int64_t x128 = x16 + int64_t(nhead) * 16;
   const int64_t xb = x16 + int64_t(nall) * 16;
   if (x16 > x0) elements<Op>(s, d, x0, x16);
   if (x1 > xb) elements<Op>(s, d, xb, x1);

@@ -280,12 +280,27 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
 }
 
 // ---- calibration copy ------------------------------------------------------
+// A plain streaming copy with the same access style as the collectives (16-byte
+// nontemporal loads and stores, 4 per lane in flight): the reference for HBM
+// counters and the copy ceiling the collectives are compared with.
 __global__ void __launch_bounds__(kThreads) stream_copy_kernel(atom::u32x4 *dst,
                                                                 const atom::u32x4 *src,
                                                                 int64_t n16) {
-  const int64_t stride = int64_t(gridDim.x) * kThreads;
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += stride)
-    dst[i] = src[i];
+  constexpr int kU = 4;
+  const int64_t stride = int64_t(gridDim.x) * kThreads * kU;
+  for (int64_t b = int64_t(blockIdx.x) * kThreads * kU + threadIdx.x; b < n16; b += stride) {
+    atom::u32x4 v[kU];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const int64_t i = b + int64_t(k) * kThreads;
+      if (i < n16) v[k] = atom::ld16<true>(uint64_t(src + i));
+    }
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const int64_t i = b + int64_t(k) * kThreads;
+      if (i < n16) atom::st16<true>(uint64_t(dst + i), v[k]);
+    }
+  }
 }
 
 template <class Op, int kU, bool kNT>

@@ -168,13 +168,28 @@ KernelKind kind_of(purlin_op op, purlin_dtype dtype) {
   return dtype == PURLIN_F32 ? KernelKind::kSumF32 : KernelKind::kSumBf16;
 }
 
-// Chunk size when the policy leaves it open: small chunks while the message
-// cannot fill the resident grid, growing so that large messages get about
-// 16 chunks per resident workgroup, never above 64 KiB.
-int64_t auto_chunk(int64_t out_bytes, int capacity) {
-  int64_t c = 4096;
-  while (c < (int64_t(64) << 10) && out_bytes / c > int64_t(capacity) * 16) c *= 2;
-  return c;
+// Policy table ("codesign policies tune execution", Figure 1 caption), from
+// sweeps of grid, chunk and unroll at 64 MiB - 1 GiB per rank on MI355X:
+// reductions and broadcasts prefer about two workgroups per CU and short
+// chunks, point-to-point copies four per CU and longer chunks.  Fewer, deeper
+// workgroups keep fewer DRAM pages open than a full grid.
+struct AutoPolicy {
+  int wgs_per_rank;
+  int64_t chunk;
+  int unroll_sel;
+};
+
+AutoPolicy auto_policy(KernelKind kind, bool broadcast) {
+  if (kind != KernelKind::kCopy) return {64, int64_t(16) << 10, 0};
+  if (broadcast) return {64, int64_t(16) << 10, 0};
+  return {128, int64_t(64) << 10, 0};
+}
+
+// Small messages get smaller chunks, so that the default grid still sees
+// about four chunks per workgroup; never below 4 KiB.
+int64_t fit_chunk(int64_t chunk, int64_t job_bytes, int64_t grid) {
+  while (chunk > 4096 && job_bytes / chunk < grid * 4) chunk /= 2;
+  return chunk;
 }
 
 void fill_tiles(LaunchPlan &lp, const std::vector<Job> &jobs, int64_t chunk) {
@@ -264,17 +279,22 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
   const purlin_policy pol = effective_policy();
   const KernelKind kind = kind_of(op, dtype);
   const bool nt = nt_env(true);
-  int unroll_sel = unroll_env();
-  if (unroll_sel < 0 || unroll_sel > 2) unroll_sel = 1;
 
   std::vector<Job> jobs;
   std::vector<int> owners;
   launch_jobs(*d, reinterpret_cast<char *const *>(out->bufs), &jobs, &owners);
 
   const bool staged = pol.zero_staging == PURLIN_STAGING_STAGED;
+  bool broadcast = false;
+  int64_t job_bytes = 0;
+  for (const Job &jb : jobs) {
+    job_bytes += jb.nbytes;
+    broadcast |= jb.dst < 0;
+  }
+  const AutoPolicy ap = auto_policy(kind, broadcast);
+  int unroll_sel = unroll_env();
+  if (unroll_sel < 0 || unroll_sel > 2) unroll_sel = ap.unroll_sel;
   const int capacity = ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel);
-  int64_t out_bytes = 0;
-  for (const Job &jb : jobs) out_bytes += jb.nbytes * (jb.dst < 0 ? P : 1);
 
   if (++ds->epoch == 0) ds->epoch = 1;  // epoch 0 would match freshly cleared flags
   const int64_t wd_ns = pol.watchdog_ns ? pol.watchdog_ns : kDefaultWatchdogNs;
@@ -296,12 +316,14 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
 
   hipError_t err;
   if (!staged) {
-    const int64_t chunk = pol.chunk_bytes ? pol.chunk_bytes : auto_chunk(out_bytes, capacity);
+    const int64_t want_grid =
+        std::min<int64_t>(capacity, int64_t(P) * (pol.wgs_per_rank ? pol.wgs_per_rank
+                                                                    : ap.wgs_per_rank));
+    const int64_t chunk =
+        pol.chunk_bytes ? pol.chunk_bytes : fit_chunk(ap.chunk, job_bytes, want_grid);
     lp.chunk_bytes = chunk;
     fill_tiles(lp, jobs, chunk);
-    int grid = std::min<int64_t>(lp.total_tiles, capacity);
-    if (pol.wgs_per_rank) grid = std::min<int64_t>(grid, int64_t(P) * pol.wgs_per_rank);
-    grid = std::max(grid, 1);
+    const int grid = int(std::max<int64_t>(1, std::min<int64_t>(lp.total_tiles, want_grid)));
     lp.sync = pol.sync == 2 ? 0 : 1;
     lp.exit_expect = ds->exit_total[(ds->epoch - 1u) & 1u];
     err = launch_zs(lp, kind, nt, unroll_sel, grid, stream);
@@ -397,7 +419,7 @@ purlin_status purlin_stream_copy(void *dst, const void *src, int64_t bytes, hipS
   DeviceState *ds = nullptr;
   purlin_status st = device_state(&ds);
   if (st != PURLIN_OK) return st;
-  const int grid = ds->cus * 8;
+  const int grid = ds->cus * 2;
   return launch_stream_copy(dst, src, bytes, grid, stream) == hipSuccess ? PURLIN_OK
                                                                            : PURLIN_ERR_HIP;
 }
