@@ -153,6 +153,91 @@ def calibrate_copy(purlin, T, steps, warmup, dev):
                       "hbm_frac": round(2 * T / p50 / HBM_PEAK, 4)}), flush=True)
 
 
+def sweep(purlin, T_max, variant, path, dev):
+    """p50 per-call latency from HIP events, T = 1 KiB .. T_max per rank.
+
+    Latency regime (T <= 512 KiB), warm caches, two figures:
+      p50_us       device latency: a spin kernel is queued first, so every
+                   timed launch is already enqueued when the GPU reaches it
+                   and the events bracket only GPU work (back to back);
+      submit_p50_us  the same call timed from an idle GPU, so host-side
+                   argument marshalling (Python, ctypes) and launch are in it.
+    Bandwidth regime (T >= 1 MiB): a 1 GiB fill runs between calls, outside
+    the events, so inputs come from HBM, not the 256 MiB Infinity Cache;
+    100 timed calls up to 64 MiB, 20 above.  The empty-kernel floor is
+    measured both ways too."""
+    import torch
+    import workloads
+    purlin.set_policy(zero_staging=variant)
+    stream = torch.cuda.current_stream()
+    n_max = T_max // ESZ
+    ins = [workloads.device_values(n_max, "normal", "bf16", 3, r, dev) for r in range(P)]
+    shapes_max = collective_shapes(T_max)
+    out_len = max(max(s["outs"]) for s in shapes_max.values())
+    outs = [torch.empty(out_len, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    empty = torch.empty(1, device=dev)
+
+    def timed(fn, reps, cold, queued=False):
+        ev = []
+        if queued:
+            torch.cuda._sleep(20_000_000)          # ~10 ms at 2.4 GHz: covers the enqueues
+        for _ in range(reps):
+            if cold:
+                flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+        return ts[len(ts) // 10], ts[len(ts) // 2], ts[(9 * len(ts)) // 10]
+
+    floor = timed(lambda: empty.add_(0), 200, False, queued=True)[1]
+    floor_submit = timed(lambda: empty.add_(0), 200, False)[1]
+    rows = []
+    with open(path, "w") as f:
+        for lg in range(10, T_max.bit_length()):
+            T = 1 << lg
+            shapes = collective_shapes(T)
+            cold = T >= (1 << 20)
+            reps = 200 if not cold else (100 if T <= (64 << 20) else 20)
+            for name, s in shapes.items():
+                in_n, out_n, op = SPECS[name]
+                xi = [ins[r][:s["ins"][r]] for r in range(P)]
+                yo = [outs[r][:s["outs"][r]] for r in range(P)]
+
+                def fn():
+                    purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
+
+                for _ in range(3):
+                    fn()
+                submit = None
+                if cold:
+                    p10, p50, p90 = timed(fn, reps, cold)
+                else:
+                    p10, p50, p90 = timed(fn, 200, cold, queued=True)
+                    submit = round(timed(fn, 200, cold)[1] * 1e6, 2)
+                purlin.check(stream)
+                info = purlin.last_launch()
+                row = {"collective": name, "variant": variant, "dtype": "bf16", "P": P,
+                       "T_bytes": T, "cold": cold, "reps": reps,
+                       "p10_us": round(p10 * 1e6, 2), "p50_us": round(p50 * 1e6, 2),
+                       "p90_us": round(p90 * 1e6, 2), "algbw_GBps": round(T / p50 / 1e9, 2),
+                       "hbm_frac": round(s["bmin"] / p50 / HBM_PEAK, 4), "bmin": s["bmin"],
+                       "submit_p50_us": submit,
+                       "grid": info["grid"], "chunk_bytes": info["chunk_bytes"],
+                       "empty_kernel_p50_us": round(floor * 1e6, 2),
+                       "empty_kernel_submit_p50_us": round(floor_submit * 1e6, 2)}
+                f.write(json.dumps(row) + "\n")
+                f.flush()
+                rows.append(row)
+            print("T=%d KiB done" % (T >> 10), flush=True)
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +248,9 @@ def main():
     ap.add_argument("--only", default="", help="comma-separated subset of collectives")
     ap.add_argument("--cpu-sample", type=int, default=256 << 20,
                     help="T of the oracle sample, bytes per rank (0 skips it)")
+    ap.add_argument("--sweep", default="",
+                    help="write p50 latency / algorithm bandwidth of every collective over "
+                         "T = 1 KiB .. --size to this JSONL file instead of the step benchmark")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time only the plain 128-bit streaming copy of --size bytes "
                          "(HBM counter calibration and copy ceiling)")
@@ -186,6 +274,9 @@ def main():
     T = args.size
     if args.calibrate_copy:
         calibrate_copy(purlin, T, args.steps, args.warmup, dev)
+        return
+    if args.sweep:
+        sweep(purlin, T, args.variant, args.sweep, dev)
         return
     names = [n for n in SPECS if not args.only or n in args.only.split(",")]
     shapes = collective_shapes(T)

@@ -340,12 +340,12 @@ __device__ __forceinline__ void units(const uint64_t *sa, int ns, const uint64_t
 //   [x16, x128)  < 8 units before the first 128-byte boundary: plain stores
 //   [x128, xb)   the body: whole lines, nontemporal stores when kNT
 //   [xb, x1)     < 16 bytes of tail: element ops
-// Loads are nontemporal only when every source sits on the same 128-byte
-// phase as the destinations: a line shared by two wavefronts is then never
-// fetched twice, which the L2 would otherwise prevent.  A tile spans less
-// than 4 GiB.
+// Loads are nontemporal when every source sits on the destinations' 128-byte
+// phase, or when nt_any_phase asks for it (measured faster for misaligned
+// variable-length partitions too).  A tile spans less than 4 GiB.
 template <class Op, int kU, bool kNT>
-__device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1) {
+__device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
+                                     bool nt_any_phase = false) {
   if (x1 <= x0) return;
   const uint64_t b0 = d.b[0];
   int64_t x16 = x0 + int64_t((16u - uint32_t((b0 + uint64_t(x0)) & 15u)) & 15u);
@@ -378,7 +378,8 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
   for (int i = 0; i < kMaxRanks; ++i) sa[i] += uint64_t(nhead) * 16u;
 #pragma unroll
   for (int j = 0; j < kMaxRanks + 1; ++j) db[j] += uint64_t(nhead) * 16u;
-  if (kNT && phase == 0) units<Op, kU, true, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
+  if (kNT && (phase == 0 || nt_any_phase))
+    units<Op, kU, true, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
   else units<Op, kU, false, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
 }
 

@@ -25,6 +25,19 @@ __device__ __forceinline__ void job_srcs(const LaunchPlan &p, const Job &jb, ato
   }
 }
 
+// Index of the job holding tile t: the last j with tile_begin[j] <= t
+// (binary search over the prefix table, so a workgroup far down the list
+// does not walk it one dependent load at a time).
+__device__ __forceinline__ int job_of_tile(const LaunchPlan &p, int t) {
+  int lo = 0, hi = p.njobs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.tile_begin[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // Job byte range of tile tl (of ntl) of a job of n bytes whose first
 // destination byte is at address b0: tile 0 also takes the bytes before the
 // first 128-byte boundary, so every later tile starts on a line.
@@ -50,9 +63,10 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
   // A workgroup whose entry wait failed skips its tiles but still counts
   // itself out, so the next launch's exit check is not poisoned.
   const bool run = !p.sync || snac::entry(p);
-  int j = 0;
-  for (int t = run ? int(blockIdx.x) : p.total_tiles; t < p.total_tiles; t += gridDim.x) {
-    while (t >= p.tile_begin[j + 1]) ++j;
+  int t = run ? int(blockIdx.x) : p.total_tiles;
+  int j = t < p.total_tiles ? job_of_tile(p, t) : 0;
+  for (; t < p.total_tiles; t += gridDim.x) {
+    if (t >= p.tile_begin[j + 1]) j = job_of_tile(p, t);
     const Job jb = p.jobs[j];
     atom::Srcs s;
     job_srcs(p, jb, s);
@@ -71,7 +85,7 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     int64_t x0, x1;
     tile_bounds(d.b[0], jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
                 p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
-    atom::tile<Op, kU, kNTL>(s, d, x0, x1);
+    atom::tile<Op, kU, kNTL>(s, d, x0, x1, p.nt_any_phase != 0);
   }
   if (p.sync) snac::exit_notify(p);
 }
@@ -120,8 +134,16 @@ template <class Op, int kU, bool kNTL, bool kNTS>
 __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
   const LaunchPlan &p = sp.base;
   __shared__ int ok;
+  // job of this workgroup: the last j with role_begin[j] <= blockIdx.x
   int j = 0;
-  while (j + 1 < p.njobs && int(blockIdx.x) >= sp.sj[j + 1].role_begin) ++j;
+  {
+    int hi = p.njobs - 1;
+    while (j < hi) {
+      const int mid = (j + hi + 1) >> 1;
+      if (sp.sj[mid].role_begin <= int(blockIdx.x)) j = mid;
+      else hi = mid - 1;
+    }
+  }
   const StagedJob sj = sp.sj[j];
   const Job jb = p.jobs[j];
   const int L = sp.lanes;

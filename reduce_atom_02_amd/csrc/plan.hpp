@@ -60,6 +60,7 @@ struct LaunchPlan {
   uint64_t watchdog_ticks;  // bound of every spin wait, in wall-clock ticks
   uint32_t exit_expect;     // exit-counter value of the previous launch (sync)
   int32_t sync;             // 1: entry/exit notify flags on
+  int32_t nt_any_phase;     // 1: nontemporal loads even for sources off the line phase
   int32_t tile_begin[kMaxJobs + 1];
   Job jobs[kMaxJobs];
 };

@@ -269,6 +269,8 @@ purlin_status derive_cached(purlin_naming in_naming, purlin_naming out_naming, p
   CacheEntry e;
   purlin_status s = derive(in_naming, out_naming, op, dtype, P, counts, displs, &e.d);
   if (s != PURLIN_OK) return s;
+  static uint64_t next_id = 0;
+  e.d.id = ++next_id;
   e.in_n = in_naming; e.out_n = out_naming; e.op = op; e.dtype = dtype; e.P = P;
   e.has_displs = displs != nullptr;
   e.counts.assign(counts, counts + nn);

@@ -16,6 +16,7 @@ struct ByteRange {
 // What a (naming, naming, op, dtype, P, counts, displs) specification
 // derives into.  It depends on no pointer, so it is cached across calls.
 struct Derived {
+  uint64_t id = 0;                   // unique per cached derivation (never reused)
   int P = 0;
   int esz = 0;
   purlin_op op = PURLIN_OP_COPY;

@@ -187,3 +187,25 @@ def test_large_unaligned_tiles(purlin, name, dtype, chunk):
             os.environ.pop("PURLIN_UNROLL", None)
     purlin.set_policy(chunk_bytes=chunk, zero_staging="staged", depth=2)
     oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, None, shifts, out_shift)
+
+
+def test_overlap_checks_survive_the_pointer_cache(purlin):
+    """The per-call overlap check is skipped only for the same plan and buffers."""
+    import torch
+    P = 8
+    ins = [torch.zeros(64, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    outs = [torch.zeros(64 * P, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    purlin.all_gather([x[:8] for x in ins], [y[:64] for y in outs], [8] * P)
+    purlin.check()
+    # same buffers, another plan whose output partitions overlap
+    displs = [0] * P + [0, 8, 16, 24, 32, 40, 48, 50]
+    with pytest.raises(purlin.PurlinError) as e:
+        purlin.collective([x[:8] for x in ins], [y[:64] for y in outs], "by_rank", "by_index",
+                          "copy", [8] * P, displs)
+    assert e.value.status == "INVALID_ARG"
+    # same plan as the valid call, but an input inside an output
+    with pytest.raises(purlin.PurlinError) as e:
+        purlin.all_gather([outs[r][60:68] for r in range(P)], [y[:64] for y in outs], [8] * P)
+    assert e.value.status == "INVALID_ARG"
+    purlin.all_gather([x[:8] for x in ins], [y[:64] for y in outs], [8] * P)
+    purlin.check()
