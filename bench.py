@@ -128,6 +128,46 @@ def cpu_baseline(T_sample, names):
                       % (T_sample >> 20, "the timed size", total_t)}
 
 
+def ceilings(purlin, T, steps, dev):
+    """HBM ceiling of each collective's access pattern: n read streams and m
+    write streams, 16-byte nontemporal accesses, no planning or flags
+    (purlin_stream_pattern); a 1 GiB fill between calls (cold caches).
+    1->1 over P*T bytes is AllToAll's pattern and footprint, 1->8 of T bytes
+    AllGather's, 8->1 ReduceScatter's, 8->8 AllReduce's."""
+    import torch
+    big_src = torch.ones(P * T // 4, dtype=torch.float32, device=dev)
+    big_dst = torch.empty(P * T // 4, dtype=torch.float32, device=dev)
+    srcs = [big_src[r * (T // 4):(r + 1) * (T // 4)] for r in range(P)]
+    dsts = [big_dst[r * (T // 4):(r + 1) * (T // 4)] for r in range(P)]
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {}
+    # (sources, destinations, bytes per stream): the 1->1 stream spans the
+    # P*T bytes AllToAll moves, since the sustained rate drops with footprint
+    for nr, nw, nbytes, label in ((1, 1, P * T, "1->1 (alltoall)"),
+                                  (1, 8, T, "1->8 (allgather)"),
+                                  (8, 1, T, "8->1 (reducescatter)"),
+                                  (8, 8, T, "8->8 (allreduce)")):
+        s_, d_ = ([big_src], [big_dst]) if nr == 1 and nw == 1 else (srcs[:nr], dsts[:nw])
+        purlin.stream_pattern(s_, d_, nbytes, stream=stream)
+        ev = []
+        for _ in range(steps):
+            flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            purlin.stream_pattern(s_, d_, nbytes, stream=stream)
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+        p50 = ts[len(ts) // 2]
+        out[label] = round((nr + nw) * nbytes / p50 / HBM_PEAK, 4)
+    del srcs, dsts, big_src, big_dst, flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def calibrate_copy(purlin, T, steps, warmup, dev):
     import torch
     src = torch.empty(T // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -251,6 +291,11 @@ def main():
     ap.add_argument("--sweep", default="",
                     help="write p50 latency / algorithm bandwidth of every collective over "
                          "T = 1 KiB .. --size to this JSONL file instead of the step benchmark")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="time the bare read/write patterns of the collectives (1->1, 1->8, "
+                         "8->1, 8->8 streams of --size bytes) with cold caches")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the pattern-ceiling measurement after the timed steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time only the plain 128-bit streaming copy of --size bytes "
                          "(HBM counter calibration and copy ceiling)")
@@ -277,6 +322,10 @@ def main():
         return
     if args.sweep:
         sweep(purlin, T, args.variant, args.sweep, dev)
+        return
+    if args.ceilings:
+        print(json.dumps({"ceilings_hbm_frac": ceilings(purlin, T, args.steps, dev),
+                          "T_bytes_per_stream": T, "cold": True}), flush=True)
         return
     names = [n for n in SPECS if not args.only or n in args.only.split(",")]
     shapes = collective_shapes(T)
@@ -348,6 +397,11 @@ def main():
     total_bmin = sum(shapes[n_]["bmin"] for n_ in names) * args.steps
     value = total_T / elapsed / 1e9
     cpu = cpu_baseline(min(args.cpu_sample, T), names) if args.cpu_sample else None
+    del ins, outs
+    torch.cuda.empty_cache()
+    # context, after the timed region: what HBM sustains for each collective's
+    # bare read/write pattern at this size (cold caches)
+    pattern = ceilings(purlin, T, 5, dev) if not args.no_ceilings else None
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -375,6 +429,7 @@ def main():
                      "avg_launch_us": round(dom["time"] / dom["launches"] * 1e6, 2),
                      "bytes_per_launch": dom["bytes"] // dom["launches"]},
         "cpu_baseline": cpu,
+        "pattern_ceilings_hbm_frac": pattern,
         "collectives": per,
     }
     print(json.dumps(out), flush=True)

@@ -12,7 +12,9 @@
 //    destination's modulo 16 is read in aligned 16-byte blocks, and each
 //    lane shifts its block and its neighbour lane's block into place in
 //    registers (lane shuffle + v_alignbyte), never by unaligned or byte-wise
-//    memory accesses;
+//    memory accesses; wavefront rows follow the destination's 128-byte
+//    lines when there are several destinations and the sources' lines when
+//    there is one, so the larger side never touches a line twice;
 //  * the reduce is a per-lane fold over the sources in ascending rank, in
 //    fp32 (bf16 widened exactly), with one final round to nearest even for
 //    a bf16 output; there is no cross-lane tree, so the summation order is
@@ -268,7 +270,7 @@ __device__ __forceinline__ void pass_shifted(const uint64_t *base, const uint32_
   u32x4 x[kU][kS];
 #pragma unroll
   for (int k = 0; k < kU; ++k) {
-    const uint32_t u = u0 + (uint32_t(k) * (kThreads / 64) + wave) * kRow + lane;
+    const uint32_t u = u0 + (wave * kU + uint32_t(k)) * kRow + lane;
 #pragma unroll
     for (int i = 0; i < kS; ++i) {
       // Unguarded passes: lanes past 56 read blocks of the next row, still
@@ -280,7 +282,7 @@ __device__ __forceinline__ void pass_shifted(const uint64_t *base, const uint32_
   }
 #pragma unroll
   for (int k = 0; k < kU; ++k) {
-    const uint32_t u = u0 + (uint32_t(k) * (kThreads / 64) + wave) * kRow + lane;
+    const uint32_t u = u0 + (wave * kU + uint32_t(k)) * kRow + lane;
     u32x4 y[kS];
 #pragma unroll
     for (int i = 0; i < kS; ++i) y[i] = funnel(x[k][i], next_lane(x[k][i]), sh[i]);
@@ -302,8 +304,12 @@ __device__ __forceinline__ void pass_shifted(const uint64_t *base, const uint32_
 // row loads 57 consecutive aligned 16-byte blocks of each source, one per
 // lane, takes its right neighbour's block with a lane shuffle, and shifts
 // the pair into place, producing 56 destination units: 896 bytes, seven
-// whole 128-byte lines, so no store writes part of a line.  Every source
-// byte is loaded once per row.  Source i's blocks start at the aligned
+// whole 128-byte lines, so no store writes part of a line.  Consecutive rows
+// share one source line, which nontemporal loads fetch from HBM twice (one
+// line in eight more read traffic, measured), even when one wavefront takes
+// the two rows back to back as here; a tile with one destination therefore
+// uses the source-aligned body, and this one serves broadcasts, where the
+// reads are one stream of several.  Source i's blocks start at the aligned
 // address sa[i] - sh[i]; a source with sh[i] > 0 needs one block past its
 // last unit, which holds that unit's last bytes.
 template <class Op, int kU, bool kNTL, bool kNTS>
@@ -327,11 +333,110 @@ __device__ __forceinline__ void body_shifted(const uint64_t *sa, int ns, const u
     pass_shifted<Op, kU, kNTL, kNTS, true>(base, lim, ns, db, nd, nunits, sh, u0);
 }
 
+__device__ __forceinline__ u32x4 lane0(u32x4 v) {
+  u32x4 o;
+  o.x = __builtin_amdgcn_readfirstlane(v.x);
+  o.y = __builtin_amdgcn_readfirstlane(v.y);
+  o.z = __builtin_amdgcn_readfirstlane(v.z);
+  o.w = __builtin_amdgcn_readfirstlane(v.w);
+  return o;
+}
+
+// One pass of the source-aligned body (see body_src_aligned).
+template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard>
+__device__ __forceinline__ void pass_src_aligned(const uint64_t *base, const uint32_t *lim, int ns,
+                                                 uint64_t db, uint32_t nunits, const uint32_t *sh,
+                                                 uint32_t u0) {
+  constexpr int kS = Op::kSum ? kMaxRanks : 1;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t r0 = u0 + wave * kU * 64u;  // this wavefront's rows start here
+  u32x4 edge[kS];
+  u32x4 x[kU][kS];
+  // The block after the wavefront's last row, the same address in every
+  // lane, first and through the cache (see body_src_aligned).
+#pragma unroll
+  for (int i = 0; i < kS; ++i) {
+    uint32_t b = r0 + uint32_t(kU) * 64u;
+    if (b >= lim[i]) b = lim[i] - 1;
+    edge[i] = ld16<false>(base[i] + uint64_t(b) * 16u);
+  }
+#pragma unroll
+  for (int k = 0; k < kU; ++k) {
+    const uint32_t u = r0 + uint32_t(k) * 64u + lane;
+#pragma unroll
+    for (int i = 0; i < kS; ++i) {
+      const uint32_t b = (kGuard && u >= lim[i]) ? lim[i] - 1 : u;
+      x[k][i] = ld16<kNTL>(base[i] + uint64_t(b) * 16u);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kU; ++k) {
+    const uint32_t u = r0 + uint32_t(k) * 64u + lane;
+    u32x4 y[kS];
+#pragma unroll
+    for (int i = 0; i < kS; ++i) {
+      // lane 63's right neighbour: the next row's first block, or the edge
+      const u32x4 after = k + 1 < kU ? lane0(x[k + 1 < kU ? k + 1 : k][i]) : edge[i];
+      u32x4 hi = next_lane(x[k][i]);
+      if (lane == 63u) hi = after;
+      y[i] = funnel(x[k][i], hi, sh[i]);
+    }
+    if (!kGuard || u < nunits) {
+      u32x4 v;
+      if constexpr (!Op::kSum) v = y[0];
+      else if constexpr (Op::kElem == 4) v = fold_f32(y, ns);
+      else v = fold_bf16(y, ns);
+      st16<kNTS>(db + uint64_t(u) * 16u, v);
+    }
+  }
+}
+
+// Body for one destination whose sources are not aligned like it
+// (variable-length partitions at arbitrary element offsets).  Rows are
+// aligned to the *sources'* 128-byte lines: a wavefront row loads 64
+// consecutive aligned blocks, exactly eight lines of source 0 and no block
+// of any other row, and produces the 64 destination units those blocks
+// cover; each wavefront takes kU consecutive rows.  Lane 63 of a row needs
+// one block past the row: the next row's first block, read from lane 0, or
+// after the wavefront's last row one extra block.  That extra block lies in
+// a line another wavefront streams; it is loaded first and as an ordinary
+// (cached) load, which measured fewer HBM bytes and more bandwidth than a
+// nontemporal one or a hand-over in LDS behind a barrier.  The stores are
+// off the destination's line phase: a wavefront's first and last lines are
+// shared with neighbour rows, which costs less than the alternative of
+// rows aligned to the destination, where every row re-reads a source line.
+// sa[] holds the sources at the first unit, where source 0's aligned blocks
+// start on a 128-byte line; block b of source i is at sa[i] - sh[i] + 16 b,
+// and a source with sh[i] > 0 needs block nunits too, which holds its last
+// unit's last bytes.  An unguarded pass reads blocks up to u0 + kPass, so it
+// needs u0 + kPass < nunits.
+template <class Op, int kU, bool kNTL, bool kNTS>
+__device__ __forceinline__ void body_src_aligned(const uint64_t *sa, int ns, uint64_t db,
+                                                 uint32_t nunits, const uint32_t *sh) {
+  constexpr int kS = Op::kSum ? kMaxRanks : 1;
+  constexpr uint32_t kPass = 64u * (kThreads / 64) * kU;
+  uint64_t base[kS];
+  uint32_t lim[kS];
+#pragma unroll
+  for (int i = 0; i < kS; ++i) {
+    base[i] = sa[i] - sh[i];
+    lim[i] = nunits + (sh[i] ? 1u : 0u);
+  }
+  uint32_t u0 = 0;
+  for (; u0 + kPass < nunits; u0 += kPass)
+    pass_src_aligned<Op, kU, kNTL, kNTS, false>(base, lim, ns, db, nunits, sh, u0);
+  for (; u0 < nunits; u0 += kPass)
+    pass_src_aligned<Op, kU, kNTL, kNTS, true>(base, lim, ns, db, nunits, sh, u0);
+}
+
 template <class Op, int kU, bool kNTL, bool kNTS>
 __device__ __forceinline__ void units(const uint64_t *sa, int ns, const uint64_t *db, int nd,
                                       uint32_t n, const uint32_t *sh, bool aligned) {
+  // the realigning body takes at least two consecutive rows per wavefront
+  constexpr int kUs = kU < 2 ? 2 : kU;
   if (aligned) body_aligned<Op, kU, kNTL, kNTS>(sa, ns, db, nd, n);
-  else body_shifted<Op, kU, kNTL, kNTS>(sa, ns, db, nd, n, sh);
+  else body_shifted<Op, kUs, kNTL, kNTS>(sa, ns, db, nd, n, sh);
 }
 
 // One tile: job bytes [x0, x1).  x0 is 0 or on a 128-byte boundary of the
@@ -340,8 +445,10 @@ __device__ __forceinline__ void units(const uint64_t *sa, int ns, const uint64_t
 //   [x16, x128)  < 8 units before the first 128-byte boundary: plain stores
 //   [x128, xb)   the body: whole lines, nontemporal stores when kNT
 //   [xb, x1)     < 16 bytes of tail: element ops
-// Loads are nontemporal when every source sits on the destinations' 128-byte
-// phase, or when nt_any_phase asks for it (measured faster for misaligned
+// One destination with sources off its 16-byte phase instead takes the
+// source-aligned body after a head up to source 0's first line.  Loads are
+// nontemporal when every source sits on the destinations' 128-byte phase,
+// or when nt_any_phase asks for it (measured faster for misaligned
 // variable-length partitions too).  A tile spans less than 4 GiB.
 template <class Op, int kU, bool kNT>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
@@ -351,9 +458,6 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
   int64_t x16 = x0 + int64_t((16u - uint32_t((b0 + uint64_t(x0)) & 15u)) & 15u);
   if (x16 > x1) x16 = x1;
   const uint32_t nall = uint32_t((x1 - x16) >> 4);
-  uint32_t nhead = ((128u - uint32_t((b0 + uint64_t(x16)) & 127u)) & 127u) >> 4;
-  if (nhead > nall) nhead = nall;
-  const uint32_t nbody = nall - nhead;
   const int64_t xb = x16 + int64_t(nall) * 16;
   if (x16 > x0) elements<Op>(s, d, x0, x16);
   if (x1 > xb) elements<Op>(s, d, xb, x1);
@@ -372,14 +476,32 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
 #pragma unroll
   for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(x16);
   const bool aligned = any == 0;
+  const bool ntl = kNT && (phase == 0 || nt_any_phase);
+  if (!aligned && d.n == 1) {
+    uint32_t nh = ((128u - uint32_t((sa[0] - sh[0]) & 127u)) & 127u) >> 4;
+    if (nh > nall) nh = nall;
+    if (nh) units<Op, kU, false, false>(sa, s.n, db, 1, nh, sh, false);
+    if (nall == nh) return;
+#pragma unroll
+    for (int i = 0; i < kMaxRanks; ++i) sa[i] += uint64_t(nh) * 16u;
+    const uint64_t d1 = db[0] + uint64_t(nh) * 16u;
+    // a sum holds eight sources per row, so two rows per wavefront (more
+    // measured slower); a copy holds one and takes the tile's unroll
+    constexpr int kUr = Op::kSum ? 2 : kU;
+    if (ntl) body_src_aligned<Op, kUr, true, kNT>(sa, s.n, d1, nall - nh, sh);
+    else body_src_aligned<Op, kUr, false, kNT>(sa, s.n, d1, nall - nh, sh);
+    return;
+  }
+  uint32_t nhead = ((128u - uint32_t((b0 + uint64_t(x16)) & 127u)) & 127u) >> 4;
+  if (nhead > nall) nhead = nall;
+  const uint32_t nbody = nall - nhead;
   if (nhead) units<Op, kU, false, false>(sa, s.n, db, d.n, nhead, sh, aligned);
   if (nbody == 0) return;
 #pragma unroll
   for (int i = 0; i < kMaxRanks; ++i) sa[i] += uint64_t(nhead) * 16u;
 #pragma unroll
   for (int j = 0; j < kMaxRanks + 1; ++j) db[j] += uint64_t(nhead) * 16u;
-  if (kNT && (phase == 0 || nt_any_phase))
-    units<Op, kU, true, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
+  if (ntl) units<Op, kU, true, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
   else units<Op, kU, false, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
 }
 

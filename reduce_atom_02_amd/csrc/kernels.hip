@@ -325,6 +325,61 @@ __global__ void __launch_bounds__(kThreads) stream_copy_kernel(atom::u32x4 *dst,
   }
 }
 
+// Bare pattern of a collective (ceiling measurement): kR sources added as
+// integers, written to kW destinations, same offset everywhere.
+struct PatternPtrs {
+  const atom::u32x4 *src[kMaxRanks];
+  atom::u32x4 *dst[kMaxRanks];
+};
+
+template <int kR, int kW, int kU>
+__global__ void __launch_bounds__(kThreads) pattern_kernel(PatternPtrs p, int64_t n16) {
+  const int64_t stride = int64_t(gridDim.x) * kThreads * kU;
+  for (int64_t b = int64_t(blockIdx.x) * kThreads * kU + threadIdx.x; b < n16; b += stride) {
+    atom::u32x4 v[kU][kR];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      int64_t i = b + int64_t(k) * kThreads;
+      if (i >= n16) i = n16 - 1;
+#pragma unroll
+      for (int r = 0; r < kR; ++r) v[k][r] = atom::ld16<true>(uint64_t(p.src[r] + i));
+    }
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const int64_t i = b + int64_t(k) * kThreads;
+      atom::u32x4 a = v[k][0];
+#pragma unroll
+      for (int r = 1; r < kR; ++r) a += v[k][r];
+      if (i < n16) {
+#pragma unroll
+        for (int w = 0; w < kW; ++w) atom::st16<true>(uint64_t(p.dst[w] + i), a);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts, int n_dst,
+                          int64_t bytes, int grid, hipStream_t stream) {
+  PatternPtrs p{};
+  for (int r = 0; r < kMaxRanks; ++r) {
+    p.src[r] = static_cast<const atom::u32x4 *>(srcs[r < n_src ? r : 0]);
+    p.dst[r] = static_cast<atom::u32x4 *>(dsts[r < n_dst ? r : 0]);
+  }
+  const int64_t n16 = bytes / 16;
+  void *args[] = {&p, const_cast<int64_t *>(&n16)};
+  const void *fn = nullptr;
+  if (n_src == 1 && n_dst == 1) fn = reinterpret_cast<const void *>(&pattern_kernel<1, 1, 4>);
+  else if (n_src == 1 && n_dst == 8) fn = reinterpret_cast<const void *>(&pattern_kernel<1, 8, 4>);
+  else if (n_src == 8 && n_dst == 1) fn = reinterpret_cast<const void *>(&pattern_kernel<8, 1, 2>);
+  else if (n_src == 8 && n_dst == 8) fn = reinterpret_cast<const void *>(&pattern_kernel<8, 8, 2>);
+  else return hipErrorInvalidValue;
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
+}
+
+namespace {
+
 template <class Op, int kU, bool kNT>
 void *zs_fn() { return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT>); }
 template <class Op, int kU, bool kNT>

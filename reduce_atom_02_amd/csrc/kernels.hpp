@@ -16,6 +16,8 @@ hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStrea
 int unroll_of(KernelKind kind, int unroll_sel);
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,
                               hipStream_t stream);
+hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts, int n_dst,
+                          int64_t bytes, int grid, hipStream_t stream);
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel,
                                int *blocks);
 

@@ -170,19 +170,21 @@ KernelKind kind_of(purlin_op op, purlin_dtype dtype) {
 
 // Policy table ("codesign policies tune execution", Figure 1 caption), from
 // sweeps of grid, chunk and unroll at 64 MiB - 1 GiB per rank on MI355X:
-// reductions and broadcasts prefer about two workgroups per CU and short
-// chunks, point-to-point copies four per CU and longer chunks.  Fewer, deeper
-// workgroups keep fewer DRAM pages open than a full grid.
+// reductions and broadcasts prefer about two workgroups per CU,
+// point-to-point copies four per CU, all with 16 KiB chunks.  Fewer, deeper
+// workgroups keep fewer DRAM pages open than a full grid.  The grid is a
+// whole-device figure (all P ranks share one GPU), so it does not shrink
+// for P < 8.
 struct AutoPolicy {
-  int wgs_per_rank;
+  int grid;
   int64_t chunk;
   int unroll_sel;
 };
 
 AutoPolicy auto_policy(KernelKind kind, bool broadcast) {
-  if (kind != KernelKind::kCopy) return {64, int64_t(16) << 10, 0};
-  if (broadcast) return {64, int64_t(16) << 10, 0};
-  return {128, int64_t(64) << 10, 0};
+  if (kind != KernelKind::kCopy) return {512, int64_t(16) << 10, 0};
+  if (broadcast) return {512, int64_t(16) << 10, 0};
+  return {1024, int64_t(16) << 10, 0};
 }
 
 // Small messages get smaller chunks, so that the default grid still sees
@@ -329,9 +331,8 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
 
   hipError_t err;
   if (!staged) {
-    const int64_t want_grid =
-        std::min<int64_t>(capacity, int64_t(P) * (pol.wgs_per_rank ? pol.wgs_per_rank
-                                                                    : ap.wgs_per_rank));
+    const int64_t want_grid = std::min<int64_t>(
+        capacity, pol.wgs_per_rank ? int64_t(P) * pol.wgs_per_rank : int64_t(ap.grid));
     const int64_t chunk =
         pol.chunk_bytes ? pol.chunk_bytes : fit_chunk(ap.chunk, job_bytes, want_grid);
     lp.chunk_bytes = chunk;
@@ -447,6 +448,24 @@ purlin_status purlin_stream_copy(void *dst, const void *src, int64_t bytes, hipS
   const int grid = ds->cus * 2;
   return launch_stream_copy(dst, src, bytes, grid, stream) == hipSuccess ? PURLIN_OK
                                                                            : PURLIN_ERR_HIP;
+}
+
+purlin_status purlin_stream_pattern(const void *const *srcs, int n_src, void *const *dsts,
+                                    int n_dst, int64_t bytes, hipStream_t stream) {
+  if (!srcs || !dsts || (n_src != 1 && n_src != 8) || (n_dst != 1 && n_dst != 8) ||
+      bytes < 0 || (bytes & 15))
+    return PURLIN_ERR_INVALID_ARG;
+  for (int r = 0; r < n_src; ++r)
+    if (!srcs[r] || (uintptr_t(srcs[r]) & 15)) return PURLIN_ERR_INVALID_ARG;
+  for (int r = 0; r < n_dst; ++r)
+    if (!dsts[r] || (uintptr_t(dsts[r]) & 15)) return PURLIN_ERR_INVALID_ARG;
+  if (bytes == 0) return PURLIN_OK;
+  DeviceState *ds = nullptr;
+  purlin_status st = device_state(&ds);
+  if (st != PURLIN_OK) return st;
+  return launch_pattern(srcs, n_src, dsts, n_dst, bytes, ds->cus * 4, stream) == hipSuccess
+             ? PURLIN_OK
+             : PURLIN_ERR_HIP;
 }
 
 void purlin_release(void) {

@@ -16,7 +16,7 @@ import os
 __all__ = [
     "LIB_PATH", "NAMINGS", "OPS", "DTYPES", "STATUS", "PurlinError", "collective",
     "all_reduce", "reduce_scatter", "all_gather", "all_to_all", "check",
-    "set_policy", "get_policy", "plan_describe", "last_launch", "stream_copy",
+    "set_policy", "get_policy", "plan_describe", "last_launch", "stream_copy", "stream_pattern",
     "release", "exported_symbols",
 ]
 
@@ -92,6 +92,10 @@ def _load():
     lib.purlin_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p]
     lib.purlin_stream_copy.restype = ctypes.c_int
+    lib.purlin_stream_pattern.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                          ctypes.c_int64, ctypes.c_void_p]
+    lib.purlin_stream_pattern.restype = ctypes.c_int
     lib.purlin_strerror.argtypes = [ctypes.c_int]
     lib.purlin_strerror.restype = ctypes.c_char_p
     lib.purlin_release.argtypes = []
@@ -106,7 +110,7 @@ def exported_symbols():
     """Names of the C ABI functions the loaded library resolves."""
     names = ["purlin_collective", "purlin_check", "purlin_set_policy", "purlin_get_policy",
              "purlin_plan_describe", "purlin_last_launch", "purlin_stream_copy",
-             "purlin_strerror", "purlin_release"]
+             "purlin_stream_pattern", "purlin_strerror", "purlin_release"]
     return [n for n in names if hasattr(_lib, n)]
 
 
@@ -274,6 +278,14 @@ def stream_copy(dst, src, nbytes, stream=None):
     _raise(_lib.purlin_stream_copy(ctypes.c_void_p(_ptr(dst)), ctypes.c_void_p(_ptr(src)),
                                    int(nbytes), ctypes.c_void_p(_stream(stream))),
            "purlin_stream_copy")
+
+
+def stream_pattern(srcs, dsts, nbytes, stream=None):
+    """Bare read/write pattern of a collective (ceiling measurement)."""
+    sa = (ctypes.c_void_p * len(srcs))(*[_ptr(x) for x in srcs])
+    da = (ctypes.c_void_p * max(1, len(dsts)))(*[_ptr(x) for x in dsts])
+    _raise(_lib.purlin_stream_pattern(sa, len(srcs), da, len(dsts), int(nbytes),
+                                      ctypes.c_void_p(_stream(stream))), "purlin_stream_pattern")
 
 
 def release():

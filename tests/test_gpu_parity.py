@@ -189,6 +189,29 @@ def test_large_unaligned_tiles(purlin, name, dtype, chunk):
     oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, None, shifts, out_shift)
 
 
+@pytest.mark.parametrize("chunk", [4096, 65536, 0])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_reduce_one_destination_shifted_sources(purlin, dtype, chunk):
+    """ReduceScatter whose sources all share one shift off the destination's
+    16-byte phase (as with variable-length partitions): rows aligned to the
+    sources, tiles whose unit counts sit on and around the 512-unit passes."""
+    P = 8
+    print("case reduce-shifted", dtype, chunk, flush=True)
+    esz = 4 if dtype == "f32" else 2
+    per = 16 // esz
+    rng = np.random.default_rng([23, esz, chunk])
+    units = [1, 7, 8, 9, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025, 3000]
+    sizes = [u * per + int(rng.integers(0, per)) for u in units[:P]]
+    sizes2 = [u * per + int(rng.integers(0, per)) for u in units[P:]] + [5, 40000]
+    for sz in (sizes, sizes2):
+        counts = pins.counts_for("reducescatter", P, sz)
+        ins, outs = pins.make_case("reducescatter", P, counts, dtype, rng, None, sentinel=0x3C3C)
+        for shift in range(1, per):
+            purlin.set_policy(chunk_bytes=chunk, zero_staging="zs")
+            oracle_and_gpu(purlin, "reducescatter", P, counts, dtype, ins, outs, None,
+                           [shift] * P, [0] * P)
+
+
 def test_overlap_checks_survive_the_pointer_cache(purlin):
     """The per-call overlap check is skipped only for the same plan and buffers."""
     import torch
