@@ -439,8 +439,33 @@ __device__ __forceinline__ void units(const uint64_t *sa, int ns, const uint64_t
   else body_shifted<Op, kUs, kNTL, kNTS>(sa, ns, db, nd, n, sh);
 }
 
+// Whether a job's tiles take the source-aligned body: one destination, and
+// some source off the destination's 16-byte phase (the offset between a
+// source and the destination is the same at every byte of a job).
+__device__ __forceinline__ bool src_rows(const Srcs &s, const Dsts &d) {
+  if (d.n != 1) return false;
+  uint32_t any = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxRanks; ++i) any |= uint32_t(s.a[i] - d.b[0]) & 15u;
+  return any != 0;
+}
+
+// The address whose 128-byte lines a job's tile boundaries follow (a
+// boundary x satisfies (line_ref + x) % 128 == 0): the destination's, or for
+// the source-aligned body the destination shifted so that at a boundary the
+// destination is on a 16-byte unit and source 0's block containing it
+// starts a 128-byte line.  Then a full tile is whole source-aligned rows
+// with no head pass.  With e = (dst - src0) mod 128 the boundary sits where
+// the destination is at ceil16(e) mod 128, and src0 there is < 16 bytes
+// past a line start.
+__device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
+  if (!src_rows(s, d)) return d.b[0];
+  const uint32_t e = uint32_t(d.b[0] - s.a[0]) & 127u;
+  return d.b[0] - uint64_t((e + 15u) & 112u);
+}
+
 // One tile: job bytes [x0, x1).  x0 is 0 or on a 128-byte boundary of the
-// destinations, x1 is the job's end or on such a boundary.  Layout:
+// job's line_ref, x1 is the job's end or on such a boundary.  Layout:
 //   [x0, x16)    < 16 bytes before the first 16-byte boundary: element ops
 //   [x16, x128)  < 8 units before the first 128-byte boundary: plain stores
 //   [x128, xb)   the body: whole lines, nontemporal stores when kNT
@@ -477,7 +502,7 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
   for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(x16);
   const bool aligned = any == 0;
   const bool ntl = kNT && (phase == 0 || nt_any_phase);
-  if (!aligned && d.n == 1) {
+  if (src_rows(s, d)) {
     uint32_t nh = ((128u - uint32_t((sa[0] - sh[0]) & 127u)) & 127u) >> 4;
     if (nh > nall) nh = nall;
     if (nh) units<Op, kU, false, false>(sa, s.n, db, 1, nh, sh, false);

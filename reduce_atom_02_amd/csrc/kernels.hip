@@ -38,12 +38,13 @@ __device__ __forceinline__ int job_of_tile(const LaunchPlan &p, int t) {
   return lo;
 }
 
-// Job byte range of tile tl (of ntl) of a job of n bytes whose first
-// destination byte is at address b0: tile 0 also takes the bytes before the
-// first 128-byte boundary, so every later tile starts on a line.
-__device__ __forceinline__ void tile_bounds(uint64_t b0, int64_t n, int64_t C, int tl, int ntl,
+// Job byte range of tile tl (of ntl) of a job of n bytes whose lines follow
+// address ref (its first destination byte, or atom::line_ref): tile 0 also
+// takes the bytes before the first 128-byte boundary, so every later tile
+// starts on a line.
+__device__ __forceinline__ void tile_bounds(uint64_t ref, int64_t n, int64_t C, int tl, int ntl,
                                             int64_t &x0, int64_t &x1) {
-  int64_t h = int64_t((128u - uint32_t(b0 & 127u)) & 127u);
+  int64_t h = int64_t((128u - uint32_t(ref & 127u)) & 127u);
   if (h > n) h = n;
   x0 = tl == 0 ? 0 : h + int64_t(tl) * C;
   x1 = tl == ntl - 1 ? n : h + int64_t(tl + 1) * C;
@@ -83,7 +84,7 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     }
     d.b[kMaxRanks] = d.b[0];
     int64_t x0, x1;
-    tile_bounds(d.b[0], jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
+    tile_bounds(atom::line_ref(s, d), jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
                 p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
     atom::tile<Op, kU, kNTL>(s, d, x0, x1, p.nt_any_phase != 0);
   }
@@ -182,7 +183,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
           const SlotRef o = slot_ref(sp, ring0 + sj.n_stage, slot);
           if (round == 0) {
             __hip_atomic_store(o.credit, tag(e, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } else if (!snac::wait_geq<uint64_t>(o.credit, tag(e, round * sj.n_scatter), p)) {
+          } else if (!snac::wait_geq<uint64_t, false>(o.credit, tag(e, round * sj.n_scatter), p)) {
             ok = 0;
           }
         }
@@ -245,7 +246,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       if (threadIdx.x == 0) {
         if (round == 0) {
           __hip_atomic_store(o.credit, tag(e, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else if (!snac::wait_geq<uint64_t>(o.credit, tag(e, round), p)) {
+        } else if (!snac::wait_geq<uint64_t, false>(o.credit, tag(e, round), p)) {
           ok = 0;
         }
       }

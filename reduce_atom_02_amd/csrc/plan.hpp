@@ -17,15 +17,24 @@ constexpr int kMaxRanks = 8;
 constexpr int kMaxJobs = kMaxRanks * kMaxRanks;
 constexpr int kThreads = 256;           // 4 wavefronts of 64
 constexpr int kFlagStride = 32;          // u32 words between flags (128 bytes)
+// The exit count of a launch is spread over this many counters (workgroup b
+// counts on b % kExitSlots): one counter taking an atomic add from each of
+// ~1000 workgroups serialises them, measured at ~18 us per launch.
+constexpr int kExitSlots = 32;
 
 // Flag block layout (u32 words, each flag on its own 128-byte line).
 enum FlagWord : int {
-  kFlagEntry = 0,                              // kMaxRanks entry epochs
-  kFlagExit = kMaxRanks * kFlagStride,         // 2 exit counters (epoch parity)
-  kFlagStatus = (kMaxRanks + 2) * kFlagStride, // sticky device status bits
-  kFlagAbort = (kMaxRanks + 3) * kFlagStride,  // epoch of an aborted launch
-  kFlagWords = (kMaxRanks + 4) * kFlagStride,
+  kFlagEntry = 0,                                            // kMaxRanks entry epochs
+  kFlagExit = kMaxRanks * kFlagStride,                       // 2 x kExitSlots exit counters
+  kFlagStatus = (kMaxRanks + 2 * kExitSlots) * kFlagStride,  // sticky device status bits
+  kFlagAbort = (kMaxRanks + 2 * kExitSlots + 1) * kFlagStride,  // epoch of an aborted launch
+  kFlagWords = (kMaxRanks + 2 * kExitSlots + 2) * kFlagStride,
 };
+
+// Word of exit counter `slot` of epoch parity `parity`.
+constexpr int exit_word(uint32_t parity, int slot) {
+  return kFlagExit + (int(parity) * kExitSlots + slot) * kFlagStride;
+}
 constexpr uint32_t kStatusTimeout = 1u;
 
 struct Job {
@@ -58,10 +67,10 @@ struct LaunchPlan {
   uint32_t epoch;           // increases by one per launch on a device
   int64_t chunk_bytes;      // bytes per tile (multiple of 4096)
   uint64_t watchdog_ticks;  // bound of every spin wait, in wall-clock ticks
-  uint32_t exit_expect;     // exit-counter value of the previous launch (sync)
   int32_t sync;             // 1: entry/exit notify flags on
   int32_t nt_any_phase;     // 1: nontemporal loads even for sources off the line phase
   int32_t tile_begin[kMaxJobs + 1];
+  uint32_t exit_expect[kExitSlots];  // exit counters after the previous launch (sync)
   Job jobs[kMaxJobs];
 };
 

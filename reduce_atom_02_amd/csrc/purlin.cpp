@@ -28,7 +28,7 @@ struct DeviceState {
   uint64_t *slot_flags = nullptr;
   int64_t slot_flag_bytes = 0;
   uint32_t epoch = 0;
-  uint32_t exit_total[2] = {0, 0};
+  uint32_t exit_total[2][kExitSlots] = {};  // per parity and slot, all launches so far
   int occ[3][2][2][3] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
 };
 
@@ -118,7 +118,8 @@ purlin_status device_state(DeviceState **out) {
       return PURLIN_ERR_HIP;
     }
     s.flags = static_cast<uint32_t *>(f);
-    s.exit_total[0] = s.exit_total[1] = 0;
+    for (auto &par : s.exit_total)
+      for (uint32_t &v : par) v = 0;
   }
   *out = &s;
   return PURLIN_OK;
@@ -170,8 +171,8 @@ KernelKind kind_of(purlin_op op, purlin_dtype dtype) {
 
 // Policy table ("codesign policies tune execution", Figure 1 caption), from
 // sweeps of grid, chunk and unroll at 64 MiB - 1 GiB per rank on MI355X:
-// reductions and broadcasts prefer about two workgroups per CU,
-// point-to-point copies four per CU, all with 16 KiB chunks.  Fewer, deeper
+// reductions and broadcasts prefer about two workgroups per CU and 16 KiB
+// chunks, point-to-point copies four per CU and 32 KiB chunks.  Fewer, deeper
 // workgroups keep fewer DRAM pages open than a full grid.  The grid is a
 // whole-device figure (all P ranks share one GPU), so it does not shrink
 // for P < 8.
@@ -184,7 +185,7 @@ struct AutoPolicy {
 AutoPolicy auto_policy(KernelKind kind, bool broadcast) {
   if (kind != KernelKind::kCopy) return {512, int64_t(16) << 10, 0};
   if (broadcast) return {512, int64_t(16) << 10, 0};
-  return {1024, int64_t(16) << 10, 0};
+  return {1024, int64_t(32) << 10, 0};
 }
 
 // Small messages get smaller chunks, so that the default grid still sees
@@ -342,9 +343,14 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     // Nontemporal loads pay off for sources off the destination's line
     // phase too (variable-length partitions), measured at 16 MiB - 1 GiB.
     lp.nt_any_phase = env_i64("PURLIN_NT_ANY_PHASE", 1) ? 1 : 0;
-    lp.exit_expect = ds->exit_total[(ds->epoch - 1u) & 1u];
+    for (int k = 0; k < kExitSlots; ++k) lp.exit_expect[k] = ds->exit_total[(ds->epoch - 1u) & 1u][k];
     err = launch_zs(lp, kind, nt, unroll_sel, grid, stream);
-    if (err == hipSuccess && lp.sync) ds->exit_total[ds->epoch & 1u] += uint32_t(grid);
+    if (err == hipSuccess && lp.sync) {
+      // workgroup b counts on slot b % kExitSlots
+      for (int k = 0; k < kExitSlots; ++k)
+        ds->exit_total[ds->epoch & 1u][k] +=
+            uint32_t(grid / kExitSlots + (k < grid % kExitSlots ? 1 : 0));
+    }
     info.grid = grid;
     info.zero_staging = 1;
     info.chunk_bytes = chunk;

@@ -7,7 +7,9 @@
 //    release writes it back, so neither may sit inside a spin loop;
 //  * a wait therefore polls with relaxed agent-scope loads (which bypass the
 //    non-coherent caches) and issues one acquire fence once the value is
-//    seen;
+//    seen, and only when it is about to read data the flag publishes; a
+//    wait for "done reading" (credits, exit counts, entry) orders later
+//    stores only and takes no acquire;
 //  * a notify that publishes data ("ready") is a release store, so the
 //    chunk written by one workgroup is visible on every XCD;
 //  * a notify that only says "I have finished reading" (a credit, the exit
@@ -69,15 +71,18 @@ __device__ __forceinline__ void raise_timeout(const LaunchPlan &p) {
   __hip_atomic_store(&p.flags[kFlagAbort], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Spin until *f - target >= 0 (wrap-aware), then acquire; false if the
-// watchdog expired or the launch was aborted.
-template <class W>
+// Spin until *f - target >= 0 (wrap-aware), then acquire (kAcquire) ;
+// false if the watchdog expired or the launch was aborted.  A wait that only
+// orders this workgroup's later accesses after another's earlier *reads*
+// (a credit-like "done reading" flag) needs no acquire: no store is issued
+// before the load that saw the flag has returned.
+template <class W, bool kAcquire = true>
 __device__ __forceinline__ bool wait_geq(const W *f, W target, const LaunchPlan &p) {
   using S = typename std::conditional<sizeof(W) == 8, int64_t, int32_t>::type;
   const uint64_t t0 = wall_clock64();
   while (true) {
     if (S(load_rlx(f) - target) >= 0) {
-      acquire_fence();
+      if (kAcquire) acquire_fence();
       return true;
     }
     if (aborted(p)) return false;
@@ -90,24 +95,33 @@ __device__ __forceinline__ bool wait_geq(const W *f, W target, const LaunchPlan 
 }
 
 // Entry notify: rank r may let peers read its input and write its output
-// once every reader of the previous collective is done (exit counter), and
-// announces that with entry[r] = epoch.  Every workgroup then waits for the
-// entry flag of every rank before its first access.  Workgroup b announces
-// ranks b, b + grid, ...; all workgroups are resident at once (the grid
-// never exceeds what the device holds), so the announcements always happen.
+// once every reader of the previous collective is done (its exit counters),
+// and announces that with entry[r] = epoch.  Every workgroup then waits for
+// the entry flag of every rank before its first access.  Workgroup b
+// announces ranks b, b + grid, ...; all workgroups are resident at once (the
+// grid never exceeds what the device holds), so the announcements always
+// happen.  Both waits order later writes after earlier reads only (the data
+// a collective reads reaches it through stream order), so they poll without
+// an acquire: an acquire here would invalidate the XCD's L2 once per
+// workgroup and rank, thousands of times per launch.
 __device__ __forceinline__ bool entry(const LaunchPlan &p) {
   __shared__ int ok;
   if (threadIdx.x == 0) ok = 1;
   __syncthreads();
   uint32_t *f = p.flags;
-  if (threadIdx.x == 0 && int(blockIdx.x) < p.P) {
+  const bool announcer = int(blockIdx.x) < p.P;
+  if (announcer && int(threadIdx.x) < kExitSlots) {
     const uint32_t prev = (p.epoch - 1u) & 1u;
-    if (!wait_geq<uint32_t>(&f[kFlagExit + prev * kFlagStride], p.exit_expect, p)) ok = 0;
+    if (!wait_geq<uint32_t, false>(&f[exit_word(prev, threadIdx.x)], p.exit_expect[threadIdx.x], p))
+      ok = 0;
+  }
+  __syncthreads();
+  if (announcer && threadIdx.x == 0 && ok) {
     for (int r = blockIdx.x; r < p.P; r += gridDim.x) store_rel(&f[kFlagEntry + r * kFlagStride], p.epoch);
   }
   __syncthreads();
   if (int(threadIdx.x) < p.P && ok) {
-    if (!wait_geq<uint32_t>(&f[kFlagEntry + threadIdx.x * kFlagStride], p.epoch, p)) ok = 0;
+    if (!wait_geq<uint32_t, false>(&f[kFlagEntry + threadIdx.x * kFlagStride], p.epoch, p)) ok = 0;
   }
   __syncthreads();
   return ok != 0;
@@ -118,7 +132,7 @@ __device__ __forceinline__ bool entry(const LaunchPlan &p) {
 // separate GPUs would need a system-scope release here.)
 __device__ __forceinline__ void exit_notify(const LaunchPlan &p) {
   drain_workgroup();
-  if (threadIdx.x == 0) add_rlx(&p.flags[kFlagExit + (p.epoch & 1u) * kFlagStride], 1u);
+  if (threadIdx.x == 0) add_rlx(&p.flags[exit_word(p.epoch & 1u, blockIdx.x % kExitSlots)], 1u);
 }
 
 }  // namespace snac
