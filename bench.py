@@ -121,19 +121,29 @@ def cpu_baseline(T_sample, names):
         oracle.collective(in_n, out_n, op, "bf16", P, s["counts"], None, xs, ys)
         total_t += time.perf_counter() - t0
         total_T += s["T"]
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": round(total_T / total_t / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": "the same seven collectives, bf16, P=8, at %d MiB per rank instead of "
-                      "%s; numpy oracle single-threaded; %.1f s of oracle time"
-                      % (T_sample >> 20, "the timed size", total_t)}
+                      "%s; numpy oracle single-threaded; %.1f s of oracle time; host: %d CPUs, "
+                      "%d in this process's affinity, %s"
+                      % (T_sample >> 20, "the timed size", total_t, os.cpu_count() or 0,
+                         len(os.sched_getaffinity(0)), model)}
 
 
 def ceilings(purlin, T, steps, dev):
     """HBM ceiling of each collective's access pattern: n read streams and m
-    write streams, 16-byte nontemporal accesses, no planning or flags
-    (purlin_stream_pattern); a 1 GiB fill between calls (cold caches).
-    1->1 over P*T bytes is AllToAll's pattern and footprint, 1->8 of T bytes
-    AllGather's, 8->1 ReduceScatter's, 8->8 AllReduce's."""
+    write streams, 16-byte nontemporal accesses over 16 KiB tiles, no
+    planning or flags (purlin_stream_pattern), the best of three grid sizes;
+    a 1 GiB fill between calls (cold caches).  1->1 over P*T bytes is
+    AllToAll's pattern and footprint, 1->8 of T bytes AllGather's, 8->1
+    ReduceScatter's, 8->8 AllReduce's.  Also hipMemcpyAsync device to device
+    (torch's copy_) over the P*T bytes, as a context figure."""
     import torch
     big_src = torch.ones(P * T // 4, dtype=torch.float32, device=dev)
     big_dst = torch.empty(P * T // 4, dtype=torch.float32, device=dev)
@@ -141,28 +151,33 @@ def ceilings(purlin, T, steps, dev):
     dsts = [big_dst[r * (T // 4):(r + 1) * (T // 4)] for r in range(P)]
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    out = {}
-    # (sources, destinations, bytes per stream): the 1->1 stream spans the
-    # P*T bytes AllToAll moves, since the sustained rate drops with footprint
-    for nr, nw, nbytes, label in ((1, 1, P * T, "1->1 (alltoall)"),
-                                  (1, 8, T, "1->8 (allgather)"),
-                                  (8, 1, T, "8->1 (reducescatter)"),
-                                  (8, 8, T, "8->8 (allreduce)")):
-        s_, d_ = ([big_src], [big_dst]) if nr == 1 and nw == 1 else (srcs[:nr], dsts[:nw])
-        purlin.stream_pattern(s_, d_, nbytes, stream=stream)
+
+    def p50_of(fn):
+        fn()
         ev = []
         for _ in range(steps):
             flush.fill_(1.0)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            purlin.stream_pattern(s_, d_, nbytes, stream=stream)
+            fn()
             e1.record(stream)
             ev.append((e0, e1))
         torch.cuda.synchronize()
         ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
-        p50 = ts[len(ts) // 2]
-        out[label] = round((nr + nw) * nbytes / p50 / HBM_PEAK, 4)
+        return ts[len(ts) // 2]
+
+    out = {}
+    for nr, nw, nbytes, label in ((1, 1, P * T, "1->1 (alltoall)"),
+                                  (1, 8, T, "1->8 (allgather)"),
+                                  (8, 1, T, "8->1 (reducescatter)"),
+                                  (8, 8, T, "8->8 (allreduce)")):
+        s_, d_ = ([big_src], [big_dst]) if nr == 1 and nw == 1 else (srcs[:nr], dsts[:nw])
+        best = min(p50_of(lambda: purlin.stream_pattern(s_, d_, nbytes, grid=g, stream=stream))
+                   for g in (512, 1024, 2048))
+        out[label] = round((nr + nw) * nbytes / best / HBM_PEAK, 4)
+    t = p50_of(lambda: big_dst.copy_(big_src))
+    out["hipMemcpyAsync D2D"] = round(2 * P * T / t / HBM_PEAK, 4)
     del srcs, dsts, big_src, big_dst, flush
     torch.cuda.empty_cache()
     return out
@@ -196,16 +211,21 @@ def calibrate_copy(purlin, T, steps, warmup, dev):
 def sweep(purlin, T_max, variant, path, dev):
     """p50 per-call latency from HIP events, T = 1 KiB .. T_max per rank.
 
-    Latency regime (T <= 512 KiB), warm caches, two figures:
-      p50_us       device latency: a spin kernel is queued first, so every
-                   timed launch is already enqueued when the GPU reaches it
-                   and the events bracket only GPU work (back to back);
-      submit_p50_us  the same call timed from an idle GPU, so host-side
-                   argument marshalling (Python, ctypes) and launch are in it.
+    Every point: 20 warm-up calls first.
+    Latency regime (T <= 512 KiB), warm caches, 1000 timed calls, three figures:
+      p50_us       device latency: a spin kernel is queued before each batch
+                   of 200 calls, so every timed launch is already enqueued
+                   when the GPU reaches it and the events bracket only GPU
+                   work (back to back);
+      submit_p50_us  the same call timed with events from an idle GPU, so
+                   host-side argument marshalling (Python, ctypes) and the
+                   launch are in it;
+      host_p50_us  call to completion on the host: perf_counter around the
+                   call and a stream synchronize.
     Bandwidth regime (T >= 1 MiB): a 1 GiB fill runs between calls, outside
     the events, so inputs come from HBM, not the 256 MiB Infinity Cache;
     100 timed calls up to 64 MiB, 20 above.  The empty-kernel floor is
-    measured both ways too."""
+    measured the same three ways."""
     import torch
     import workloads
     purlin.set_policy(zero_staging=variant)
@@ -220,9 +240,10 @@ def sweep(purlin, T_max, variant, path, dev):
 
     def timed(fn, reps, cold, queued=False):
         ev = []
-        if queued:
-            torch.cuda._sleep(20_000_000)          # ~10 ms at 2.4 GHz: covers the enqueues
-        for _ in range(reps):
+        for k in range(reps):
+            if queued and k % 200 == 0:
+                torch.cuda.synchronize()
+                torch.cuda._sleep(20_000_000)      # ~10 ms at 2.4 GHz: covers 200 enqueues
             if cold:
                 flush.fill_(1.0)
             e0 = torch.cuda.Event(enable_timing=True)
@@ -235,15 +256,29 @@ def sweep(purlin, T_max, variant, path, dev):
         ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
         return ts[len(ts) // 10], ts[len(ts) // 2], ts[(9 * len(ts)) // 10]
 
-    floor = timed(lambda: empty.add_(0), 200, False, queued=True)[1]
-    floor_submit = timed(lambda: empty.add_(0), 200, False)[1]
+    def host_p50(fn, reps):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            stream.synchronize()
+            ts.append(time.perf_counter() - t0)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    def empty_kernel():
+        empty.add_(0)
+
+    floor = timed(empty_kernel, 1000, False, queued=True)[1]
+    floor_submit = timed(empty_kernel, 1000, False)[1]
+    floor_host = host_p50(empty_kernel, 1000)
     rows = []
     with open(path, "w") as f:
         for lg in range(10, T_max.bit_length()):
             T = 1 << lg
             shapes = collective_shapes(T)
             cold = T >= (1 << 20)
-            reps = 200 if not cold else (100 if T <= (64 << 20) else 20)
+            reps = 1000 if not cold else (100 if T <= (64 << 20) else 20)
             for name, s in shapes.items():
                 in_n, out_n, op = SPECS[name]
                 xi = [ins[r][:s["ins"][r]] for r in range(P)]
@@ -252,14 +287,15 @@ def sweep(purlin, T_max, variant, path, dev):
                 def fn():
                     purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
 
-                for _ in range(3):
+                for _ in range(20):
                     fn()
-                submit = None
+                submit = host = None
                 if cold:
                     p10, p50, p90 = timed(fn, reps, cold)
                 else:
-                    p10, p50, p90 = timed(fn, 200, cold, queued=True)
-                    submit = round(timed(fn, 200, cold)[1] * 1e6, 2)
+                    p10, p50, p90 = timed(fn, 1000, cold, queued=True)
+                    submit = round(timed(fn, 1000, cold)[1] * 1e6, 2)
+                    host = round(host_p50(fn, 1000) * 1e6, 2)
                 purlin.check(stream)
                 info = purlin.last_launch()
                 row = {"collective": name, "variant": variant, "dtype": "bf16", "P": P,
@@ -267,10 +303,11 @@ def sweep(purlin, T_max, variant, path, dev):
                        "p10_us": round(p10 * 1e6, 2), "p50_us": round(p50 * 1e6, 2),
                        "p90_us": round(p90 * 1e6, 2), "algbw_GBps": round(T / p50 / 1e9, 2),
                        "hbm_frac": round(s["bmin"] / p50 / HBM_PEAK, 4), "bmin": s["bmin"],
-                       "submit_p50_us": submit,
+                       "submit_p50_us": submit, "host_p50_us": host,
                        "grid": info["grid"], "chunk_bytes": info["chunk_bytes"],
                        "empty_kernel_p50_us": round(floor * 1e6, 2),
-                       "empty_kernel_submit_p50_us": round(floor_submit * 1e6, 2)}
+                       "empty_kernel_submit_p50_us": round(floor_submit * 1e6, 2),
+                       "empty_kernel_host_p50_us": round(floor_host * 1e6, 2)}
                 f.write(json.dumps(row) + "\n")
                 f.flush()
                 rows.append(row)

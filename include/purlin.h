@@ -182,12 +182,13 @@ PURLIN_API purlin_status purlin_stream_copy(void *dst, const void *src, int64_t 
  * 16-byte unit u < bytes/16 is read from n_src sources (added as integers)
  * and the result written to n_dst destinations, at the same offset in every
  * buffer; n_src and n_dst in {1, 8}, all pointers 16-byte aligned and every
- * destination disjoint from every source.
- * Same access style as the collectives (16-byte nontemporal, grid-stride),
- * with no planning, tiling or flags.  Asynchronous on `stream`. */
+ * destination disjoint from every source.  `grid` workgroups (0: four per
+ * CU, at most 65536) walk 16 KiB tiles in grid-stride order with 16-byte
+ * nontemporal accesses, as the collectives do, with no planning or flags.
+ * Asynchronous on `stream`. */
 PURLIN_API purlin_status purlin_stream_pattern(const void *const *srcs, int n_src,
                                                void *const *dsts, int n_dst, int64_t bytes,
-                                               hipStream_t stream);
+                                               int grid, hipStream_t stream);
 
 /* Static text for a status code. */
 PURLIN_API const char *purlin_strerror(purlin_status s);

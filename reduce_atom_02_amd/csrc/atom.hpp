@@ -118,11 +118,17 @@ struct Dsts {
   int n;
 };
 
+// Element-wise [y0, y1) of a job, one element per thread from thread t0
+// on (at most kThreads - t0 elements).  Every source is loaded before any is
+// added (entries past n repeat source 0, so the loads need no guard), so
+// the loads are in flight together: one memory round trip.
 template <class Op>
-__device__ __forceinline__ void elements(const Srcs &s, const Dsts &d, int64_t y0, int64_t y1) {
+__device__ __forceinline__ void elements(const Srcs &s, const Dsts &d, int64_t y0, int64_t y1,
+                                         int t0 = 0) {
   const int64_t n = (y1 - y0) / Op::kElem;
-  if (threadIdx.x >= n) return;
-  const int64_t x = y0 + int64_t(threadIdx.x) * Op::kElem;
+  const int idx = int(threadIdx.x) - t0;
+  if (idx < 0 || idx >= n) return;
+  const int64_t x = y0 + int64_t(idx) * Op::kElem;
   // Loops over sources and destinations are fully unrolled with a guard so
   // that the pointer arrays stay in registers.
   if constexpr (!Op::kSum) {
@@ -131,18 +137,24 @@ __device__ __forceinline__ void elements(const Srcs &s, const Dsts &d, int64_t y
     for (int k = 0; k < kMaxRanks + 1; ++k)
       if (k < d.n) *gp<uint16_t>(d.b[k] + x) = v;
   } else if constexpr (Op::kElem == 4) {
-    float acc = *gp<const float>(s.a[0] + x);
+    float v[kMaxRanks];
+#pragma unroll
+    for (int i = 0; i < kMaxRanks; ++i) v[i] = *gp<const float>(s.a[i] + x);
+    float acc = v[0];
 #pragma unroll
     for (int i = 1; i < kMaxRanks; ++i)
-      if (i < s.n) acc = acc + *gp<const float>(s.a[i] + x);
+      if (i < s.n) acc = acc + v[i];
 #pragma unroll
     for (int k = 0; k < kMaxRanks + 1; ++k)
       if (k < d.n) *gp<float>(d.b[k] + x) = acc;
   } else {
-    float acc = bf16_lo(*gp<const uint16_t>(s.a[0] + x));
+    uint16_t v[kMaxRanks];
+#pragma unroll
+    for (int i = 0; i < kMaxRanks; ++i) v[i] = *gp<const uint16_t>(s.a[i] + x);
+    float acc = bf16_lo(v[0]);
 #pragma unroll
     for (int i = 1; i < kMaxRanks; ++i)
-      if (i < s.n) acc = acc + bf16_lo(*gp<const uint16_t>(s.a[i] + x));
+      if (i < s.n) acc = acc + bf16_lo(v[i]);
     const uint16_t r = uint16_t(bf16_rne(acc));
 #pragma unroll
     for (int k = 0; k < kMaxRanks + 1; ++k)
@@ -466,12 +478,15 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
 
 // One tile: job bytes [x0, x1).  x0 is 0 or on a 128-byte boundary of the
 // job's line_ref, x1 is the job's end or on such a boundary.  Layout:
-//   [x0, x16)    < 16 bytes before the first 16-byte boundary: element ops
-//   [x16, x128)  < 8 units before the first 128-byte boundary: plain stores
-//   [x128, xb)   the body: whole lines, nontemporal stores when kNT
-//   [xb, x1)     < 16 bytes of tail: element ops
-// One destination with sources off its 16-byte phase instead takes the
-// source-aligned body after a head up to source 0's first line.  Loads are
+//   [x0, xh)   the head, < 128 bytes: the bytes before the first 16-byte
+//              unit of the destination and the units before the first row
+//              start (a destination line, or with the source-aligned body a
+//              unit whose source-0 block starts a line); element operations
+//              on wavefront 0
+//   [xh, xb)   the body: whole units, nontemporal stores when kNT
+//   [xb, x1)   < 16 bytes of tail: element operations on wavefront 3, in
+//              parallel with the head
+// A tile of at most one element per thread is one element pass.  Loads are
 // nontemporal when every source sits on the destinations' 128-byte phase,
 // or when nt_any_phase asks for it (measured faster for misaligned
 // variable-length partitions too).  A tile spans less than 4 GiB.
@@ -479,14 +494,16 @@ template <class Op, int kU, bool kNT>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
                                      bool nt_any_phase = false) {
   if (x1 <= x0) return;
+  if (x1 - x0 <= int64_t(kThreads) * Op::kElem) {
+    elements<Op>(s, d, x0, x1);
+    return;
+  }
+  // from here on the tile holds more than 16 units, so the head (< 8 units
+  // past x16) leaves a non-empty body
   const uint64_t b0 = d.b[0];
-  int64_t x16 = x0 + int64_t((16u - uint32_t((b0 + uint64_t(x0)) & 15u)) & 15u);
-  if (x16 > x1) x16 = x1;
+  const int64_t x16 = x0 + int64_t((16u - uint32_t((b0 + uint64_t(x0)) & 15u)) & 15u);
   const uint32_t nall = uint32_t((x1 - x16) >> 4);
   const int64_t xb = x16 + int64_t(nall) * 16;
-  if (x16 > x0) elements<Op>(s, d, x0, x16);
-  if (x1 > xb) elements<Op>(s, d, xb, x1);
-  if (nall == 0) return;
   uint64_t sa[kMaxRanks];
   uint64_t db[kMaxRanks + 1];
   uint32_t sh[kMaxRanks];
@@ -498,34 +515,30 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
     any |= sh[i];
     phase |= uint32_t((s.a[i] - b0) & 127u);
   }
+  const bool srows = src_rows(s, d);
+  // units before the first row start
+  const uint64_t line = srows ? sa[0] - sh[0] : b0 + uint64_t(x16);
+  uint32_t nh = ((128u - uint32_t(line & 127u)) & 127u) >> 4;
+  if (nh > nall) nh = nall;
+  const int64_t xh = x16 + int64_t(nh) * 16;
+  elements<Op>(s, d, x0, xh);
+  elements<Op>(s, d, xb, x1, kThreads - 64);
+  const uint32_t nbody = nall - nh;
+  if (nbody == 0) return;
 #pragma unroll
-  for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(x16);
-  const bool aligned = any == 0;
+  for (int i = 0; i < kMaxRanks; ++i) sa[i] += uint64_t(nh) * 16u;
+#pragma unroll
+  for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(xh);
   const bool ntl = kNT && (phase == 0 || nt_any_phase);
-  if (src_rows(s, d)) {
-    uint32_t nh = ((128u - uint32_t((sa[0] - sh[0]) & 127u)) & 127u) >> 4;
-    if (nh > nall) nh = nall;
-    if (nh) units<Op, kU, false, false>(sa, s.n, db, 1, nh, sh, false);
-    if (nall == nh) return;
-#pragma unroll
-    for (int i = 0; i < kMaxRanks; ++i) sa[i] += uint64_t(nh) * 16u;
-    const uint64_t d1 = db[0] + uint64_t(nh) * 16u;
+  if (srows) {
     // a sum holds eight sources per row, so two rows per wavefront (more
     // measured slower); a copy holds one and takes the tile's unroll
     constexpr int kUr = Op::kSum ? 2 : kU;
-    if (ntl) body_src_aligned<Op, kUr, true, kNT>(sa, s.n, d1, nall - nh, sh);
-    else body_src_aligned<Op, kUr, false, kNT>(sa, s.n, d1, nall - nh, sh);
+    if (ntl) body_src_aligned<Op, kUr, true, kNT>(sa, s.n, db[0], nbody, sh);
+    else body_src_aligned<Op, kUr, false, kNT>(sa, s.n, db[0], nbody, sh);
     return;
   }
-  uint32_t nhead = ((128u - uint32_t((b0 + uint64_t(x16)) & 127u)) & 127u) >> 4;
-  if (nhead > nall) nhead = nall;
-  const uint32_t nbody = nall - nhead;
-  if (nhead) units<Op, kU, false, false>(sa, s.n, db, d.n, nhead, sh, aligned);
-  if (nbody == 0) return;
-#pragma unroll
-  for (int i = 0; i < kMaxRanks; ++i) sa[i] += uint64_t(nhead) * 16u;
-#pragma unroll
-  for (int j = 0; j < kMaxRanks + 1; ++j) db[j] += uint64_t(nhead) * 16u;
+  const bool aligned = any == 0;
   if (ntl) units<Op, kU, true, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
   else units<Op, kU, false, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
 }

@@ -327,7 +327,8 @@ __global__ void __launch_bounds__(kThreads) stream_copy_kernel(atom::u32x4 *dst,
 }
 
 // Bare pattern of a collective (ceiling measurement): kR sources added as
-// integers, written to kW destinations, same offset everywhere.
+// integers, written to kW destinations, same offset everywhere.  Walks
+// 16 KiB tiles in grid-stride order, as the collectives do.
 struct PatternPtrs {
   const atom::u32x4 *src[kMaxRanks];
   atom::u32x4 *dst[kMaxRanks];
@@ -335,25 +336,29 @@ struct PatternPtrs {
 
 template <int kR, int kW, int kU>
 __global__ void __launch_bounds__(kThreads) pattern_kernel(PatternPtrs p, int64_t n16) {
-  const int64_t stride = int64_t(gridDim.x) * kThreads * kU;
-  for (int64_t b = int64_t(blockIdx.x) * kThreads * kU + threadIdx.x; b < n16; b += stride) {
-    atom::u32x4 v[kU][kR];
+  constexpr int64_t kTile = 1024;  // units of 16 bytes; a multiple of kThreads * kU
+  static_assert(kTile % (kThreads * kU) == 0, "tile is whole passes");
+  const int64_t ntiles = (n16 + kTile - 1) / kTile;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    for (int64_t b = t * kTile + threadIdx.x; b < (t + 1) * kTile; b += kThreads * kU) {
+      atom::u32x4 v[kU][kR];
 #pragma unroll
-    for (int k = 0; k < kU; ++k) {
-      int64_t i = b + int64_t(k) * kThreads;
-      if (i >= n16) i = n16 - 1;
+      for (int k = 0; k < kU; ++k) {
+        int64_t i = b + int64_t(k) * kThreads;
+        if (i >= n16) i = n16 - 1;
 #pragma unroll
-      for (int r = 0; r < kR; ++r) v[k][r] = atom::ld16<true>(uint64_t(p.src[r] + i));
-    }
+        for (int r = 0; r < kR; ++r) v[k][r] = atom::ld16<true>(uint64_t(p.src[r] + i));
+      }
 #pragma unroll
-    for (int k = 0; k < kU; ++k) {
-      const int64_t i = b + int64_t(k) * kThreads;
-      atom::u32x4 a = v[k][0];
+      for (int k = 0; k < kU; ++k) {
+        const int64_t i = b + int64_t(k) * kThreads;
+        atom::u32x4 a = v[k][0];
 #pragma unroll
-      for (int r = 1; r < kR; ++r) a += v[k][r];
-      if (i < n16) {
+        for (int r = 1; r < kR; ++r) a += v[k][r];
+        if (i < n16) {
 #pragma unroll
-        for (int w = 0; w < kW; ++w) atom::st16<true>(uint64_t(p.dst[w] + i), a);
+          for (int w = 0; w < kW; ++w) atom::st16<true>(uint64_t(p.dst[w] + i), a);
+        }
       }
     }
   }

@@ -457,9 +457,9 @@ purlin_status purlin_stream_copy(void *dst, const void *src, int64_t bytes, hipS
 }
 
 purlin_status purlin_stream_pattern(const void *const *srcs, int n_src, void *const *dsts,
-                                    int n_dst, int64_t bytes, hipStream_t stream) {
+                                    int n_dst, int64_t bytes, int grid, hipStream_t stream) {
   if (!srcs || !dsts || (n_src != 1 && n_src != 8) || (n_dst != 1 && n_dst != 8) ||
-      bytes < 0 || (bytes & 15))
+      bytes < 0 || (bytes & 15) || grid < 0 || grid > 65536)
     return PURLIN_ERR_INVALID_ARG;
   for (int r = 0; r < n_src; ++r)
     if (!srcs[r] || (uintptr_t(srcs[r]) & 15)) return PURLIN_ERR_INVALID_ARG;
@@ -469,7 +469,8 @@ purlin_status purlin_stream_pattern(const void *const *srcs, int n_src, void *co
   DeviceState *ds = nullptr;
   purlin_status st = device_state(&ds);
   if (st != PURLIN_OK) return st;
-  return launch_pattern(srcs, n_src, dsts, n_dst, bytes, ds->cus * 4, stream) == hipSuccess
+  return launch_pattern(srcs, n_src, dsts, n_dst, bytes, grid ? grid : ds->cus * 4, stream) ==
+                 hipSuccess
              ? PURLIN_OK
              : PURLIN_ERR_HIP;
 }

@@ -94,7 +94,7 @@ def _load():
     lib.purlin_stream_copy.restype = ctypes.c_int
     lib.purlin_stream_pattern.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
-                                          ctypes.c_int64, ctypes.c_void_p]
+                                          ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     lib.purlin_stream_pattern.restype = ctypes.c_int
     lib.purlin_strerror.argtypes = [ctypes.c_int]
     lib.purlin_strerror.restype = ctypes.c_char_p
@@ -280,11 +280,12 @@ def stream_copy(dst, src, nbytes, stream=None):
            "purlin_stream_copy")
 
 
-def stream_pattern(srcs, dsts, nbytes, stream=None):
-    """Bare read/write pattern of a collective (ceiling measurement)."""
+def stream_pattern(srcs, dsts, nbytes, grid=0, stream=None):
+    """Bare read/write pattern of a collective (ceiling measurement); grid 0
+    is four workgroups per CU."""
     sa = (ctypes.c_void_p * len(srcs))(*[_ptr(x) for x in srcs])
     da = (ctypes.c_void_p * max(1, len(dsts)))(*[_ptr(x) for x in dsts])
-    _raise(_lib.purlin_stream_pattern(sa, len(srcs), da, len(dsts), int(nbytes),
+    _raise(_lib.purlin_stream_pattern(sa, len(srcs), da, len(dsts), int(nbytes), int(grid),
                                       ctypes.c_void_p(_stream(stream))), "purlin_stream_pattern")
 
 
