@@ -11,6 +11,7 @@ Names follow include/purlin.h: namings ``whole``, ``by_rank``, ``by_index``,
 ``f32`` and ``bf16``.
 """
 import ctypes
+import itertools
 import os
 
 __all__ = [
@@ -120,14 +121,14 @@ def _raise(status, what):
 
 
 def _ptr(x):
-    if x is None:
-        return None
-    if isinstance(x, int):
+    if x is None or isinstance(x, int):
         return x
     return x.data_ptr()          # torch tensor
 
 
 def _dtype_of(bufs, dtype):
+    """The element type: `dtype`, else that of the first tensor in `bufs`
+    (every buffer is taken to hold it)."""
     if dtype is not None:
         return dtype
     for b in bufs:
@@ -150,16 +151,38 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+# Marshalled arguments of recent calls, keyed by value: building ctypes
+# arrays costs microseconds per call, and loops repeat the same buffers and
+# counts.  The library only reads them.  Bounded; cleared when full.
+_CACHE = {}
+_CACHE_MAX = 512
+
+
+def _cached(key, make):
+    v = _CACHE.get(key)
+    if v is None:
+        if len(_CACHE) >= _CACHE_MAX:
+            _CACHE.clear()
+        v = _CACHE[key] = make()
+    return v
+
+
 def _layout(naming, bufs):
-    arr = (ctypes.c_void_p * len(bufs))(*[_ptr(b) for b in bufs])
-    return Layout(NAMINGS[naming], arr), arr
+    ptrs = tuple(map(_ptr, bufs))
+
+    def make():
+        arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+        return Layout(NAMINGS[naming], arr), arr
+
+    return _cached(("layout", naming, ptrs), make)
 
 
 def _i64(values):
     if values is None:
         return None
-    vals = [int(v) for v in values]
-    return (ctypes.c_int64 * max(1, len(vals)))(*vals)
+    vals = tuple(values)             # ints of any integer type hash by value
+    return _cached(("i64", vals),
+                   lambda: (ctypes.c_int64 * max(1, len(vals)))(*map(int, vals)))
 
 
 def collective(ins, outs, in_naming, out_naming, op, counts, displs=None, dtype=None,
@@ -173,7 +196,7 @@ def collective(ins, outs, in_naming, out_naming, op, counts, displs=None, dtype=
     P = len(ins)
     if len(outs) != P:
         raise ValueError("need as many output buffers as input buffers")
-    dt = _dtype_of(list(ins) + list(outs), dtype)
+    dt = _dtype_of(itertools.chain(ins, outs), dtype)
     lin, keep_in = _layout(in_naming, ins)
     lout, keep_out = _layout(out_naming, outs)
     c = _i64(counts)
