@@ -12,9 +12,11 @@
 //    destination's modulo 16 is read in aligned 16-byte blocks, and each
 //    lane shifts its block and its neighbour lane's block into place in
 //    registers (lane shuffle + v_alignbyte), never by unaligned or byte-wise
-//    memory accesses; wavefront rows follow the destination's 128-byte
-//    lines when there are several destinations and the sources' lines when
-//    there is one, so the larger side never touches a line twice;
+//    memory accesses; such wavefront rows follow the sources' 128-byte
+//    lines when there is one destination, so no source line is loaded by
+//    two rows (a second nontemporal load of a line fetches it from HBM
+//    again, while split destination lines merge in L2), and the
+//    destinations' lines for broadcasts, whose reads are a small share;
 //  * the reduce is a per-lane fold over the sources in ascending rank, in
 //    fp32 (bf16 widened exactly), with one final round to nearest even for
 //    a bf16 output; there is no cross-lane tree, so the summation order is
@@ -267,84 +269,6 @@ __device__ __forceinline__ u32x4 next_lane(u32x4 v) {
   return o;
 }
 
-constexpr uint32_t kRow = 56;  // units a wavefront row of the realigning body produces
-
-// One pass of the realigning body (see body_shifted).  kGuard = false for
-// passes whose every row, including the extra block each lane 56 reads, lies
-// inside the tile.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard>
-__device__ __forceinline__ void pass_shifted(const uint64_t *base, const uint32_t *lim, int ns,
-                                             const uint64_t *db, int nd, uint32_t nunits,
-                                             const uint32_t *sh, uint32_t u0) {
-  constexpr int kS = Op::kSum ? kMaxRanks : 1;
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t wave = threadIdx.x >> 6;
-  u32x4 x[kU][kS];
-#pragma unroll
-  for (int k = 0; k < kU; ++k) {
-    const uint32_t u = u0 + (wave * kU + uint32_t(k)) * kRow + lane;
-#pragma unroll
-    for (int i = 0; i < kS; ++i) {
-      // Unguarded passes: lanes past 56 read blocks of the next row, still
-      // inside the tile.  The tail pass clamps every lane to the source's
-      // last block instead of branching (see pass_aligned).
-      const uint32_t uc = (kGuard && u >= lim[i]) ? lim[i] - 1 : u;
-      x[k][i] = ld16<kNTL>(base[i] + uint64_t(uc * 16u));
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kU; ++k) {
-    const uint32_t u = u0 + (wave * kU + uint32_t(k)) * kRow + lane;
-    u32x4 y[kS];
-#pragma unroll
-    for (int i = 0; i < kS; ++i) y[i] = funnel(x[k][i], next_lane(x[k][i]), sh[i]);
-    if (lane < kRow && (!kGuard || u < nunits)) {
-      u32x4 v;
-      if constexpr (!Op::kSum) v = y[0];
-      else if constexpr (Op::kElem == 4) v = fold_f32(y, ns);
-      else v = fold_bf16(y, ns);
-      const uint64_t o = uint64_t(u * 16u);
-#pragma unroll
-      for (int j = 0; j < kMaxRanks + 1; ++j)
-        if (j < nd) st16<kNTS>(db[j] + o, v);
-    }
-  }
-}
-
-// Body of a tile when some source is not aligned like the destinations
-// (variable-length partitions at arbitrary element offsets).  A wavefront
-// row loads 57 consecutive aligned 16-byte blocks of each source, one per
-// lane, takes its right neighbour's block with a lane shuffle, and shifts
-// the pair into place, producing 56 destination units: 896 bytes, seven
-// whole 128-byte lines, so no store writes part of a line.  Consecutive rows
-// share one source line, which nontemporal loads fetch from HBM twice (one
-// line in eight more read traffic, measured), even when one wavefront takes
-// the two rows back to back as here; a tile with one destination therefore
-// uses the source-aligned body, and this one serves broadcasts, where the
-// reads are one stream of several.  Source i's blocks start at the aligned
-// address sa[i] - sh[i]; a source with sh[i] > 0 needs one block past its
-// last unit, which holds that unit's last bytes.
-template <class Op, int kU, bool kNTL, bool kNTS>
-__device__ __forceinline__ void body_shifted(const uint64_t *sa, int ns, const uint64_t *db,
-                                             int nd, uint32_t nunits, const uint32_t *sh) {
-  constexpr int kS = Op::kSum ? kMaxRanks : 1;
-  constexpr uint32_t kPass = kRow * (kThreads / 64) * kU;
-  uint64_t base[kS];
-  uint32_t lim[kS];
-#pragma unroll
-  for (int i = 0; i < kS; ++i) {
-    base[i] = sa[i] - sh[i];
-    lim[i] = nunits + (sh[i] ? 1u : 0u);               // blocks this source may load
-  }
-  uint32_t u0 = 0;
-  // an unguarded pass reads up to block u0 + kPass + 7 (lanes 57..63 of the
-  // last row), which must lie below every source's limit
-  for (; u0 + kPass + 8 <= nunits; u0 += kPass)
-    pass_shifted<Op, kU, kNTL, kNTS, false>(base, lim, ns, db, nd, nunits, sh, u0);
-  for (; u0 < nunits; u0 += kPass)
-    pass_shifted<Op, kU, kNTL, kNTS, true>(base, lim, ns, db, nd, nunits, sh, u0);
-}
-
 __device__ __forceinline__ u32x4 lane0(u32x4 v) {
   u32x4 o;
   o.x = __builtin_amdgcn_readfirstlane(v.x);
@@ -354,11 +278,12 @@ __device__ __forceinline__ u32x4 lane0(u32x4 v) {
   return o;
 }
 
-// One pass of the source-aligned body (see body_src_aligned).
-template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard>
-__device__ __forceinline__ void pass_src_aligned(const uint64_t *base, const uint32_t *lim, int ns,
-                                                 uint64_t db, uint32_t nunits, const uint32_t *sh,
-                                                 uint32_t u0) {
+// One pass of the row body (see body_rows).  kOne: a single destination
+// (a store without the guarded loop over destinations).
+template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard, bool kOne>
+__device__ __forceinline__ void pass_rows(const uint64_t *base, const uint32_t *lim, int ns,
+                                          const uint64_t *db, int nd, uint32_t nunits,
+                                          const uint32_t *sh, uint32_t u0) {
   constexpr int kS = Op::kSum ? kMaxRanks : 1;
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = threadIdx.x >> 6;
@@ -366,7 +291,7 @@ __device__ __forceinline__ void pass_src_aligned(const uint64_t *base, const uin
   u32x4 edge[kS];
   u32x4 x[kU][kS];
   // The block after the wavefront's last row, the same address in every
-  // lane, first and through the cache (see body_src_aligned).
+  // lane, first and through the cache (see body_rows).
 #pragma unroll
   for (int i = 0; i < kS; ++i) {
     uint32_t b = r0 + uint32_t(kU) * 64u;
@@ -399,33 +324,45 @@ __device__ __forceinline__ void pass_src_aligned(const uint64_t *base, const uin
       if constexpr (!Op::kSum) v = y[0];
       else if constexpr (Op::kElem == 4) v = fold_f32(y, ns);
       else v = fold_bf16(y, ns);
-      st16<kNTS>(db + uint64_t(u) * 16u, v);
+      const uint64_t o = uint64_t(u) * 16u;
+      if constexpr (kOne) {
+        st16<kNTS>(db[0] + o, v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kMaxRanks + 1; ++j)
+          if (j < nd) st16<kNTS>(db[j] + o, v);
+      }
     }
   }
 }
 
-// Body for one destination whose sources are not aligned like it
-// (variable-length partitions at arbitrary element offsets).  Rows are
-// aligned to the *sources'* 128-byte lines: a wavefront row loads 64
-// consecutive aligned blocks, exactly eight lines of source 0 and no block
-// of any other row, and produces the 64 destination units those blocks
-// cover; each wavefront takes kU consecutive rows.  Lane 63 of a row needs
-// one block past the row: the next row's first block, read from lane 0, or
-// after the wavefront's last row one extra block.  That extra block lies in
-// a line another wavefront streams; it is loaded first and as an ordinary
-// (cached) load, which measured fewer HBM bytes and more bandwidth than a
-// nontemporal one or a hand-over in LDS behind a barrier.  The stores are
-// off the destination's line phase: a wavefront's first and last lines are
-// shared with neighbour rows, which costs less than the alternative of
-// rows aligned to the destination, where every row re-reads a source line.
-// sa[] holds the sources at the first unit, where source 0's aligned blocks
-// start on a 128-byte line; block b of source i is at sa[i] - sh[i] + 16 b,
-// and a source with sh[i] > 0 needs block nunits too, which holds its last
-// unit's last bytes.  An unguarded pass reads blocks up to u0 + kPass, so it
-// needs u0 + kPass < nunits.
-template <class Op, int kU, bool kNTL, bool kNTS>
-__device__ __forceinline__ void body_src_aligned(const uint64_t *sa, int ns, uint64_t db,
-                                                 uint32_t nunits, const uint32_t *sh) {
+// Body of a tile when some source is not on the destinations' 16-byte
+// phase (variable-length partitions at arbitrary element offsets).  Each
+// source is read as aligned 16-byte blocks; a wavefront row loads 64
+// consecutive blocks, one per lane, and each lane shifts its block and its
+// right neighbour's into place in registers (lane shuffle + v_alignbyte),
+// producing the 64 destination units the row covers; each wavefront takes
+// kU consecutive rows.  Lane 63 of a row needs one block past the row: the
+// next row's first block, read from lane 0, or after the wavefront's last
+// row one extra block, which lies in a line another wavefront streams: it
+// is loaded first and as an ordinary (cached) load, which measured fewer
+// HBM bytes and more bandwidth than a nontemporal one or a hand-over in LDS
+// behind a barrier.
+// Rows start on a 128-byte line of source 0 when there is one destination,
+// and on a destination line when there are several.  One side's lines are
+// then split between neighbouring rows.  Two nontemporal loads of one line
+// fetch it from HBM twice (measured: one line in eight more read traffic,
+// even when one wavefront takes both rows back to back), while two partial
+// stores to one line mostly merge in L2; so one destination gets
+// source-aligned rows (ReduceScatterV, AllToAllV), and a broadcast, whose
+// reads are one stream of several, gets destination-aligned ones.
+// sa[] holds the sources at the first unit; block b of source i is at
+// sa[i] - sh[i] + 16 b, and a source with sh[i] > 0 needs block nunits too,
+// which holds its last unit's last bytes.  An unguarded pass reads blocks
+// up to u0 + kPass, so it needs u0 + kPass < nunits.
+template <class Op, int kU, bool kNTL, bool kNTS, bool kOne>
+__device__ __forceinline__ void body_rows(const uint64_t *sa, int ns, const uint64_t *db, int nd,
+                                          uint32_t nunits, const uint32_t *sh) {
   constexpr int kS = Op::kSum ? kMaxRanks : 1;
   constexpr uint32_t kPass = 64u * (kThreads / 64) * kU;
   uint64_t base[kS];
@@ -437,21 +374,12 @@ __device__ __forceinline__ void body_src_aligned(const uint64_t *sa, int ns, uin
   }
   uint32_t u0 = 0;
   for (; u0 + kPass < nunits; u0 += kPass)
-    pass_src_aligned<Op, kU, kNTL, kNTS, false>(base, lim, ns, db, nunits, sh, u0);
+    pass_rows<Op, kU, kNTL, kNTS, false, kOne>(base, lim, ns, db, nd, nunits, sh, u0);
   for (; u0 < nunits; u0 += kPass)
-    pass_src_aligned<Op, kU, kNTL, kNTS, true>(base, lim, ns, db, nunits, sh, u0);
+    pass_rows<Op, kU, kNTL, kNTS, true, kOne>(base, lim, ns, db, nd, nunits, sh, u0);
 }
 
-template <class Op, int kU, bool kNTL, bool kNTS>
-__device__ __forceinline__ void units(const uint64_t *sa, int ns, const uint64_t *db, int nd,
-                                      uint32_t n, const uint32_t *sh, bool aligned) {
-  // the realigning body takes at least two consecutive rows per wavefront
-  constexpr int kUs = kU < 2 ? 2 : kU;
-  if (aligned) body_aligned<Op, kU, kNTL, kNTS>(sa, ns, db, nd, n);
-  else body_shifted<Op, kUs, kNTL, kNTS>(sa, ns, db, nd, n, sh);
-}
-
-// Whether a job's tiles take the source-aligned body: one destination, and
+// Whether a job's rows are aligned to its sources: one destination, and
 // some source off the destination's 16-byte phase (the offset between a
 // source and the destination is the same at every byte of a job).
 __device__ __forceinline__ bool src_rows(const Srcs &s, const Dsts &d) {
@@ -464,7 +392,7 @@ __device__ __forceinline__ bool src_rows(const Srcs &s, const Dsts &d) {
 
 // The address whose 128-byte lines a job's tile boundaries follow (a
 // boundary x satisfies (line_ref + x) % 128 == 0): the destination's, or for
-// the source-aligned body the destination shifted so that at a boundary the
+// rows aligned to the sources the destination shifted so that at a boundary the
 // destination is on a 16-byte unit and source 0's block containing it
 // starts a 128-byte line.  Then a full tile is whole source-aligned rows
 // with no head pass.  With e = (dst - src0) mod 128 the boundary sits where
@@ -480,8 +408,8 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
 // job's line_ref, x1 is the job's end or on such a boundary.  Layout:
 //   [x0, xh)   the head, < 128 bytes: the bytes before the first 16-byte
 //              unit of the destination and the units before the first row
-//              start (a destination line, or with the source-aligned body a
-//              unit whose source-0 block starts a line); element operations
+//              start (a destination line, or with rows aligned to the
+//              sources a unit whose source-0 block starts a line); element operations
 //              on wavefront 0
 //   [xh, xb)   the body: whole units, nontemporal stores when kNT
 //   [xb, x1)   < 16 bytes of tail: element operations on wavefront 3, in
@@ -530,17 +458,21 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
 #pragma unroll
   for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(xh);
   const bool ntl = kNT && (phase == 0 || nt_any_phase);
-  if (srows) {
-    // a sum holds eight sources per row, so two rows per wavefront (more
-    // measured slower); a copy holds one and takes the tile's unroll
-    constexpr int kUr = Op::kSum ? 2 : kU;
-    if (ntl) body_src_aligned<Op, kUr, true, kNT>(sa, s.n, db[0], nbody, sh);
-    else body_src_aligned<Op, kUr, false, kNT>(sa, s.n, db[0], nbody, sh);
+  if (any == 0) {
+    if (ntl) body_aligned<Op, kU, true, kNT>(sa, s.n, db, d.n, nbody);
+    else body_aligned<Op, kU, false, kNT>(sa, s.n, db, d.n, nbody);
     return;
   }
-  const bool aligned = any == 0;
-  if (ntl) units<Op, kU, true, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
-  else units<Op, kU, false, kNT>(sa, s.n, db, d.n, nbody, sh, aligned);
+  // a sum holds eight sources per row, so two rows per wavefront (more
+  // measured slower); a copy holds one and takes the tile's unroll
+  constexpr int kUr = Op::kSum ? 2 : kU;
+  if (d.n == 1) {
+    if (ntl) body_rows<Op, kUr, true, kNT, true>(sa, s.n, db, 1, nbody, sh);
+    else body_rows<Op, kUr, false, kNT, true>(sa, s.n, db, 1, nbody, sh);
+  } else {
+    if (ntl) body_rows<Op, kUr, true, kNT, false>(sa, s.n, db, d.n, nbody, sh);
+    else body_rows<Op, kUr, false, kNT, false>(sa, s.n, db, d.n, nbody, sh);
+  }
 }
 
 }  // namespace atom
