@@ -260,12 +260,24 @@ __device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const u
   if (u0 < nunits) pass_aligned<Op, kU, kNTL, kNTS, true>(sa, ns, db, nd, nunits, u0);
 }
 
+// Lane l receives lane l + 1's value (lane 63: unspecified).  kDpp: a DPP
+// wavefront shift (wave_shl:1), a plain VALU move; else __shfl_down, which
+// goes through the LDS crossbar (ds_bpermute).  Copies take the DPP move;
+// a sum row keeps the VALU busy (eight sources widened, added and rounded),
+// so there the crossbar, which runs beside it, measured faster.
+template <bool kDpp>
+__device__ __forceinline__ uint32_t next_lane(uint32_t v) {
+  if constexpr (kDpp) return uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x130, 0xF, 0xF, false));
+  else return __shfl_down(v, 1);
+}
+
+template <bool kDpp>
 __device__ __forceinline__ u32x4 next_lane(u32x4 v) {
   u32x4 o;
-  o.x = __shfl_down(v.x, 1);
-  o.y = __shfl_down(v.y, 1);
-  o.z = __shfl_down(v.z, 1);
-  o.w = __shfl_down(v.w, 1);
+  o.x = next_lane<kDpp>(v.x);
+  o.y = next_lane<kDpp>(v.y);
+  o.z = next_lane<kDpp>(v.z);
+  o.w = next_lane<kDpp>(v.w);
   return o;
 }
 
@@ -315,7 +327,7 @@ __device__ __forceinline__ void pass_rows(const uint64_t *base, const uint32_t *
     for (int i = 0; i < kS; ++i) {
       // lane 63's right neighbour: the next row's first block, or the edge
       const u32x4 after = k + 1 < kU ? lane0(x[k + 1 < kU ? k + 1 : k][i]) : edge[i];
-      u32x4 hi = next_lane(x[k][i]);
+      u32x4 hi = next_lane<!Op::kSum>(x[k][i]);
       if (lane == 63u) hi = after;
       y[i] = funnel(x[k][i], hi, sh[i]);
     }

@@ -212,6 +212,36 @@ def test_reduce_one_destination_shifted_sources(purlin, dtype, chunk):
                            [shift] * P, [0] * P)
 
 
+@pytest.mark.parametrize("unroll", ["0", "1", "2"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", NAMES)
+def test_rows_at_pass_boundaries(purlin, name, dtype, unroll):
+    """Misaligned partitions whose unit counts sit on and around the row
+    body's passes (512 units for sums, 1024 / 2048 / 4096 for copies at
+    unroll 0 / 1 / 2), at every source phase; one chunk per job so a tile
+    is a whole partition."""
+    import os
+    P = 8
+    print("case rows-pass", name, dtype, unroll, flush=True)
+    esz = 4 if dtype == "f32" else 2
+    per = 16 // esz
+    rng = np.random.default_rng([29, NAMES.index(name), esz, int(unroll)])
+    kpass = 512 if name in ("allreduce", "reducescatter") else 1024 << int(unroll)
+    units = [kpass - 1, kpass, kpass + 1, 2 * kpass - 1, 2 * kpass + 1, 63, 64, 65]
+    nparts = P * P if name == "alltoall" else P
+    sizes = [units[k % len(units)] * per + int(rng.integers(0, per)) for k in range(nparts)]
+    counts = pins.counts_for(name, P, sizes)
+    ins, outs = pins.make_case(name, P, counts, dtype, rng, None, sentinel=0x7E7E)
+    os.environ["PURLIN_UNROLL"] = unroll
+    try:
+        purlin.set_policy(chunk_bytes=1 << 20, zero_staging="zs")
+        for shift in (1, per // 2, per - 1):
+            in_shifts = [(shift + r) % per for r in range(P)] if name == "allreduce" else [shift] * P
+            oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, None, in_shifts, [0] * P)
+    finally:
+        os.environ.pop("PURLIN_UNROLL", None)
+
+
 def test_overlap_checks_survive_the_pointer_cache(purlin):
     """The per-call overlap check is skipped only for the same plan and buffers."""
     import torch
