@@ -291,8 +291,12 @@ __device__ __forceinline__ u32x4 lane0(u32x4 v) {
 }
 
 // One pass of the row body (see body_rows).  kOne: a single destination
-// (a store without the guarded loop over destinations).
-template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard, bool kOne>
+// (a store without the guarded loop over destinations).  kFold (sums whose
+// sources all share one 16-byte phase): a block of every source then holds
+// the same elements at the same places, so the raw blocks are folded first
+// and only the folded block is shifted into place: one shift per unit
+// instead of one per source, and the same rounded values.
+template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard, bool kOne, bool kFold>
 __device__ __forceinline__ void pass_rows(const uint64_t *base, const uint32_t *lim, int ns,
                                           const uint64_t *db, int nd, uint32_t nunits,
                                           const uint32_t *sh, uint32_t u0) {
@@ -318,6 +322,32 @@ __device__ __forceinline__ void pass_rows(const uint64_t *base, const uint32_t *
       const uint32_t b = (kGuard && u >= lim[i]) ? lim[i] - 1 : u;
       x[k][i] = ld16<kNTL>(base[i] + uint64_t(b) * 16u);
     }
+  }
+  if constexpr (kFold) {
+    static_assert(Op::kSum, "folding first applies to sums");
+    u32x4 f[kU];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) f[k] = Op::kElem == 4 ? fold_f32(x[k], ns) : fold_bf16(x[k], ns);
+    const u32x4 fe = Op::kElem == 4 ? fold_f32(edge, ns) : fold_bf16(edge, ns);
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const uint32_t u = r0 + uint32_t(k) * 64u + lane;
+      const u32x4 after = k + 1 < kU ? lane0(f[k + 1 < kU ? k + 1 : k]) : fe;
+      u32x4 hi = next_lane<false>(f[k]);
+      if (lane == 63u) hi = after;
+      const u32x4 v = funnel(f[k], hi, sh[0]);
+      if (!kGuard || u < nunits) {
+        const uint64_t o = uint64_t(u) * 16u;
+        if constexpr (kOne) {
+          st16<kNTS>(db[0] + o, v);
+        } else {
+#pragma unroll
+          for (int j = 0; j < kMaxRanks + 1; ++j)
+            if (j < nd) st16<kNTS>(db[j] + o, v);
+        }
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int k = 0; k < kU; ++k) {
@@ -372,7 +402,7 @@ __device__ __forceinline__ void pass_rows(const uint64_t *base, const uint32_t *
 // sa[i] - sh[i] + 16 b, and a source with sh[i] > 0 needs block nunits too,
 // which holds its last unit's last bytes.  An unguarded pass reads blocks
 // up to u0 + kPass, so it needs u0 + kPass < nunits.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kOne>
+template <class Op, int kU, bool kNTL, bool kNTS, bool kOne, bool kFoldOk>
 __device__ __forceinline__ void body_rows(const uint64_t *sa, int ns, const uint64_t *db, int nd,
                                           uint32_t nunits, const uint32_t *sh) {
   constexpr int kS = Op::kSum ? kMaxRanks : 1;
@@ -384,11 +414,22 @@ __device__ __forceinline__ void body_rows(const uint64_t *sa, int ns, const uint
     base[i] = sa[i] - sh[i];
     lim[i] = nunits + (sh[i] ? 1u : 0u);
   }
+  uint32_t same = 1;
+#pragma unroll
+  for (int i = 1; i < kS; ++i) same &= sh[i] == sh[0] ? 1u : 0u;
   uint32_t u0 = 0;
+  if (kFoldOk && Op::kSum && same) {
+    constexpr bool kF = kFoldOk && Op::kSum;
+    for (; u0 + kPass < nunits; u0 += kPass)
+      pass_rows<Op, kU, kNTL, kNTS, false, kOne, kF>(base, lim, ns, db, nd, nunits, sh, u0);
+    for (; u0 < nunits; u0 += kPass)
+      pass_rows<Op, kU, kNTL, kNTS, true, kOne, kF>(base, lim, ns, db, nd, nunits, sh, u0);
+    return;
+  }
   for (; u0 + kPass < nunits; u0 += kPass)
-    pass_rows<Op, kU, kNTL, kNTS, false, kOne>(base, lim, ns, db, nd, nunits, sh, u0);
+    pass_rows<Op, kU, kNTL, kNTS, false, kOne, false>(base, lim, ns, db, nd, nunits, sh, u0);
   for (; u0 < nunits; u0 += kPass)
-    pass_rows<Op, kU, kNTL, kNTS, true, kOne>(base, lim, ns, db, nd, nunits, sh, u0);
+    pass_rows<Op, kU, kNTL, kNTS, true, kOne, false>(base, lim, ns, db, nd, nunits, sh, u0);
 }
 
 // Whether a job's rows are aligned to its sources: one destination, and
@@ -416,7 +457,11 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
   return d.b[0] - uint64_t((e + 15u) & 112u);
 }
 
-// One tile: job bytes [x0, x1).  x0 is 0 or on a 128-byte boundary of the
+// One tile: job bytes [x0, x1).  kFoldOk: sum rows whose sources share one
+// phase may fold before shifting (more registers; the staged kernel, whose
+// owner mixes its own input with staging slots, leaves it out).  kRows =
+// false builds the tile without the row bodies, for launches whose every
+// job is aligned: a smaller kernel.  x0 is 0 or on a 128-byte boundary of the
 // job's line_ref, x1 is the job's end or on such a boundary.  Layout:
 //   [x0, xh)   the head, < 128 bytes: the bytes before the first 16-byte
 //              unit of the destination and the units before the first row
@@ -430,7 +475,7 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
 // nontemporal when every source sits on the destinations' 128-byte phase,
 // or when nt_any_phase asks for it (measured faster for misaligned
 // variable-length partitions too).  A tile spans less than 4 GiB.
-template <class Op, int kU, bool kNT>
+template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
                                      bool nt_any_phase = false) {
   if (x1 <= x0) return;
@@ -475,15 +520,23 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
     else body_aligned<Op, kU, false, kNT>(sa, s.n, db, d.n, nbody);
     return;
   }
+  if constexpr (!kRows) {
+    // Built without the row bodies (the launch checked that every job is
+    // aligned); should a misaligned tile arrive anyway, it is still right,
+    // element by element.
+    for (int64_t y = xh; y < xb; y += int64_t(kThreads) * Op::kElem)
+      elements<Op>(s, d, y, y + int64_t(kThreads) * Op::kElem < xb ? y + int64_t(kThreads) * Op::kElem : xb);
+    return;
+  }
   // a sum holds eight sources per row, so two rows per wavefront (more
   // measured slower); a copy holds one and takes the tile's unroll
   constexpr int kUr = Op::kSum ? 2 : kU;
   if (d.n == 1) {
-    if (ntl) body_rows<Op, kUr, true, kNT, true>(sa, s.n, db, 1, nbody, sh);
-    else body_rows<Op, kUr, false, kNT, true>(sa, s.n, db, 1, nbody, sh);
+    if (ntl) body_rows<Op, kUr, true, kNT, true, kFoldOk>(sa, s.n, db, 1, nbody, sh);
+    else body_rows<Op, kUr, false, kNT, true, kFoldOk>(sa, s.n, db, 1, nbody, sh);
   } else {
-    if (ntl) body_rows<Op, kUr, true, kNT, false>(sa, s.n, db, d.n, nbody, sh);
-    else body_rows<Op, kUr, false, kNT, false>(sa, s.n, db, d.n, nbody, sh);
+    if (ntl) body_rows<Op, kUr, true, kNT, false, kFoldOk>(sa, s.n, db, d.n, nbody, sh);
+    else body_rows<Op, kUr, false, kNT, false, kFoldOk>(sa, s.n, db, d.n, nbody, sh);
   }
 }
 

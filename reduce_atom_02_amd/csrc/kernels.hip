@@ -59,7 +59,7 @@ __device__ __forceinline__ void tile_bounds(uint64_t ref, int64_t n, int64_t C, 
 // reaches all ranks without a second pass).  Tiles are dealt to a resident
 // grid in grid-stride order; the tile list holds the share of rank 0, then
 // rank 1, and so on.
-template <class Op, int kU, bool kNTL, bool kNTS>
+template <class Op, int kU, bool kNTL, bool kNTS, bool kRows>
 __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
   // A workgroup whose entry wait failed skips its tiles but still counts
   // itself out, so the next launch's exit check is not poisoned.
@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     int64_t x0, x1;
     tile_bounds(atom::line_ref(s, d), jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
                 p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
-    atom::tile<Op, kU, kNTL>(s, d, x0, x1, p.nt_any_phase != 0);
+    atom::tile<Op, kU, kNTL, true, kRows>(s, d, x0, x1, p.nt_any_phase != 0);
   }
   if (p.sync) snac::exit_notify(p);
 }
@@ -221,7 +221,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       d.b[0] = to_own ? own : scat;
 #pragma unroll
       for (int k = 1; k < kMaxRanks + 1; ++k) d.b[k] = scat;
-      atom::tile<Op, kU, kNTL>(s, d, x0, x1);
+      atom::tile<Op, kU, kNTL, false>(s, d, x0, x1);
       snac::drain_workgroup();
       if (threadIdx.x == 0) {
         for (int k = 0; k < sj.n_stage; ++k)
@@ -387,18 +387,21 @@ hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts,
 namespace {
 
 template <class Op, int kU, bool kNT>
-void *zs_fn() { return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT>); }
+void *zs_fn(bool rows) {
+  return rows ? reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true>)
+              : reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, false>);
+}
 template <class Op, int kU, bool kNT>
 void *st_fn() { return reinterpret_cast<void *>(&staged_kernel<Op, kU, kNT, kNT>); }
 
 // Unroll depth: 16-byte units each lane keeps in flight per source.
 template <class Op, int kU0, int kU1, int kU2>
-void *pick(bool staged, bool nt, int unroll_sel) {
+void *pick(bool staged, bool nt, int unroll_sel, bool rows) {
   if (staged) return nt ? st_fn<Op, kU1, true>() : st_fn<Op, kU1, false>();
   switch (unroll_sel) {
-    case 0: return nt ? zs_fn<Op, kU0, true>() : zs_fn<Op, kU0, false>();
-    case 2: return nt ? zs_fn<Op, kU2, true>() : zs_fn<Op, kU2, false>();
-    default: return nt ? zs_fn<Op, kU1, true>() : zs_fn<Op, kU1, false>();
+    case 0: return nt ? zs_fn<Op, kU0, true>(rows) : zs_fn<Op, kU0, false>(rows);
+    case 2: return nt ? zs_fn<Op, kU2, true>(rows) : zs_fn<Op, kU2, false>(rows);
+    default: return nt ? zs_fn<Op, kU1, true>(rows) : zs_fn<Op, kU1, false>(rows);
   }
 }
 
@@ -411,25 +414,25 @@ int unroll_of(KernelKind kind, int unroll_sel) {
   return kind == KernelKind::kCopy ? copy_u[sel] : sum_u[sel];
 }
 
-void *kernel_fn(KernelKind kind, bool staged, bool nt, int unroll_sel) {
+void *kernel_fn(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows) {
   switch (kind) {
-    case KernelKind::kCopy: return pick<atom::CopyOp, 4, 8, 16>(staged, nt, unroll_sel);
-    case KernelKind::kSumF32: return pick<atom::SumF32, 1, 2, 4>(staged, nt, unroll_sel);
-    default: return pick<atom::SumBf16, 1, 2, 4>(staged, nt, unroll_sel);
+    case KernelKind::kCopy: return pick<atom::CopyOp, 4, 8, 16>(staged, nt, unroll_sel, rows);
+    case KernelKind::kSumF32: return pick<atom::SumF32, 1, 2, 4>(staged, nt, unroll_sel, rows);
+    default: return pick<atom::SumBf16, 1, 2, 4>(staged, nt, unroll_sel, rows);
   }
 }
 
-hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, int grid,
-                     hipStream_t stream) {
+hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, bool rows,
+                     int grid, hipStream_t stream) {
   void *args[] = {const_cast<LaunchPlan *>(&p)};
-  return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel), dim3(grid), dim3(kThreads), args,
-                         0, stream);
+  return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel, rows), dim3(grid), dim3(kThreads),
+                         args, 0, stream);
 }
 
 hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStream_t stream) {
   void *args[] = {const_cast<StagedPlan *>(&p)};
-  return hipLaunchKernel(kernel_fn(kind, true, nt, 1), dim3(p.total_roles), dim3(kThreads), args,
-                         0, stream);
+  return hipLaunchKernel(kernel_fn(kind, true, nt, 1, true), dim3(p.total_roles), dim3(kThreads),
+                         args, 0, stream);
 }
 
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,
@@ -440,10 +443,10 @@ hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int gri
   return hipGetLastError();
 }
 
-hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel,
+hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
                                int *blocks) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      blocks, kernel_fn(kind, staged, nt, staged ? 1 : unroll_sel), kThreads, 0);
+      blocks, kernel_fn(kind, staged, nt, staged ? 1 : unroll_sel, staged || rows), kThreads, 0);
 }
 
 }  // namespace purlin

@@ -10,15 +10,17 @@ enum class KernelKind { kCopy, kSumF32, kSumBf16 };
 
 // nt: nontemporal loads and stores.  unroll_sel picks one of three unroll
 // depths (units in flight per lane and source): copy 4 / 8 / 16, sum 1 / 2 / 4.
-hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, int grid,
-                     hipStream_t stream);
+// rows = false: the kernel built without the row bodies, for launches whose
+// every job has its sources on its destinations' 16-byte phase.
+hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, bool rows,
+                     int grid, hipStream_t stream);
 hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStream_t stream);
 int unroll_of(KernelKind kind, int unroll_sel);
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,
                               hipStream_t stream);
 hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts, int n_dst,
                           int64_t bytes, int grid, hipStream_t stream);
-hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel,
+hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
                                int *blocks);
 
 }  // namespace purlin

@@ -29,7 +29,7 @@ struct DeviceState {
   int64_t slot_flag_bytes = 0;
   uint32_t epoch = 0;
   uint32_t exit_total[2][kExitSlots] = {};  // per parity and slot, all launches so far
-  int occ[3][2][2][3] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
+  int occ[3][2][2][3][2] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
 };
 
 std::vector<DeviceState> &devices() {
@@ -125,11 +125,11 @@ purlin_status device_state(DeviceState **out) {
   return PURLIN_OK;
 }
 
-int occupancy(DeviceState &s, KernelKind kind, bool staged, bool nt, int unroll_sel) {
-  int &o = s.occ[int(kind)][staged ? 1 : 0][nt ? 1 : 0][unroll_sel];
+int occupancy(DeviceState &s, KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows) {
+  int &o = s.occ[int(kind)][staged ? 1 : 0][nt ? 1 : 0][unroll_sel][rows ? 1 : 0];
   if (o == 0) {
     int b = 0;
-    if (max_resident_per_cu(kind, staged, nt, unroll_sel, &b) != hipSuccess || b < 1) b = 1;
+    if (max_resident_per_cu(kind, staged, nt, unroll_sel, rows, &b) != hipSuccess || b < 1) b = 1;
     o = b;
   }
   return o;
@@ -310,7 +310,19 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
   const AutoPolicy ap = auto_policy(kind, broadcast);
   int unroll_sel = unroll_env();
   if (unroll_sel < 0 || unroll_sel > 2) unroll_sel = ap.unroll_sel;
-  const int capacity = ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel);
+  // Whether some job has a source off its destinations' 16-byte phase and
+  // so needs the kernel with the row bodies.  (Broadcast destinations are
+  // congruent modulo 16 once launch_jobs has split the others.)
+  bool rows = false;
+  for (const Job &jb : jobs) {
+    const uint64_t d0 = uint64_t(reinterpret_cast<uintptr_t>(out->bufs[jb.dst < 0 ? 0 : jb.dst])) +
+                        uint64_t(jb.dst_off);
+    for (int i = jb.src < 0 ? 0 : jb.src; i < (jb.src < 0 ? P : jb.src + 1); ++i) {
+      const uint64_t a = uint64_t(reinterpret_cast<uintptr_t>(in->bufs[i])) + uint64_t(jb.src_off);
+      rows |= ((a - d0) & 15u) != 0;
+    }
+  }
+  const int capacity = ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows);
 
   if (++ds->epoch == 0) ds->epoch = 1;  // epoch 0 would match freshly cleared flags
   const int64_t wd_ns = pol.watchdog_ns ? pol.watchdog_ns : kDefaultWatchdogNs;
@@ -344,7 +356,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     // phase too (variable-length partitions), measured at 16 MiB - 1 GiB.
     lp.nt_any_phase = env_i64("PURLIN_NT_ANY_PHASE", 1) ? 1 : 0;
     for (int k = 0; k < kExitSlots; ++k) lp.exit_expect[k] = ds->exit_total[(ds->epoch - 1u) & 1u][k];
-    err = launch_zs(lp, kind, nt, unroll_sel, grid, stream);
+    err = launch_zs(lp, kind, nt, unroll_sel, rows, grid, stream);
     if (err == hipSuccess && lp.sync) {
       // workgroup b counts on slot b % kExitSlots
       for (int k = 0; k < kExitSlots; ++k)
