@@ -98,8 +98,13 @@ def measured_traffic(kernel, T, names, variant):
     return None if k is None else int(k["traffic_per_launch"])
 
 
-def kernel_of(name):
-    return "zs_kernel<SumBf16>" if SPECS[name][2] == "sum" else "zs_kernel<CopyOp>"
+def kernel_of(name, rows):
+    """The kernel a collective's launch ran, named as in the rocprofv3
+    summaries: the operation and whether it was the build with the
+    realigning row bodies (some source off its destinations' 16-byte phase)
+    or the aligned-only one."""
+    op = "SumBf16" if SPECS[name][2] == "sum" else "CopyOp"
+    return "zs_kernel<%s,%s>" % (op, "rows" if rows else "aligned")
 
 
 def cpu_baseline(T_sample, names):
@@ -423,7 +428,8 @@ def main():
                      "hbm_frac": round(s["bmin"] / p50 / HBM_PEAK, 4),
                      "bmin_bytes": s["bmin"], "grid": launch[name]["grid"],
                      "chunk_bytes": launch[name]["chunk_bytes"]}
-        k = kern.setdefault(kernel_of(name), {"bytes": 0, "time": 0.0, "launches": 0})
+        k = kern.setdefault(kernel_of(name, launch[name]["rows"]),
+                            {"bytes": 0, "time": 0.0, "launches": 0})
         k["bytes"] += s["bmin"] * len(ts)
         k["time"] += sum(ts)
         k["launches"] += len(ts)

@@ -108,6 +108,9 @@ typedef struct {
   int64_t bytes_min;     /* compulsory HBM bytes: inputs read once + outputs written once */
   int32_t njobs;
   int32_t sync;
+  int32_t rows;          /* 1 if the kernel with the realigning row bodies ran (some source
+                            off its destinations' 16-byte phase), 0 if the aligned-only one */
+  int32_t reserved;
 } purlin_launch_info;
 
 /*

@@ -365,6 +365,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     }
     info.grid = grid;
     info.zero_staging = 1;
+    info.rows = rows ? 1 : 0;
     info.chunk_bytes = chunk;
     info.tiles = lp.total_tiles;
     info.sync = lp.sync;
@@ -423,6 +424,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     err = launch_staged(sp, kind, nt, stream);
     info.grid = sp.total_roles;
     info.zero_staging = 0;
+    info.rows = 1;
     info.depth = sp.depth;
     info.chunk_bytes = chunk;
     info.tiles = sp.base.total_tiles;
