@@ -119,6 +119,24 @@ def moe_rows(rank, seed=0, tokens=4096, experts=256, topk=8, P=8, dedup=True):
     return rows
 
 
+def moe_weights(rank, seed=0, tokens=4096, experts=256, topk=8, P=8):
+    """Combine weights aligned with ``moe_rows(rank)`` (deduplicated routing):
+    for each (token, destination rank) the sum of the token's softmax gate
+    values (over its top-k logits, float32) of the experts on that rank."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 5, rank, 1]))
+    logits = rng.standard_normal((tokens, experts), dtype=np.float32)
+    top = np.argsort(-logits, axis=1, kind="stable")[:, :topk]
+    sel = np.take_along_axis(logits, top, axis=1)
+    g = np.exp(sel - sel.max(axis=1, keepdims=True)).astype(np.float32)
+    g = (g / g.sum(axis=1, keepdims=True)).astype(np.float32)
+    dest = top // (experts // P)
+    out = []
+    for j in range(P):
+        per_tok = np.where(dest == j, g, np.float32(0)).sum(axis=1, dtype=np.float32)
+        out.append(per_tok[(dest == j).any(axis=1)].astype(np.float32))
+    return out
+
+
 def moe_counts(P=8, hidden=7168, seed=0, **kw):
     """P x P element counts (row-major, [src * P + dst]) of the MoE dispatch."""
     counts = []
