@@ -153,7 +153,9 @@ PURLIN_API purlin_status purlin_collective(const purlin_layout *in, const purlin
 
 /* Synchronize `stream`, then read and clear the device status word of the
  * current device: PURLIN_ERR_TIMEOUT if any wait expired since the last
- * check, PURLIN_ERR_HIP if the synchronization failed, else PURLIN_OK. */
+ * check, else PURLIN_ERR_INVALID_ARG if a device-side argument check failed
+ * (MoE indices), PURLIN_ERR_HIP if the synchronization failed, else
+ * PURLIN_OK. */
 PURLIN_API purlin_status purlin_check(hipStream_t stream);
 
 /* Replace the policy (NULL restores the defaults).  Environment variables
@@ -173,7 +175,58 @@ PURLIN_API purlin_status purlin_plan_describe(const purlin_layout *in, const pur
                                    const int64_t *counts, const int64_t *displs,
                                    purlin_segment *segs, int64_t *n_segs);
 
-/* Measurement: the launch shape of the most recent successful call. */
+/*
+ * MoE dispatch (expert parallelism; the MoE call sites of AllToAll in Table 2
+ * of the Purlin pages) with the token permutation folded into the exchange:
+ * an AllToAllV whose send rows are read by token index.
+ *
+ *   x[i]       rank i's token rows, x_rows[i] rows of row_bytes bytes (input)
+ *   idx[i]     device int32 array: rank i's entries, the row indices to send,
+ *              grouped by destination rank: counts[i*P + j] entries for rank j,
+ *              group j after group j-1 (input)
+ *   counts     host, P*P row counts, [i*P + j] = rows from rank i to rank j
+ *   x_rows     host, P row counts of the x[i]
+ *   y[j]       rank j's received rows, sum_i counts[i*P + j] rows: for i
+ *              ascending, rows x[i][idx[i][group j]] in entry order (output)
+ *
+ * Rows are moved as bytes (row_bytes even, buffers 2-byte aligned; 16-byte
+ * alignment takes the faster kernel).  Ownership as purlin_collective.
+ * Synchronous errors: INVALID_ARG for P outside [1, 8], a NULL array or
+ * buffer that holds data, a negative count, odd row_bytes, entries for a
+ * rank with no rows, an output overlapping an input or another output.
+ * Asynchronous: an index outside [0, x_rows[i]) skips its row and makes the
+ * next purlin_check return INVALID_ARG.  Asynchronous on `stream`.
+ */
+PURLIN_API purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P,
+                                             int64_t row_bytes, const int32_t *const *idx,
+                                             const int64_t *counts, const int64_t *x_rows,
+                                             hipStream_t stream);
+
+/*
+ * MoE combine: the reverse exchange of purlin_moe_dispatch with a weighted
+ * sum per token.  y[j] holds rank j's rows in dispatch order (bf16, input);
+ * w[i] is a device float array, one weight per entry of idx[i] (input);
+ * out[i] gets x_rows[i] bf16 rows:
+ *
+ *   out[i][t] = RNE_bf16( fp32 left fold from +0, over the entries (j, k)
+ *               of idx[i] with idx[i][group j + k] == t in ascending j then
+ *               k, of  w[i][entry] * y[j][row of (i, j) + k] )
+ *
+ * each product rounded to fp32 before its add.  A token routed nowhere gets
+ * +0.  One row per (token, destination rank): a token twice in one group is
+ * reported.  row_bytes a multiple of 16 and every buffer 16-byte aligned.
+ * The library keeps a table of sum(x_rows) * P 8-byte words (allocated on
+ * the first call that needs it, freed by purlin_release).  Errors as
+ * purlin_moe_dispatch, plus INVALID_ARG for misalignment or a NULL weight
+ * array that holds entries; a duplicate token in a group also makes the
+ * next purlin_check return INVALID_ARG (that token's row is unspecified).
+ */
+PURLIN_API purlin_status purlin_moe_combine(void *const *y, void *const *out, int P,
+                                            int64_t row_bytes, const int32_t *const *idx,
+                                            const float *const *w, const int64_t *counts,
+                                            const int64_t *x_rows, hipStream_t stream);
+
+/* Measurement: the launch shape of the most recent successful call. *//* Measurement: the launch shape of the most recent successful call. */
 PURLIN_API purlin_status purlin_last_launch(purlin_launch_info *info);
 
 /* Measurement: a plain 128-bit streaming copy of `bytes` bytes (both

@@ -302,6 +302,153 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
   }
 }
 
+// ---- MoE dispatch / combine --------------------------------------------------
+// Expert-parallel dispatch and combine are among the inference call sites of
+// Purlin's AllToAll (Table 2).  Here the token permutation is folded into the
+// exchange: dispatch reads each send row by its token index (no permuted send
+// buffer), and combine reads the returned rows and folds them per token.
+
+__device__ __forceinline__ void flag_bad_arg(const LaunchPlan &p) {
+  __hip_atomic_fetch_or(&p.flags[kFlagStatus], kStatusBadArg, __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One row per tile: row k of pair (i, j) is row idx[i][group j + k] of x[i],
+// written to row pos_ij + k of y[j]; an index outside x[i] is skipped and
+// reported through the status word.
+template <int kU, bool kNT, bool kRows>
+__global__ void __launch_bounds__(kThreads) moe_dispatch_kernel(const MoePlan m) {
+  const LaunchPlan &p = m.base;
+  const bool run = !p.sync || snac::entry(p);
+  int t = run ? int(blockIdx.x) : p.total_tiles;
+  int q = t < p.total_tiles ? job_of_tile(p, t) : 0;
+  for (; t < p.total_tiles; t += gridDim.x) {
+    if (t >= p.tile_begin[q + 1]) q = job_of_tile(p, t);
+    const Job jb = p.jobs[q];
+    const int64_t k = t - p.tile_begin[q];
+    const int64_t tok = m.idx[jb.src][jb.src_off + k];
+    if (tok < 0 || tok >= m.x_rows[jb.src]) {
+      if (threadIdx.x == 0) flag_bad_arg(p);
+      continue;
+    }
+    atom::Srcs s;
+    s.n = 1;
+    const uint64_t a = uint64_t(p.in[jb.src]) + uint64_t(tok) * uint64_t(m.row_bytes);
+#pragma unroll
+    for (int r = 0; r < kMaxRanks; ++r) s.a[r] = a;
+    atom::Dsts d;
+    d.n = 1;
+    const uint64_t b = uint64_t(p.out[jb.dst]) + uint64_t(jb.dst_off) + uint64_t(k) * uint64_t(m.row_bytes);
+#pragma unroll
+    for (int r = 0; r < kMaxRanks + 1; ++r) d.b[r] = b;
+    atom::tile<atom::CopyOp, kU, kNT, true, kRows>(s, d, 0, m.row_bytes, true);
+  }
+  if (p.sync) snac::exit_notify(p);
+}
+
+// Combine, first pass: for every entry (i, j, k) the slot (token, j) of
+// rank i's table gets (epoch, k + 1).  Entries of earlier launches carry an
+// older epoch, so the table is never cleared; a slot already holding this
+// launch's epoch is a token twice in one group, which is reported.
+__global__ void __launch_bounds__(kThreads) moe_inverse_kernel(const MoePlan m) {
+  const LaunchPlan &p = m.base;
+  const int64_t total = m.ent_base[p.P];
+  for (int64_t e = int64_t(blockIdx.x) * kThreads + threadIdx.x; e < total;
+       e += int64_t(gridDim.x) * kThreads) {
+    int i = 0;
+    for (int r = 1; r < kMaxRanks; ++r)
+      if (r < p.P && m.ent_base[r] <= e) i = r;
+    const int64_t ei = e - m.ent_base[i];
+    int j = 0;
+    for (int r = 1; r < kMaxRanks; ++r)
+      if (r < p.P && p.jobs[i * p.P + r].src_off <= ei) j = r;
+    const int64_t k = ei - p.jobs[i * p.P + j].src_off;
+    const int64_t tok = m.idx[i][ei];
+    if (tok < 0 || tok >= m.x_rows[i]) {
+      flag_bad_arg(p);
+      continue;
+    }
+    const uint64_t v = (uint64_t(p.epoch) << 32) | uint64_t(k + 1);
+    const uint64_t old = __hip_atomic_exchange(&m.inv[(m.inv_base[i] + tok) * p.P + j], v,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (uint32_t(old >> 32) == p.epoch) flag_bad_arg(p);
+  }
+}
+
+// Combine, second pass: one token row per tile.  The row's contributions
+// are the table's slots of this epoch, in ascending destination rank; each
+// lane folds its 16-byte units as acc = acc + w * y from +0 in fp32, every
+// product rounded before the add (no contraction), then rounds once to
+// bf16.  Rows and buffers are 16-byte aligned (checked by the host).
+template <int kU, bool kNT>
+__global__ void __launch_bounds__(kThreads) moe_combine_kernel(const MoePlan m) {
+#pragma clang fp contract(off)
+  const LaunchPlan &p = m.base;
+  const bool run = !p.sync || snac::entry(p);
+  const int64_t rows = m.inv_base[p.P];
+  const uint32_t nunits = uint32_t(m.row_bytes >> 4);
+  for (int64_t r = run ? int64_t(blockIdx.x) : rows; r < rows; r += gridDim.x) {
+    int i = 0;
+    for (int q = 1; q < kMaxRanks; ++q)
+      if (q < p.P && m.inv_base[q] <= r) i = q;
+    const int64_t t = r - m.inv_base[i];
+    const uint64_t dst = uint64_t(p.out[i]) + uint64_t(t) * uint64_t(m.row_bytes);
+    uint64_t src[kMaxRanks];
+    float wt[kMaxRanks];
+    bool on[kMaxRanks];
+#pragma unroll
+    for (int j = 0; j < kMaxRanks; ++j) {
+      on[j] = false;
+      src[j] = dst;  // a harmless address for the unconditional loads below
+      wt[j] = 0.0f;
+      if (j < p.P) {
+        const uint64_t v = m.inv[(m.inv_base[i] + t) * p.P + j];
+        if (uint32_t(v >> 32) == p.epoch) {
+          const int64_t k = int64_t(uint32_t(v)) - 1;
+          const Job jb = p.jobs[i * p.P + j];
+          on[j] = true;
+          src[j] = uint64_t(p.in[j]) + uint64_t(jb.dst_off) + uint64_t(k) * uint64_t(m.row_bytes);
+          wt[j] = m.w[i][jb.src_off + k];
+        }
+      }
+    }
+    for (uint32_t u0 = 0; u0 < nunits; u0 += kThreads * kU) {
+      atom::u32x4 x[kU][kMaxRanks];
+#pragma unroll
+      for (int kk = 0; kk < kU; ++kk) {
+        uint32_t u = u0 + uint32_t(kk) * kThreads + threadIdx.x;
+        if (u >= nunits) u = nunits - 1;
+#pragma unroll
+        for (int j = 0; j < kMaxRanks; ++j) x[kk][j] = atom::ld16<kNT>(src[j] + uint64_t(u) * 16u);
+      }
+#pragma unroll
+      for (int kk = 0; kk < kU; ++kk) {
+        const uint32_t u = u0 + uint32_t(kk) * kThreads + threadIdx.x;
+        if (u >= nunits) continue;
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kMaxRanks; ++j) {
+          if (on[j]) {
+            const atom::u32x4 v = x[kk][j];
+            const float w = wt[j];
+            a[0] = a[0] + w * atom::bf16_lo(v.x); a[1] = a[1] + w * atom::bf16_hi(v.x);
+            a[2] = a[2] + w * atom::bf16_lo(v.y); a[3] = a[3] + w * atom::bf16_hi(v.y);
+            a[4] = a[4] + w * atom::bf16_lo(v.z); a[5] = a[5] + w * atom::bf16_hi(v.z);
+            a[6] = a[6] + w * atom::bf16_lo(v.w); a[7] = a[7] + w * atom::bf16_hi(v.w);
+          }
+        }
+        atom::u32x4 o;
+        o.x = atom::bf16_rne(a[0]) | (atom::bf16_rne(a[1]) << 16);
+        o.y = atom::bf16_rne(a[2]) | (atom::bf16_rne(a[3]) << 16);
+        o.z = atom::bf16_rne(a[4]) | (atom::bf16_rne(a[5]) << 16);
+        o.w = atom::bf16_rne(a[6]) | (atom::bf16_rne(a[7]) << 16);
+        atom::st16<kNT>(dst + uint64_t(u) * 16u, o);
+      }
+    }
+  }
+  if (p.sync) snac::exit_notify(p);
+}
+
 // ---- calibration copy ------------------------------------------------------
 // A plain streaming copy with the same access style as the collectives (16-byte
 // nontemporal loads and stores, 4 per lane in flight): the reference for HBM
@@ -433,6 +580,25 @@ hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStrea
   void *args[] = {const_cast<StagedPlan *>(&p)};
   return hipLaunchKernel(kernel_fn(kind, true, nt, 1, true), dim3(p.total_roles), dim3(kThreads),
                          args, 0, stream);
+}
+
+void *moe_kernel_fn(MoeKernel which, bool rows) {
+  switch (which) {
+    case MoeKernel::kDispatch:
+      return rows ? reinterpret_cast<void *>(&moe_dispatch_kernel<4, true, true>)
+                  : reinterpret_cast<void *>(&moe_dispatch_kernel<4, true, false>);
+    case MoeKernel::kInverse: return reinterpret_cast<void *>(&moe_inverse_kernel);
+    default: return reinterpret_cast<void *>(&moe_combine_kernel<1, true>);
+  }
+}
+
+hipError_t launch_moe(const MoePlan &m, MoeKernel which, bool rows, int grid, hipStream_t stream) {
+  void *args[] = {const_cast<MoePlan *>(&m)};
+  return hipLaunchKernel(moe_kernel_fn(which, rows), dim3(grid), dim3(kThreads), args, 0, stream);
+}
+
+hipError_t moe_resident_per_cu(MoeKernel which, bool rows, int *blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, moe_kernel_fn(which, rows), kThreads, 0);
 }
 
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,

@@ -23,4 +23,10 @@ hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts,
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
                                int *blocks);
 
+// MoE dispatch (rows: the build with the realigning row bodies), the
+// combine's inverse-map pass and its folding pass.
+enum class MoeKernel { kDispatch, kInverse, kCombine };
+hipError_t launch_moe(const MoePlan &m, MoeKernel which, bool rows, int grid, hipStream_t stream);
+hipError_t moe_resident_per_cu(MoeKernel which, bool rows, int *blocks);
+
 }  // namespace purlin

@@ -36,6 +36,7 @@ constexpr int exit_word(uint32_t parity, int slot) {
   return kFlagExit + (int(parity) * kExitSlots + slot) * kFlagStride;
 }
 constexpr uint32_t kStatusTimeout = 1u;
+constexpr uint32_t kStatusBadArg = 2u;   // a device-side argument check failed (MoE indices)
 
 struct Job {
   int64_t src_off;  // byte offset into in[src] (into every in[i] when src < 0)
@@ -86,7 +87,25 @@ struct StagedPlan {
   StagedJob sj[kMaxJobs];
 };
 
+// MoE dispatch / combine (expert parallelism, Table 2 of the Purlin pages):
+// AllToAllV whose rows are gathered by token index, and its reverse with a
+// weighted sum per token.  base.jobs[i * P + j] is the pair (source rank i,
+// destination rank j): src_off = first entry of group j in idx[i], dst_off =
+// byte offset of the pair's rows in y[j], nbytes = rows * row_bytes;
+// base.tile_begin is the row prefix over the pairs (a tile is one row).
+struct MoePlan {
+  LaunchPlan base;               // in = x (dispatch) or y (combine), out = y or out
+  const int32_t *idx[kMaxRanks]; // token index of each entry, grouped by destination
+  const float *w[kMaxRanks];     // combine weight of each entry
+  uint64_t *inv;                 // combine: (token, destination rank) -> tagged entry
+  int64_t inv_base[kMaxRanks + 1];  // first token row of rank i in inv (prefix of x_rows)
+  int64_t ent_base[kMaxRanks + 1];  // first entry of rank i in the entry numbering
+  int64_t x_rows[kMaxRanks];
+  int64_t row_bytes;
+};
+
 static_assert(sizeof(LaunchPlan) <= 3072, "launch plan must fit in kernel arguments");
+static_assert(sizeof(MoePlan) <= 3840, "MoE plan must fit in kernel arguments");
 static_assert(sizeof(StagedPlan) <= 3840, "staged plan must fit in kernel arguments");
 
 }  // namespace purlin

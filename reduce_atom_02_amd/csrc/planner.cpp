@@ -217,7 +217,12 @@ purlin_status check_pointers(const Derived &d, void *const *in, void *const *out
     if (!b || (b & a)) return PURLIN_ERR_INVALID_ARG;
     ins.push_back({b + r.off, b + r.off + r.len});
   }
-  if (ranges_overlap(outs)) return PURLIN_ERR_INVALID_ARG;  // sorts outs
+  return ranges_disjoint(ins, outs) ? PURLIN_OK : PURLIN_ERR_INVALID_ARG;
+}
+
+bool ranges_disjoint(const std::vector<std::pair<uintptr_t, uintptr_t>> &ins,
+                     std::vector<std::pair<uintptr_t, uintptr_t>> outs) {
+  if (ranges_overlap(outs)) return false;  // sorts outs
   for (const auto &r : ins) {
     // first output range ending after r starts
     auto it = std::lower_bound(outs.begin(), outs.end(), r,
@@ -225,9 +230,9 @@ purlin_status check_pointers(const Derived &d, void *const *in, void *const *out
                                   const std::pair<uintptr_t, uintptr_t> &x) {
                                  return o.second <= x.first;
                                });
-    if (it != outs.end() && it->first < r.second) return PURLIN_ERR_INVALID_ARG;
+    if (it != outs.end() && it->first < r.second) return false;
   }
-  return PURLIN_OK;
+  return true;
 }
 
 namespace {

@@ -1,6 +1,7 @@
 // Host planner: argument validation and derivation of a collective's jobs
 // from its specification (no HIP call in here, so it runs without a GPU).
 #pragma once
+#include <utility>
 #include <vector>
 
 #include "../../include/purlin.h"
@@ -35,6 +36,11 @@ purlin_status derive(purlin_naming in_naming, purlin_naming out_naming, purlin_o
 // Pointer checks of one call: NULL and misaligned buffers, overlapping output
 // partitions, input bytes overlapping output bytes.
 purlin_status check_pointers(const Derived &d, void *const *in, void *const *out);
+
+// Byte ranges [first, second): the outputs pairwise disjoint and no input
+// overlapping an output.  Empty ranges are ignored by construction.
+bool ranges_disjoint(const std::vector<std::pair<uintptr_t, uintptr_t>> &ins,
+                     std::vector<std::pair<uintptr_t, uintptr_t>> outs);
 
 // Cached derive(): same result, reused when the specification repeats.
 purlin_status derive_cached(purlin_naming in_naming, purlin_naming out_naming, purlin_op op,

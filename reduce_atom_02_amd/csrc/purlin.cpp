@@ -27,6 +27,8 @@ struct DeviceState {
   int64_t ring_bytes = 0;
   uint64_t *slot_flags = nullptr;
   int64_t slot_flag_bytes = 0;
+  uint64_t *inv = nullptr;     // MoE combine: (token, destination rank) -> tagged entry
+  int64_t inv_bytes = 0;
   uint32_t epoch = 0;
   uint32_t exit_total[2][kExitSlots] = {};  // per parity and slot, all launches so far
   int occ[3][2][2][3][2] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
@@ -164,6 +166,25 @@ purlin_status ensure_staging(DeviceState &s, int64_t ring_bytes, int64_t flag_by
   return PURLIN_OK;
 }
 
+// The MoE combine's inverse table, zeroed when (re)allocated; its entries
+// carry the launch epoch, so it is never cleared again.
+purlin_status ensure_inverse(DeviceState &s, int64_t bytes) {
+  if (bytes <= s.inv_bytes) return PURLIN_OK;
+  if (hipDeviceSynchronize() != hipSuccess) return PURLIN_ERR_HIP;  // a launch may still use it
+  if (s.inv) (void)hipFree(s.inv);
+  s.inv = nullptr;
+  s.inv_bytes = 0;
+  void *f = nullptr;
+  if (hipMalloc(&f, size_t(bytes)) != hipSuccess) return PURLIN_ERR_NO_MEMORY;
+  if (hipMemset(f, 0, size_t(bytes)) != hipSuccess) {
+    (void)hipFree(f);
+    return PURLIN_ERR_HIP;
+  }
+  s.inv = static_cast<uint64_t *>(f);
+  s.inv_bytes = bytes;
+  return PURLIN_OK;
+}
+
 KernelKind kind_of(purlin_op op, purlin_dtype dtype) {
   if (op == PURLIN_OP_COPY) return KernelKind::kCopy;
   return dtype == PURLIN_F32 ? KernelKind::kSumF32 : KernelKind::kSumBf16;
@@ -206,6 +227,113 @@ void fill_tiles(LaunchPlan &lp, const std::vector<Job> &jobs, int64_t chunk) {
   lp.tile_begin[jobs.size()] = int32_t(t);
   for (size_t k = jobs.size() + 1; k <= size_t(kMaxJobs); ++k) lp.tile_begin[k] = int32_t(t);
   lp.total_tiles = int32_t(t);
+}
+
+// Shared argument checks and plan of the MoE entry points.  counts[i * P + j]
+// rows go from rank i to rank j; rank i's entries (idx[i], w[i]) are the
+// groups j = 0 .. P-1 in turn; pair (i, j)'s rows sit in the exchanged
+// buffer of rank j after those of ranks 0 .. i-1.
+purlin_status moe_plan(void *const *rowsrc, void *const *rowdst, int P, int64_t row_bytes,
+                       const int32_t *const *idx, const int64_t *counts, const int64_t *x_rows,
+                       bool combine, MoePlan *m, int64_t *total_rows, int64_t *y_rows_out) {
+  if (!rowsrc || !rowdst || !idx || !counts || !x_rows || P < 1 || P > kMaxRanks ||
+      row_bytes <= 0 || (row_bytes & 1))
+    return PURLIN_ERR_INVALID_ARG;
+  int64_t n_ent[kMaxRanks] = {}, y_rows[kMaxRanks] = {};
+  int64_t total = 0, x_total = 0;
+  for (int i = 0; i < P; ++i) {
+    if (x_rows[i] < 0) return PURLIN_ERR_INVALID_ARG;
+    x_total += x_rows[i];
+    for (int j = 0; j < P; ++j) {
+      const int64_t c = counts[i * P + j];
+      if (c < 0) return PURLIN_ERR_INVALID_ARG;
+      n_ent[i] += c;
+      y_rows[j] += c;
+      total += c;
+    }
+  }
+  if (total >= (int64_t(1) << 31) || x_total >= (int64_t(1) << 40)) return PURLIN_ERR_INVALID_ARG;
+  // x: token rows (dispatch input, combine output); y: exchanged rows
+  void *const *x = combine ? rowdst : rowsrc;
+  void *const *y = combine ? rowsrc : rowdst;
+  std::vector<std::pair<uintptr_t, uintptr_t>> xr, yr;
+  for (int i = 0; i < P; ++i) {
+    if (n_ent[i] > 0 && (!idx[i] || x_rows[i] == 0)) return PURLIN_ERR_INVALID_ARG;
+    const int64_t xb = x_rows[i] * row_bytes, yb = y_rows[i] * row_bytes;
+    if ((combine ? x_rows[i] : n_ent[i]) > 0 || xb > 0) {
+      if (!x[i] || (uintptr_t(x[i]) & 1)) return PURLIN_ERR_INVALID_ARG;
+      if (xb > 0) xr.push_back({uintptr_t(x[i]), uintptr_t(x[i]) + uintptr_t(xb)});
+    }
+    if (yb > 0) {
+      if (!y[i] || (uintptr_t(y[i]) & 1)) return PURLIN_ERR_INVALID_ARG;
+      yr.push_back({uintptr_t(y[i]), uintptr_t(y[i]) + uintptr_t(yb)});
+    }
+  }
+  if (!(combine ? ranges_disjoint(yr, xr) : ranges_disjoint(xr, yr))) return PURLIN_ERR_INVALID_ARG;
+
+  MoePlan &mp = *m;
+  mp = MoePlan{};
+  LaunchPlan &lp = mp.base;
+  for (int r = 0; r < kMaxRanks; ++r) {
+    lp.in[r] = r < P ? static_cast<const char *>(rowsrc[r]) : nullptr;
+    lp.out[r] = r < P ? static_cast<char *>(rowdst[r]) : nullptr;
+    mp.idx[r] = r < P ? idx[r] : nullptr;
+    mp.x_rows[r] = r < P ? x_rows[r] : 0;
+  }
+  lp.P = P;
+  lp.njobs = P * P;
+  int64_t t = 0;
+  int64_t pos[kMaxRanks] = {};
+  for (int i = 0; i < P; ++i) {
+    int64_t off = 0;
+    for (int j = 0; j < P; ++j) {
+      const int q = i * P + j;
+      const int64_t c = counts[q];
+      lp.jobs[q] = Job{off, pos[j] * row_bytes, c * row_bytes, int32_t(i), int32_t(j)};
+      lp.tile_begin[q] = int32_t(t);
+      t += c;
+      off += c;
+      pos[j] += c;
+    }
+  }
+  for (int q = P * P; q <= kMaxJobs; ++q) lp.tile_begin[q] = int32_t(t);
+  lp.total_tiles = int32_t(t);
+  for (int i = 0; i < P; ++i) {
+    mp.ent_base[i + 1] = mp.ent_base[i] + n_ent[i];
+    mp.inv_base[i + 1] = mp.inv_base[i] + x_rows[i];
+  }
+  for (int i = P; i < kMaxRanks; ++i) {
+    mp.ent_base[i + 1] = mp.ent_base[i];
+    mp.inv_base[i + 1] = mp.inv_base[i];
+  }
+  mp.row_bytes = row_bytes;
+  *total_rows = total;
+  *y_rows_out = 0;
+  for (int j = 0; j < P; ++j) *y_rows_out += y_rows[j];
+  return PURLIN_OK;
+}
+
+// The launch-wide fields of a plan: flags, epoch, watchdog and handshake.
+void moe_launch_fields(DeviceState &ds, LaunchPlan &lp, const purlin_policy &pol) {
+  if (++ds.epoch == 0) ds.epoch = 1;
+  lp.flags = ds.flags;
+  lp.epoch = ds.epoch;
+  const int64_t wd_ns = pol.watchdog_ns ? pol.watchdog_ns : kDefaultWatchdogNs;
+  lp.watchdog_ticks = uint64_t(wd_ns) * ds.wall_khz / 1000000u + 1;
+  lp.sync = pol.sync == 2 ? 0 : 1;
+  for (int k = 0; k < kExitSlots; ++k) lp.exit_expect[k] = ds.exit_total[(ds.epoch - 1u) & 1u][k];
+}
+
+void moe_count_exit(DeviceState &ds, const LaunchPlan &lp, int grid) {
+  if (!lp.sync) return;
+  for (int k = 0; k < kExitSlots; ++k)
+    ds.exit_total[lp.epoch & 1u][k] += uint32_t(grid / kExitSlots + (k < grid % kExitSlots ? 1 : 0));
+}
+
+int moe_grid(DeviceState &ds, MoeKernel which, bool rows, int64_t work, int64_t cap) {
+  int b = 0;
+  if (moe_resident_per_cu(which, rows, &b) != hipSuccess || b < 1) b = 1;
+  return int(std::max<int64_t>(1, std::min<int64_t>({work, cap, int64_t(ds.cus) * b})));
 }
 
 }  // namespace
@@ -436,6 +564,86 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
   return PURLIN_OK;
 }
 
+purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t row_bytes,
+                                  const int32_t *const *idx, const int64_t *counts,
+                                  const int64_t *x_rows, hipStream_t stream) {
+  MoePlan m;
+  int64_t total = 0, y_total = 0;
+  purlin_status st = moe_plan(x, y, P, row_bytes, idx, counts, x_rows, false, &m, &total, &y_total);
+  if (st != PURLIN_OK) return st;
+  if (total == 0) return PURLIN_OK;
+  DeviceState *ds = nullptr;
+  st = device_state(&ds);
+  if (st != PURLIN_OK) return st;
+  moe_launch_fields(*ds, m.base, effective_policy());
+  bool rows = (row_bytes & 15) != 0;
+  for (int r = 0; r < P; ++r)
+    rows |= ((uintptr_t(x[r]) | uintptr_t(y[r])) & 15) != 0;
+  // the copy policy's grid: four workgroups per CU
+  const int grid = moe_grid(*ds, MoeKernel::kDispatch, rows, total, int64_t(ds->cus) * 4);
+  m.base.chunk_bytes = row_bytes;
+  if (launch_moe(m, MoeKernel::kDispatch, rows, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
+  moe_count_exit(*ds, m.base, grid);
+  purlin_launch_info info{};
+  info.grid = grid;
+  info.threads = kThreads;
+  info.zero_staging = 1;
+  info.chunk_bytes = row_bytes;
+  info.tiles = total;
+  info.bytes_min = 2 * total * row_bytes;
+  info.njobs = P * P;
+  info.sync = m.base.sync;
+  info.rows = rows ? 1 : 0;
+  g_last = info;
+  g_have_last = true;
+  return PURLIN_OK;
+}
+
+purlin_status purlin_moe_combine(void *const *y, void *const *out, int P, int64_t row_bytes,
+                                 const int32_t *const *idx, const float *const *w,
+                                 const int64_t *counts, const int64_t *x_rows, hipStream_t stream) {
+  MoePlan m;
+  int64_t total = 0, y_total = 0;
+  purlin_status st = moe_plan(y, out, P, row_bytes, idx, counts, x_rows, true, &m, &total, &y_total);
+  if (st != PURLIN_OK) return st;
+  if (!w || (row_bytes & 15)) return PURLIN_ERR_INVALID_ARG;
+  for (int r = 0; r < P; ++r) {
+    if (m.ent_base[r + 1] > m.ent_base[r] && !w[r]) return PURLIN_ERR_INVALID_ARG;
+    if ((uintptr_t(y[r]) | uintptr_t(out[r])) & 15) return PURLIN_ERR_INVALID_ARG;
+    m.w[r] = w[r];
+  }
+  const int64_t out_rows = m.inv_base[P];
+  if (out_rows == 0) return PURLIN_OK;
+  DeviceState *ds = nullptr;
+  st = device_state(&ds);
+  if (st != PURLIN_OK) return st;
+  st = ensure_inverse(*ds, out_rows * P * int64_t(sizeof(uint64_t)));
+  if (st != PURLIN_OK) return st;
+  m.inv = ds->inv;
+  moe_launch_fields(*ds, m.base, effective_policy());
+  m.base.chunk_bytes = row_bytes;
+  if (total > 0) {
+    const int g0 = moe_grid(*ds, MoeKernel::kInverse, false, (total + kThreads - 1) / kThreads,
+                            int64_t(ds->cus) * 8);
+    if (launch_moe(m, MoeKernel::kInverse, false, g0, stream) != hipSuccess) return PURLIN_ERR_HIP;
+  }
+  const int grid = moe_grid(*ds, MoeKernel::kCombine, false, out_rows, int64_t(ds->cus) * 4);
+  if (launch_moe(m, MoeKernel::kCombine, false, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
+  moe_count_exit(*ds, m.base, grid);
+  purlin_launch_info info{};
+  info.grid = grid;
+  info.threads = kThreads;
+  info.zero_staging = 1;
+  info.chunk_bytes = row_bytes;
+  info.tiles = out_rows;
+  info.bytes_min = (y_total + out_rows) * row_bytes;
+  info.njobs = P * P;
+  info.sync = m.base.sync;
+  g_last = info;
+  g_have_last = true;
+  return PURLIN_OK;
+}
+
 purlin_status purlin_check(hipStream_t stream) {
   if (hipStreamSynchronize(stream) != hipSuccess) return PURLIN_ERR_HIP;
   int dev = 0;
@@ -448,7 +656,8 @@ purlin_status purlin_check(hipStream_t stream) {
     return PURLIN_ERR_HIP;
   if (status == 0) return PURLIN_OK;
   if (hipMemset(word, 0, sizeof(uint32_t)) != hipSuccess) return PURLIN_ERR_HIP;
-  return (status & kStatusTimeout) ? PURLIN_ERR_TIMEOUT : PURLIN_ERR_HIP;
+  if (status & kStatusTimeout) return PURLIN_ERR_TIMEOUT;
+  return (status & kStatusBadArg) ? PURLIN_ERR_INVALID_ARG : PURLIN_ERR_HIP;
 }
 
 purlin_status purlin_last_launch(purlin_launch_info *info) {
@@ -495,16 +704,18 @@ void purlin_release(void) {
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
   for (size_t dev = 0; dev < all.size(); ++dev) {
     DeviceState &s = all[dev];
-    if (!s.flags && !s.ring && !s.slot_flags) continue;
+    if (!s.flags && !s.ring && !s.slot_flags && !s.inv) continue;
     if (hipSetDevice(int(dev)) != hipSuccess) continue;
     (void)hipDeviceSynchronize();
     if (s.flags) (void)hipFree(s.flags);
     if (s.ring) (void)hipFree(s.ring);
     if (s.slot_flags) (void)hipFree(s.slot_flags);
+    if (s.inv) (void)hipFree(s.inv);
     s.flags = nullptr;
     s.ring = nullptr;
     s.slot_flags = nullptr;
-    s.ring_bytes = s.slot_flag_bytes = 0;
+    s.inv = nullptr;
+    s.ring_bytes = s.slot_flag_bytes = s.inv_bytes = 0;
   }
   if (have_cur) (void)hipSetDevice(cur);
 }

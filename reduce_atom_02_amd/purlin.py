@@ -18,7 +18,7 @@ __all__ = [
     "LIB_PATH", "NAMINGS", "OPS", "DTYPES", "STATUS", "PurlinError", "collective",
     "all_reduce", "reduce_scatter", "all_gather", "all_to_all", "check",
     "set_policy", "get_policy", "plan_describe", "last_launch", "stream_copy", "stream_pattern",
-    "release", "exported_symbols",
+    "moe_dispatch", "moe_combine", "release", "exported_symbols",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpurlin.so")
@@ -96,6 +96,13 @@ def _load():
     lib.purlin_stream_pattern.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                           ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    P_VP = ctypes.POINTER(ctypes.c_void_p)
+    lib.purlin_moe_dispatch.argtypes = [P_VP, P_VP, ctypes.c_int, ctypes.c_int64, P_VP, P_I64,
+                                        P_I64, ctypes.c_void_p]
+    lib.purlin_moe_dispatch.restype = ctypes.c_int
+    lib.purlin_moe_combine.argtypes = [P_VP, P_VP, ctypes.c_int, ctypes.c_int64, P_VP, P_VP,
+                                       P_I64, P_I64, ctypes.c_void_p]
+    lib.purlin_moe_combine.restype = ctypes.c_int
     lib.purlin_stream_pattern.restype = ctypes.c_int
     lib.purlin_strerror.argtypes = [ctypes.c_int]
     lib.purlin_strerror.restype = ctypes.c_char_p
@@ -111,7 +118,8 @@ def exported_symbols():
     """Names of the C ABI functions the loaded library resolves."""
     names = ["purlin_collective", "purlin_check", "purlin_set_policy", "purlin_get_policy",
              "purlin_plan_describe", "purlin_last_launch", "purlin_stream_copy",
-             "purlin_stream_pattern", "purlin_strerror", "purlin_release"]
+             "purlin_stream_pattern", "purlin_moe_dispatch", "purlin_moe_combine",
+             "purlin_strerror", "purlin_release"]
     return [n for n in names if hasattr(_lib, n)]
 
 
@@ -310,6 +318,38 @@ def stream_pattern(srcs, dsts, nbytes, grid=0, stream=None):
     da = (ctypes.c_void_p * max(1, len(dsts)))(*[_ptr(x) for x in dsts])
     _raise(_lib.purlin_stream_pattern(sa, len(srcs), da, len(dsts), int(nbytes), int(grid),
                                       ctypes.c_void_p(_stream(stream))), "purlin_stream_pattern")
+
+
+def _ptrs(bufs):
+    vals = tuple(map(_ptr, bufs))
+    return _cached(("ptrs", vals), lambda: (ctypes.c_void_p * max(1, len(vals)))(*vals))
+
+
+def moe_dispatch(x, y, idx, counts, x_rows=None, row_bytes=None, stream=None):
+    """MoE dispatch: y[j] = for i ascending, x[i] rows idx[i][group j] (see
+    include/purlin.h).  x, y: P tensors (or addresses) of rows; idx: P int32
+    device tensors grouped by destination; counts: P*P rows [i*P + j]."""
+    P = len(x)
+    if row_bytes is None:
+        row_bytes = x[0].shape[-1] * x[0].element_size()
+    if x_rows is None:
+        x_rows = [xi.shape[0] for xi in x]
+    _raise(_lib.purlin_moe_dispatch(_ptrs(x), _ptrs(y), P, int(row_bytes), _ptrs(idx),
+                                    _i64(counts), _i64(x_rows), ctypes.c_void_p(_stream(stream))),
+           "purlin_moe_dispatch")
+
+
+def moe_combine(y, out, idx, w, counts, x_rows=None, row_bytes=None, stream=None):
+    """MoE combine: out[i][t] = bf16 of the fp32 fold, ascending (rank,
+    entry), of w * y rows routed back to token t (see include/purlin.h)."""
+    P = len(out)
+    if row_bytes is None:
+        row_bytes = out[0].shape[-1] * out[0].element_size()
+    if x_rows is None:
+        x_rows = [o.shape[0] for o in out]
+    _raise(_lib.purlin_moe_combine(_ptrs(y), _ptrs(out), P, int(row_bytes), _ptrs(idx), _ptrs(w),
+                                   _i64(counts), _i64(x_rows), ctypes.c_void_p(_stream(stream))),
+           "purlin_moe_combine")
 
 
 def release():

@@ -30,7 +30,7 @@ def header_functions():
 def test_every_declared_symbol_is_exported(purlin):
     import ctypes
     declared = header_functions()
-    assert len(declared) == 10, declared
+    assert len(declared) == 12, declared
     lib = ctypes.CDLL(purlin.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -173,3 +173,38 @@ def test_policy_roundtrip_and_validation(purlin):
 def test_strerror(purlin):
     assert purlin._lib.purlin_strerror(5) == b"device wait timed out"
     assert purlin._lib.purlin_strerror(42) == b"unknown status"
+
+
+def test_moe_argument_checks(purlin):
+    """MoE dispatch / combine reject bad arguments before any HIP call."""
+    import ctypes
+    lib = purlin._lib
+    P = 2
+    V = ctypes.c_void_p * P
+    x = V(A_IN, A_IN + (1 << 30))
+    y = V(A_OUT, A_OUT + (1 << 30))
+    idx = V(0x10000, 0x20000)
+    w = V(0x30000, 0x40000)
+    I64 = ctypes.c_int64
+
+    def disp(counts, x_rows, row_bytes=64, P_=P, idx_=idx, y_=y):
+        return lib.purlin_moe_dispatch(x, y_, P_, row_bytes, idx_, (I64 * len(counts))(*counts),
+                                       (I64 * len(x_rows))(*x_rows), None)
+
+    def comb(counts, x_rows, row_bytes=64, w_=w, out=x):
+        return lib.purlin_moe_combine(y, out, P, row_bytes, idx, w_, (I64 * len(counts))(*counts),
+                                      (I64 * len(x_rows))(*x_rows), None)
+
+    assert disp([1, 1, 1, 1], [4, 4], P_=0) == 1
+    assert disp([1, 1, 1, 1], [4, 4], P_=9) == 1
+    assert disp([1, -1, 1, 1], [4, 4]) == 1                 # negative count
+    assert disp([1, 1, 1, 1], [4, -4]) == 1                 # negative row count
+    assert disp([1, 1, 1, 1], [4, 4], row_bytes=63) == 1    # odd row
+    assert disp([1, 1, 1, 1], [4, 4], row_bytes=0) == 1
+    assert disp([1, 1, 1, 1], [4, 0]) == 1                  # entries for a rank with no rows
+    assert disp([1, 1, 1, 1], [4, 4], idx_=V(0x10000, 0)) == 1   # NULL index array with entries
+    assert disp([1, 1, 1, 1], [4, 4], y_=V(A_OUT, A_OUT + 64)) == 1  # outputs overlap
+    assert disp([1, 1, 1, 1], [4, 4], y_=V(A_IN + 64, A_OUT)) == 1   # output inside an input
+    assert comb([1, 1, 1, 1], [4, 4], row_bytes=24) == 1    # combine rows: 16-byte multiples
+    assert comb([1, 1, 1, 1], [4, 4], w_=V(0x30000, 0)) == 1     # NULL weights with entries
+    assert comb([1, 1, 1, 1], [4, 4], out=V(A_IN + 8, A_IN + (1 << 30))) == 1  # misaligned
