@@ -320,6 +320,79 @@ def sweep(purlin, T_max, variant, path, dev):
     return rows
 
 
+def moe_bench(purlin, steps, warmup, dev):
+    """MoE dispatch and combine at the configuration of the pages' expert-
+    parallel call sites: 4096 tokens x 7168 bf16 per rank, top-8 of 256
+    experts on P = 8 ranks, one row per (token, destination rank).  Timed
+    with HIP events, p50 over `steps` calls: the by-token dispatch (each
+    token row read once), the row-by-row dispatch, the unfused path (torch
+    index_select into a send buffer, then the AllToAllV) as context, and
+    combine.  B_min: dispatch reads every routed token row once and writes
+    every sent row; combine reads every sent row and writes every token row."""
+    import numpy as np
+    import torch
+    import workloads
+    H, tokens = 7168, 4096
+    rb = H * 2
+    rows = [workloads.moe_rows(i) for i in range(P)]
+    wts = [workloads.moe_weights(i) for i in range(P)]
+    counts = [len(rows[i][j]) for i in range(P) for j in range(P)]
+    idx = [torch.from_numpy(np.concatenate(rows[i]).astype(np.int32)).to(dev) for i in range(P)]
+    w = [torch.from_numpy(np.concatenate(wts[i]).astype(np.float32)).to(dev) for i in range(P)]
+    x = [workloads.device_values(tokens * H, "normal", "bf16", 5, i, dev).view(tokens, H)
+         for i in range(P)]
+    y_rows = [sum(counts[i * P + j] for i in range(P)) for j in range(P)]
+    y = [torch.empty(y_rows[j], H, dtype=torch.bfloat16, device=dev) for j in range(P)]
+    out = [torch.empty(tokens, H, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    send = [torch.empty(sum(counts[i * P:(i + 1) * P]), H, dtype=torch.bfloat16, device=dev)
+            for i in range(P)]
+    sent = sum(counts)
+    routed = sum(len(np.unique(np.concatenate(rows[i]))) for i in range(P))
+    stream = torch.cuda.current_stream()
+    a2a_counts = [c * H for c in counts]
+
+    def unfused():
+        for i in range(P):
+            torch.index_select(x[i], 0, idx[i], out=send[i])
+        purlin.all_to_all([s_.view(-1) for s_ in send], [t.view(-1) for t in y], a2a_counts,
+                          stream=stream)
+
+    cases = {
+        "dispatch_by_token": (lambda: purlin.moe_dispatch(x, y, idx, counts, unique=True, stream=stream),
+                              (routed + sent) * rb),
+        "dispatch_by_row": (lambda: purlin.moe_dispatch(x, y, idx, counts, unique=False, stream=stream),
+                            2 * sent * rb),
+        "unfused_index_select_then_alltoallv": (unfused, (routed + sent) * rb),
+        "combine": (lambda: purlin.moe_combine(y, out, idx, w, counts, stream=stream),
+                    (sent + P * tokens) * rb),
+    }
+    res = {}
+    for name, (fn, bmin) in cases.items():
+        for _ in range(warmup):
+            fn()
+        purlin.check(stream)
+        ev = []
+        for _ in range(steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        purlin.check(stream)
+        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+        p50 = ts[len(ts) // 2]
+        res[name] = {"p50_us": round(p50 * 1e6, 1), "bmin_bytes": bmin,
+                     "hbm_frac": round(bmin / p50 / HBM_PEAK, 4)}
+        if name != "unfused_index_select_then_alltoallv":
+            res[name]["grid"] = purlin.last_launch()["grid"]
+    return {"moe": res, "config": {"P": P, "tokens_per_rank": tokens, "hidden": H,
+                                   "dtype": "bf16", "experts": 256, "topk": 8,
+                                   "rows_sent": sent, "token_rows_routed": routed},
+            "steps": steps, "data": "synthetic"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +411,8 @@ def main():
                          "8->1, 8->8 streams of --size bytes) with cold caches")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the pattern-ceiling measurement after the timed steps")
+    ap.add_argument("--moe", action="store_true",
+                    help="time MoE dispatch / combine at 4096 x 7168 bf16 per rank, top-8 of 256")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time only the plain 128-bit streaming copy of --size bytes "
                          "(HBM counter calibration and copy ceiling)")
@@ -361,6 +436,9 @@ def main():
     T = args.size
     if args.calibrate_copy:
         calibrate_copy(purlin, T, args.steps, args.warmup, dev)
+        return
+    if args.moe:
+        print(json.dumps(moe_bench(purlin, args.steps, args.warmup, dev)), flush=True)
         return
     if args.sweep:
         sweep(purlin, T, args.variant, args.sweep, dev)

@@ -189,8 +189,15 @@ PURLIN_API purlin_status purlin_plan_describe(const purlin_layout *in, const pur
  *   y[j]       rank j's received rows, sum_i counts[i*P + j] rows: for i
  *              ascending, rows x[i][idx[i][group j]] in entry order (output)
  *
+ * unique != 0 promises one row per (token, destination rank) (the
+ * deduplicated routing): each token row is then read once and written to
+ * every rank it goes to, through a table of sum(x_rows) * P 8-byte words the
+ * library keeps (as purlin_moe_combine); a token twice in one group is then
+ * reported.  unique == 0 gathers row by row and allows repeats.
+ *
  * Rows are moved as bytes (row_bytes even, buffers 2-byte aligned; 16-byte
- * alignment takes the faster kernel).  Ownership as purlin_collective.
+ * alignment of every buffer and of row_bytes takes the faster kernels, and
+ * is needed for the by-token path).  Ownership as purlin_collective.
  * Synchronous errors: INVALID_ARG for P outside [1, 8], a NULL array or
  * buffer that holds data, a negative count, odd row_bytes, entries for a
  * rank with no rows, an output overlapping an input or another output.
@@ -200,7 +207,7 @@ PURLIN_API purlin_status purlin_plan_describe(const purlin_layout *in, const pur
 PURLIN_API purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P,
                                              int64_t row_bytes, const int32_t *const *idx,
                                              const int64_t *counts, const int64_t *x_rows,
-                                             hipStream_t stream);
+                                             int unique, hipStream_t stream);
 
 /*
  * MoE combine: the reverse exchange of purlin_moe_dispatch with a weighted

@@ -346,6 +346,61 @@ __global__ void __launch_bounds__(kThreads) moe_dispatch_kernel(const MoePlan m)
   if (p.sync) snac::exit_notify(p);
 }
 
+// Dispatch with one row per (token, destination rank), after the inverse
+// pass below: one tile per token row, read once and written to every rank
+// the token goes to (a broadcast with the token's own destination set).
+// Rows and buffers are 16-byte aligned, so the destinations are congruent.
+template <int kU, bool kNT>
+__global__ void __launch_bounds__(kThreads) moe_dispatch_tokens_kernel(const MoePlan m) {
+  const LaunchPlan &p = m.base;
+  const bool run = !p.sync || snac::entry(p);
+  const int64_t rows = m.inv_base[p.P];
+  for (int64_t r = run ? int64_t(blockIdx.x) : rows; r < rows; r += gridDim.x) {
+    int i = 0;
+    for (int q = 1; q < kMaxRanks; ++q)
+      if (q < p.P && m.inv_base[q] <= r) i = q;
+    const int64_t t = r - m.inv_base[i];
+    atom::Dsts d;
+    d.n = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxRanks; ++j) {
+      d.b[j] = 0;
+      if (j < p.P) {
+        const uint64_t v = m.inv[(m.inv_base[i] + t) * p.P + j];
+        if (uint32_t(v >> 32) == p.epoch) {
+          const int64_t k = int64_t(uint32_t(v)) - 1;
+          d.b[j] = uint64_t(p.out[j]) + uint64_t(p.jobs[i * p.P + j].dst_off) +
+                   uint64_t(k) * uint64_t(m.row_bytes);
+        }
+      }
+    }
+    // compact the present destinations to the front (unrolled, so the
+    // array stays in registers)
+    uint64_t b[kMaxRanks + 1];
+#pragma unroll
+    for (int j = 0; j < kMaxRanks + 1; ++j) b[j] = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxRanks; ++j) {
+      if (d.b[j]) {
+#pragma unroll
+        for (int q = 0; q < kMaxRanks; ++q)
+          if (q == d.n) b[q] = d.b[j];
+        ++d.n;
+      }
+    }
+    if (d.n == 0) continue;
+#pragma unroll
+    for (int j = 0; j < kMaxRanks + 1; ++j) d.b[j] = j < d.n ? b[j] : b[0];
+    atom::Srcs s;
+    s.n = 1;
+    const uint64_t a = uint64_t(p.in[i]) + uint64_t(t) * uint64_t(m.row_bytes);
+#pragma unroll
+    for (int q = 0; q < kMaxRanks; ++q) s.a[q] = a;
+    atom::tile<atom::CopyOp, kU, kNT, true, false>(s, d, 0, m.row_bytes, true);
+  }
+  if (p.sync) snac::exit_notify(p);
+}
+
 // Combine, first pass: for every entry (i, j, k) the slot (token, j) of
 // rank i's table gets (epoch, k + 1).  Entries of earlier launches carry an
 // older epoch, so the table is never cleared; a slot already holding this
@@ -399,7 +454,7 @@ __global__ void __launch_bounds__(kThreads) moe_combine_kernel(const MoePlan m) 
 #pragma unroll
     for (int j = 0; j < kMaxRanks; ++j) {
       on[j] = false;
-      src[j] = dst;  // a harmless address for the unconditional loads below
+      src[j] = dst;
       wt[j] = 0.0f;
       if (j < p.P) {
         const uint64_t v = m.inv[(m.inv_base[i] + t) * p.P + j];
@@ -418,8 +473,10 @@ __global__ void __launch_bounds__(kThreads) moe_combine_kernel(const MoePlan m) 
       for (int kk = 0; kk < kU; ++kk) {
         uint32_t u = u0 + uint32_t(kk) * kThreads + threadIdx.x;
         if (u >= nunits) u = nunits - 1;
+        // absent contributions load nothing (the branch is the same in every lane)
 #pragma unroll
-        for (int j = 0; j < kMaxRanks; ++j) x[kk][j] = atom::ld16<kNT>(src[j] + uint64_t(u) * 16u);
+        for (int j = 0; j < kMaxRanks; ++j)
+          x[kk][j] = on[j] ? atom::ld16<kNT>(src[j] + uint64_t(u) * 16u) : atom::u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int kk = 0; kk < kU; ++kk) {
@@ -588,7 +645,9 @@ void *moe_kernel_fn(MoeKernel which, bool rows) {
       return rows ? reinterpret_cast<void *>(&moe_dispatch_kernel<4, true, true>)
                   : reinterpret_cast<void *>(&moe_dispatch_kernel<4, true, false>);
     case MoeKernel::kInverse: return reinterpret_cast<void *>(&moe_inverse_kernel);
-    default: return reinterpret_cast<void *>(&moe_combine_kernel<1, true>);
+    case MoeKernel::kDispatchTokens:
+      return reinterpret_cast<void *>(&moe_dispatch_tokens_kernel<4, true>);
+    default: return reinterpret_cast<void *>(&moe_combine_kernel<2, true>);
   }
 }
 

@@ -23,9 +23,10 @@ hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts,
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
                                int *blocks);
 
-// MoE dispatch (rows: the build with the realigning row bodies), the
-// combine's inverse-map pass and its folding pass.
-enum class MoeKernel { kDispatch, kInverse, kCombine };
+// MoE dispatch one row at a time (rows: the build with the realigning row
+// bodies), the inverse-map pass, dispatch one token at a time (after the
+// inverse pass) and the combine's folding pass.
+enum class MoeKernel { kDispatch, kInverse, kDispatchTokens, kCombine };
 hipError_t launch_moe(const MoePlan &m, MoeKernel which, bool rows, int grid, hipStream_t stream);
 hipError_t moe_resident_per_cu(MoeKernel which, bool rows, int *blocks);
 

@@ -330,7 +330,11 @@ void moe_count_exit(DeviceState &ds, const LaunchPlan &lp, int grid) {
     ds.exit_total[lp.epoch & 1u][k] += uint32_t(grid / kExitSlots + (k < grid % kExitSlots ? 1 : 0));
 }
 
+// Workgroups of an MoE launch: the policy's wgs_per_rank when set, else
+// `cap`; never more than the work or than the device holds resident.
 int moe_grid(DeviceState &ds, MoeKernel which, bool rows, int64_t work, int64_t cap) {
+  const purlin_policy pol = effective_policy();
+  if (pol.wgs_per_rank && which != MoeKernel::kInverse) cap = int64_t(pol.wgs_per_rank) * kMaxRanks;
   int b = 0;
   if (moe_resident_per_cu(which, rows, &b) != hipSuccess || b < 1) b = 1;
   return int(std::max<int64_t>(1, std::min<int64_t>({work, cap, int64_t(ds.cus) * b})));
@@ -566,7 +570,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
 
 purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t row_bytes,
                                   const int32_t *const *idx, const int64_t *counts,
-                                  const int64_t *x_rows, hipStream_t stream) {
+                                  const int64_t *x_rows, int unique, hipStream_t stream) {
   MoePlan m;
   int64_t total = 0, y_total = 0;
   purlin_status st = moe_plan(x, y, P, row_bytes, idx, counts, x_rows, false, &m, &total, &y_total);
@@ -579,18 +583,36 @@ purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t
   bool rows = (row_bytes & 15) != 0;
   for (int r = 0; r < P; ++r)
     rows |= ((uintptr_t(x[r]) | uintptr_t(y[r])) & 15) != 0;
-  // the copy policy's grid: four workgroups per CU
-  const int grid = moe_grid(*ds, MoeKernel::kDispatch, rows, total, int64_t(ds->cus) * 4);
   m.base.chunk_bytes = row_bytes;
-  if (launch_moe(m, MoeKernel::kDispatch, rows, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
+  int grid = 0;
+  const bool by_token = unique && !rows;
+  if (by_token) {
+    // each token row read once and written to all its ranks: the (token,
+    // rank) -> entry table first
+    st = ensure_inverse(*ds, m.inv_base[P] * P * int64_t(sizeof(uint64_t)));
+    if (st != PURLIN_OK) return st;
+    m.inv = ds->inv;
+    const int g0 = moe_grid(*ds, MoeKernel::kInverse, false, (total + kThreads - 1) / kThreads,
+                            int64_t(ds->cus) * 8);
+    if (launch_moe(m, MoeKernel::kInverse, false, g0, stream) != hipSuccess) return PURLIN_ERR_HIP;
+    grid = moe_grid(*ds, MoeKernel::kDispatchTokens, false, m.inv_base[P], int64_t(ds->cus) * 4);
+    if (launch_moe(m, MoeKernel::kDispatchTokens, false, grid, stream) != hipSuccess)
+      return PURLIN_ERR_HIP;
+  } else {
+    // the copy policy's grid: four workgroups per CU
+    grid = moe_grid(*ds, MoeKernel::kDispatch, rows, total, int64_t(ds->cus) * 4);
+    if (launch_moe(m, MoeKernel::kDispatch, rows, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
+  }
   moe_count_exit(*ds, m.base, grid);
   purlin_launch_info info{};
   info.grid = grid;
   info.threads = kThreads;
   info.zero_staging = 1;
   info.chunk_bytes = row_bytes;
-  info.tiles = total;
-  info.bytes_min = 2 * total * row_bytes;
+  info.tiles = by_token ? m.inv_base[P] : total;
+  // rows written, plus rows read: one per entry, or (by token) at most one
+  // per token row
+  info.bytes_min = (total + (by_token ? std::min(total, m.inv_base[P]) : total)) * row_bytes;
   info.njobs = P * P;
   info.sync = m.base.sync;
   info.rows = rows ? 1 : 0;

@@ -98,7 +98,7 @@ def _load():
                                           ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     P_VP = ctypes.POINTER(ctypes.c_void_p)
     lib.purlin_moe_dispatch.argtypes = [P_VP, P_VP, ctypes.c_int, ctypes.c_int64, P_VP, P_I64,
-                                        P_I64, ctypes.c_void_p]
+                                        P_I64, ctypes.c_int, ctypes.c_void_p]
     lib.purlin_moe_dispatch.restype = ctypes.c_int
     lib.purlin_moe_combine.argtypes = [P_VP, P_VP, ctypes.c_int, ctypes.c_int64, P_VP, P_VP,
                                        P_I64, P_I64, ctypes.c_void_p]
@@ -325,17 +325,19 @@ def _ptrs(bufs):
     return _cached(("ptrs", vals), lambda: (ctypes.c_void_p * max(1, len(vals)))(*vals))
 
 
-def moe_dispatch(x, y, idx, counts, x_rows=None, row_bytes=None, stream=None):
+def moe_dispatch(x, y, idx, counts, x_rows=None, row_bytes=None, unique=False, stream=None):
     """MoE dispatch: y[j] = for i ascending, x[i] rows idx[i][group j] (see
     include/purlin.h).  x, y: P tensors (or addresses) of rows; idx: P int32
-    device tensors grouped by destination; counts: P*P rows [i*P + j]."""
+    device tensors grouped by destination; counts: P*P rows [i*P + j];
+    unique: one row per (token, destination rank), each token row read once."""
     P = len(x)
     if row_bytes is None:
         row_bytes = x[0].shape[-1] * x[0].element_size()
     if x_rows is None:
         x_rows = [xi.shape[0] for xi in x]
     _raise(_lib.purlin_moe_dispatch(_ptrs(x), _ptrs(y), P, int(row_bytes), _ptrs(idx),
-                                    _i64(counts), _i64(x_rows), ctypes.c_void_p(_stream(stream))),
+                                    _i64(counts), _i64(x_rows), 1 if unique else 0,
+                                    ctypes.c_void_p(_stream(stream))),
            "purlin_moe_dispatch")
 
 

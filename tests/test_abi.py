@@ -189,7 +189,7 @@ def test_moe_argument_checks(purlin):
 
     def disp(counts, x_rows, row_bytes=64, P_=P, idx_=idx, y_=y):
         return lib.purlin_moe_dispatch(x, y_, P_, row_bytes, idx_, (I64 * len(counts))(*counts),
-                                       (I64 * len(x_rows))(*x_rows), None)
+                                       (I64 * len(x_rows))(*x_rows), 0, None)
 
     def comb(counts, x_rows, row_bytes=64, w_=w, out=x):
         return lib.purlin_moe_combine(y, out, P, row_bytes, idx, w_, (I64 * len(counts))(*counts),

@@ -65,16 +65,19 @@ def run_case(purlin, P, H, x_rows, rng, fanout=3, shift=0):
     # dispatch of random bits, bit for bit
     dx = [dev_rows(x[i], shift) for i in range(P)]
     dy = [dev_rows(np.zeros((y_rows[j], H), np.uint16), shift) for j in range(P)]
-    purlin.moe_dispatch(dx, dy, d_idx, counts, x_rows, H * 2)
-    purlin.check()
     want = moe.dispatch(x, idx, counts, P)
-    for j in range(P):
-        assert np.array_equal(host_rows(dy[j]), want[j]), ("dispatch", j)
+    for unique in (False, True):
+        for t in dy:
+            t.view(torch.int16).fill_(0x5A5A)
+        purlin.moe_dispatch(dx, dy, d_idx, counts, x_rows, H * 2, unique=unique)
+        purlin.check()
+        for j in range(P):
+            assert np.array_equal(host_rows(dy[j]), want[j]), ("dispatch", unique, j)
     if (H * 2) % 16 or shift:
         return
     # combine of the dispatched finite rows
     dxv = [dev_rows(xv[i]) for i in range(P)]
-    purlin.moe_dispatch(dxv, dy, d_idx, counts, x_rows, H * 2)
+    purlin.moe_dispatch(dxv, dy, d_idx, counts, x_rows, H * 2, unique=True)
     out = [dev_rows(np.full((x_rows[i], H), 0x7E7E, np.uint16)) for i in range(P)]
     purlin.moe_combine(dy, out, d_idx, d_w, counts, x_rows, H * 2)
     purlin.check()
@@ -125,6 +128,16 @@ def test_moe_device_side_errors(purlin):
     purlin.check()                                   # the status word was cleared
     dup = [torch.tensor([1, 1], dtype=torch.int32, device="cuda"),
            torch.tensor([0, 3], dtype=torch.int32, device="cuda")]
+    # a repeat is fine for the row-by-row dispatch, reported for the unique one
+    purlin.moe_dispatch(dx, [dev_rows(np.zeros((3, H), np.uint16)), dev_rows(np.zeros((1, H), np.uint16))],
+                        dup, [2, 0, 1, 1], x_rows, H * 2, unique=False)
+    purlin.check()
+    purlin.moe_dispatch(dx, [dev_rows(np.zeros((3, H), np.uint16)), dev_rows(np.zeros((1, H), np.uint16))],
+                        dup, [2, 0, 1, 1], x_rows, H * 2, unique=True)
+    with pytest.raises(purlin.PurlinError) as e:
+        purlin.check()
+    assert e.value.status == "INVALID_ARG"
+    purlin.check()
     w = [torch.ones(2, device="cuda"), torch.ones(2, device="cuda")]
     out = [dev_rows(np.zeros((4, H), np.uint16)) for _ in range(P)]
     purlin.moe_combine(dy, out, dup, w, [2, 0, 1, 1], x_rows, H * 2)
@@ -150,11 +163,14 @@ def test_moe_full_configuration(purlin):
          for i in range(P)]
     y_rows = [sum(counts[i * P + j] for i in range(P)) for j in range(P)]
     y = [torch.empty(y_rows[j], H, dtype=torch.bfloat16, device=dev) for j in range(P)]
-    purlin.moe_dispatch(x, y, idx, counts)
-    purlin.check()
-    for j in range(P):
-        want = torch.cat([x[i][torch.as_tensor(rows[i][j], device=dev)] for i in range(P)])
-        assert torch.equal(y[j], want), j
+    for unique in (False, True):
+        for t in y:
+            t.zero_()
+        purlin.moe_dispatch(x, y, idx, counts, unique=unique)
+        purlin.check()
+        for j in range(P):
+            want = torch.cat([x[i][torch.as_tensor(rows[i][j], device=dev)] for i in range(P)])
+            assert torch.equal(y[j], want), (unique, j)
     out = [torch.empty(tokens, H, dtype=torch.bfloat16, device=dev) for _ in range(P)]
     purlin.moe_combine(y, out, idx, w, counts)
     purlin.check()
