@@ -161,12 +161,16 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
   // first destination address of the job (alignment reference for the slots)
   const uint64_t b0 =
       uint64_t(p.out[jb.dst < 0 ? 0 : jb.dst]) + uint64_t(jb.dst_off);
-  if (threadIdx.x == 0) ok = 1;
+  // Entry notify as in the zero-staging kernel; a workgroup whose entry wait
+  // failed skips its role but still counts itself out at the end.
+  const bool run = !p.sync || snac::entry(p);
+  if (threadIdx.x == 0) ok = run ? 1 : 0;
   __syncthreads();
 
-  if (kind == 0) {
+  if (!run) {
+    // nothing: fall through to the exit count
+  } else if (kind == 0) {
     // ---------------- owner ----------------
-    int notified = 0;
     for (int m = 0;; ++m) {
       const int c = lane + L * m;
       if (c >= ntl) break;
@@ -229,9 +233,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
         if (sj.n_scatter > 0)
           snac::store_rel(slot_ref(sp, ring0 + sj.n_stage, slot).ready, tag(e, round + 1));
       }
-      ++notified;
     }
-    (void)notified;
   } else if (kind <= sj.n_stage) {
     // ---------------- stager ----------------
     const int k = kind - 1;
@@ -300,6 +302,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       if (threadIdx.x == 0) snac::add_rlx(o.credit, uint64_t(1));
     }
   }
+  if (p.sync) snac::exit_notify(p);
 }
 
 // ---- MoE dispatch / combine --------------------------------------------------

@@ -552,15 +552,22 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     if (st != PURLIN_OK) return st;
     sp.ring = ds->ring;
     sp.slot_flags = ds->slot_flags;
-    sp.base.sync = 0;
+    sp.base.sync = pol.sync == 2 ? 0 : 1;
+    for (int k = 0; k < kExitSlots; ++k)
+      sp.base.exit_expect[k] = ds->exit_total[(ds->epoch - 1u) & 1u][k];
     err = launch_staged(sp, kind, nt, stream);
+    if (err == hipSuccess && sp.base.sync) {
+      const int g = sp.total_roles;
+      for (int k = 0; k < kExitSlots; ++k)
+        ds->exit_total[ds->epoch & 1u][k] += uint32_t(g / kExitSlots + (k < g % kExitSlots ? 1 : 0));
+    }
     info.grid = sp.total_roles;
     info.zero_staging = 0;
     info.rows = 1;
     info.depth = sp.depth;
     info.chunk_bytes = chunk;
     info.tiles = sp.base.total_tiles;
-    info.sync = 0;
+    info.sync = sp.base.sync;
   }
   if (err != hipSuccess) return PURLIN_ERR_HIP;
   g_last = info;
