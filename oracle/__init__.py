@@ -10,7 +10,8 @@ output layout plus a copy or a reduction), Figure 4 (ReduceScatter,
 AllGather and AllToAll layouts), Figure 6 (AllReduce composed of both) and
 Table 2 / Figure 16 (variable-length variants), and ``moe.py``: MoE dispatch
 and combine with the token permutation folded in (Table 2's expert-parallel
-call sites).
+call sites), and ``ulysses.py``: the sequence-parallel AllToAll between
+sequence-sharded and head-sharded layouts (Table 2's Ulysses call site).
 
 Every function is pinned by the oracle tests; the readings it takes where the
 pages are silent are documented in ``semantics.py``.
@@ -19,10 +20,10 @@ from .bf16 import widen_bf16, round_bf16
 from .semantics import (NAMINGS, OPS, DTYPES, ELEM_BYTES, COLLECTIVES,
                          name_count, partitions, collective, OracleError)
 from .brute import collective_brute
-from . import moe
+from . import moe, ulysses
 
 __all__ = [
     "widen_bf16", "round_bf16", "NAMINGS", "OPS", "DTYPES", "ELEM_BYTES",
     "COLLECTIVES", "name_count", "partitions", "collective", "OracleError",
-    "collective_brute", "moe",
+    "collective_brute", "moe", "ulysses",
 ]
