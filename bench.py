@@ -393,6 +393,82 @@ def moe_bench(purlin, steps, warmup, dev):
             "steps": steps, "data": "synthetic"}
 
 
+def ulysses_bench(purlin, steps, warmup, dev):
+    """The Ulysses exchange (the pages' diffusion workload: Qwen-Image with
+    Ulysses sequence parallelism) at the 1024x1024 attention shape, query /
+    key / value fused into one call to the head layout and the attention
+    output back to the sequence layout, and at about 64 MiB per rank each
+    way.  Timed with HIP events, p50 over `steps` back-to-back calls (inputs
+    stay hot in the caches between calls, as they would after the producing
+    projection).  Context: the unfused path, a torch transpose into a packed
+    send buffer, then the contiguous AllToAll.  B_min: every byte read once
+    and written once."""
+    import torch
+    import workloads
+    stream = torch.cuda.current_stream()
+    res = {}
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        purlin.check(stream)
+        ev = []
+        for _ in range(steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        purlin.check(stream)
+        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+        return ts[len(ts) // 2]
+
+    for label, cfg in (("qwen_image_1024", workloads.ULYSSES_QWEN_IMAGE_1024),
+                       ("64MiB_per_rank", workloads.ULYSSES_64MIB)):
+        H, D = cfg["heads"], cfg["head_dim"]
+        g = H // P
+        for direction, n_pack in (("to_heads", cfg["n_pack"]), ("to_sequence", 1)):
+            rows = [s_ * n_pack for s_ in cfg["seq"]]
+            S = sum(rows)
+            seq_bufs = [workloads.device_values(rows[i] * H * D, "normal", "bf16", 7, i, dev)
+                        for i in range(P)]
+            head_bufs = [torch.empty(S * g * D, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+            to_seq = direction == "to_sequence"
+            if to_seq:
+                purlin.ulysses(seq_bufs, head_bufs, H, seq=rows, head_bytes=2 * D, stream=stream)
+                ins, outs = head_bufs, seq_bufs
+            else:
+                ins, outs = seq_bufs, head_bufs
+            nbytes = sum(rows) * H * D * 2
+            t = timed(lambda: purlin.ulysses(ins, outs, H, seq=rows, head_bytes=2 * D,
+                                             to_sequence=to_seq, stream=stream))
+            info = purlin.last_launch()
+            entry = {"p50_us": round(t * 1e6, 2), "bytes_each_way": nbytes,
+                     "hbm_frac": round(2 * nbytes / t / HBM_PEAK, 4), "grid": info["grid"],
+                     "chunk_bytes": info["chunk_bytes"], "unit": info["unit"],
+                     "tokens_per_rank": rows[0], "heads": H, "head_dim": D}
+            if not to_seq:
+                # unfused: pack each rank's rows by destination, then the plain AllToAll
+                send = [torch.empty(rows[i] * H * D, dtype=torch.bfloat16, device=dev)
+                        for i in range(P)]
+                counts = [rows[i] * g * D for i in range(P) for _ in range(P)]
+
+                def unfused():
+                    for i in range(P):
+                        send[i].view(P, rows[i], g, D).copy_(
+                            seq_bufs[i].view(rows[i], P, g, D).transpose(0, 1))
+                    purlin.all_to_all(send, head_bufs, counts, stream=stream)
+                tu = timed(unfused)
+                entry["unfused_pack_then_alltoall_p50_us"] = round(tu * 1e6, 2)
+                del send
+            res["%s_%s" % (label, direction)] = entry
+            del seq_bufs, head_bufs, ins, outs
+            torch.cuda.empty_cache()
+    return {"ulysses": res, "P": P, "steps": steps, "dtype": "bf16", "data": "synthetic"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -413,6 +489,9 @@ def main():
                     help="skip the pattern-ceiling measurement after the timed steps")
     ap.add_argument("--moe", action="store_true",
                     help="time MoE dispatch / combine at 4096 x 7168 bf16 per rank, top-8 of 256")
+    ap.add_argument("--ulysses", action="store_true",
+                    help="time the Ulysses sequence <-> head exchange (Qwen-Image 1024x1024 "
+                         "attention shape and ~64 MiB per rank)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time only the plain 128-bit streaming copy of --size bytes "
                          "(HBM counter calibration and copy ceiling)")
@@ -439,6 +518,9 @@ def main():
         return
     if args.moe:
         print(json.dumps(moe_bench(purlin, args.steps, args.warmup, dev)), flush=True)
+        return
+    if args.ulysses:
+        print(json.dumps(ulysses_bench(purlin, args.steps, args.warmup, dev)), flush=True)
         return
     if args.sweep:
         sweep(purlin, T, args.variant, args.sweep, dev)

@@ -110,7 +110,8 @@ typedef struct {
   int32_t sync;
   int32_t rows;          /* 1 if the kernel with the realigning row bodies ran (some source
                             off its destinations' 16-byte phase), 0 if the aligned-only one */
-  int32_t reserved;
+  int32_t unit;          /* purlin_ulysses: bytes each lane access moved (16, 8, 4 or 2);
+                            0 for the other calls */
 } purlin_launch_info;
 
 /*
@@ -233,7 +234,35 @@ PURLIN_API purlin_status purlin_moe_combine(void *const *y, void *const *out, in
                                             const float *const *w, const int64_t *counts,
                                             const int64_t *x_rows, hipStream_t stream);
 
-/* Measurement: the launch shape of the most recent successful call. *//* Measurement: the launch shape of the most recent successful call. */
+/*
+ * Ulysses sequence-parallel AllToAll (Purlin pages, Table 2: the diffusion
+ * workload's AllToAll that redistributes sequence and attention-head
+ * partitions).  P ranks, `heads` attention heads (a multiple of P), each
+ * head `head_bytes` bytes per token (head dimension x element size; even),
+ * seq[i] >= 0 tokens on rank i (host array of P), S = sum of seq.  Layouts,
+ * row-major, tokens of rank 0 first in the head layout:
+ *
+ *   sequence layout  rank i:  [seq[i], heads, head_bytes]
+ *   head layout      rank j:  [S, heads / P, head_bytes]   (head group j)
+ *
+ * to_sequence = 0: in = sequence layout, out = head layout,
+ *   out[j][off_i + s][h] = in[i][s][j * heads / P + h],  off_i = seq[0] + ... + seq[i-1];
+ * to_sequence = 1: the inverse (in = head layout, out = sequence layout).
+ * Bytes are copied as they are (any element type).  Several tensors that
+ * share a token axis, laid out [tokens, n, heads, head_bytes] (query, key and
+ * value of a fused projection), exchange in one call with seq[i] * n as the
+ * token counts.  in and out are host arrays of P device pointers (a pointer
+ * may be NULL only where its buffer is empty); every out buffer is disjoint
+ * from every in buffer.  Returns INVALID_ARG for a bad count, size,
+ * alignment (odd addresses) or overlap, HIP for a launch failure.
+ * Asynchronous on `stream`; runs the entry / exit handshake like
+ * purlin_collective.
+ */
+PURLIN_API purlin_status purlin_ulysses(void *const *in, void *const *out, int P,
+                                        const int64_t *seq, int64_t heads, int64_t head_bytes,
+                                        int to_sequence, hipStream_t stream);
+
+/* Measurement: the launch shape of the most recent successful call. */
 PURLIN_API purlin_status purlin_last_launch(purlin_launch_info *info);
 
 /* Measurement: a plain 128-bit streaming copy of `bytes` bytes (both

@@ -509,6 +509,62 @@ __global__ void __launch_bounds__(kThreads) moe_combine_kernel(const MoePlan m) 
   if (p.sync) snac::exit_notify(p);
 }
 
+// ---- Ulysses strided exchange -----------------------------------------------
+// Ulysses sequence parallelism is one of the call sites of Purlin's AllToAll
+// (Table 2, the diffusion workload): each pair of ranks exchanges the rows of
+// one attention-head group, which are strided in the sequence-sharded layout
+// and contiguous in the head-sharded one.  No intermediate packed buffer:
+// lanes walk the pair's rows laid end to end in units of kUnit bytes, and each
+// unit finds its row with one multiply-high (the host's magic divisor), so
+// consecutive lanes read and write consecutive bytes of a row and a wavefront
+// crosses row ends without idle lanes, whatever the row size.
+
+template <int kUnit> struct UnitOf;
+template <> struct UnitOf<16> { typedef atom::u32x4 T; };
+template <> struct UnitOf<8> { typedef uint32_t T __attribute__((ext_vector_type(2))); };
+template <> struct UnitOf<4> { typedef uint32_t T; };
+template <> struct UnitOf<2> { typedef uint16_t T; };
+
+template <int kUnit, int kU>
+__global__ void __launch_bounds__(kThreads) strided_kernel(const StridedPlan sp) {
+  typedef typename UnitOf<kUnit>::T T;
+  const LaunchPlan &p = sp.base;
+  const bool run = !p.sync || snac::entry(p);
+  const uint32_t per_row = uint32_t(sp.row_bytes / kUnit);
+  const int64_t per_tile = p.chunk_bytes / kUnit;
+  int t = run ? int(blockIdx.x) : p.total_tiles;
+  int q = t < p.total_tiles ? job_of_tile(p, t) : 0;
+  for (; t < p.total_tiles; t += gridDim.x) {
+    if (t >= p.tile_begin[q + 1]) q = job_of_tile(p, t);
+    const Job jb = p.jobs[q];
+    const uint64_t sb = uint64_t(p.in[jb.src]) + uint64_t(jb.src_off);
+    const uint64_t db = uint64_t(p.out[jb.dst]) + uint64_t(jb.dst_off);
+    const int64_t u0 = int64_t(t - p.tile_begin[q]) * per_tile;
+    const int64_t n = jb.nbytes / kUnit;
+    // units of the pair are < 2^31 (checked by the host)
+    const uint32_t u1 = uint32_t(u0 + per_tile < n ? u0 + per_tile : n);
+    for (uint32_t u = uint32_t(u0) + threadIdx.x; u < u1; u += kThreads * kU) {
+      T v[kU];
+      uint64_t dst[kU];
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const uint32_t uk = u + uint32_t(k) * kThreads;
+        if (uk < u1) {
+          const uint32_t r = uint32_t((uint64_t(uk) * sp.magic) >> sp.shift);
+          const uint32_t c = uk - r * per_row;
+          v[k] = __builtin_nontemporal_load(atom::gp<const T>(
+              sb + uint64_t(r) * uint64_t(sp.src_stride) + uint64_t(c) * kUnit));
+          dst[k] = db + uint64_t(r) * uint64_t(sp.dst_stride) + uint64_t(c) * kUnit;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kU; ++k)
+        if (u + uint32_t(k) * kThreads < u1) __builtin_nontemporal_store(v[k], atom::gp<T>(dst[k]));
+    }
+  }
+  if (p.sync) snac::exit_notify(p);
+}
+
 // ---- calibration copy ------------------------------------------------------
 // A plain streaming copy with the same access style as the collectives (16-byte
 // nontemporal loads and stores, 4 per lane in flight): the reference for HBM
@@ -661,6 +717,25 @@ hipError_t launch_moe(const MoePlan &m, MoeKernel which, bool rows, int grid, hi
 
 hipError_t moe_resident_per_cu(MoeKernel which, bool rows, int *blocks) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, moe_kernel_fn(which, rows), kThreads, 0);
+}
+
+// Units in flight per lane: 16 KiB per workgroup pass for 16-byte units.
+static void *strided_fn(int unit) {
+  switch (unit) {
+    case 16: return reinterpret_cast<void *>(&strided_kernel<16, 4>);
+    case 8: return reinterpret_cast<void *>(&strided_kernel<8, 8>);
+    case 4: return reinterpret_cast<void *>(&strided_kernel<4, 8>);
+    default: return reinterpret_cast<void *>(&strided_kernel<2, 16>);
+  }
+}
+
+hipError_t launch_strided(const StridedPlan &sp, int unit, int grid, hipStream_t stream) {
+  void *args[] = {const_cast<StridedPlan *>(&sp)};
+  return hipLaunchKernel(strided_fn(unit), dim3(grid), dim3(kThreads), args, 0, stream);
+}
+
+hipError_t strided_resident_per_cu(int unit, int *blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, strided_fn(unit), kThreads, 0);
 }
 
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,

@@ -104,8 +104,26 @@ struct MoePlan {
   int64_t row_bytes;
 };
 
+// Strided-row AllToAll: the Ulysses exchange between sequence-sharded and
+// head-sharded activations (Table 2 of the Purlin pages, the diffusion
+// workload).  base.jobs[q] moves rows of row_bytes bytes from rank jobs[q].src
+// to rank jobs[q].dst: row k is read at in[src] + src_off + k * src_stride and
+// written at out[dst] + dst_off + k * dst_stride, nbytes = rows * row_bytes.
+// Work is counted in units of `unit` bytes, the largest power of two up to 16
+// that divides every row size, stride, offset and buffer address; a tile is
+// chunk_bytes of the pair's rows laid end to end.
+struct StridedPlan {
+  LaunchPlan base;
+  int64_t row_bytes;
+  int64_t src_stride;
+  int64_t dst_stride;
+  uint32_t magic;   // row of unit u (u < 2^31) = (u * magic) >> shift
+  int32_t shift;
+};
+
 static_assert(sizeof(LaunchPlan) <= 3072, "launch plan must fit in kernel arguments");
 static_assert(sizeof(MoePlan) <= 3840, "MoE plan must fit in kernel arguments");
+static_assert(sizeof(StridedPlan) <= 3840, "strided plan must fit in kernel arguments");
 static_assert(sizeof(StagedPlan) <= 3840, "staged plan must fit in kernel arguments");
 
 }  // namespace purlin

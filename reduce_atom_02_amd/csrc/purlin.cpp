@@ -313,8 +313,9 @@ purlin_status moe_plan(void *const *rowsrc, void *const *rowdst, int P, int64_t 
   return PURLIN_OK;
 }
 
-// The launch-wide fields of a plan: flags, epoch, watchdog and handshake.
-void moe_launch_fields(DeviceState &ds, LaunchPlan &lp, const purlin_policy &pol) {
+// The launch-wide fields of an MoE or strided plan: flags, epoch, watchdog
+// and handshake.
+void side_launch_fields(DeviceState &ds, LaunchPlan &lp, const purlin_policy &pol) {
   if (++ds.epoch == 0) ds.epoch = 1;
   lp.flags = ds.flags;
   lp.epoch = ds.epoch;
@@ -324,10 +325,100 @@ void moe_launch_fields(DeviceState &ds, LaunchPlan &lp, const purlin_policy &pol
   for (int k = 0; k < kExitSlots; ++k) lp.exit_expect[k] = ds.exit_total[(ds.epoch - 1u) & 1u][k];
 }
 
-void moe_count_exit(DeviceState &ds, const LaunchPlan &lp, int grid) {
+void side_count_exit(DeviceState &ds, const LaunchPlan &lp, int grid) {
   if (!lp.sync) return;
   for (int k = 0; k < kExitSlots; ++k)
     ds.exit_total[lp.epoch & 1u][k] += uint32_t(grid / kExitSlots + (k < grid % kExitSlots ? 1 : 0));
+}
+
+// Divisor d of the strided kernel's row lookup: floor(u / d) = (u * m) >> s
+// for every 0 <= u < 2^31, with l = ceil(log2 d), s = 31 + l and
+// m = ceil(2^s / d) (Granlund and Montgomery, "Division by invariant integers
+// using multiplication", 1994, Theorem 4.2 with N = 31: m * d - 2^s < d <= 2^l).
+// m < 2^32 for every d < 2^31.
+void magic_divisor(uint32_t d, uint32_t *m, int32_t *s) {
+  int l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t two_s = uint64_t(1) << (31 + l);
+  *m = uint32_t((two_s + d - 1) / d);
+  *s = 31 + l;
+}
+
+// Plan of the Ulysses exchange.  Sequence layout: rank i holds
+// [seq[i], heads, head_bytes]; head layout: rank j holds [S, heads / P,
+// head_bytes], the tokens of rank 0 first.  Pair (i, j) moves rank i's
+// tokens' slice of head group j.
+purlin_status ulysses_plan(void *const *in, void *const *out, int P, const int64_t *seq,
+                           int64_t heads, int64_t head_bytes, int to_sequence, StridedPlan *sp,
+                           int *unit_out, int64_t *total_out) {
+  if (!in || !out || !seq || P < 1 || P > kMaxRanks || heads < 1 || heads % P ||
+      head_bytes <= 0 || (head_bytes & 1) || (to_sequence != 0 && to_sequence != 1))
+    return PURLIN_ERR_INVALID_ARG;
+  const int64_t kLimit = int64_t(1) << 40;
+  if (heads > kLimit / head_bytes) return PURLIN_ERR_INVALID_ARG;
+  const int64_t token_bytes = heads * head_bytes;        // one token, all heads
+  const int64_t row = token_bytes / P;                   // one token, one head group
+  int64_t S = 0;
+  int64_t off[kMaxRanks + 1] = {};
+  for (int i = 0; i < P; ++i) {
+    if (seq[i] < 0 || seq[i] > kLimit) return PURLIN_ERR_INVALID_ARG;
+    S += seq[i];
+    off[i + 1] = S;
+  }
+  if (S > kLimit / token_bytes) return PURLIN_ERR_INVALID_ARG;
+  // seq-layout and head-layout buffers of each rank
+  void *const *sq = to_sequence ? out : in;
+  void *const *hd = to_sequence ? in : out;
+  std::vector<std::pair<uintptr_t, uintptr_t>> sr, hr;
+  uint64_t align = uint64_t(row) | uint64_t(token_bytes) | 16u;
+  for (int r = 0; r < P; ++r) {
+    const int64_t sb = seq[r] * token_bytes, hb = S * row;
+    if (sb > 0) {
+      if (!sq[r]) return PURLIN_ERR_INVALID_ARG;
+      sr.push_back({uintptr_t(sq[r]), uintptr_t(sq[r]) + uintptr_t(sb)});
+      align |= uint64_t(uintptr_t(sq[r]));
+    }
+    if (hb > 0) {
+      if (!hd[r]) return PURLIN_ERR_INVALID_ARG;
+      hr.push_back({uintptr_t(hd[r]), uintptr_t(hd[r]) + uintptr_t(hb)});
+      align |= uint64_t(uintptr_t(hd[r]));
+    }
+  }
+  if (align & 1) return PURLIN_ERR_INVALID_ARG;
+  if (!(to_sequence ? ranges_disjoint(hr, sr) : ranges_disjoint(sr, hr)))
+    return PURLIN_ERR_INVALID_ARG;
+  const int unit = int(align & (~align + 1));   // lowest set bit, at most 16
+  // every pair's units must stay below 2^31
+  for (int i = 0; i < P; ++i)
+    if (seq[i] * row / unit >= (int64_t(1) << 31)) return PURLIN_ERR_INVALID_ARG;
+
+  *sp = StridedPlan{};
+  LaunchPlan &lp = sp->base;
+  for (int r = 0; r < kMaxRanks; ++r) {
+    lp.in[r] = r < P ? static_cast<const char *>(in[r]) : nullptr;
+    lp.out[r] = r < P ? static_cast<char *>(out[r]) : nullptr;
+  }
+  lp.P = P;
+  lp.njobs = P * P;
+  int64_t total = 0;
+  for (int a = 0; a < P; ++a) {      // source rank
+    for (int b = 0; b < P; ++b) {    // destination rank
+      // i: the sequence rank of the pair, j: its head group
+      const int i = to_sequence ? b : a, j = to_sequence ? a : b;
+      const int64_t seq_off = int64_t(j) * row;      // head group j inside a token
+      const int64_t head_off = off[i] * row;         // rank i's tokens in the head layout
+      lp.jobs[a * P + b] = Job{to_sequence ? head_off : seq_off, to_sequence ? seq_off : head_off,
+                               seq[i] * row, int32_t(a), int32_t(b)};
+      total += seq[i] * row;
+    }
+  }
+  sp->row_bytes = row;
+  sp->src_stride = to_sequence ? row : token_bytes;
+  sp->dst_stride = to_sequence ? token_bytes : row;
+  magic_divisor(uint32_t(row / unit), &sp->magic, &sp->shift);
+  *unit_out = unit;
+  *total_out = total;
+  return PURLIN_OK;
 }
 
 // Workgroups of an MoE launch: the policy's wgs_per_rank when set, else
@@ -586,7 +677,7 @@ purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t
   DeviceState *ds = nullptr;
   st = device_state(&ds);
   if (st != PURLIN_OK) return st;
-  moe_launch_fields(*ds, m.base, effective_policy());
+  side_launch_fields(*ds, m.base, effective_policy());
   bool rows = (row_bytes & 15) != 0;
   for (int r = 0; r < P; ++r)
     rows |= ((uintptr_t(x[r]) | uintptr_t(y[r])) & 15) != 0;
@@ -610,7 +701,7 @@ purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t
     grid = moe_grid(*ds, MoeKernel::kDispatch, rows, total, int64_t(ds->cus) * 4);
     if (launch_moe(m, MoeKernel::kDispatch, rows, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
   }
-  moe_count_exit(*ds, m.base, grid);
+  side_count_exit(*ds, m.base, grid);
   purlin_launch_info info{};
   info.grid = grid;
   info.threads = kThreads;
@@ -649,7 +740,7 @@ purlin_status purlin_moe_combine(void *const *y, void *const *out, int P, int64_
   st = ensure_inverse(*ds, out_rows * P * int64_t(sizeof(uint64_t)));
   if (st != PURLIN_OK) return st;
   m.inv = ds->inv;
-  moe_launch_fields(*ds, m.base, effective_policy());
+  side_launch_fields(*ds, m.base, effective_policy());
   m.base.chunk_bytes = row_bytes;
   if (total > 0) {
     const int g0 = moe_grid(*ds, MoeKernel::kInverse, false, (total + kThreads - 1) / kThreads,
@@ -658,7 +749,7 @@ purlin_status purlin_moe_combine(void *const *y, void *const *out, int P, int64_
   }
   const int grid = moe_grid(*ds, MoeKernel::kCombine, false, out_rows, int64_t(ds->cus) * 4);
   if (launch_moe(m, MoeKernel::kCombine, false, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
-  moe_count_exit(*ds, m.base, grid);
+  side_count_exit(*ds, m.base, grid);
   purlin_launch_info info{};
   info.grid = grid;
   info.threads = kThreads;
@@ -668,6 +759,52 @@ purlin_status purlin_moe_combine(void *const *y, void *const *out, int P, int64_
   info.bytes_min = (y_total + out_rows) * row_bytes;
   info.njobs = P * P;
   info.sync = m.base.sync;
+  g_last = info;
+  g_have_last = true;
+  return PURLIN_OK;
+}
+
+purlin_status purlin_ulysses(void *const *in, void *const *out, int P, const int64_t *seq,
+                             int64_t heads, int64_t head_bytes, int to_sequence,
+                             hipStream_t stream) {
+  StridedPlan sp;
+  int unit = 16;
+  int64_t total = 0;
+  purlin_status st = ulysses_plan(in, out, P, seq, heads, head_bytes, to_sequence, &sp, &unit, &total);
+  if (st != PURLIN_OK) return st;
+  if (total == 0) return PURLIN_OK;
+  DeviceState *ds = nullptr;
+  st = device_state(&ds);
+  if (st != PURLIN_OK) return st;
+  const purlin_policy pol = effective_policy();
+  side_launch_fields(*ds, sp.base, pol);
+  // the point-to-point copy policy: four workgroups per CU, 32 KiB tiles,
+  // smaller tiles for small exchanges
+  const int64_t cap = pol.wgs_per_rank ? int64_t(pol.wgs_per_rank) * kMaxRanks : int64_t(ds->cus) * 4;
+  const int64_t chunk = pol.chunk_bytes ? pol.chunk_bytes : fit_chunk(int64_t(32) << 10, total, cap);
+  sp.base.chunk_bytes = chunk;
+  int64_t t = 0;
+  for (int q = 0; q < P * P; ++q) {
+    sp.base.tile_begin[q] = int32_t(t);
+    t += (sp.base.jobs[q].nbytes + chunk - 1) / chunk;
+  }
+  for (int q = P * P; q <= kMaxJobs; ++q) sp.base.tile_begin[q] = int32_t(t);
+  sp.base.total_tiles = int32_t(t);
+  int b = 0;
+  if (strided_resident_per_cu(unit, &b) != hipSuccess || b < 1) b = 1;
+  const int grid = int(std::max<int64_t>(1, std::min<int64_t>({t, cap, int64_t(ds->cus) * b})));
+  if (launch_strided(sp, unit, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
+  side_count_exit(*ds, sp.base, grid);
+  purlin_launch_info info{};
+  info.grid = grid;
+  info.threads = kThreads;
+  info.zero_staging = 1;
+  info.chunk_bytes = chunk;
+  info.tiles = t;
+  info.bytes_min = 2 * total;
+  info.njobs = P * P;
+  info.sync = sp.base.sync;
+  info.unit = unit;
   g_last = info;
   g_have_last = true;
   return PURLIN_OK;

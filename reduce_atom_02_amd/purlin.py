@@ -18,7 +18,7 @@ __all__ = [
     "LIB_PATH", "NAMINGS", "OPS", "DTYPES", "STATUS", "PurlinError", "collective",
     "all_reduce", "reduce_scatter", "all_gather", "all_to_all", "check",
     "set_policy", "get_policy", "plan_describe", "last_launch", "stream_copy", "stream_pattern",
-    "moe_dispatch", "moe_combine", "release", "exported_symbols",
+    "moe_dispatch", "moe_combine", "ulysses", "release", "exported_symbols",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpurlin.so")
@@ -65,7 +65,7 @@ class LaunchInfo(ctypes.Structure):
                 ("zero_staging", ctypes.c_int32), ("depth", ctypes.c_int32),
                 ("chunk_bytes", ctypes.c_int64), ("tiles", ctypes.c_int64),
                 ("bytes_min", ctypes.c_int64), ("njobs", ctypes.c_int32),
-                ("sync", ctypes.c_int32), ("rows", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("sync", ctypes.c_int32), ("rows", ctypes.c_int32), ("unit", ctypes.c_int32)]
 
 
 def _load():
@@ -103,6 +103,9 @@ def _load():
     lib.purlin_moe_combine.argtypes = [P_VP, P_VP, ctypes.c_int, ctypes.c_int64, P_VP, P_VP,
                                        P_I64, P_I64, ctypes.c_void_p]
     lib.purlin_moe_combine.restype = ctypes.c_int
+    lib.purlin_ulysses.argtypes = [P_VP, P_VP, ctypes.c_int, P_I64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_void_p]
+    lib.purlin_ulysses.restype = ctypes.c_int
     lib.purlin_stream_pattern.restype = ctypes.c_int
     lib.purlin_strerror.argtypes = [ctypes.c_int]
     lib.purlin_strerror.restype = ctypes.c_char_p
@@ -119,7 +122,7 @@ def exported_symbols():
     names = ["purlin_collective", "purlin_check", "purlin_set_policy", "purlin_get_policy",
              "purlin_plan_describe", "purlin_last_launch", "purlin_stream_copy",
              "purlin_stream_pattern", "purlin_moe_dispatch", "purlin_moe_combine",
-             "purlin_strerror", "purlin_release"]
+             "purlin_ulysses", "purlin_strerror", "purlin_release"]
     return [n for n in names if hasattr(_lib, n)]
 
 
@@ -352,6 +355,23 @@ def moe_combine(y, out, idx, w, counts, x_rows=None, row_bytes=None, stream=None
     _raise(_lib.purlin_moe_combine(_ptrs(y), _ptrs(out), P, int(row_bytes), _ptrs(idx), _ptrs(w),
                                    _i64(counts), _i64(x_rows), ctypes.c_void_p(_stream(stream))),
            "purlin_moe_combine")
+
+
+def ulysses(ins, outs, heads, seq=None, head_bytes=None, to_sequence=False, stream=None):
+    """Ulysses AllToAll (see include/purlin.h): sequence layout [seq[i], heads,
+    head] on rank i <-> head layout [S, heads / P, head] on rank j.  ins, outs:
+    P tensors (or addresses); seq and head_bytes default to what the
+    sequence-layout tensors hold (their bytes / (heads * head_bytes) tokens,
+    their last dimension times the element size)."""
+    P = len(ins)
+    sq = outs if to_sequence else ins
+    if head_bytes is None:
+        head_bytes = sq[0].shape[-1] * sq[0].element_size()
+    if seq is None:
+        seq = [t.numel() * t.element_size() // (int(heads) * int(head_bytes)) for t in sq]
+    _raise(_lib.purlin_ulysses(_ptrs(ins), _ptrs(outs), P, _i64(seq), int(heads), int(head_bytes),
+                               1 if to_sequence else 0, ctypes.c_void_p(_stream(stream))),
+           "purlin_ulysses")
 
 
 def release():

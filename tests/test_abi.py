@@ -30,7 +30,7 @@ def header_functions():
 def test_every_declared_symbol_is_exported(purlin):
     import ctypes
     declared = header_functions()
-    assert len(declared) == 12, declared
+    assert len(declared) == 13, declared
     lib = ctypes.CDLL(purlin.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -208,3 +208,34 @@ def test_moe_argument_checks(purlin):
     assert comb([1, 1, 1, 1], [4, 4], row_bytes=24) == 1    # combine rows: 16-byte multiples
     assert comb([1, 1, 1, 1], [4, 4], w_=V(0x30000, 0)) == 1     # NULL weights with entries
     assert comb([1, 1, 1, 1], [4, 4], out=V(A_IN + 8, A_IN + (1 << 30))) == 1  # misaligned
+
+
+def test_ulysses_argument_checks(purlin):
+    """The Ulysses exchange rejects bad arguments before any HIP call."""
+    import ctypes
+    lib = purlin._lib
+    P = 2
+    V = ctypes.c_void_p * P
+    I64 = ctypes.c_int64
+    ins = V(A_IN, A_IN + (1 << 30))
+    outs = V(A_OUT, A_OUT + (1 << 30))
+
+    def uly(seq, heads=4, head_bytes=256, to_sequence=0, P_=P, in_=ins, out_=outs):
+        return lib.purlin_ulysses(in_, out_, P_, (I64 * len(seq))(*seq), heads, head_bytes,
+                                  to_sequence, None)
+
+    assert uly([4, 4], P_=0) == 1
+    assert uly([4, 4], P_=9) == 1
+    assert uly([4, 4], heads=3) == 1                 # heads not a multiple of P
+    assert uly([4, 4], heads=0) == 1
+    assert uly([4, 4], head_bytes=255) == 1          # odd head size
+    assert uly([4, 4], head_bytes=0) == 1
+    assert uly([4, -1]) == 1                         # negative token count
+    assert uly([4, 4], to_sequence=2) == 1
+    assert uly([4, 4], in_=V(A_IN, 0)) == 1          # NULL buffer that holds tokens
+    assert uly([4, 4], in_=V(A_IN + 1, A_IN + (1 << 30))) == 1          # odd address
+    assert uly([4, 4], out_=V(A_IN + 512, A_OUT)) == 1                  # output inside an input
+    assert uly([4, 4], to_sequence=1, out_=V(A_OUT, A_IN)) == 1         # and the other way
+    assert uly([4, 4], out_=V(A_OUT, A_OUT + 1024)) == 1                # outputs overlap
+    assert uly([1 << 41, 4]) == 1                                       # too many tokens
+    assert uly([0, 0], in_=V(0, 0), out_=V(0, 0)) == 0                  # nothing to move

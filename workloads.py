@@ -25,6 +25,14 @@ library.  Recipes (all seeded, all synthetic):
   top-k of the softmax is the top-k of the logits), ties to the lower expert;
   expert e lives on rank e // (experts / P); one row per (token, destination
   rank), deduplicated, rows grouped by destination in ascending token order.
+* Ulysses exchanges (Purlin, Table 2 and Figure 12(c): Qwen-Image with
+  Ulysses sequence parallelism on eight GPUs): the attention of a 1024x1024
+  image, 64x64 = 4096 image tokens (8x latent downsampling, 2x2 patches)
+  plus 256 text tokens (a stated choice: the pages give no prompt length),
+  split evenly over the ranks, 24 heads of 128 bf16 (the model's published
+  attention shape, not given on the pages), query / key / value fused;
+  values are uniform random bit patterns (the exchange copies bytes).  The
+  bandwidth case keeps that head shape at about 64 MiB per rank.
 """
 import numpy as np
 
@@ -144,3 +152,9 @@ def moe_counts(P=8, hidden=7168, seed=0, **kw):
         rows = moe_rows(i, seed=seed, P=P, **kw)
         counts.extend(int(len(r)) * hidden for r in rows)
     return counts
+
+
+# Ulysses exchange shapes (see the module docstring).
+ULYSSES_QWEN_IMAGE_1024 = {"P": 8, "seq": [(4096 + 256) // 8] * 8, "heads": 24, "head_dim": 128,
+                           "n_pack": 3}
+ULYSSES_64MIB = {"P": 8, "seq": [10922] * 8, "heads": 24, "head_dim": 128, "n_pack": 1}
