@@ -112,6 +112,9 @@ typedef struct {
                             off its destinations' 16-byte phase), 0 if the aligned-only one */
   int32_t unit;          /* purlin_ulysses: bytes each lane access moved (16, 8, 4 or 2);
                             0 for the other calls */
+  int32_t one;           /* zero-staging launch: 1 if the build for single-destination jobs
+                            ran (no broadcast in the launch), 0 otherwise */
+  int32_t reserved;
 } purlin_launch_info;
 
 /*

@@ -77,6 +77,13 @@ __device__ __forceinline__ u32x4 funnel(u32x4 lo, u32x4 hi, uint32_t sh) {
   return o;
 }
 
+// Wait until every vector memory access of this wave has completed.  Put at
+// the end of a guarded pass (whose stores may be skipped, leaving their loads
+// unconsumed), it lets the compiler's wait insertion know that no load is
+// still pending there, so the unguarded loops of the next tile issue their
+// loads without first draining the stores of this one.
+__device__ __forceinline__ void drain_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---- bf16 <-> fp32 -------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -250,11 +257,35 @@ __device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const u
 // uniform 64-bit base per buffer plus one 32-bit lane offset shared by all
 // buffers, so the loads use the scalar-base form and the sources cost no
 // per-lane address registers.
-template <class Op, int kU, bool kNTL, bool kNTS>
+template <class Op, int kU, bool kNTL, bool kNTS, bool kOne = false>
 __device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const uint64_t *db,
                                              int nd, uint32_t nunits) {
   constexpr uint32_t kPass = uint32_t(kThreads) * kU;
   uint32_t u0 = 0;
+  if constexpr (!Op::kSum && kOne) {
+    if (nd == 1) {
+      // One destination: every store of a full pass is unconditional, so
+      // each load is consumed in its own pass and a wave's next loads go
+      // out while its stores drain (measured +4-5% on AllToAll at 64-256
+      // MiB per rank).  Only in the single-destination build: elsewhere the
+      // extra path measured slower on AllToAllV and AllGather.
+      const uint32_t tid = threadIdx.x;
+      for (; u0 + kPass <= nunits; u0 += kPass) {
+        u32x4 x[kU];
+#pragma unroll
+        for (int k = 0; k < kU; ++k)
+          x[k] = ld16<kNTL>(sa[0] + uint64_t((u0 + uint32_t(k) * kThreads + tid) * 16u));
+#pragma unroll
+        for (int k = 0; k < kU; ++k)
+          st16<kNTS>(db[0] + uint64_t((u0 + uint32_t(k) * kThreads + tid) * 16u), x[k]);
+      }
+      if (u0 < nunits) {
+        pass_aligned<Op, kU, kNTL, kNTS, true>(sa, ns, db, nd, nunits, u0);
+        drain_vm();
+      }
+      return;
+    }
+  }
   for (; u0 + kPass <= nunits; u0 += kPass)
     pass_aligned<Op, kU, kNTL, kNTS, false>(sa, ns, db, nd, nunits, u0);
   if (u0 < nunits) pass_aligned<Op, kU, kNTL, kNTS, true>(sa, ns, db, nd, nunits, u0);
@@ -475,7 +506,7 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
 // nontemporal when every source sits on the destinations' 128-byte phase,
 // or when nt_any_phase asks for it (measured faster for misaligned
 // variable-length partitions too).  A tile spans less than 4 GiB.
-template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true>
+template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true, bool kOne = false>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
                                      bool nt_any_phase = false) {
   if (x1 <= x0) return;
@@ -516,8 +547,8 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
   for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(xh);
   const bool ntl = kNT && (phase == 0 || nt_any_phase);
   if (any == 0) {
-    if (ntl) body_aligned<Op, kU, true, kNT>(sa, s.n, db, d.n, nbody);
-    else body_aligned<Op, kU, false, kNT>(sa, s.n, db, d.n, nbody);
+    if (ntl) body_aligned<Op, kU, true, kNT, kOne>(sa, s.n, db, d.n, nbody);
+    else body_aligned<Op, kU, false, kNT, kOne>(sa, s.n, db, d.n, nbody);
     return;
   }
   if constexpr (!kRows) {

@@ -59,7 +59,7 @@ __device__ __forceinline__ void tile_bounds(uint64_t ref, int64_t n, int64_t C, 
 // reaches all ranks without a second pass).  Tiles are dealt to a resident
 // grid in grid-stride order; the tile list holds the share of rank 0, then
 // rank 1, and so on.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kRows>
+template <class Op, int kU, bool kNTL, bool kNTS, bool kRows, bool kOne>
 __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
   // A workgroup whose entry wait failed skips its tiles but still counts
   // itself out, so the next launch's exit check is not poisoned.
@@ -72,7 +72,10 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     atom::Srcs s;
     job_srcs(p, jb, s);
     atom::Dsts d;
-    if (jb.dst < 0) {
+    // kOne: built for launches whose every job has one destination rank, so
+    // every destination loop below folds to a single store
+    if (kOne && jb.dst < 0) continue;
+    if (!kOne && jb.dst < 0) {
       d.n = p.P;
 #pragma unroll
       for (int k = 0; k < kMaxRanks; ++k)
@@ -86,7 +89,7 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     int64_t x0, x1;
     tile_bounds(atom::line_ref(s, d), jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
                 p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
-    atom::tile<Op, kU, kNTL, true, kRows>(s, d, x0, x1, p.nt_any_phase != 0);
+    atom::tile<Op, kU, kNTL, true, kRows, kOne>(s, d, x0, x1, p.nt_any_phase != 0);
   }
   if (p.sync) snac::exit_notify(p);
 }
@@ -543,12 +546,30 @@ __global__ void __launch_bounds__(kThreads) strided_kernel(const StridedPlan sp)
     const int64_t n = jb.nbytes / kUnit;
     // units of the pair are < 2^31 (checked by the host)
     const uint32_t u1 = uint32_t(u0 + per_tile < n ? u0 + per_tile : n);
-    for (uint32_t u = uint32_t(u0) + threadIdx.x; u < u1; u += kThreads * kU) {
+    // full passes: every load and store unconditional (no pass waits for
+    // the previous pass's stores); then one guarded pass for the rest
+    uint32_t p0 = uint32_t(u0);
+    for (; p0 + kThreads * kU <= u1; p0 += kThreads * kU) {
       T v[kU];
       uint64_t dst[kU];
 #pragma unroll
       for (int k = 0; k < kU; ++k) {
-        const uint32_t uk = u + uint32_t(k) * kThreads;
+        const uint32_t uk = p0 + uint32_t(k) * kThreads + threadIdx.x;
+        const uint32_t r = uint32_t((uint64_t(uk) * sp.magic) >> sp.shift);
+        const uint32_t c = uk - r * per_row;
+        v[k] = __builtin_nontemporal_load(atom::gp<const T>(
+            sb + uint64_t(r) * uint64_t(sp.src_stride) + uint64_t(c) * kUnit));
+        dst[k] = db + uint64_t(r) * uint64_t(sp.dst_stride) + uint64_t(c) * kUnit;
+      }
+#pragma unroll
+      for (int k = 0; k < kU; ++k) __builtin_nontemporal_store(v[k], atom::gp<T>(dst[k]));
+    }
+    if (p0 < u1) {
+      T v[kU];
+      uint64_t dst[kU];
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const uint32_t uk = p0 + uint32_t(k) * kThreads + threadIdx.x;
         if (uk < u1) {
           const uint32_t r = uint32_t((uint64_t(uk) * sp.magic) >> sp.shift);
           const uint32_t c = uk - r * per_row;
@@ -559,7 +580,9 @@ __global__ void __launch_bounds__(kThreads) strided_kernel(const StridedPlan sp)
       }
 #pragma unroll
       for (int k = 0; k < kU; ++k)
-        if (u + uint32_t(k) * kThreads < u1) __builtin_nontemporal_store(v[k], atom::gp<T>(dst[k]));
+        if (p0 + uint32_t(k) * kThreads + threadIdx.x < u1)
+          __builtin_nontemporal_store(v[k], atom::gp<T>(dst[k]));
+      atom::drain_vm();
     }
   }
   if (p.sync) snac::exit_notify(p);
@@ -649,26 +672,40 @@ hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts,
 
 namespace {
 
+// The single-destination builds exist for the default (nontemporal) form,
+// without row bodies, and with row bodies for sums; one_build says which
+// launches get one.
 template <class Op, int kU, bool kNT>
-void *zs_fn(bool rows) {
-  return rows ? reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true>)
-              : reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, false>);
+void *zs_fn(bool rows, bool one) {
+  if constexpr (kNT) {
+    if (one && !rows) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, false, true>);
+    if constexpr (Op::kSum)
+      if (one && rows) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true, true>);
+  }
+  return rows ? reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true, false>)
+              : reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, false, false>);
 }
 template <class Op, int kU, bool kNT>
 void *st_fn() { return reinterpret_cast<void *>(&staged_kernel<Op, kU, kNT, kNT>); }
 
 // Unroll depth: 16-byte units each lane keeps in flight per source.
 template <class Op, int kU0, int kU1, int kU2>
-void *pick(bool staged, bool nt, int unroll_sel, bool rows) {
+void *pick(bool staged, bool nt, int unroll_sel, bool rows, bool one) {
   if (staged) return nt ? st_fn<Op, kU1, true>() : st_fn<Op, kU1, false>();
   switch (unroll_sel) {
-    case 0: return nt ? zs_fn<Op, kU0, true>(rows) : zs_fn<Op, kU0, false>(rows);
-    case 2: return nt ? zs_fn<Op, kU2, true>(rows) : zs_fn<Op, kU2, false>(rows);
-    default: return nt ? zs_fn<Op, kU1, true>(rows) : zs_fn<Op, kU1, false>(rows);
+    case 0: return nt ? zs_fn<Op, kU0, true>(rows, one) : zs_fn<Op, kU0, false>(rows, one);
+    case 2: return nt ? zs_fn<Op, kU2, true>(rows, one) : zs_fn<Op, kU2, false>(rows, one);
+    default: return nt ? zs_fn<Op, kU1, true>(rows, one) : zs_fn<Op, kU1, false>(rows, one);
   }
 }
 
 }  // namespace
+
+bool one_build(KernelKind kind, bool nt, bool rows, bool single_dst) {
+  // measured: the single-destination build of the copy with row bodies is
+  // 1.5% slower on AllToAllV at 64 MiB per rank than the general one
+  return single_dst && nt && (!rows || kind != KernelKind::kCopy);
+}
 
 int unroll_of(KernelKind kind, int unroll_sel) {
   static const int copy_u[3] = {4, 8, 16};
@@ -677,24 +714,24 @@ int unroll_of(KernelKind kind, int unroll_sel) {
   return kind == KernelKind::kCopy ? copy_u[sel] : sum_u[sel];
 }
 
-void *kernel_fn(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows) {
+void *kernel_fn(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows, bool one) {
   switch (kind) {
-    case KernelKind::kCopy: return pick<atom::CopyOp, 4, 8, 16>(staged, nt, unroll_sel, rows);
-    case KernelKind::kSumF32: return pick<atom::SumF32, 1, 2, 4>(staged, nt, unroll_sel, rows);
-    default: return pick<atom::SumBf16, 1, 2, 4>(staged, nt, unroll_sel, rows);
+    case KernelKind::kCopy: return pick<atom::CopyOp, 4, 8, 16>(staged, nt, unroll_sel, rows, one);
+    case KernelKind::kSumF32: return pick<atom::SumF32, 1, 2, 4>(staged, nt, unroll_sel, rows, one);
+    default: return pick<atom::SumBf16, 1, 2, 4>(staged, nt, unroll_sel, rows, one);
   }
 }
 
 hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, bool rows,
-                     int grid, hipStream_t stream) {
+                     bool one, int grid, hipStream_t stream) {
   void *args[] = {const_cast<LaunchPlan *>(&p)};
-  return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel, rows), dim3(grid), dim3(kThreads),
+  return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel, rows, one), dim3(grid), dim3(kThreads),
                          args, 0, stream);
 }
 
 hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStream_t stream) {
   void *args[] = {const_cast<StagedPlan *>(&p)};
-  return hipLaunchKernel(kernel_fn(kind, true, nt, 1, true), dim3(p.total_roles), dim3(kThreads),
+  return hipLaunchKernel(kernel_fn(kind, true, nt, 1, true, false), dim3(p.total_roles), dim3(kThreads),
                          args, 0, stream);
 }
 
@@ -747,9 +784,10 @@ hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int gri
 }
 
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
-                               int *blocks) {
+                               bool one, int *blocks) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      blocks, kernel_fn(kind, staged, nt, staged ? 1 : unroll_sel, staged || rows), kThreads, 0);
+      blocks, kernel_fn(kind, staged, nt, staged ? 1 : unroll_sel, staged || rows, !staged && one),
+      kThreads, 0);
 }
 
 }  // namespace purlin

@@ -11,17 +11,22 @@ enum class KernelKind { kCopy, kSumF32, kSumBf16 };
 // nt: nontemporal loads and stores.  unroll_sel picks one of three unroll
 // depths (units in flight per lane and source): copy 4 / 8 / 16, sum 1 / 2 / 4.
 // rows = false: the kernel built without the row bodies, for launches whose
-// every job has its sources on its destinations' 16-byte phase.
+// every job has its sources on its destinations' 16-byte phase.  one = true:
+// the kernel built for launches whose every job has a single destination
+// rank (no broadcast), whose destination loops fold to one store.
 hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, bool rows,
-                     int grid, hipStream_t stream);
+                     bool one, int grid, hipStream_t stream);
 hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStream_t stream);
 int unroll_of(KernelKind kind, int unroll_sel);
+// Whether a launch whose jobs all have one destination rank (single_dst) runs
+// the single-destination build (the `one` argument of launch_zs).
+bool one_build(KernelKind kind, bool nt, bool rows, bool single_dst);
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,
                               hipStream_t stream);
 hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts, int n_dst,
                           int64_t bytes, int grid, hipStream_t stream);
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
-                               int *blocks);
+                               bool one, int *blocks);
 
 // MoE dispatch one row at a time (rows: the build with the realigning row
 // bodies), the inverse-map pass, dispatch one token at a time (after the

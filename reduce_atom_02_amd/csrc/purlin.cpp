@@ -31,7 +31,7 @@ struct DeviceState {
   int64_t inv_bytes = 0;
   uint32_t epoch = 0;
   uint32_t exit_total[2][kExitSlots] = {};  // per parity and slot, all launches so far
-  int occ[3][2][2][3][2] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
+  int occ[3][2][2][3][2][2] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
 };
 
 std::vector<DeviceState> &devices() {
@@ -127,11 +127,13 @@ purlin_status device_state(DeviceState **out) {
   return PURLIN_OK;
 }
 
-int occupancy(DeviceState &s, KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows) {
-  int &o = s.occ[int(kind)][staged ? 1 : 0][nt ? 1 : 0][unroll_sel][rows ? 1 : 0];
+int occupancy(DeviceState &s, KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
+              bool one) {
+  int &o = s.occ[int(kind)][staged ? 1 : 0][nt ? 1 : 0][unroll_sel][rows ? 1 : 0][one ? 1 : 0];
   if (o == 0) {
     int b = 0;
-    if (max_resident_per_cu(kind, staged, nt, unroll_sel, rows, &b) != hipSuccess || b < 1) b = 1;
+    if (max_resident_per_cu(kind, staged, nt, unroll_sel, rows, one, &b) != hipSuccess || b < 1)
+      b = 1;
     o = b;
   }
   return o;
@@ -545,7 +547,12 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
       rows |= ((a - d0) & 15u) != 0;
     }
   }
-  const int capacity = ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows);
+  // every job writes one destination rank (no broadcast): the build whose
+  // destination loops fold to a single store
+  bool single_dst = true;
+  for (const Job &jb : jobs) single_dst &= jb.dst >= 0;
+  const bool one = !staged && one_build(kind, nt, rows, single_dst);
+  const int capacity = ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows, one);
 
   if (++ds->epoch == 0) ds->epoch = 1;  // epoch 0 would match freshly cleared flags
   const int64_t wd_ns = pol.watchdog_ns ? pol.watchdog_ns : kDefaultWatchdogNs;
@@ -579,7 +586,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     // phase too (variable-length partitions), measured at 16 MiB - 1 GiB.
     lp.nt_any_phase = env_i64("PURLIN_NT_ANY_PHASE", 1) ? 1 : 0;
     for (int k = 0; k < kExitSlots; ++k) lp.exit_expect[k] = ds->exit_total[(ds->epoch - 1u) & 1u][k];
-    err = launch_zs(lp, kind, nt, unroll_sel, rows, grid, stream);
+    err = launch_zs(lp, kind, nt, unroll_sel, rows, one, grid, stream);
     if (err == hipSuccess && lp.sync) {
       // workgroup b counts on slot b % kExitSlots
       for (int k = 0; k < kExitSlots; ++k)
@@ -589,6 +596,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     info.grid = grid;
     info.zero_staging = 1;
     info.rows = rows ? 1 : 0;
+    info.one = one ? 1 : 0;
     info.chunk_bytes = chunk;
     info.tiles = lp.total_tiles;
     info.sync = lp.sync;
@@ -781,7 +789,11 @@ purlin_status purlin_ulysses(void *const *in, void *const *out, int P, const int
   // the point-to-point copy policy: four workgroups per CU, 32 KiB tiles,
   // smaller tiles for small exchanges
   const int64_t cap = pol.wgs_per_rank ? int64_t(pol.wgs_per_rank) * kMaxRanks : int64_t(ds->cus) * 4;
-  const int64_t chunk = pol.chunk_bytes ? pol.chunk_bytes : fit_chunk(int64_t(32) << 10, total, cap);
+  // at least one full 16 KiB pass per tile: a tile shorter than a pass
+  // takes the guarded path only, measured slower at the Qwen-Image sizes
+  const int64_t chunk = pol.chunk_bytes
+                            ? pol.chunk_bytes
+                            : std::max<int64_t>(int64_t(16) << 10, fit_chunk(int64_t(32) << 10, total, cap));
   sp.base.chunk_bytes = chunk;
   int64_t t = 0;
   for (int q = 0; q < P * P; ++q) {

@@ -65,7 +65,8 @@ class LaunchInfo(ctypes.Structure):
                 ("zero_staging", ctypes.c_int32), ("depth", ctypes.c_int32),
                 ("chunk_bytes", ctypes.c_int64), ("tiles", ctypes.c_int64),
                 ("bytes_min", ctypes.c_int64), ("njobs", ctypes.c_int32),
-                ("sync", ctypes.c_int32), ("rows", ctypes.c_int32), ("unit", ctypes.c_int32)]
+                ("sync", ctypes.c_int32), ("rows", ctypes.c_int32), ("unit", ctypes.c_int32),
+                ("one", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 def _load():
