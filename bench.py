@@ -103,9 +103,9 @@ def kernel_of(name, rows, one):
     summaries: the operation, whether it was the build with the realigning
     row bodies (some source off its destinations' 16-byte phase) or the
     aligned-only one, and whether it was the build for single-destination
-    jobs ("one") or the one with broadcasts ("bcast")."""
+    jobs ("one") or the general one ("general")."""
     op = "SumBf16" if SPECS[name][2] == "sum" else "CopyOp"
-    return "zs_kernel<%s,%s,%s>" % (op, "rows" if rows else "aligned", "one" if one else "bcast")
+    return "zs_kernel<%s,%s,%s>" % (op, "rows" if rows else "aligned", "one" if one else "general")
 
 
 def cpu_baseline(T_sample, names):
