@@ -470,6 +470,87 @@ def ulysses_bench(purlin, steps, warmup, dev):
     return {"ulysses": res, "P": P, "steps": steps, "dtype": "bf16", "data": "synthetic"}
 
 
+def pipeline_sweep(purlin, T, names, path, dev):
+    """Staged SNAC pipeline against zero staging, in the shape of the pages'
+    pipelining figure (a 256 MiB one-sided transfer; pipeline depth 1-8;
+    eight or sixteen workgroups): for each name in `names` at T bytes per
+    rank -- a collective, or "onesided", rank 0's T bytes to rank 1 --
+    every depth D in 1..8, staging chunk C in 16 KiB .. 1 MiB and
+    workgroups per job (lanes: 8, 16 for the one-sided transfer, 1-8 for a
+    collective), the p50 over 10 cold calls (a 1 GiB fill between calls,
+    outside the events), and the zero-staging kernel at its default policy
+    and at several grid sizes.  B_min
+    fraction as everywhere: compulsory bytes / (p50 x 8 TB/s); staging's
+    extra passes show up as lost fraction."""
+    import torch
+    import workloads
+    stream = torch.cuda.current_stream()
+    shapes = collective_shapes(T)
+    n = T // ESZ
+    ins = [workloads.device_values(n, "normal", "bf16", 3, r, dev) for r in range(P)]
+    out_len = max(max(shapes[nm]["outs"]) if nm in shapes else n for nm in names)
+    outs = [torch.empty(out_len, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def p50(fn, reps=10):
+        fn()
+        ev = []
+        for _ in range(reps):
+            flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        purlin.check(stream)
+        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+        return ts[len(ts) // 2]
+
+    rows = []
+    with open(path, "w") as f:
+        for name in names:
+            if name == "onesided":
+                # the pages' two-GPU transfer: rank 0's T bytes to rank 1, as
+                # an AllToAllV over two ranks with one non-empty partition
+                s = {"counts": [0, n, 0, 0], "bmin": 2 * T}
+                in_n, out_n, op = SPECS["alltoall"]
+                xi, yo = ins[:2], outs[:2]
+                wgs = (0, 2, 4, 8, 16, 64)
+                lanes = (8, 16)
+            else:
+                s = shapes[name]
+                in_n, out_n, op = SPECS[name]
+                xi = [ins[r][:s["ins"][r]] for r in range(P)]
+                yo = [outs[r][:s["outs"][r]] for r in range(P)]
+                wgs = (0, 32, 64, 128, 256)
+                lanes = (1, 2, 4, 8)
+
+            def fn():
+                purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
+
+            points = [("zs", 0, 0, g) for g in wgs]
+            points += [("staged", d, c, l) for l in lanes for c in (16 << 10, 64 << 10,
+                                                                    256 << 10, 1 << 20)
+                       for d in range(1, 9)]
+            for variant, d, c, g in points:
+                purlin.set_policy(zero_staging=variant, depth=d, chunk_bytes=c, wgs_per_rank=g)
+                t = p50(fn)
+                info = purlin.last_launch()
+                row = {"collective": name, "variant": variant, "T_bytes": T, "depth": info["depth"],
+                       "chunk_bytes": info["chunk_bytes"], "wgs_per_rank_policy": g,
+                       "grid": info["grid"], "p50_us": round(t * 1e6, 1),
+                       "algbw_GBps": round(T / t / 1e9, 2),
+                       "hbm_frac": round(s["bmin"] / t / HBM_PEAK, 4)}
+                f.write(json.dumps(row) + "\n")
+                f.flush()
+                rows.append(row)
+            print("%s done" % name, flush=True)
+    purlin.set_policy(reset=True)
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -493,6 +574,10 @@ def main():
     ap.add_argument("--ulysses", action="store_true",
                     help="time the Ulysses sequence <-> head exchange (Qwen-Image 1024x1024 "
                          "attention shape and ~64 MiB per rank)")
+    ap.add_argument("--pipeline", default="",
+                    help="write the staged pipeline sweep (depth 1-8 x chunk x workgroups per "
+                         "job, against zero staging) of --only (default alltoall) at --size "
+                         "bytes per rank to this JSONL file")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time only the plain 128-bit streaming copy of --size bytes "
                          "(HBM counter calibration and copy ceiling)")
@@ -522,6 +607,10 @@ def main():
         return
     if args.ulysses:
         print(json.dumps(ulysses_bench(purlin, args.steps, args.warmup, dev)), flush=True)
+        return
+    if args.pipeline:
+        names = args.only.split(",") if args.only else ["alltoall"]
+        pipeline_sweep(purlin, T, names, args.pipeline, dev)
         return
     if args.sweep:
         sweep(purlin, T, args.variant, args.sweep, dev)
