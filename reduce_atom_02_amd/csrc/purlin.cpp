@@ -193,22 +193,26 @@ KernelKind kind_of(purlin_op op, purlin_dtype dtype) {
 }
 
 // Policy table ("codesign policies tune execution", Figure 1 caption), from
-// sweeps of grid, chunk and unroll at 64 MiB - 1 GiB per rank on MI355X:
-// reductions and broadcasts prefer about two workgroups per CU and 16 KiB
-// chunks, point-to-point copies four per CU and 32 KiB chunks.  Fewer, deeper
-// workgroups keep fewer DRAM pages open than a full grid.  The grid is a
-// whole-device figure (all P ranks share one GPU), so it does not shrink
-// for P < 8.
+// sweeps of grid, chunk and unroll at 1 MiB - 1 GiB per rank on MI355X, the
+// policies alternated call by call on the same buffers: reductions and
+// broadcasts prefer two workgroups per CU and 16 KiB chunks; point-to-point
+// copies two per CU and 32 KiB chunks once the launch moves 32 MiB or more
+// (AllToAll +2-3%, AllToAllV +4-9% at 64 MiB - 1 GiB per rank against four
+// per CU), four per CU below that, where the extra workgroups cut the
+// latency (1 MiB per rank: 14 us against 17 us).  Grids of 1.5 or 2.5
+// workgroups per CU measured 2-8% slower than either neighbour.  The grid
+// is a whole-device figure (all P ranks share one GPU), so it does not
+// shrink for P < 8.
 struct AutoPolicy {
   int grid;
   int64_t chunk;
   int unroll_sel;
 };
 
-AutoPolicy auto_policy(KernelKind kind, bool broadcast) {
+AutoPolicy auto_policy(KernelKind kind, bool broadcast, int64_t job_bytes) {
   if (kind != KernelKind::kCopy) return {512, int64_t(16) << 10, 0};
   if (broadcast) return {512, int64_t(16) << 10, 0};
-  return {1024, int64_t(32) << 10, 0};
+  return {job_bytes >= (int64_t(32) << 20) ? 512 : 1024, int64_t(32) << 10, 0};
 }
 
 // Small messages get smaller chunks, so that the default grid still sees
@@ -532,7 +536,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     job_bytes += jb.nbytes;
     broadcast |= jb.dst < 0;
   }
-  const AutoPolicy ap = auto_policy(kind, broadcast);
+  const AutoPolicy ap = auto_policy(kind, broadcast, job_bytes);
   int unroll_sel = unroll_env();
   if (unroll_sel < 0 || unroll_sel > 2) unroll_sel = ap.unroll_sel;
   // Whether some job has a source off its destinations' 16-byte phase and
