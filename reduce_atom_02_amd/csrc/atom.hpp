@@ -13,10 +13,10 @@
 //    lane shifts its block and its neighbour lane's block into place in
 //    registers (lane shuffle + v_alignbyte), never by unaligned or byte-wise
 //    memory accesses; such wavefront rows follow the sources' 128-byte
-//    lines when there is one destination, so no source line is loaded by
-//    two rows (a second nontemporal load of a line fetches it from HBM
-//    again, while split destination lines merge in L2), and the
-//    destinations' lines for broadcasts, whose reads are a small share;
+//    lines for a sum with one destination, so none of its eight sources'
+//    lines is loaded by two rows (a second nontemporal load of a line
+//    fetches it from HBM again, while split destination lines merge in
+//    L2), and the destinations' lines for copies, which read one stream;
 //  * the reduce is a per-lane fold over the sources in ascending rank, in
 //    fp32 (bf16 widened exactly), with one final round to nearest even for
 //    a bf16 output; there is no cross-lane tree, so the summation order is
@@ -421,14 +421,17 @@ __device__ __forceinline__ void pass_rows(const uint64_t *base, const uint32_t *
 // is loaded first and as an ordinary (cached) load, which measured fewer
 // HBM bytes and more bandwidth than a nontemporal one or a hand-over in LDS
 // behind a barrier.
-// Rows start on a 128-byte line of source 0 when there is one destination,
-// and on a destination line when there are several.  One side's lines are
-// then split between neighbouring rows.  Two nontemporal loads of one line
-// fetch it from HBM twice (measured: one line in eight more read traffic,
-// even when one wavefront takes both rows back to back), while two partial
-// stores to one line mostly merge in L2; so one destination gets
-// source-aligned rows (ReduceScatterV, AllToAllV), and a broadcast, whose
-// reads are one stream of several, gets destination-aligned ones.
+// Rows start on a 128-byte line of source 0 for a sum with one destination,
+// and on a destination line otherwise.  One side's lines are then split
+// between neighbouring rows.  Two nontemporal loads of one line fetch it
+// from HBM twice (measured: one line in eight more read traffic for
+// ReduceScatterV, even when one wavefront takes both rows back to back),
+// while two partial stores to one line mostly merge in L2; so a sum with
+// one destination, whose eight source streams are almost all its traffic,
+// gets source-aligned rows (ReduceScatterV).  A copy reads one stream, and
+// whole-line stores measured faster there: destination-aligned rows for
+// AllToAllV (+2-4% at 64 MiB - 1 GiB per rank, paired on the same
+// buffers) and for broadcasts (AllGatherV).
 // sa[] holds the sources at the first unit; block b of source i is at
 // sa[i] - sh[i] + 16 b, and a source with sh[i] > 0 needs block nunits too,
 // which holds its last unit's last bytes.  An unguarded pass reads blocks
@@ -463,10 +466,13 @@ __device__ __forceinline__ void body_rows(const uint64_t *sa, int ns, const uint
     pass_rows<Op, kU, kNTL, kNTS, true, kOne, false>(base, lim, ns, db, nd, nunits, sh, u0);
 }
 
-// Whether a job's rows are aligned to its sources: one destination, and
-// some source off the destination's 16-byte phase (the offset between a
-// source and the destination is the same at every byte of a job).
+// Whether a job's rows are aligned to its sources: a sum with one
+// destination, and some source off the destination's 16-byte phase (the
+// offset between a source and the destination is the same at every byte of
+// a job).
+template <class Op>
 __device__ __forceinline__ bool src_rows(const Srcs &s, const Dsts &d) {
+  if constexpr (!Op::kSum) return false;
   if (d.n != 1) return false;
   uint32_t any = 0;
 #pragma unroll
@@ -482,8 +488,9 @@ __device__ __forceinline__ bool src_rows(const Srcs &s, const Dsts &d) {
 // with no head pass.  With e = (dst - src0) mod 128 the boundary sits where
 // the destination is at ceil16(e) mod 128, and src0 there is < 16 bytes
 // past a line start.
+template <class Op>
 __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
-  if (!src_rows(s, d)) return d.b[0];
+  if (!src_rows<Op>(s, d)) return d.b[0];
   const uint32_t e = uint32_t(d.b[0] - s.a[0]) & 127u;
   return d.b[0] - uint64_t((e + 15u) & 112u);
 }
@@ -531,7 +538,7 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
     any |= sh[i];
     phase |= uint32_t((s.a[i] - b0) & 127u);
   }
-  const bool srows = src_rows(s, d);
+  const bool srows = src_rows<Op>(s, d);
   // units before the first row start
   const uint64_t line = srows ? sa[0] - sh[0] : b0 + uint64_t(x16);
   uint32_t nh = ((128u - uint32_t(line & 127u)) & 127u) >> 4;
