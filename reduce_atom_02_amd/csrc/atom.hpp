@@ -100,6 +100,11 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 // ---- element operations (head and tail of a tile, < 16 bytes) -------------
 
+// Elements per thread of the wide element pass that small misaligned tiles
+// take instead of a row body: enough for a 4 KiB tile plus the bytes before
+// its first line (4224 bytes of 2-byte elements).
+constexpr int kWideElems = 9;
+
 // Copy moves 2-byte elements: every offset of an fp32 or bf16 buffer is a
 // multiple of 2.
 struct CopyOp {
@@ -168,6 +173,79 @@ __device__ __forceinline__ void elements(const Srcs &s, const Dsts &d, int64_t y
 #pragma unroll
     for (int k = 0; k < kMaxRanks + 1; ++k)
       if (k < d.n) *gp<uint16_t>(d.b[k] + x) = r;
+  }
+}
+
+// Element-wise [y0, y1) of a job with kE elements per thread (element
+// t + e * kThreads for e < kE): every load of every element is issued before
+// any is used (indexes past the end are clamped to the last element, so the
+// loads need no branch), so the whole range is one memory round trip.  The
+// caller guarantees 0 < (y1 - y0) / kElem <= kE * kThreads.
+template <class Op, int kE>
+__device__ __forceinline__ void elements_wide(const Srcs &s, const Dsts &d, int64_t y0, int64_t y1) {
+  const int64_t n = (y1 - y0) / Op::kElem;
+  const int64_t tid = int64_t(threadIdx.x);
+  if constexpr (!Op::kSum) {
+    uint16_t v[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int64_t i = tid + e * kThreads;
+      v[e] = *gp<const uint16_t>(s.a[0] + y0 + (i < n ? i : n - 1) * 2);
+    }
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int64_t i = tid + e * kThreads;
+      if (i < n) {
+#pragma unroll
+        for (int k = 0; k < kMaxRanks + 1; ++k)
+          if (k < d.n) *gp<uint16_t>(d.b[k] + y0 + i * 2) = v[e];
+      }
+    }
+  } else if constexpr (Op::kElem == 4) {
+    float v[kE][kMaxRanks];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int64_t i = tid + e * kThreads;
+      const int64_t x = y0 + (i < n ? i : n - 1) * 4;
+#pragma unroll
+      for (int r = 0; r < kMaxRanks; ++r) v[e][r] = *gp<const float>(s.a[r] + x);
+    }
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int64_t i = tid + e * kThreads;
+      float acc = v[e][0];
+#pragma unroll
+      for (int r = 1; r < kMaxRanks; ++r)
+        if (r < s.n) acc = acc + v[e][r];
+      if (i < n) {
+#pragma unroll
+        for (int k = 0; k < kMaxRanks + 1; ++k)
+          if (k < d.n) *gp<float>(d.b[k] + y0 + i * 4) = acc;
+      }
+    }
+  } else {
+    uint16_t v[kE][kMaxRanks];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int64_t i = tid + e * kThreads;
+      const int64_t x = y0 + (i < n ? i : n - 1) * 2;
+#pragma unroll
+      for (int r = 0; r < kMaxRanks; ++r) v[e][r] = *gp<const uint16_t>(s.a[r] + x);
+    }
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int64_t i = tid + e * kThreads;
+      float acc = bf16_lo(v[e][0]);
+#pragma unroll
+      for (int r = 1; r < kMaxRanks; ++r)
+        if (r < s.n) acc = acc + bf16_lo(v[e][r]);
+      const uint16_t o = uint16_t(bf16_rne(acc));
+      if (i < n) {
+#pragma unroll
+        for (int k = 0; k < kMaxRanks + 1; ++k)
+          if (k < d.n) *gp<uint16_t>(d.b[k] + y0 + i * 2) = o;
+      }
+    }
   }
 }
 
@@ -451,18 +529,22 @@ __device__ __forceinline__ void body_rows(const uint64_t *sa, int ns, const uint
   uint32_t same = 1;
 #pragma unroll
   for (int i = 1; i < kS; ++i) same &= sh[i] == sh[0] ? 1u : 0u;
+  // Offset of this wavefront's first row in a pass.  The last pass (at most
+  // one is guarded) is skipped by a wavefront whose rows all lie past the
+  // body, which then issues no loads at all.
+  const uint32_t first = uint32_t(__builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6))) * 64u * kU;
   uint32_t u0 = 0;
   if (kFoldOk && Op::kSum && same) {
     constexpr bool kF = kFoldOk && Op::kSum;
     for (; u0 + kPass < nunits; u0 += kPass)
       pass_rows<Op, kU, kNTL, kNTS, false, kOne, kF>(base, lim, ns, db, nd, nunits, sh, u0);
-    for (; u0 < nunits; u0 += kPass)
+    if (u0 + first < nunits)
       pass_rows<Op, kU, kNTL, kNTS, true, kOne, kF>(base, lim, ns, db, nd, nunits, sh, u0);
     return;
   }
   for (; u0 + kPass < nunits; u0 += kPass)
     pass_rows<Op, kU, kNTL, kNTS, false, kOne, false>(base, lim, ns, db, nd, nunits, sh, u0);
-  for (; u0 < nunits; u0 += kPass)
+  if (u0 + first < nunits)
     pass_rows<Op, kU, kNTL, kNTS, true, kOne, false>(base, lim, ns, db, nd, nunits, sh, u0);
 }
 
@@ -504,8 +586,9 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
 //   [x0, xh)   the head, < 128 bytes: the bytes before the first 16-byte
 //              unit of the destination and the units before the first row
 //              start (a destination line, or with rows aligned to the
-//              sources a unit whose source-0 block starts a line); element operations
-//              on wavefront 0
+//              sources a unit whose source-0 block starts a line); element
+//              operations on wavefront 0, or on wavefront 2 when a row body
+//              leaves it idle
 //   [xh, xb)   the body: whole units, nontemporal stores when kNT
 //   [xb, x1)   < 16 bytes of tail: element operations on wavefront 3, in
 //              parallel with the head
@@ -515,11 +598,28 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
 // variable-length partitions too).  A tile spans less than 4 GiB.
 template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true, bool kOne = false>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
-                                     bool nt_any_phase = false) {
+                                     bool nt_any_phase = false, int64_t wide_max = 0) {
   if (x1 <= x0) return;
   if (x1 - x0 <= int64_t(kThreads) * Op::kElem) {
     elements<Op>(s, d, x0, x1);
     return;
+  }
+  if constexpr (kRows) {
+    // In the latency regime (the launch sets wide_max), a single-
+    // destination tile that would take a row body (some source off the
+    // destination's 16-byte phase) is one wide element pass instead: one
+    // round trip, and none of the row body's much larger code to fetch.
+    // A broadcast would store every element to each destination
+    // separately, and at larger sizes the 2-byte accesses cost more than
+    // the row body's 16-byte ones: those keep the row body.
+    uint32_t off = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxRanks; ++i) off |= uint32_t(s.a[i] - d.b[0]) & 15u;
+    if (off != 0 && d.n == 1 && x1 - x0 <= wide_max &&
+        x1 - x0 <= int64_t(kThreads) * Op::kElem * kWideElems) {
+      elements_wide<Op, kWideElems>(s, d, x0, x1);
+      return;
+    }
   }
   // from here on the tile holds more than 16 units, so the head (< 8 units
   // past x16) leaves a non-empty body
@@ -544,9 +644,16 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
   uint32_t nh = ((128u - uint32_t(line & 127u)) & 127u) >> 4;
   if (nh > nall) nh = nall;
   const int64_t xh = x16 + int64_t(nh) * 16;
-  elements<Op>(s, d, x0, xh);
-  elements<Op>(s, d, xb, x1, kThreads - 64);
   const uint32_t nbody = nall - nh;
+  // a sum holds eight sources per row, so two rows per wavefront (more
+  // measured slower); a copy holds one and takes the tile's unroll
+  constexpr int kUr = Op::kSum ? 2 : kU;
+  // The head goes to wavefront 2 when the row body leaves wavefronts 2 and
+  // 3 without rows (small tiles, the latency regime), so that no wavefront
+  // makes two round trips; otherwise to wavefront 0.
+  const int t_head = (kRows && any != 0 && nbody <= 2u * uint32_t(kUr) * 64u) ? 128 : 0;
+  elements<Op>(s, d, x0, xh, t_head);
+  elements<Op>(s, d, xb, x1, kThreads - 64);
   if (nbody == 0) return;
 #pragma unroll
   for (int i = 0; i < kMaxRanks; ++i) sa[i] += uint64_t(nh) * 16u;
@@ -566,9 +673,6 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
       elements<Op>(s, d, y, y + int64_t(kThreads) * Op::kElem < xb ? y + int64_t(kThreads) * Op::kElem : xb);
     return;
   }
-  // a sum holds eight sources per row, so two rows per wavefront (more
-  // measured slower); a copy holds one and takes the tile's unroll
-  constexpr int kUr = Op::kSum ? 2 : kU;
   if (d.n == 1) {
     if (ntl) body_rows<Op, kUr, true, kNT, true, kFoldOk>(sa, s.n, db, 1, nbody, sh);
     else body_rows<Op, kUr, false, kNT, true, kFoldOk>(sa, s.n, db, 1, nbody, sh);

@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     int64_t x0, x1;
     tile_bounds(atom::line_ref<Op>(s, d), jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
                 p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
-    atom::tile<Op, kU, kNTL, true, kRows, kOne>(s, d, x0, x1, p.nt_any_phase != 0);
+    atom::tile<Op, kU, kNTL, true, kRows, kOne>(s, d, x0, x1, p.nt_any_phase != 0, p.wide_max);
   }
   if (p.sync) snac::exit_notify(p);
 }

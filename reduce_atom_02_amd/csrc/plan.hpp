@@ -70,6 +70,8 @@ struct LaunchPlan {
   uint64_t watchdog_ticks;  // bound of every spin wait, in wall-clock ticks
   int32_t sync;             // 1: entry/exit notify flags on
   int32_t nt_any_phase;     // 1: nontemporal loads even for sources off the line phase
+  int32_t wide_max;         // tiles up to this many bytes that would take a row body
+                            // take one wide element pass instead (0: never)
   int32_t tile_begin[kMaxJobs + 1];
   uint32_t exit_expect[kExitSlots];  // exit counters after the previous launch (sync)
   Job jobs[kMaxJobs];

@@ -589,6 +589,11 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     // Nontemporal loads pay off for sources off the destination's line
     // phase too (variable-length partitions), measured at 16 MiB - 1 GiB.
     lp.nt_any_phase = env_i64("PURLIN_NT_ANY_PHASE", 1) ? 1 : 0;
+    // Latency regime (at most 512 KiB of jobs, 4 KiB tiles): small
+    // misaligned single-destination tiles take one wide element pass
+    // instead of a row body (ReduceScatterV at 8 - 16 KiB per rank: 8.9 us
+    // against 10.3 us); from 1 MiB per rank on, the row body is faster.
+    lp.wide_max = (chunk <= 4096 && job_bytes <= (int64_t(512) << 10)) ? int32_t(chunk + 128) : 0;
     for (int k = 0; k < kExitSlots; ++k) lp.exit_expect[k] = ds->exit_total[(ds->epoch - 1u) & 1u][k];
     err = launch_zs(lp, kind, nt, unroll_sel, rows, one, grid, stream);
     if (err == hipSuccess && lp.sync) {

@@ -242,6 +242,32 @@ def test_rows_at_pass_boundaries(purlin, name, dtype, unroll):
         os.environ.pop("PURLIN_UNROLL", None)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", ["reducescatter", "alltoall"])
+def test_wide_element_pass_at_its_size_limit(purlin, name, dtype):
+    """Small misaligned single-destination tiles in the latency regime (4 KiB
+    chunks, under 512 KiB of jobs) take one wide element pass instead of a
+    row body when they hold at most 4224 bytes: partitions on both sides of
+    that limit and of one-element-per-thread, at every source phase."""
+    P = 8
+    print("case wide-pass", name, dtype, flush=True)
+    esz = 4 if dtype == "f32" else 2
+    per = 16 // esz
+    rng = np.random.default_rng([31, esz, len(name)])
+    lim = 4224 // esz
+    elems = [lim - 1, lim, lim + 1, 4096 // esz, 4096 // esz + 1, 512 // esz, 512 // esz + 1,
+             lim - per]
+    nparts = P * P if name == "alltoall" else P
+    sizes = [elems[k % len(elems)] for k in range(nparts)]
+    counts = pins.counts_for(name, P, sizes)
+    ins, outs = pins.make_case(name, P, counts, dtype, rng, None, sentinel=0x6B6B)
+    purlin.set_policy(zero_staging="zs")
+    for shift in range(1, per):
+        oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, None, [shift] * P, [0] * P)
+        info = purlin.last_launch()
+        assert info["chunk_bytes"] == 4096, info
+
+
 def test_overlap_checks_survive_the_pointer_cache(purlin):
     """The per-call overlap check is skipped only for the same plan and buffers."""
     import torch
