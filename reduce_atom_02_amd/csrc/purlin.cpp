@@ -710,7 +710,10 @@ purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t
     const int g0 = moe_grid(*ds, MoeKernel::kInverse, false, (total + kThreads - 1) / kThreads,
                             int64_t(ds->cus) * 8);
     if (launch_moe(m, MoeKernel::kInverse, false, g0, stream) != hipSuccess) return PURLIN_ERR_HIP;
-    grid = moe_grid(*ds, MoeKernel::kDispatchTokens, false, m.inv_base[P], int64_t(ds->cus) * 4);
+    // one workgroup per CU: at 4096 x 7168 per rank, top-8 of 256, 569 us
+    // against 649 us with four per CU (two: 660 us, three: 650 us; 0.75 or
+    // 1.25 per CU: 713 / 728 us), the calls alternated on the same buffers
+    grid = moe_grid(*ds, MoeKernel::kDispatchTokens, false, m.inv_base[P], int64_t(ds->cus));
     if (launch_moe(m, MoeKernel::kDispatchTokens, false, grid, stream) != hipSuccess)
       return PURLIN_ERR_HIP;
   } else {
