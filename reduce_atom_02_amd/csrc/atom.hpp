@@ -581,7 +581,9 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
 // phase may fold before shifting (more registers; the staged kernel, whose
 // owner mixes its own input with staging slots, leaves it out).  kRows =
 // false builds the tile without the row bodies, for launches whose every
-// job is aligned: a smaller kernel.  x0 is 0 or on a 128-byte boundary of the
+// job is aligned: a smaller kernel.  kWide builds in the wide element pass
+// for small misaligned tiles (its registers would cost the staged kernel,
+// which never takes it, a workgroup per CU of occupancy).  x0 is 0 or on a 128-byte boundary of the
 // job's line_ref, x1 is the job's end or on such a boundary.  Layout:
 //   [x0, xh)   the head, < 128 bytes: the bytes before the first 16-byte
 //              unit of the destination and the units before the first row
@@ -596,7 +598,8 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
 // nontemporal when every source sits on the destinations' 128-byte phase,
 // or when nt_any_phase asks for it (measured faster for misaligned
 // variable-length partitions too).  A tile spans less than 4 GiB.
-template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true, bool kOne = false>
+template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true, bool kOne = false,
+          bool kWide = false>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
                                      bool nt_any_phase = false, int64_t wide_max = 0) {
   if (x1 <= x0) return;
@@ -604,7 +607,7 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
     elements<Op>(s, d, x0, x1);
     return;
   }
-  if constexpr (kRows) {
+  if constexpr (kRows && kWide) {
     // In the latency regime (the launch sets wide_max), a single-
     // destination tile that would take a row body (some source off the
     // destination's 16-byte phase) is one wide element pass instead: one

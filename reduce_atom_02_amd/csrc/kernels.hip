@@ -89,7 +89,8 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     int64_t x0, x1;
     tile_bounds(atom::line_ref<Op>(s, d), jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
                 p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
-    atom::tile<Op, kU, kNTL, true, kRows, kOne>(s, d, x0, x1, p.nt_any_phase != 0, p.wide_max);
+    atom::tile<Op, kU, kNTL, true, kRows, kOne, kRows>(s, d, x0, x1, p.nt_any_phase != 0,
+                                                  p.wide_max);
   }
   if (p.sync) snac::exit_notify(p);
 }
@@ -100,7 +101,12 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
 //   owner    combines chunk c: its own rank's input read directly, every other
 //            source taken from that source's staging ring after its ready
 //            notify, in ascending rank; writes the owner's output and, when
-//            other ranks need the result, stages it in the scatter ring.
+//            other ranks need the result, stages it in the scatter ring.  A
+//            reduction has a team of owners per lane, each combining its own
+//            slice of the chunk (whole 128-byte lines of the destination), so
+//            that the owners, who read every source, keep pace with the
+//            stagers, who copy one; each owner notifies on its own ready word
+//            and returns its own credit to every stager.
 //   stager   (one per source rank other than the owner) copies its rank's
 //            chunk into a ring slot, then notifies (Stage, Notify).
 //   scatter  (one per destination rank other than the owner) waits for the
@@ -119,7 +125,7 @@ __device__ __forceinline__ SlotRef slot_ref(const StagedPlan &sp, int ring, int 
   const int64_t g = int64_t(ring) * sp.depth + slot;
   SlotRef r;
   r.data = uint64_t(sp.ring) + uint64_t(g * sp.slot_stride);
-  r.ready = sp.slot_flags + g * 32;
+  r.ready = sp.slot_flags + g * 32;        // + t for owner t of a team
   r.credit = sp.slot_flags + g * 32 + 16;
   return r;
 }
@@ -153,7 +159,8 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
   const int L = sp.lanes;
   const int r = int(blockIdx.x) - sj.role_begin;
   const int lane = r % L;
-  const int kind = r / L;  // 0 owner, 1..n_stage stager, then scatter
+  const int team = sj.team;
+  const int kind = r / L;  // 0..team-1 owners, then n_stage stagers, then scatter
   const int owner = sj.owner;
   const int rings_per_lane = sj.n_stage + (sj.n_scatter > 0 ? 1 : 0);
   const int ring0 = sj.ring_begin + lane * rings_per_lane;
@@ -172,8 +179,8 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
 
   if (!run) {
     // nothing: fall through to the exit count
-  } else if (kind == 0) {
-    // ---------------- owner ----------------
+  } else if (kind < team) {
+    // ---------------- owner (member `kind` of the lane's team) ----------------
     for (int m = 0;; ++m) {
       const int c = lane + L * m;
       if (c >= ntl) break;
@@ -183,9 +190,13 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       tile_bounds(b0, jb.nbytes, p.chunk_bytes, c, ntl, x0, x1);
       // wait for every staged source chunk, and for the scatter slot's credits
       if (threadIdx.x == 0) {
+        // relaxed polls, then one acquire for all of them: a fence after the
+        // loads that saw the release stores synchronizes with each of them,
+        // and an acquire invalidates the XCD's L2, so one is enough
         for (int k = 0; k < sj.n_stage && ok; ++k)
-          if (!snac::wait_geq<uint64_t>(slot_ref(sp, ring0 + k, slot).ready, tag(e, round + 1), p))
+          if (!snac::wait_geq<uint64_t, false>(slot_ref(sp, ring0 + k, slot).ready, tag(e, round + 1), p))
             ok = 0;
+        if (sj.n_stage > 0 && ok) snac::acquire_fence();
         if (sj.n_scatter > 0 && ok) {
           const SlotRef o = slot_ref(sp, ring0 + sj.n_stage, slot);
           if (round == 0) {
@@ -228,18 +239,38 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       d.b[0] = to_own ? own : scat;
 #pragma unroll
       for (int k = 1; k < kMaxRanks + 1; ++k) d.b[k] = scat;
-      atom::tile<Op, kU, kNTL, false>(s, d, x0, x1);
+      // this owner's slice: split points on the destination's 128-byte lines
+      // (32-bit offsets, made wavefront-uniform again after the division,
+      // which the compiler expands on the vector unit: tile bounds held in
+      // vector registers would cost the kernel a workgroup per CU)
+      int64_t y0 = x0, y1 = x1;
+      if (team > 1) {
+        const uint32_t len = uint32_t(x1 - x0);  // a tile is at most 64 MiB + 128 bytes
+        const uint32_t part = ((len + uint32_t(team) - 1u) / uint32_t(team) + 127u) & ~127u;
+        auto split = [&](int t) -> uint32_t {
+          if (t == 0) return 0u;
+          uint32_t y = uint32_t(t) * part;
+          y += (128u - uint32_t((b0 + uint64_t(x0) + y) & 127u)) & 127u;
+          return y < len ? y : len;
+        };
+        const uint32_t a = uint32_t(__builtin_amdgcn_readfirstlane(int(split(kind))));
+        const uint32_t z = kind + 1 == team ? len
+                                            : uint32_t(__builtin_amdgcn_readfirstlane(int(split(kind + 1))));
+        y0 = x0 + int64_t(a);
+        y1 = x0 + int64_t(z);
+      }
+      atom::tile<Op, kU, kNTL, false>(s, d, y0, y1);
       snac::drain_workgroup();
       if (threadIdx.x == 0) {
         for (int k = 0; k < sj.n_stage; ++k)
           snac::add_rlx(slot_ref(sp, ring0 + k, slot).credit, uint64_t(1));
         if (sj.n_scatter > 0)
-          snac::store_rel(slot_ref(sp, ring0 + sj.n_stage, slot).ready, tag(e, round + 1));
+          snac::store_rel(slot_ref(sp, ring0 + sj.n_stage, slot).ready + kind, tag(e, round + 1));
       }
     }
-  } else if (kind <= sj.n_stage) {
+  } else if (kind < team + sj.n_stage) {
     // ---------------- stager ----------------
-    const int k = kind - 1;
+    const int k = kind - team;
     const int src = jb.src >= 0 ? jb.src : (k < owner ? k : k + 1);
     const int ring = ring0 + k;
     for (int m = 0;; ++m) {
@@ -249,9 +280,10 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       const uint64_t round = uint64_t(m / D);
       const SlotRef o = slot_ref(sp, ring, slot);
       if (threadIdx.x == 0) {
+        // every owner of the team returns one credit per round
         if (round == 0) {
           __hip_atomic_store(o.credit, tag(e, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else if (!snac::wait_geq<uint64_t, false>(o.credit, tag(e, round), p)) {
+        } else if (!snac::wait_geq<uint64_t, false>(o.credit, tag(e, round * uint64_t(team)), p)) {
           ok = 0;
         }
       }
@@ -277,7 +309,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
     }
   } else {
     // ---------------- scatter consumer ----------------
-    const int k = kind - 1 - sj.n_stage;
+    const int k = kind - team - sj.n_stage;
     const int dst = k < owner ? k : k + 1;
     const int ring = ring0 + sj.n_stage;
     for (int m = 0;; ++m) {
@@ -286,7 +318,13 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       const int slot = m % D;
       const uint64_t round = uint64_t(m / D);
       const SlotRef o = slot_ref(sp, ring, slot);
-      if (threadIdx.x == 0 && !snac::wait_geq<uint64_t>(o.ready, tag(e, round + 1), p)) ok = 0;
+      // the chunk is whole once every owner of the team has notified;
+      // relaxed polls, then one acquire (as in the owner)
+      if (threadIdx.x == 0) {
+        for (int t = 0; t < team && ok; ++t)
+          if (!snac::wait_geq<uint64_t, false>(o.ready + t, tag(e, round + 1), p)) ok = 0;
+        if (ok) snac::acquire_fence();
+      }
       __syncthreads();
       if (!ok) break;
       int64_t x0, x1;

@@ -53,7 +53,7 @@ struct StagedJob {
   int16_t owner;        // rank that combines the chunk (reducer / root)
   int16_t n_stage;      // sources other than the owner (0 or P-1)
   int16_t n_scatter;    // destinations other than the owner (0 or P-1)
-  int16_t pad;
+  int16_t team;         // owner workgroups per lane, each combining 1/team of a chunk
   int32_t role_begin;   // first workgroup of this job
   int32_t ring_begin;   // first ring of this job
 };
@@ -80,7 +80,8 @@ struct LaunchPlan {
 struct StagedPlan {
   LaunchPlan base;
   char *ring;               // staging rings
-  uint64_t *slot_flags;     // per slot: ready at [2*s*8], credit at [2*s*8 + 8] (u64)
+  uint64_t *slot_flags;     // per slot (256 bytes): ready words at [32*s + t] (one per owner
+                            // of the team), credit at [32*s + 16] (u64)
   int64_t slot_stride;      // bytes per slot (chunk_bytes + 256)
   int32_t depth;            // slots per ring
   int32_t lanes;            // parallel rings per (job, source)

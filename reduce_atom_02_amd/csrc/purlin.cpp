@@ -17,6 +17,10 @@ namespace {
 
 constexpr int64_t kDefaultWatchdogNs = 2000000000;  // 2 s
 constexpr int kMaxLanes = 32;
+// Owner workgroups per lane of a staged reduction (PURLIN_OWNER_TEAM
+// overrides, 1 - kMaxTeam): each combines a slice of every chunk.
+constexpr int kOwnerTeam = 8;
+constexpr int kMaxTeam = 8;
 
 struct DeviceState {
   bool ready = false;
@@ -628,6 +632,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     sp.slot_stride = chunk + 256;
     sp.withhold = pol.test_withhold;
     // roles and rings per lane
+    const int owner_team = int(std::min<int64_t>(kMaxTeam, std::max<int64_t>(1, env_i64("PURLIN_OWNER_TEAM", kOwnerTeam))));
     int roles_per_lane = 0, max_tiles = 1;
     std::vector<StagedJob> sj(jobs.size());
     for (size_t k = 0; k < jobs.size(); ++k) {
@@ -636,7 +641,11 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
       sj[k].owner = int16_t(owner);
       sj[k].n_stage = int16_t(jb.src < 0 ? P - 1 : (jb.src != owner ? 1 : 0));
       sj[k].n_scatter = int16_t(jb.dst < 0 ? P - 1 : 0);
-      roles_per_lane += 1 + sj[k].n_stage + sj[k].n_scatter;
+      // A reduction's owner reads every source of a chunk while a stager
+      // copies one: a team of owners, each combining a slice of the chunk,
+      // keeps pace with the stagers.
+      sj[k].team = int16_t(kind != KernelKind::kCopy && sj[k].n_stage > 0 ? owner_team : 1);
+      roles_per_lane += sj[k].team + sj[k].n_stage + sj[k].n_scatter;
       max_tiles = std::max(max_tiles, sp.base.tile_begin[k + 1] - sp.base.tile_begin[k]);
     }
     int lanes = pol.wgs_per_rank ? pol.wgs_per_rank : capacity / std::max(1, roles_per_lane);
@@ -648,7 +657,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     for (size_t k = 0; k < jobs.size(); ++k) {
       sj[k].role_begin = role;
       sj[k].ring_begin = ring;
-      role += (1 + sj[k].n_stage + sj[k].n_scatter) * lanes;
+      role += (sj[k].team + sj[k].n_stage + sj[k].n_scatter) * lanes;
       ring += (sj[k].n_stage + (sj[k].n_scatter > 0 ? 1 : 0)) * lanes;
       sp.sj[k] = sj[k];
     }

@@ -9,13 +9,15 @@
 //   stager s   copies its rank's chunk m into slot m % D of its ring, after
 //              the owner's credit for the slot's previous round, and
 //              notifies "ready" with (epoch, round + 1);
-//   owner      waits for every stager's ready, folds its own input and the
-//              staged chunks in ascending rank into its own output and into
-//              slot m % D of its scatter ring (after the scatter threads'
-//              credits for that slot's previous round), returns a credit to
-//              each stager's slot and notifies its scatter ring;
-//   scatter d  waits for the owner's notify, copies the slot into rank d's
-//              output and returns a credit.
+//   owner t    (one of a team of T per piece and lane) waits for every
+//              stager's ready, folds its own input and the staged chunks in
+//              ascending rank into its own output and into slot m % D of its
+//              scatter ring (after the scatter threads' credits for that
+//              slot's previous round), for its slice t of the chunk only;
+//              returns a credit to each stager's slot (a stager waits for T
+//              per round) and notifies its own ready word of the scatter slot;
+//   scatter d  waits for the notify of every owner of the team, copies the
+//              slot into rank d's output and returns a credit.
 // Flags are 64-bit words tagged with the launch epoch in the high half and
 // are never reset; a waiter waits for (flag - target) >= 0.  Every wait has
 // a wall-clock watchdog; on expiry it sets the status word and the launch's
@@ -38,10 +40,13 @@
 //
 // Usage: snac_model P D lanes chunks chunk_elems launches seed
 //                   [withhold_launch withhold_chunk] [watchdog_ms]
+// SNAC_TEAM=T sets the owners per piece and lane (default 1).
 // SNAC_MUTATION=n plants a protocol mistake, so a test can check that the
 // model catches it: 1 a stager reuses a slot without its credit wait, 2 the
 // owner notifies its scatter ring before writing the slot, 3 a scatter
-// consumer returns its credit before copying the slot.
+// consumer returns its credit before copying the slot, 4 a scatter consumer
+// waits for the first owner of the team only, 5 a stager waits for one
+// owner's credit per round instead of the team's.
 // Exit status 0: every launch correct, or with withholding: the withheld
 // launch ended in TIMEOUT, every thread returned, and the launches after it
 // are correct again.
@@ -68,6 +73,7 @@ uint64_t tag(uint32_t epoch, uint64_t v) { return (uint64_t(epoch) << 32) | v; }
 
 struct Model {
   int P, D, L, chunks, C;
+  int T = 1;  // owners per piece and lane
   long watchdog_ms;
   // buffers: in[r], out[r] of P * pieceN elements, piece k = [k * pieceN, (k+1) * pieceN)
   int pieceN;
@@ -76,6 +82,7 @@ struct Model {
   int rings_per_lane;
   std::vector<int64_t> ring;  // [piece][lane][ring][slot][C]
   std::vector<Flag> ready, credit;
+  std::vector<Flag> team_ready;  // scatter slots: one ready word per owner of the team
   Flag entry[64];
   Flag exits[2][kExitSlots];
   uint64_t exit_total[2][kExitSlots] = {};
@@ -134,8 +141,9 @@ struct Model {
       const int slot = m % D;
       const uint64_t round = uint64_t(m / D);
       const int g = slot_index(piece, lane, k, slot);
+      const uint64_t per_round = mutation == 5 ? 1 : uint64_t(T);
       if (round == 0) credit[g].v.store(tag(e, 0), std::memory_order_relaxed);
-      else if (mutation != 1 && !wait_geq(credit[g].v, tag(e, round), e, rng)) return;
+      else if (mutation != 1 && !wait_geq(credit[g].v, tag(e, round * per_round), e, rng)) return;
       int x0, x1;
       bounds(lane, m, x0, x1);
       int64_t *d = slot_data(piece, lane, k, slot);
@@ -147,7 +155,7 @@ struct Model {
     }
   }
 
-  void owner(int piece, int lane, uint32_t e, unsigned seed) {
+  void owner(int piece, int lane, int t, uint32_t e, unsigned seed) {
     std::mt19937 rng(seed);
     const int scat = P - 1;  // scatter ring index
     for (int m = 0; m < lane_chunks(lane); ++m) {
@@ -158,11 +166,17 @@ struct Model {
       const int gs = slot_index(piece, lane, scat, slot);
       if (round == 0) credit[gs].v.store(tag(e, 0), std::memory_order_relaxed);
       else if (!wait_geq(credit[gs].v, tag(e, round * uint64_t(P - 1)), e, rng)) return;
-      int x0, x1;
-      bounds(lane, m, x0, x1);
+      int c0, c1;
+      bounds(lane, m, c0, c1);
+      const int x0 = c0;
       int64_t *sd = slot_data(piece, lane, scat, slot);
-      if (mutation == 2) ready[gs].v.store(tag(e, round + 1), std::memory_order_release);
-      for (int x = x0; x < x1; ++x) {
+      // this owner's slice of the chunk
+      const int part = (c1 - c0 + T - 1) / T;
+      const int lo = c0 + (t * part < c1 - c0 ? t * part : c1 - c0);
+      const int hi = c0 + ((t + 1) * part < c1 - c0 ? (t + 1) * part : c1 - c0);
+      std::atomic<uint64_t> &mine = team_ready[size_t(gs) * T + t].v;
+      if (mutation == 2) mine.store(tag(e, round + 1), std::memory_order_release);
+      for (int x = lo; x < hi; ++x) {
         int64_t acc = 0;
         for (int r = 0; r < P; ++r) {  // ascending rank: own input or staged chunk
           if (r == piece) acc += in[r][piece * pieceN + x];
@@ -174,7 +188,7 @@ struct Model {
       jitter(rng);
       for (int k = 0; k < P - 1; ++k)
         credit[slot_index(piece, lane, k, slot)].v.fetch_add(1, std::memory_order_release);
-      if (mutation != 2) ready[gs].v.store(tag(e, round + 1), std::memory_order_release);
+      if (mutation != 2) mine.store(tag(e, round + 1), std::memory_order_release);
     }
   }
 
@@ -186,7 +200,10 @@ struct Model {
       const int slot = m % D;
       const uint64_t round = uint64_t(m / D);
       const int gs = slot_index(piece, lane, scat, slot);
-      if (!wait_geq(ready[gs].v, tag(e, round + 1), e, rng)) return;
+      bool ok = true;
+      for (int t = 0; t < (mutation == 4 ? 1 : T) && ok; ++t)
+        ok = wait_geq(team_ready[size_t(gs) * T + t].v, tag(e, round + 1), e, rng);
+      if (!ok) return;
       int x0, x1;
       bounds(lane, m, x0, x1);
       const int64_t *sd = slot_data(piece, lane, scat, slot);
@@ -236,7 +253,9 @@ int main(int argc, char **argv) {
   }
   M.watchdog_ms = argc >= 11 ? std::atol(argv[10]) : 20000;
   if (const char *mu = std::getenv("SNAC_MUTATION")) M.mutation = std::atoi(mu);
-  if (M.P < 2 || M.P > 16 || M.D < 1 || M.L < 1 || M.chunks < 1 || M.C < 1 || launches < 1)
+  if (const char *tm = std::getenv("SNAC_TEAM")) M.T = std::atoi(tm);
+  if (M.P < 2 || M.P > 16 || M.D < 1 || M.L < 1 || M.chunks < 1 || M.C < 1 || launches < 1 ||
+      M.T < 1 || M.T > 16)
     return 2;
   M.pieceN = M.chunks * M.C - M.C / 3;  // a ragged last chunk
   const int N = M.P * M.pieceN;
@@ -247,6 +266,7 @@ int main(int argc, char **argv) {
   M.ring.assign(nslots * M.C, 0);
   M.ready = std::vector<Flag>(nslots);
   M.credit = std::vector<Flag>(nslots);
+  M.team_ready = std::vector<Flag>(nslots * size_t(M.T));
 
   std::mt19937 rng(seed);
   int bad = 0;
@@ -256,21 +276,22 @@ int main(int argc, char **argv) {
     for (int r = 0; r < M.P; ++r)
       for (int x = 0; x < N; ++x) M.in[r][x] = int64_t(rng() % 1000003) - 500000 + launch;
     for (auto &o : M.out) std::fill(o.begin(), o.end(), int64_t(-1));
-    // one workgroup per role, as in the kernel: per piece and lane an owner,
+    // one workgroup per role, as in the kernel: per piece and lane T owners,
     // P-1 stagers and P-1 scatter consumers
     std::vector<std::thread> th;
-    int G = M.P * M.L * (2 * M.P - 1);
+    const int roles = M.T + 2 * (M.P - 1);
+    int G = M.P * M.L * roles;
     int b = 0;
     for (int piece = 0; piece < M.P; ++piece)
       for (int lane = 0; lane < M.L; ++lane)
-        for (int role = 0; role < 2 * M.P - 1; ++role, ++b) {
+        for (int role = 0; role < roles; ++role, ++b) {
           const unsigned s = unsigned(rng());
           th.emplace_back([&M, piece, lane, role, b, G, epoch, launch, s] {
             std::mt19937 r(s);
             if (M.entry_wait(b, G, epoch, r)) {
-              if (role == 0) M.owner(piece, lane, epoch, s);
-              else if (role < M.P) M.stager(piece, lane, role - 1, epoch, launch, s);
-              else M.scatter(piece, lane, role - M.P, epoch, s);
+              if (role < M.T) M.owner(piece, lane, role, epoch, s);
+              else if (role < M.T + M.P - 1) M.stager(piece, lane, role - M.T, epoch, launch, s);
+              else M.scatter(piece, lane, role - M.T - (M.P - 1), epoch, s);
             }
             M.exit_notify(b, epoch);
           });
@@ -304,7 +325,7 @@ int main(int argc, char **argv) {
         }
       }
   }
-  std::printf("%s P=%d D=%d lanes=%d chunks=%d C=%d launches=%d\n", bad ? "FAIL" : "ok", M.P, M.D,
-              M.L, M.chunks, M.C, launches);
+  std::printf("%s P=%d D=%d lanes=%d team=%d chunks=%d C=%d launches=%d\n", bad ? "FAIL" : "ok",
+              M.P, M.D, M.L, M.T, M.chunks, M.C, launches);
   return bad ? 1 : 0;
 }

@@ -1,8 +1,8 @@
 """The staged SNAC protocol and the entry / exit handshake as a CPU model
 under ThreadSanitizer (tests/snac_model/snac_model.cpp).
 
-Threads play the kernel's workgroups (owner, stagers, scatter consumers,
-announcers) over std::atomic flags with random delays; several launches
+Threads play the kernel's workgroups (owners, alone or as a team that splits
+each chunk, stagers, scatter consumers, announcers) over std::atomic flags with random delays; several launches
 reuse the rings and flags with new epochs.  Checked: every output equals the
 rank-order sum, no data race on ring slots or outputs, a withheld notify ends
 in TIMEOUT with every thread returned (and the next launch is right again),
@@ -54,8 +54,35 @@ def test_withheld_notify_times_out_and_the_next_launch_recovers(model):
     assert r.returncode == 0, r.stdout + r.stderr
 
 
+@pytest.mark.parametrize("P,D,lanes,chunks,C,team", [
+    (4, 2, 2, 9, 64, 3),    # a team of three owners per lane, uneven slices
+    (8, 3, 1, 10, 24, 8),   # eight owners, as the kernel's default for reductions
+    (3, 1, 1, 6, 5, 4),     # depth 1, slices of one or two elements, one empty
+])
+def test_owner_teams_are_race_free_and_correct(model, P, D, lanes, chunks, C, team):
+    env = dict(ENV, SNAC_TEAM=str(team))
+    r = run(model, P, D, lanes, chunks, C, 4, 13 * P + team, env=env)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.startswith("ok")
+
+
+def test_withheld_notify_with_an_owner_team(model):
+    env = dict(ENV, SNAC_TEAM="4")
+    r = run(model, 4, 2, 1, 8, 32, 4, 5, 1, 3, 300, env=env, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
 @pytest.mark.parametrize("mutation", [1, 2, 3])
 def test_planted_protocol_mistakes_are_caught(model, mutation):
     env = dict(ENV, SNAC_MUTATION=str(mutation))
+    r = run(model, 4, 2, 1, 12, 32, 3, 7, env=env)
+    assert r.returncode != 0, "mutation %d went unnoticed" % mutation
+
+
+@pytest.mark.parametrize("mutation", [1, 2, 3, 4, 5])
+def test_planted_team_mistakes_are_caught(model, mutation):
+    # 4: a scatter consumer waits for the first owner only; 5: a stager
+    # reuses a slot after one owner's credit instead of the team's
+    env = dict(ENV, SNAC_MUTATION=str(mutation), SNAC_TEAM="3")
     r = run(model, 4, 2, 1, 12, 32, 3, 7, env=env)
     assert r.returncode != 0, "mutation %d went unnoticed" % mutation
