@@ -321,6 +321,88 @@ def sweep(purlin, T_max, variant, path, dev):
     return rows
 
 
+def config_bench(purlin, path, dev):
+    """The AllReduce workloads the latency sweep does not cover, timed like
+    its latency regime (20 warm-up calls, 1000 timed calls; device p50
+    queued behind a spin kernel, p50 from an idle GPU, host call to
+    completion): the fp32 AllReduce of 262144 elements (1 MiB) per rank,
+    values 2U - 1, and the tensor-parallel AllReduce of bf16 activations
+    [t x 7168] for t in 1, 4, 16, 64, 256 (N(0,1)); both also cold (a 1 GiB
+    fill between calls, 100 calls).  P = 8, zero staging."""
+    import torch
+    import workloads
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps, cold=False, queued=False):
+        ev = []
+        for k in range(reps):
+            if queued and k % 200 == 0:
+                torch.cuda.synchronize()
+                torch.cuda._sleep(20_000_000)
+            if cold:
+                flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+        return ts[len(ts) // 10], ts[len(ts) // 2], ts[(9 * len(ts)) // 10]
+
+    def host_p50(fn, reps):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            stream.synchronize()
+            ts.append(time.perf_counter() - t0)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    cases = [("allreduce_f32_1MiB", "f32", 262144, "uniform", 0)]
+    cases += [("tp8_allreduce_bf16_%dx7168" % t, "bf16", t * 7168, "normal", 5) for t in
+              (1, 4, 16, 64, 256)]
+    rows = []
+    purlin.set_policy(reset=True)
+    with open(path, "w") as f:
+        for label, dtype, n, dist, cfg in cases:
+            esz = 4 if dtype == "f32" else 2
+            tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+            ins = [workloads.device_values(n, dist, dtype, cfg, r, dev) for r in range(P)]
+            outs = [torch.empty(n, dtype=tdt, device=dev) for _ in range(P)]
+
+            def fn():
+                purlin.collective(ins, outs, "whole", "whole", "sum", [n], stream=stream)
+
+            for _ in range(20):
+                fn()
+            purlin.check(stream)
+            p10, p50, p90 = timed(fn, 1000, queued=True)
+            submit = timed(fn, 1000)[1]
+            host = host_p50(fn, 1000)
+            cold = timed(fn, 100, cold=True)[1]
+            purlin.check(stream)
+            info = purlin.last_launch()
+            bmin = 2 * P * n * esz
+            row = {"case": label, "dtype": dtype, "P": P, "bytes_per_rank": n * esz,
+                   "p10_us": round(p10 * 1e6, 2), "p50_us": round(p50 * 1e6, 2),
+                   "p90_us": round(p90 * 1e6, 2), "submit_p50_us": round(submit * 1e6, 2),
+                   "host_p50_us": round(host * 1e6, 2), "cold_p50_us": round(cold * 1e6, 2),
+                   "algbw_GBps": round(n * esz / p50 / 1e9, 2),
+                   "hbm_frac_warm": round(bmin / p50 / HBM_PEAK, 4),
+                   "hbm_frac_cold": round(bmin / cold / HBM_PEAK, 4), "bmin": bmin,
+                   "grid": info["grid"], "chunk_bytes": info["chunk_bytes"]}
+            f.write(json.dumps(row) + "\n")
+            f.flush()
+            rows.append(row)
+            print("%s done" % label, flush=True)
+            del ins, outs
+    return rows
+
+
 def moe_bench(purlin, steps, warmup, dev):
     """MoE dispatch and combine at the configuration of the pages' expert-
     parallel call sites: 4096 tokens x 7168 bf16 per rank, top-8 of 256
@@ -578,6 +660,9 @@ def main():
                     help="write the staged pipeline sweep (depth 1-8 x chunk x workgroups per "
                          "job, against zero staging) of --only (default alltoall) at --size "
                          "bytes per rank to this JSONL file")
+    ap.add_argument("--configs", default="",
+                    help="write p50 latency of the fp32 AllReduce at 1 MiB per rank and the TP8 "
+                         "AllReduce of [t x 7168] bf16 activations to this JSONL file")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time only the plain 128-bit streaming copy of --size bytes "
                          "(HBM counter calibration and copy ceiling)")
@@ -607,6 +692,9 @@ def main():
         return
     if args.ulysses:
         print(json.dumps(ulysses_bench(purlin, args.steps, args.warmup, dev)), flush=True)
+        return
+    if args.configs:
+        config_bench(purlin, args.configs, dev)
         return
     if args.pipeline:
         names = args.only.split(",") if args.only else ["alltoall"]

@@ -301,7 +301,12 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
 #pragma unroll
       for (int q = 0; q < kMaxRanks + 1; ++q) d.b[q] = slot_base(o.data, b0, x0);
       atom::tile<atom::CopyOp, kU, kNTL>(s, d, x0, x1);
-      __syncthreads();
+      // Every wavefront's stores must be acknowledged before thread 0's
+      // release publishes the slot: a workgroup barrier alone does not wait
+      // for other wavefronts' global stores (their head and tail element
+      // passes run on wavefronts 2 and 3), so the release could overtake
+      // them and the owner read a stale line.
+      snac::drain_workgroup();
       if (threadIdx.x == 0) {
         const bool withhold = sp.withhold > 0 && ring == 0 && m + 1 == sp.withhold;
         if (!withhold) snac::store_rel(o.ready, tag(e, round + 1));

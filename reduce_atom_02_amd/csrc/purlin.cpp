@@ -198,15 +198,24 @@ KernelKind kind_of(purlin_op op, purlin_dtype dtype) {
 
 // Policy table ("codesign policies tune execution", Figure 1 caption), from
 // sweeps of grid, chunk and unroll at 1 MiB - 1 GiB per rank on MI355X, the
-// policies alternated call by call on the same buffers: reductions and
-// broadcasts prefer two workgroups per CU and 16 KiB chunks; point-to-point
-// copies two per CU and 32 KiB chunks once the launch moves 32 MiB or more
-// (AllToAll +2-3%, AllToAllV +4-9% at 64 MiB - 1 GiB per rank against four
-// per CU), four per CU below that, where the extra workgroups cut the
-// latency (1 MiB per rank: 14 us against 17 us).  Grids of 1.5 or 2.5
-// workgroups per CU measured 2-8% slower than either neighbour.  The grid
-// is a whole-device figure (all P ranks share one GPU), so it does not
-// shrink for P < 8.
+// policies alternated call by call on the same buffers.  Large messages
+// want two workgroups per CU (fewer concurrent DRAM streams), smaller ones
+// four (each workgroup has few tiles, so more of them overlap more round
+// trips); the crossover, in bytes of jobs per launch (the per-rank size T
+// for the reductions and broadcasts, P x T for AllToAll), differs by kind:
+//   reductions  16 KiB chunks; four per CU below 16 MiB (AllReduce 5-8%,
+//               ReduceScatter 5-6% faster at 4-8 MiB per rank), two from
+//               there (at 16-32 MiB the two grids traded places between
+//               sweeps; ReduceScatter 2.5% faster on two at 64 MiB);
+//   broadcasts  16 KiB chunks; four per CU below 16 MiB (AllGather 12-16%,
+//               AllGatherV 8-15% faster at 4-8 MiB), two from there
+//               (AllGatherV 4% faster at 16 MiB, AllGather 1-4% at 32-64);
+//   copies      32 KiB chunks; four per CU below 32 MiB (1 MiB per rank:
+//               14 us against 17 us), two from there (AllToAll +2-3%,
+//               AllToAllV +4-9% at 64 MiB - 1 GiB per rank).
+// Grids of 1.5 or 2.5 workgroups per CU measured 2-8% slower than either
+// neighbour.  The grid is a whole-device figure (all P ranks share one
+// GPU), so it does not shrink for P < 8.
 struct AutoPolicy {
   int grid;
   int64_t chunk;
@@ -214,9 +223,10 @@ struct AutoPolicy {
 };
 
 AutoPolicy auto_policy(KernelKind kind, bool broadcast, int64_t job_bytes) {
-  if (kind != KernelKind::kCopy) return {512, int64_t(16) << 10, 0};
-  if (broadcast) return {512, int64_t(16) << 10, 0};
-  return {job_bytes >= (int64_t(32) << 20) ? 512 : 1024, int64_t(32) << 10, 0};
+  const int64_t MiB = int64_t(1) << 20;
+  if (kind != KernelKind::kCopy) return {job_bytes >= 16 * MiB ? 512 : 1024, 16 << 10, 0};
+  if (broadcast) return {job_bytes >= 16 * MiB ? 512 : 1024, 16 << 10, 0};
+  return {job_bytes >= 32 * MiB ? 512 : 1024, 32 << 10, 0};
 }
 
 // Small messages get smaller chunks, so that the default grid still sees

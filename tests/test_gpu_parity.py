@@ -268,6 +268,26 @@ def test_wide_element_pass_at_its_size_limit(purlin, name, dtype):
         assert info["chunk_bytes"] == 4096, info
 
 
+@pytest.mark.parametrize("name", ["alltoall", "allgather", "reducescatter"])
+def test_staged_small_misaligned_chunks_repeated(purlin, name):
+    """Staged chunks of 4 KiB at shifted offsets, several launches in a row:
+    a stager's head and tail element passes run on wavefronts 2 and 3, and
+    its ready notify must not overtake their stores (every wavefront drains
+    before the release), or the owner reads a stale line."""
+    P = 8
+    print("case staged-small-repeated", name, flush=True)
+    rng = np.random.default_rng([37, len(name)])
+    nparts = P * P if name == "alltoall" else P
+    hi = 30000 if name == "alltoall" else 90000
+    sizes = [int(v) | 1 for v in rng.integers(hi // 3, hi, nparts)]
+    counts = pins.counts_for(name, P, sizes)
+    ins, outs = pins.make_case(name, P, counts, "bf16", rng, None, sentinel=0x2D2D)
+    purlin.set_policy(chunk_bytes=4096, zero_staging="staged", depth=2)
+    for rep in range(4):
+        shifts = [(rep + 3 * r) % 8 for r in range(P)]
+        oracle_and_gpu(purlin, name, P, counts, "bf16", ins, outs, None, shifts, [rep % 8] * P)
+
+
 def test_overlap_checks_survive_the_pointer_cache(purlin):
     """The per-call overlap check is skipped only for the same plan and buffers."""
     import torch
