@@ -73,11 +73,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zs_kernels_seven_collectives_1GiB
 
 
 def kernel_source_hash():
-    """Hash of the HIP sources: counters taken from other sources do not apply."""
+    """Hash of the HIP and host sources with comments and whitespace removed:
+    counters taken from other code do not apply (a comment edit changes no
+    kernel)."""
+    import re
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "reduce_atom_02_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + fh.read())
+        with open(f, "r", encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(os.path.basename(f).encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 
