@@ -59,7 +59,10 @@ __device__ __forceinline__ void tile_bounds(uint64_t ref, int64_t n, int64_t C, 
 // reaches all ranks without a second pass).  Tiles are dealt to a resident
 // grid in grid-stride order; the tile list holds the share of rank 0, then
 // rank 1, and so on.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kRows, bool kOne>
+// kWide: the build for the latency regime, whose small misaligned tiles may
+// take the wide element pass; the others leave that pass out, whose
+// registers would cost a row-body kernel a workgroup per CU.
+template <class Op, int kU, bool kNTL, bool kNTS, bool kRows, bool kOne, bool kWide = false>
 __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
   // A workgroup whose entry wait failed skips its tiles but still counts
   // itself out, so the next launch's exit check is not poisoned.
@@ -89,7 +92,7 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     int64_t x0, x1;
     tile_bounds(atom::line_ref<Op>(s, d), jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
                 p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
-    atom::tile<Op, kU, kNTL, true, kRows, kOne, kRows>(s, d, x0, x1, p.nt_any_phase != 0,
+    atom::tile<Op, kU, kNTL, true, kRows, kOne, kWide>(s, d, x0, x1, p.nt_any_phase != 0,
                                                   p.wide_max);
   }
   if (p.sync) snac::exit_notify(p);
@@ -717,13 +720,20 @@ namespace {
 
 // The single-destination builds exist for the default (nontemporal) form,
 // without row bodies, and with row bodies for sums; one_build says which
-// launches get one.
-template <class Op, int kU, bool kNT>
-void *zs_fn(bool rows, bool one) {
+// launches get one.  The wide builds (latency regime) exist for the row
+// bodies of the default form and unroll.
+template <class Op, int kU, bool kNT, bool kWideOk = false>
+void *zs_fn(bool rows, bool one, bool wide) {
   if constexpr (kNT) {
     if (one && !rows) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, false, true>);
     if constexpr (Op::kSum)
-      if (one && rows) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true, true>);
+      if (one && rows) {
+        if constexpr (kWideOk)
+          if (wide) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true, true, true>);
+        return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true, true>);
+      }
+    if constexpr (kWideOk)
+      if (rows && wide) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true, false, true>);
   }
   return rows ? reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true, false>)
               : reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, false, false>);
@@ -733,12 +743,12 @@ void *st_fn() { return reinterpret_cast<void *>(&staged_kernel<Op, kU, kNT, kNT>
 
 // Unroll depth: 16-byte units each lane keeps in flight per source.
 template <class Op, int kU0, int kU1, int kU2>
-void *pick(bool staged, bool nt, int unroll_sel, bool rows, bool one) {
+void *pick(bool staged, bool nt, int unroll_sel, bool rows, bool one, bool wide) {
   if (staged) return nt ? st_fn<Op, kU1, true>() : st_fn<Op, kU1, false>();
   switch (unroll_sel) {
-    case 0: return nt ? zs_fn<Op, kU0, true>(rows, one) : zs_fn<Op, kU0, false>(rows, one);
-    case 2: return nt ? zs_fn<Op, kU2, true>(rows, one) : zs_fn<Op, kU2, false>(rows, one);
-    default: return nt ? zs_fn<Op, kU1, true>(rows, one) : zs_fn<Op, kU1, false>(rows, one);
+    case 0: return nt ? zs_fn<Op, kU0, true, true>(rows, one, wide) : zs_fn<Op, kU0, false>(rows, one, false);
+    case 2: return nt ? zs_fn<Op, kU2, true>(rows, one, false) : zs_fn<Op, kU2, false>(rows, one, false);
+    default: return nt ? zs_fn<Op, kU1, true>(rows, one, false) : zs_fn<Op, kU1, false>(rows, one, false);
   }
 }
 
@@ -757,19 +767,20 @@ int unroll_of(KernelKind kind, int unroll_sel) {
   return kind == KernelKind::kCopy ? copy_u[sel] : sum_u[sel];
 }
 
-void *kernel_fn(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows, bool one) {
+void *kernel_fn(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows, bool one,
+                bool wide = false) {
   switch (kind) {
-    case KernelKind::kCopy: return pick<atom::CopyOp, 4, 8, 16>(staged, nt, unroll_sel, rows, one);
-    case KernelKind::kSumF32: return pick<atom::SumF32, 1, 2, 4>(staged, nt, unroll_sel, rows, one);
-    default: return pick<atom::SumBf16, 1, 2, 4>(staged, nt, unroll_sel, rows, one);
+    case KernelKind::kCopy: return pick<atom::CopyOp, 4, 8, 16>(staged, nt, unroll_sel, rows, one, wide);
+    case KernelKind::kSumF32: return pick<atom::SumF32, 1, 2, 4>(staged, nt, unroll_sel, rows, one, wide);
+    default: return pick<atom::SumBf16, 1, 2, 4>(staged, nt, unroll_sel, rows, one, wide);
   }
 }
 
 hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, bool rows,
-                     bool one, int grid, hipStream_t stream) {
+                     bool one, bool wide, int grid, hipStream_t stream) {
   void *args[] = {const_cast<LaunchPlan *>(&p)};
-  return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel, rows, one), dim3(grid), dim3(kThreads),
-                         args, 0, stream);
+  return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel, rows, one, wide), dim3(grid),
+                         dim3(kThreads), args, 0, stream);
 }
 
 hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStream_t stream) {
@@ -827,9 +838,11 @@ hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int gri
 }
 
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
-                               bool one, int *blocks) {
+                               bool one, bool wide, int *blocks) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      blocks, kernel_fn(kind, staged, nt, staged ? 1 : unroll_sel, staged || rows, !staged && one),
+      blocks,
+      kernel_fn(kind, staged, nt, staged ? 1 : unroll_sel, staged || rows, !staged && one,
+                !staged && wide),
       kThreads, 0);
 }
 

@@ -35,7 +35,7 @@ struct DeviceState {
   int64_t inv_bytes = 0;
   uint32_t epoch = 0;
   uint32_t exit_total[2][kExitSlots] = {};  // per parity and slot, all launches so far
-  int occ[3][2][2][3][2][2] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
+  int occ[3][2][2][3][2][2][2] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
 };
 
 std::vector<DeviceState> &devices() {
@@ -132,11 +132,12 @@ purlin_status device_state(DeviceState **out) {
 }
 
 int occupancy(DeviceState &s, KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
-              bool one) {
-  int &o = s.occ[int(kind)][staged ? 1 : 0][nt ? 1 : 0][unroll_sel][rows ? 1 : 0][one ? 1 : 0];
+              bool one, bool wide) {
+  int &o = s.occ[int(kind)][staged ? 1 : 0][nt ? 1 : 0][unroll_sel][rows ? 1 : 0][one ? 1 : 0]
+                [wide ? 1 : 0];
   if (o == 0) {
     int b = 0;
-    if (max_resident_per_cu(kind, staged, nt, unroll_sel, rows, one, &b) != hipSuccess || b < 1)
+    if (max_resident_per_cu(kind, staged, nt, unroll_sel, rows, one, wide, &b) != hipSuccess || b < 1)
       b = 1;
     o = b;
   }
@@ -570,7 +571,17 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
   bool single_dst = true;
   for (const Job &jb : jobs) single_dst &= jb.dst >= 0;
   const bool one = !staged && one_build(kind, nt, rows, single_dst);
-  const int capacity = ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows, one);
+  // The build with the wide element pass (for small misaligned single-
+  // destination tiles, taken in the latency regime only: at most 512 KiB of
+  // jobs).  Larger reductions run the build without it, whose row bodies
+  // keep a workgroup per CU more (ReduceScatterV 4-11% faster at 2-8 MiB per
+  // rank, 2% at 16).  Copies run the wide build at every size: its row body
+  // measured 2-3% faster on AllToAllV at 8 MiB - 1 GiB per rank (paired on
+  // the same buffers; the pass itself is not taken there, so this is the
+  // compiled code, not the pass).
+  const bool small = job_bytes <= (int64_t(512) << 10);
+  const bool wide = !staged && rows && (small || kind == KernelKind::kCopy);
+  const int capacity = ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows, one, wide);
 
   if (++ds->epoch == 0) ds->epoch = 1;  // epoch 0 would match freshly cleared flags
   const int64_t wd_ns = pol.watchdog_ns ? pol.watchdog_ns : kDefaultWatchdogNs;
@@ -603,13 +614,13 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     // Nontemporal loads pay off for sources off the destination's line
     // phase too (variable-length partitions), measured at 16 MiB - 1 GiB.
     lp.nt_any_phase = env_i64("PURLIN_NT_ANY_PHASE", 1) ? 1 : 0;
-    // Latency regime (at most 512 KiB of jobs, 4 KiB tiles): small
-    // misaligned single-destination tiles take one wide element pass
-    // instead of a row body (ReduceScatterV at 8 - 16 KiB per rank: 8.9 us
-    // against 10.3 us); from 1 MiB per rank on, the row body is faster.
-    lp.wide_max = (chunk <= 4096 && job_bytes <= (int64_t(512) << 10)) ? int32_t(chunk + 128) : 0;
+    // Latency regime (the wide build, 4 KiB tiles): small misaligned
+    // single-destination tiles take one wide element pass instead of a row
+    // body (ReduceScatterV at 8 - 16 KiB per rank: 8.9 us against 10.3 us);
+    // from 1 MiB per rank on, the row body is faster.
+    lp.wide_max = (wide && small && chunk <= 4096) ? int32_t(chunk + 128) : 0;
     for (int k = 0; k < kExitSlots; ++k) lp.exit_expect[k] = ds->exit_total[(ds->epoch - 1u) & 1u][k];
-    err = launch_zs(lp, kind, nt, unroll_sel, rows, one, grid, stream);
+    err = launch_zs(lp, kind, nt, unroll_sel, rows, one, wide, grid, stream);
     if (err == hipSuccess && lp.sync) {
       // workgroup b counts on slot b % kExitSlots
       for (int k = 0; k < kExitSlots; ++k)
