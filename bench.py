@@ -105,14 +105,16 @@ def measured_traffic(kernel, T, names, variant):
     return None if k is None else int(k["traffic_per_launch"])
 
 
-def kernel_of(name, rows, one):
+def kernel_of(name, rows, one, plain=False):
     """The kernel a collective's launch ran, named as in the rocprofv3
     summaries: the operation, whether it was the build with the realigning
     row bodies (some source off its destinations' 16-byte phase) or the
-    aligned-only one, and whether it was the build for single-destination
-    jobs ("one") or the general one ("general")."""
+    aligned-only one, whether it was the build for single-destination jobs
+    ("one") or the general one ("general"), and ",plain" for the build with
+    plain body stores (large copy broadcasts)."""
     op = "SumBf16" if SPECS[name][2] == "sum" else "CopyOp"
-    return "zs_kernel<%s,%s,%s>" % (op, "rows" if rows else "aligned", "one" if one else "general")
+    return "zs_kernel<%s,%s,%s%s>" % (op, "rows" if rows else "aligned",
+                                      "one" if one else "general", ",plain" if plain else "")
 
 
 def cpu_baseline(T_sample, names):
@@ -773,7 +775,8 @@ def main():
                      "hbm_frac": round(s["bmin"] / p50 / HBM_PEAK, 4),
                      "bmin_bytes": s["bmin"], "grid": launch[name]["grid"],
                      "chunk_bytes": launch[name]["chunk_bytes"]}
-        k = kern.setdefault(kernel_of(name, launch[name]["rows"], launch[name]["one"]),
+        k = kern.setdefault(kernel_of(name, launch[name]["rows"], launch[name]["one"],
+                                      launch[name]["plain_stores"]),
                             {"bytes": 0, "time": 0.0, "launches": 0})
         k["bytes"] += s["bmin"] * len(ts)
         k["time"] += sum(ts)

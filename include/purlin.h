@@ -114,7 +114,8 @@ typedef struct {
                             0 for the other calls */
   int32_t one;           /* zero-staging launch: 1 if the build for single-destination jobs
                             ran (no broadcast in the launch), 0 otherwise */
-  int32_t reserved;
+  int32_t plain_stores;  /* zero-staging launch: 1 if the build with plain (not nontemporal)
+                            body stores ran (copy broadcasts of 16 MiB of jobs or more) */
 } purlin_launch_info;
 
 /*

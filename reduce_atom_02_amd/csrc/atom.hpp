@@ -581,7 +581,8 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
 // phase may fold before shifting (more registers; the staged kernel, whose
 // owner mixes its own input with staging slots, leaves it out).  kRows =
 // false builds the tile without the row bodies, for launches whose every
-// job is aligned: a smaller kernel.  kWide builds in the wide element pass
+// job is aligned: a smaller kernel.  kNTS: nontemporal stores in the body
+// (kNT by default; broadcasts store plainly).  kWide builds in the wide element pass
 // for small misaligned tiles (its registers would cost the staged kernel,
 // which never takes it, a workgroup per CU of occupancy).  x0 is 0 or on a 128-byte boundary of the
 // job's line_ref, x1 is the job's end or on such a boundary.  Layout:
@@ -599,7 +600,7 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
 // or when nt_any_phase asks for it (measured faster for misaligned
 // variable-length partitions too).  A tile spans less than 4 GiB.
 template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true, bool kOne = false,
-          bool kWide = false>
+          bool kWide = false, bool kNTS = kNT>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
                                      bool nt_any_phase = false, int64_t wide_max = 0) {
   if (x1 <= x0) return;
@@ -664,8 +665,8 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
   for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(xh);
   const bool ntl = kNT && (phase == 0 || nt_any_phase);
   if (any == 0) {
-    if (ntl) body_aligned<Op, kU, true, kNT, kOne>(sa, s.n, db, d.n, nbody);
-    else body_aligned<Op, kU, false, kNT, kOne>(sa, s.n, db, d.n, nbody);
+    if (ntl) body_aligned<Op, kU, true, kNTS, kOne>(sa, s.n, db, d.n, nbody);
+    else body_aligned<Op, kU, false, kNTS, kOne>(sa, s.n, db, d.n, nbody);
     return;
   }
   if constexpr (!kRows) {
@@ -677,11 +678,11 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
     return;
   }
   if (d.n == 1) {
-    if (ntl) body_rows<Op, kUr, true, kNT, true, kFoldOk>(sa, s.n, db, 1, nbody, sh);
-    else body_rows<Op, kUr, false, kNT, true, kFoldOk>(sa, s.n, db, 1, nbody, sh);
+    if (ntl) body_rows<Op, kUr, true, kNTS, true, kFoldOk>(sa, s.n, db, 1, nbody, sh);
+    else body_rows<Op, kUr, false, kNTS, true, kFoldOk>(sa, s.n, db, 1, nbody, sh);
   } else {
-    if (ntl) body_rows<Op, kUr, true, kNT, false, kFoldOk>(sa, s.n, db, d.n, nbody, sh);
-    else body_rows<Op, kUr, false, kNT, false, kFoldOk>(sa, s.n, db, d.n, nbody, sh);
+    if (ntl) body_rows<Op, kUr, true, kNTS, false, kFoldOk>(sa, s.n, db, d.n, nbody, sh);
+    else body_rows<Op, kUr, false, kNTS, false, kFoldOk>(sa, s.n, db, d.n, nbody, sh);
   }
 }
 

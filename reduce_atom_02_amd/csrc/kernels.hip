@@ -92,7 +92,7 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     int64_t x0, x1;
     tile_bounds(atom::line_ref<Op>(s, d), jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
                 p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
-    atom::tile<Op, kU, kNTL, true, kRows, kOne, kWide>(s, d, x0, x1, p.nt_any_phase != 0,
+    atom::tile<Op, kU, kNTL, true, kRows, kOne, kWide, kNTS>(s, d, x0, x1, p.nt_any_phase != 0,
                                                   p.wide_max);
   }
   if (p.sync) snac::exit_notify(p);
@@ -721,9 +721,10 @@ namespace {
 // The single-destination builds exist for the default (nontemporal) form,
 // without row bodies, and with row bodies for sums; one_build says which
 // launches get one.  The wide builds (latency regime) exist for the row
-// bodies of the default form and unroll.
+// bodies of the default form and unroll, and so do the builds for large copy
+// broadcasts, whose stores are plain (bcast; sums are never asked for one).
 template <class Op, int kU, bool kNT, bool kWideOk = false>
-void *zs_fn(bool rows, bool one, bool wide) {
+void *zs_fn(bool rows, bool one, bool wide, bool bcast) {
   if constexpr (kNT) {
     if (one && !rows) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, false, true>);
     if constexpr (Op::kSum)
@@ -732,6 +733,13 @@ void *zs_fn(bool rows, bool one, bool wide) {
           if (wide) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true, true, true>);
         return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true, true>);
       }
+    if constexpr (kWideOk && !Op::kSum) {
+      if (bcast) {
+        if (!rows) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, false, false, false>);
+        return wide ? reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, false, true, false, true>)
+                    : reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, false, true, false>);
+      }
+    }
     if constexpr (kWideOk)
       if (rows && wide) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, true, false, true>);
   }
@@ -743,12 +751,14 @@ void *st_fn() { return reinterpret_cast<void *>(&staged_kernel<Op, kU, kNT, kNT>
 
 // Unroll depth: 16-byte units each lane keeps in flight per source.
 template <class Op, int kU0, int kU1, int kU2>
-void *pick(bool staged, bool nt, int unroll_sel, bool rows, bool one, bool wide) {
+void *pick(bool staged, bool nt, int unroll_sel, bool rows, bool one, bool wide, bool bcast) {
   if (staged) return nt ? st_fn<Op, kU1, true>() : st_fn<Op, kU1, false>();
   switch (unroll_sel) {
-    case 0: return nt ? zs_fn<Op, kU0, true, true>(rows, one, wide) : zs_fn<Op, kU0, false>(rows, one, false);
-    case 2: return nt ? zs_fn<Op, kU2, true>(rows, one, false) : zs_fn<Op, kU2, false>(rows, one, false);
-    default: return nt ? zs_fn<Op, kU1, true>(rows, one, false) : zs_fn<Op, kU1, false>(rows, one, false);
+    case 0:
+      return nt ? zs_fn<Op, kU0, true, true>(rows, one, wide, bcast)
+                : zs_fn<Op, kU0, false>(rows, one, false, false);
+    case 2: return nt ? zs_fn<Op, kU2, true>(rows, one, false, false) : zs_fn<Op, kU2, false>(rows, one, false, false);
+    default: return nt ? zs_fn<Op, kU1, true>(rows, one, false, false) : zs_fn<Op, kU1, false>(rows, one, false, false);
   }
 }
 
@@ -768,18 +778,20 @@ int unroll_of(KernelKind kind, int unroll_sel) {
 }
 
 void *kernel_fn(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows, bool one,
-                bool wide = false) {
+                bool wide = false, bool bcast = false) {
   switch (kind) {
-    case KernelKind::kCopy: return pick<atom::CopyOp, 4, 8, 16>(staged, nt, unroll_sel, rows, one, wide);
-    case KernelKind::kSumF32: return pick<atom::SumF32, 1, 2, 4>(staged, nt, unroll_sel, rows, one, wide);
-    default: return pick<atom::SumBf16, 1, 2, 4>(staged, nt, unroll_sel, rows, one, wide);
+    case KernelKind::kCopy:
+      return pick<atom::CopyOp, 4, 8, 16>(staged, nt, unroll_sel, rows, one, wide, bcast);
+    case KernelKind::kSumF32:
+      return pick<atom::SumF32, 1, 2, 4>(staged, nt, unroll_sel, rows, one, wide, bcast);
+    default: return pick<atom::SumBf16, 1, 2, 4>(staged, nt, unroll_sel, rows, one, wide, bcast);
   }
 }
 
 hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, bool rows,
-                     bool one, bool wide, int grid, hipStream_t stream) {
+                     bool one, bool wide, bool bcast, int grid, hipStream_t stream) {
   void *args[] = {const_cast<LaunchPlan *>(&p)};
-  return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel, rows, one, wide), dim3(grid),
+  return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel, rows, one, wide, bcast), dim3(grid),
                          dim3(kThreads), args, 0, stream);
 }
 
@@ -838,11 +850,11 @@ hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int gri
 }
 
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
-                               bool one, bool wide, int *blocks) {
+                               bool one, bool wide, bool bcast, int *blocks) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(
       blocks,
       kernel_fn(kind, staged, nt, staged ? 1 : unroll_sel, staged || rows, !staged && one,
-                !staged && wide),
+                !staged && wide, !staged && bcast),
       kThreads, 0);
 }
 

@@ -15,9 +15,11 @@ enum class KernelKind { kCopy, kSumF32, kSumBf16 };
 // the kernel built for launches whose every job has a single destination
 // rank (no broadcast), whose destination loops fold to one store.  wide =
 // true: the latency-regime build with the wide element pass (row bodies of
-// the default nontemporal form and unroll only; ignored otherwise).
+// the default nontemporal form and unroll only; ignored otherwise).  bcast =
+// true: a launch with broadcast jobs, whose body stores are plain (same
+// forms only).
 hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, bool rows,
-                     bool one, bool wide, int grid, hipStream_t stream);
+                     bool one, bool wide, bool bcast, int grid, hipStream_t stream);
 hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStream_t stream);
 int unroll_of(KernelKind kind, int unroll_sel);
 // Whether a launch whose jobs all have one destination rank (single_dst) runs
@@ -28,7 +30,7 @@ hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int gri
 hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts, int n_dst,
                           int64_t bytes, int grid, hipStream_t stream);
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
-                               bool one, bool wide, int *blocks);
+                               bool one, bool wide, bool bcast, int *blocks);
 
 // MoE dispatch one row at a time (rows: the build with the realigning row
 // bodies), the inverse-map pass, dispatch one token at a time (after the

@@ -35,7 +35,7 @@ struct DeviceState {
   int64_t inv_bytes = 0;
   uint32_t epoch = 0;
   uint32_t exit_total[2][kExitSlots] = {};  // per parity and slot, all launches so far
-  int occ[3][2][2][3][2][2][2] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
+  int occ[3][2][2][3][2][2][2][2] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
 };
 
 std::vector<DeviceState> &devices() {
@@ -132,12 +132,13 @@ purlin_status device_state(DeviceState **out) {
 }
 
 int occupancy(DeviceState &s, KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
-              bool one, bool wide) {
+              bool one, bool wide, bool bcast) {
   int &o = s.occ[int(kind)][staged ? 1 : 0][nt ? 1 : 0][unroll_sel][rows ? 1 : 0][one ? 1 : 0]
-                [wide ? 1 : 0];
+                [wide ? 1 : 0][bcast ? 1 : 0];
   if (o == 0) {
     int b = 0;
-    if (max_resident_per_cu(kind, staged, nt, unroll_sel, rows, one, wide, &b) != hipSuccess || b < 1)
+    if (max_resident_per_cu(kind, staged, nt, unroll_sel, rows, one, wide, bcast, &b) != hipSuccess ||
+        b < 1)
       b = 1;
     o = b;
   }
@@ -581,7 +582,16 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
   // compiled code, not the pass).
   const bool small = job_bytes <= (int64_t(512) << 10);
   const bool wide = !staged && rows && (small || kind == KernelKind::kCopy);
-  const int capacity = ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows, one, wide);
+  // Copy broadcasts of 16 MiB of jobs or more store plainly: AllGather 5-8%,
+  // AllGatherV 4-8% faster at 64 MiB - 1 GiB per rank than with nontemporal
+  // stores (paired on the same buffers, both orders).  Nontemporal stores
+  // stay for smaller broadcasts (AllGather 6% faster with them at 4 MiB),
+  // for AllReduce's broadcast sums (2-4% faster with them at 64 MiB -
+  // 1 GiB) and for single-destination copies (AllToAllV 3-5%).
+  const bool bcast = !staged && broadcast && kind == KernelKind::kCopy &&
+                     job_bytes >= (int64_t(16) << 20) && env_i64("PURLIN_BCAST_PLAIN", 1) != 0;
+  const int capacity =
+      ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows, one, wide, bcast);
 
   if (++ds->epoch == 0) ds->epoch = 1;  // epoch 0 would match freshly cleared flags
   const int64_t wd_ns = pol.watchdog_ns ? pol.watchdog_ns : kDefaultWatchdogNs;
@@ -620,7 +630,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     // from 1 MiB per rank on, the row body is faster.
     lp.wide_max = (wide && small && chunk <= 4096) ? int32_t(chunk + 128) : 0;
     for (int k = 0; k < kExitSlots; ++k) lp.exit_expect[k] = ds->exit_total[(ds->epoch - 1u) & 1u][k];
-    err = launch_zs(lp, kind, nt, unroll_sel, rows, one, wide, grid, stream);
+    err = launch_zs(lp, kind, nt, unroll_sel, rows, one, wide, bcast, grid, stream);
     if (err == hipSuccess && lp.sync) {
       // workgroup b counts on slot b % kExitSlots
       for (int k = 0; k < kExitSlots; ++k)
@@ -631,6 +641,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     info.zero_staging = 1;
     info.rows = rows ? 1 : 0;
     info.one = one ? 1 : 0;
+    info.plain_stores = bcast ? 1 : 0;
     info.chunk_bytes = chunk;
     info.tiles = lp.total_tiles;
     info.sync = lp.sync;

@@ -66,7 +66,7 @@ class LaunchInfo(ctypes.Structure):
                 ("chunk_bytes", ctypes.c_int64), ("tiles", ctypes.c_int64),
                 ("bytes_min", ctypes.c_int64), ("njobs", ctypes.c_int32),
                 ("sync", ctypes.c_int32), ("rows", ctypes.c_int32), ("unit", ctypes.c_int32),
-                ("one", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("one", ctypes.c_int32), ("plain_stores", ctypes.c_int32)]
 
 
 def _load():
