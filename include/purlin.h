@@ -114,8 +114,9 @@ typedef struct {
                             0 for the other calls */
   int32_t one;           /* zero-staging launch: 1 if the build for single-destination jobs
                             ran (no broadcast in the launch), 0 otherwise */
-  int32_t plain_stores;  /* zero-staging launch: 1 if the build with plain (not nontemporal)
-                            body stores ran (copy broadcasts of 16 MiB of jobs or more) */
+  int32_t plain_stores;  /* 1 if the build with plain (not nontemporal) body stores ran:
+                            copy broadcasts of 16 MiB of jobs or more, Ulysses exchanges of
+                            at most 128 MiB each way */
 } purlin_launch_info;
 
 /*

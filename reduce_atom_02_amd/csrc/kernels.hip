@@ -574,7 +574,16 @@ template <> struct UnitOf<8> { typedef uint32_t T __attribute__((ext_vector_type
 template <> struct UnitOf<4> { typedef uint32_t T; };
 template <> struct UnitOf<2> { typedef uint16_t T; };
 
-template <int kUnit, int kU>
+// kNTS: nontemporal stores (large exchanges); small ones, whose bytes stay
+// largely in the caches between the producing and the consuming kernel,
+// store plainly.
+template <class T, bool kNTS>
+__device__ __forceinline__ void strided_store(uint64_t addr, T v) {
+  if constexpr (kNTS) __builtin_nontemporal_store(v, atom::gp<T>(addr));
+  else *atom::gp<T>(addr) = v;
+}
+
+template <int kUnit, int kU, bool kNTS = true>
 __global__ void __launch_bounds__(kThreads) strided_kernel(const StridedPlan sp) {
   typedef typename UnitOf<kUnit>::T T;
   const LaunchPlan &p = sp.base;
@@ -608,7 +617,7 @@ __global__ void __launch_bounds__(kThreads) strided_kernel(const StridedPlan sp)
         dst[k] = db + uint64_t(r) * uint64_t(sp.dst_stride) + uint64_t(c) * kUnit;
       }
 #pragma unroll
-      for (int k = 0; k < kU; ++k) __builtin_nontemporal_store(v[k], atom::gp<T>(dst[k]));
+      for (int k = 0; k < kU; ++k) strided_store<T, kNTS>(dst[k], v[k]);
     }
     if (p0 < u1) {
       T v[kU];
@@ -627,7 +636,7 @@ __global__ void __launch_bounds__(kThreads) strided_kernel(const StridedPlan sp)
 #pragma unroll
       for (int k = 0; k < kU; ++k)
         if (p0 + uint32_t(k) * kThreads + threadIdx.x < u1)
-          __builtin_nontemporal_store(v[k], atom::gp<T>(dst[k]));
+          strided_store<T, kNTS>(dst[k], v[k]);
       atom::drain_vm();
     }
   }
@@ -823,22 +832,27 @@ hipError_t moe_resident_per_cu(MoeKernel which, bool rows, int *blocks) {
 }
 
 // Units in flight per lane: 16 KiB per workgroup pass for 16-byte units.
-static void *strided_fn(int unit) {
+template <bool kNTS>
+static void *strided_fn_of(int unit) {
   switch (unit) {
-    case 16: return reinterpret_cast<void *>(&strided_kernel<16, 4>);
-    case 8: return reinterpret_cast<void *>(&strided_kernel<8, 8>);
-    case 4: return reinterpret_cast<void *>(&strided_kernel<4, 8>);
-    default: return reinterpret_cast<void *>(&strided_kernel<2, 16>);
+    case 16: return reinterpret_cast<void *>(&strided_kernel<16, 4, kNTS>);
+    case 8: return reinterpret_cast<void *>(&strided_kernel<8, 8, kNTS>);
+    case 4: return reinterpret_cast<void *>(&strided_kernel<4, 8, kNTS>);
+    default: return reinterpret_cast<void *>(&strided_kernel<2, 16, kNTS>);
   }
 }
-
-hipError_t launch_strided(const StridedPlan &sp, int unit, int grid, hipStream_t stream) {
-  void *args[] = {const_cast<StridedPlan *>(&sp)};
-  return hipLaunchKernel(strided_fn(unit), dim3(grid), dim3(kThreads), args, 0, stream);
+static void *strided_fn(int unit, bool plain) {
+  return plain ? strided_fn_of<false>(unit) : strided_fn_of<true>(unit);
 }
 
-hipError_t strided_resident_per_cu(int unit, int *blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, strided_fn(unit), kThreads, 0);
+hipError_t launch_strided(const StridedPlan &sp, int unit, bool plain, int grid,
+                          hipStream_t stream) {
+  void *args[] = {const_cast<StridedPlan *>(&sp)};
+  return hipLaunchKernel(strided_fn(unit, plain), dim3(grid), dim3(kThreads), args, 0, stream);
+}
+
+hipError_t strided_resident_per_cu(int unit, bool plain, int *blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, strided_fn(unit, plain), kThreads, 0);
 }
 
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,

@@ -39,8 +39,10 @@ enum class MoeKernel { kDispatch, kInverse, kDispatchTokens, kCombine };
 hipError_t launch_moe(const MoePlan &m, MoeKernel which, bool rows, int grid, hipStream_t stream);
 hipError_t moe_resident_per_cu(MoeKernel which, bool rows, int *blocks);
 
-// Strided-row exchange in units of `unit` bytes (16, 8, 4 or 2).
-hipError_t launch_strided(const StridedPlan &sp, int unit, int grid, hipStream_t stream);
-hipError_t strided_resident_per_cu(int unit, int *blocks);
+// Strided-row exchange in units of `unit` bytes (16, 8, 4 or 2); plain:
+// plain instead of nontemporal stores.
+hipError_t launch_strided(const StridedPlan &sp, int unit, bool plain, int grid,
+                          hipStream_t stream);
+hipError_t strided_resident_per_cu(int unit, bool plain, int *blocks);
 
 }  // namespace purlin

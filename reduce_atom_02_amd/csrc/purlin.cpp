@@ -856,10 +856,15 @@ purlin_status purlin_ulysses(void *const *in, void *const *out, int P, const int
   }
   for (int q = P * P; q <= kMaxJobs; ++q) sp.base.tile_begin[q] = int32_t(t);
   sp.base.total_tiles = int32_t(t);
+  // Exchanges of at most 128 MiB each way store plainly: at the Qwen-Image
+  // 1024x1024 shape (80 MB / 27 MB each way) 11% / up to 7% faster than with
+  // nontemporal stores, paired on the same buffers in both orders; at 64
+  // MiB per rank (537 MB each way) nontemporal stores are 4-8% faster.
+  const bool plain = total <= (int64_t(128) << 20);
   int b = 0;
-  if (strided_resident_per_cu(unit, &b) != hipSuccess || b < 1) b = 1;
+  if (strided_resident_per_cu(unit, plain, &b) != hipSuccess || b < 1) b = 1;
   const int grid = int(std::max<int64_t>(1, std::min<int64_t>({t, cap, int64_t(ds->cus) * b})));
-  if (launch_strided(sp, unit, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
+  if (launch_strided(sp, unit, plain, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
   side_count_exit(*ds, sp.base, grid);
   purlin_launch_info info{};
   info.grid = grid;
@@ -871,6 +876,7 @@ purlin_status purlin_ulysses(void *const *in, void *const *out, int P, const int
   info.njobs = P * P;
   info.sync = sp.base.sync;
   info.unit = unit;
+  info.plain_stores = plain ? 1 : 0;
   g_last = info;
   g_have_last = true;
   return PURLIN_OK;
