@@ -288,6 +288,31 @@ def test_staged_small_misaligned_chunks_repeated(purlin, name):
         oracle_and_gpu(purlin, name, P, counts, "bf16", ins, outs, None, shifts, [rep % 8] * P)
 
 
+@pytest.mark.parametrize("name", ["allgather", "alltoall"])
+def test_store_builds_at_the_broadcast_switch(purlin, name):
+    """Copy broadcasts of 16 MiB of jobs or more run the build with plain
+    stores, single-destination copies the nontemporal one: element-by-element
+    parity just above the switch (AllGather and AllGatherV-like odd sizes),
+    and the build the launch reports."""
+    P = 8
+    print("case store-build", name, flush=True)
+    rng = np.random.default_rng([41, len(name)])
+    nparts = P * P if name == "alltoall" else P
+    # about 16.5 MiB of bf16 jobs per launch, odd partition sizes
+    per = (33 << 20) // 4 // nparts
+    sizes = [per + 2 * k + 1 for k in range(nparts)]
+    counts = pins.counts_for(name, P, sizes)
+    ins, outs = pins.make_case(name, P, counts, "bf16", rng, None, sentinel=0x4E4E)
+    purlin.set_policy(zero_staging="zs")
+    oracle_and_gpu(purlin, name, P, counts, "bf16", ins, outs, None, [3] * P, [0] * P)
+    info = purlin.last_launch()
+    if name == "allgather":
+        assert sum(sizes) * 2 >= 16 << 20
+        assert info["plain_stores"] == 1 and info["rows"] == 1, info
+    else:
+        assert info["plain_stores"] == 0, info
+
+
 def test_overlap_checks_survive_the_pointer_cache(purlin):
     """The per-call overlap check is skipped only for the same plan and buffers."""
     import torch
