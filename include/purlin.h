@@ -21,6 +21,26 @@
  * purlin_layout are device pointers owned by the caller; nothing here takes
  * ownership of them, frees them or keeps them after the call returns.
  *
+ * Streams.  Every call is enqueued on the caller's stream and returns
+ * without synchronizing the device or the stream.  Library workspace (flag
+ * block, staging rings, MoE table) belongs to a stream: a call allocates it
+ * the first time that stream needs it, and grows it with a new allocation
+ * cleared in stream order (the old one stays allocated until
+ * purlin_release), so no call waits for other work.  Calls on one stream run
+ * in stream order; calls on different streams share no workspace and never
+ * wait for each other, so they may run concurrently.  The zero-staging
+ * collectives without the handshake (the default) use no workspace at all.
+ *
+ * HIP graphs.  Calls may be captured into a HIP graph and replayed any
+ * number of times: launch epochs are kept in device memory, so every replay
+ * gets a fresh one, and nothing the library enqueues is a memset or a copy.
+ * A captured call must not need new workspace: make the same call (or a
+ * larger one) on the capturing stream once before capture, else it returns
+ * PURLIN_ERR_UNSUPPORTED.  A replayed graph uses the workspace of the stream
+ * it was captured on; do not run it concurrently with calls on that stream.
+ * Workspace is keyed by the stream handle: a stream destroyed while its work
+ * is still running must not be replaced by a new one with the same handle.
+ *
  * Thread safety: none; serialize calls from different host threads.
  */
 #ifndef PURLIN_H_
@@ -42,7 +62,8 @@ extern "C" {
 typedef enum {
   PURLIN_OK = 0,
   PURLIN_ERR_INVALID_ARG = 1, /* bad pointer, P, count, alignment, overlap */
-  PURLIN_ERR_UNSUPPORTED = 2, /* the (naming, naming, op) triple is not a collective */
+  PURLIN_ERR_UNSUPPORTED = 2, /* the (naming, naming, op) triple is not a collective, or
+                                 the call would need new workspace during graph capture */
   PURLIN_ERR_NO_MEMORY = 3,   /* workspace allocation failed */
   PURLIN_ERR_HIP = 4,         /* a HIP call or kernel launch failed */
   PURLIN_ERR_TIMEOUT = 5      /* a bounded device wait expired (see purlin_check) */
@@ -84,7 +105,8 @@ typedef struct {
   int32_t depth;         /* staging slots per channel, 1..8 (staged only) */
   int32_t wgs_per_rank;  /* workgroups per rank; grid = P * wgs_per_rank */
   int32_t zero_staging;  /* purlin_staging */
-  int32_t sync;          /* entry/exit notify flags: 0 auto, 1 on, 2 off */
+  int32_t sync;          /* entry/exit notify (the per-rank handshake): 0 auto (off: calls
+                            on one stream are ordered by the stream), 1 on, 2 off */
   int64_t watchdog_ns;   /* bound of every device spin wait */
   int32_t test_withhold; /* test only: k > 0 withholds the k-th ready notify
                             of staging channel 0, to exercise the watchdog */
@@ -146,22 +168,29 @@ typedef struct {
  *   1 <= P <= 8; non-NULL layouts and counts; counts and displs >= 0; every
  *   buffer that holds an element non-NULL and aligned to the element size;
  *   output partitions disjoint; no input byte overlaps an output byte.
- * Other (naming, naming, op) triples return PURLIN_ERR_UNSUPPORTED.
+ * Other (naming, naming, op) triples return PURLIN_ERR_UNSUPPORTED, and so
+ * does a plan of more than 64 jobs (a sum of P partitions broadcast to every
+ * rank, by_index -> by_index, whose output buffers are not all congruent
+ * modulo 16 bytes), also checked before any HIP call.
  *
  * The call enqueues one kernel and returns; it never synchronizes.  Inputs
  * must stay valid and outputs untouched until the stream reaches that point.
- * A device-side watchdog expiry is reported by purlin_check.
+ * The staged variant's workgroups wait for each other; they are numbered so
+ * that every job's producers come before its consumers and the jobs before
+ * the one being started are wholly resident, so a kernel running beside it
+ * on another stream delays it but cannot block it.  A device-side watchdog
+ * expiry is reported by purlin_check.
  */
 PURLIN_API purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *out,
                                 purlin_op op, purlin_dtype dtype, int P,
                                 const int64_t *counts, const int64_t *displs,
                                 hipStream_t stream);
 
-/* Synchronize `stream`, then read and clear the device status word of the
- * current device: PURLIN_ERR_TIMEOUT if any wait expired since the last
- * check, else PURLIN_ERR_INVALID_ARG if a device-side argument check failed
- * (MoE indices), PURLIN_ERR_HIP if the synchronization failed, else
- * PURLIN_OK. */
+/* Synchronize `stream`, then read and clear that stream's device status
+ * word (current device): PURLIN_ERR_TIMEOUT if any wait of a call on the
+ * stream expired since the last check, else PURLIN_ERR_INVALID_ARG if a
+ * device-side argument check failed (MoE indices), PURLIN_ERR_HIP if the
+ * synchronization failed, else PURLIN_OK.  This call synchronizes. */
 PURLIN_API purlin_status purlin_check(hipStream_t stream);
 
 /* Replace the policy (NULL restores the defaults).  Environment variables
@@ -198,8 +227,8 @@ PURLIN_API purlin_status purlin_plan_describe(const purlin_layout *in, const pur
  * unique != 0 promises one row per (token, destination rank) (the
  * deduplicated routing): each token row is then read once and written to
  * every rank it goes to, through a table of sum(x_rows) * P 8-byte words the
- * library keeps (as purlin_moe_combine); a token twice in one group is then
- * reported.  unique == 0 gathers row by row and allows repeats.
+ * library keeps per stream (as purlin_moe_combine); a token twice in one
+ * group is then reported.  unique == 0 gathers row by row and allows repeats.
  *
  * Rows are moved as bytes (row_bytes even, buffers 2-byte aligned; 16-byte
  * alignment of every buffer and of row_bytes takes the faster kernels, and
@@ -228,8 +257,9 @@ PURLIN_API purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int
  * each product rounded to fp32 before its add.  A token routed nowhere gets
  * +0.  One row per (token, destination rank): a token twice in one group is
  * reported.  row_bytes a multiple of 16 and every buffer 16-byte aligned.
- * The library keeps a table of sum(x_rows) * P 8-byte words (allocated on
- * the first call that needs it, freed by purlin_release).  Errors as
+ * The library keeps a table of sum(x_rows) * P 8-byte words per stream
+ * (allocated on the first call on the stream that needs it, freed by
+ * purlin_release).  Errors as
  * purlin_moe_dispatch, plus INVALID_ARG for misalignment or a NULL weight
  * array that holds entries; a duplicate token in a group also makes the
  * next purlin_check return INVALID_ARG (that token's row is unspecified).
@@ -260,8 +290,8 @@ PURLIN_API purlin_status purlin_moe_combine(void *const *y, void *const *out, in
  * may be NULL only where its buffer is empty); every out buffer is disjoint
  * from every in buffer.  Returns INVALID_ARG for a bad count, size,
  * alignment (odd addresses) or overlap, HIP for a launch failure.
- * Asynchronous on `stream`; runs the entry / exit handshake like
- * purlin_collective.
+ * Asynchronous on `stream`; runs the entry / exit handshake when the policy
+ * asks for it, like purlin_collective.
  */
 PURLIN_API purlin_status purlin_ulysses(void *const *in, void *const *out, int P,
                                         const int64_t *seq, int64_t heads, int64_t head_bytes,
@@ -290,8 +320,10 @@ PURLIN_API purlin_status purlin_stream_pattern(const void *const *srcs, int n_sr
 /* Static text for a status code. */
 PURLIN_API const char *purlin_strerror(purlin_status s);
 
-/* Free the library-owned workspace (flags, staging ring) of every device.
- * The next purlin_collective allocates it again. */
+/* Synchronize every device the library has used and free the library-owned
+ * workspace of every stream (flags, staging rings, MoE tables, outgrown
+ * buffers).  The next call that needs workspace allocates it again.  Graphs
+ * captured before must not be replayed afterwards. */
 PURLIN_API void purlin_release(void);
 
 #ifdef __cplusplus

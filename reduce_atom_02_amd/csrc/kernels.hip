@@ -64,9 +64,14 @@ __device__ __forceinline__ void tile_bounds(uint64_t ref, int64_t n, int64_t C, 
 // registers would cost a row-body kernel a workgroup per CU.
 template <class Op, int kU, bool kNTL, bool kNTS, bool kRows, bool kOne, bool kWide = false>
 __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
-  // A workgroup whose entry wait failed skips its tiles but still counts
-  // itself out, so the next launch's exit check is not poisoned.
-  const bool run = !p.sync || snac::entry(p);
+  // With the handshake on, a workgroup whose entry wait failed skips its
+  // tiles but still counts itself out, so the stream's epoch advances.
+  uint32_t e = 0;
+  bool run = true;
+  if (p.sync) {
+    e = snac::launch_epoch(p);
+    run = snac::entry(p, e);
+  }
   int t = run ? int(blockIdx.x) : p.total_tiles;
   int j = t < p.total_tiles ? job_of_tile(p, t) : 0;
   for (; t < p.total_tiles; t += gridDim.x) {
@@ -95,12 +100,18 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     atom::tile<Op, kU, kNTL, true, kRows, kOne, kWide, kNTS>(s, d, x0, x1, p.nt_any_phase != 0,
                                                   p.wide_max);
   }
-  if (p.sync) snac::exit_notify(p);
+  if (p.sync) snac::exit_notify(p, e);
 }
 
 // ---- staged SNAC pipeline --------------------------------------------------
 // Each job runs on `lanes` parallel pipelines; chunk c goes to lane c % lanes.
-// Per lane the job has three kinds of workgroup:
+// Per lane the job has three kinds of workgroup, numbered in this order (so
+// that the dispatcher, which starts workgroups in ascending order, starts a
+// chunk's producers before its consumers, and every job's workgroups are
+// contiguous: the jobs before the one being dispatched are wholly resident
+// and finish without it, whatever else occupies the device):
+//   stager   (one per source rank other than the owner) copies its rank's
+//            chunk into a ring slot, then notifies (Stage, Notify).
 //   owner    combines chunk c: its own rank's input read directly, every other
 //            source taken from that source's staging ring after its ready
 //            notify, in ascending rank; writes the owner's output and, when
@@ -110,8 +121,6 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
 //            that the owners, who read every source, keep pace with the
 //            stagers, who copy one; each owner notifies on its own ready word
 //            and returns its own credit to every stager.
-//   stager   (one per source rank other than the owner) copies its rank's
-//            chunk into a ring slot, then notifies (Stage, Notify).
 //   scatter  (one per destination rank other than the owner) waits for the
 //            owner's notify and copies the slot into its rank's output
 //            (Consume), then returns a credit for the slot.
@@ -163,27 +172,72 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
   const int r = int(blockIdx.x) - sj.role_begin;
   const int lane = r % L;
   const int team = sj.team;
-  const int kind = r / L;  // 0..team-1 owners, then n_stage stagers, then scatter
+  const int kind = r / L;  // 0..n_stage-1 stagers, then team owners, then scatter
   const int owner = sj.owner;
   const int rings_per_lane = sj.n_stage + (sj.n_scatter > 0 ? 1 : 0);
   const int ring0 = sj.ring_begin + lane * rings_per_lane;
   const int ntl = p.tile_begin[j + 1] - p.tile_begin[j];
   const int D = sp.depth;
-  const uint32_t e = p.epoch;
+  const uint32_t e = snac::launch_epoch(p);
 
   // first destination address of the job (alignment reference for the slots)
   const uint64_t b0 =
       uint64_t(p.out[jb.dst < 0 ? 0 : jb.dst]) + uint64_t(jb.dst_off);
   // Entry notify as in the zero-staging kernel; a workgroup whose entry wait
   // failed skips its role but still counts itself out at the end.
-  const bool run = !p.sync || snac::entry(p);
+  const bool run = !p.sync || snac::entry(p, e);
   if (threadIdx.x == 0) ok = run ? 1 : 0;
   __syncthreads();
 
   if (!run) {
     // nothing: fall through to the exit count
-  } else if (kind < team) {
-    // ---------------- owner (member `kind` of the lane's team) ----------------
+  } else if (kind < sj.n_stage) {
+    // ---------------- stager ----------------
+    const int k = kind;
+    const int src = jb.src >= 0 ? jb.src : (k < owner ? k : k + 1);
+    const int ring = ring0 + k;
+    for (int m = 0;; ++m) {
+      const int c = lane + L * m;
+      if (c >= ntl) break;
+      const int slot = m % D;
+      const uint64_t round = uint64_t(m / D);
+      const SlotRef o = slot_ref(sp, ring, slot);
+      if (threadIdx.x == 0) {
+        // every owner of the team returns one credit per round
+        if (round == 0) {
+          __hip_atomic_store(o.credit, tag(e, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (!snac::wait_geq<uint64_t, false>(o.credit, tag(e, round * uint64_t(team)), p, e)) {
+          ok = 0;
+        }
+      }
+      __syncthreads();
+      if (!ok) break;
+      int64_t x0, x1;
+      tile_bounds(b0, jb.nbytes, p.chunk_bytes, c, ntl, x0, x1);
+      atom::Srcs s;
+      s.n = 1;
+      const uint64_t a = uint64_t(p.in[src]) + uint64_t(jb.src_off);
+#pragma unroll
+      for (int i = 0; i < kMaxRanks; ++i) s.a[i] = a;
+      atom::Dsts d;
+      d.n = 1;
+#pragma unroll
+      for (int q = 0; q < kMaxRanks + 1; ++q) d.b[q] = slot_base(o.data, b0, x0);
+      atom::tile<atom::CopyOp, kU, kNTL>(s, d, x0, x1);
+      // Every wavefront's stores must be acknowledged before thread 0's
+      // release publishes the slot: a workgroup barrier alone does not wait
+      // for other wavefronts' global stores (their head and tail element
+      // passes run on wavefronts 2 and 3), so the release could overtake
+      // them and the owner read a stale line.
+      snac::drain_workgroup();
+      if (threadIdx.x == 0) {
+        const bool withhold = sp.withhold > 0 && ring == 0 && m + 1 == sp.withhold;
+        if (!withhold) snac::store_rel(o.ready, tag(e, round + 1));
+      }
+    }
+  } else if (kind < sj.n_stage + team) {
+    // ---------------- owner (member t of the lane's team) ----------------
+    const int t = kind - sj.n_stage;
     for (int m = 0;; ++m) {
       const int c = lane + L * m;
       if (c >= ntl) break;
@@ -197,14 +251,14 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
         // loads that saw the release stores synchronizes with each of them,
         // and an acquire invalidates the XCD's L2, so one is enough
         for (int k = 0; k < sj.n_stage && ok; ++k)
-          if (!snac::wait_geq<uint64_t, false>(slot_ref(sp, ring0 + k, slot).ready, tag(e, round + 1), p))
+          if (!snac::wait_geq<uint64_t, false>(slot_ref(sp, ring0 + k, slot).ready, tag(e, round + 1), p, e))
             ok = 0;
         if (sj.n_stage > 0 && ok) snac::acquire_fence();
         if (sj.n_scatter > 0 && ok) {
           const SlotRef o = slot_ref(sp, ring0 + sj.n_stage, slot);
           if (round == 0) {
             __hip_atomic_store(o.credit, tag(e, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } else if (!snac::wait_geq<uint64_t, false>(o.credit, tag(e, round * sj.n_scatter), p)) {
+          } else if (!snac::wait_geq<uint64_t, false>(o.credit, tag(e, round * sj.n_scatter), p, e)) {
             ok = 0;
           }
         }
@@ -250,15 +304,15 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       if (team > 1) {
         const uint32_t len = uint32_t(x1 - x0);  // a tile is at most 64 MiB + 128 bytes
         const uint32_t part = ((len + uint32_t(team) - 1u) / uint32_t(team) + 127u) & ~127u;
-        auto split = [&](int t) -> uint32_t {
-          if (t == 0) return 0u;
-          uint32_t y = uint32_t(t) * part;
+        auto split = [&](int q) -> uint32_t {
+          if (q == 0) return 0u;
+          uint32_t y = uint32_t(q) * part;
           y += (128u - uint32_t((b0 + uint64_t(x0) + y) & 127u)) & 127u;
           return y < len ? y : len;
         };
-        const uint32_t a = uint32_t(__builtin_amdgcn_readfirstlane(int(split(kind))));
-        const uint32_t z = kind + 1 == team ? len
-                                            : uint32_t(__builtin_amdgcn_readfirstlane(int(split(kind + 1))));
+        const uint32_t a = uint32_t(__builtin_amdgcn_readfirstlane(int(split(t))));
+        const uint32_t z = t + 1 == team ? len
+                                         : uint32_t(__builtin_amdgcn_readfirstlane(int(split(t + 1))));
         y0 = x0 + int64_t(a);
         y1 = x0 + int64_t(z);
       }
@@ -268,51 +322,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
         for (int k = 0; k < sj.n_stage; ++k)
           snac::add_rlx(slot_ref(sp, ring0 + k, slot).credit, uint64_t(1));
         if (sj.n_scatter > 0)
-          snac::store_rel(slot_ref(sp, ring0 + sj.n_stage, slot).ready + kind, tag(e, round + 1));
-      }
-    }
-  } else if (kind < team + sj.n_stage) {
-    // ---------------- stager ----------------
-    const int k = kind - team;
-    const int src = jb.src >= 0 ? jb.src : (k < owner ? k : k + 1);
-    const int ring = ring0 + k;
-    for (int m = 0;; ++m) {
-      const int c = lane + L * m;
-      if (c >= ntl) break;
-      const int slot = m % D;
-      const uint64_t round = uint64_t(m / D);
-      const SlotRef o = slot_ref(sp, ring, slot);
-      if (threadIdx.x == 0) {
-        // every owner of the team returns one credit per round
-        if (round == 0) {
-          __hip_atomic_store(o.credit, tag(e, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else if (!snac::wait_geq<uint64_t, false>(o.credit, tag(e, round * uint64_t(team)), p)) {
-          ok = 0;
-        }
-      }
-      __syncthreads();
-      if (!ok) break;
-      int64_t x0, x1;
-      tile_bounds(b0, jb.nbytes, p.chunk_bytes, c, ntl, x0, x1);
-      atom::Srcs s;
-      s.n = 1;
-      const uint64_t a = uint64_t(p.in[src]) + uint64_t(jb.src_off);
-#pragma unroll
-      for (int i = 0; i < kMaxRanks; ++i) s.a[i] = a;
-      atom::Dsts d;
-      d.n = 1;
-#pragma unroll
-      for (int q = 0; q < kMaxRanks + 1; ++q) d.b[q] = slot_base(o.data, b0, x0);
-      atom::tile<atom::CopyOp, kU, kNTL>(s, d, x0, x1);
-      // Every wavefront's stores must be acknowledged before thread 0's
-      // release publishes the slot: a workgroup barrier alone does not wait
-      // for other wavefronts' global stores (their head and tail element
-      // passes run on wavefronts 2 and 3), so the release could overtake
-      // them and the owner read a stale line.
-      snac::drain_workgroup();
-      if (threadIdx.x == 0) {
-        const bool withhold = sp.withhold > 0 && ring == 0 && m + 1 == sp.withhold;
-        if (!withhold) snac::store_rel(o.ready, tag(e, round + 1));
+          snac::store_rel(slot_ref(sp, ring0 + sj.n_stage, slot).ready + t, tag(e, round + 1));
       }
     }
   } else {
@@ -329,8 +339,8 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       // the chunk is whole once every owner of the team has notified;
       // relaxed polls, then one acquire (as in the owner)
       if (threadIdx.x == 0) {
-        for (int t = 0; t < team && ok; ++t)
-          if (!snac::wait_geq<uint64_t, false>(o.ready + t, tag(e, round + 1), p)) ok = 0;
+        for (int q = 0; q < team && ok; ++q)
+          if (!snac::wait_geq<uint64_t, false>(o.ready + q, tag(e, round + 1), p, e)) ok = 0;
         if (ok) snac::acquire_fence();
       }
       __syncthreads();
@@ -351,7 +361,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       if (threadIdx.x == 0) snac::add_rlx(o.credit, uint64_t(1));
     }
   }
-  if (p.sync) snac::exit_notify(p);
+  snac::exit_notify(p, e);
 }
 
 // ---- MoE dispatch / combine --------------------------------------------------
@@ -371,7 +381,12 @@ __device__ __forceinline__ void flag_bad_arg(const LaunchPlan &p) {
 template <int kU, bool kNT, bool kRows>
 __global__ void __launch_bounds__(kThreads) moe_dispatch_kernel(const MoePlan m) {
   const LaunchPlan &p = m.base;
-  const bool run = !p.sync || snac::entry(p);
+  uint32_t e = 0;
+  bool run = true;
+  if (p.sync) {
+    e = snac::launch_epoch(p);
+    run = snac::entry(p, e);
+  }
   int t = run ? int(blockIdx.x) : p.total_tiles;
   int q = t < p.total_tiles ? job_of_tile(p, t) : 0;
   for (; t < p.total_tiles; t += gridDim.x) {
@@ -395,17 +410,20 @@ __global__ void __launch_bounds__(kThreads) moe_dispatch_kernel(const MoePlan m)
     for (int r = 0; r < kMaxRanks + 1; ++r) d.b[r] = b;
     atom::tile<atom::CopyOp, kU, kNT, true, kRows>(s, d, 0, m.row_bytes, true);
   }
-  if (p.sync) snac::exit_notify(p);
+  if (p.sync) snac::exit_notify(p, e);
 }
 
 // Dispatch with one row per (token, destination rank), after the inverse
 // pass below: one tile per token row, read once and written to every rank
 // the token goes to (a broadcast with the token's own destination set).
 // Rows and buffers are 16-byte aligned, so the destinations are congruent.
+// It reads the epoch the inverse pass wrote its entries with, and its last
+// workgroup advances it, so the next call's entries carry a new one.
 template <int kU, bool kNT>
 __global__ void __launch_bounds__(kThreads) moe_dispatch_tokens_kernel(const MoePlan m) {
   const LaunchPlan &p = m.base;
-  const bool run = !p.sync || snac::entry(p);
+  const uint32_t e = snac::launch_epoch(p);
+  const bool run = !p.sync || snac::entry(p, e);
   const int64_t rows = m.inv_base[p.P];
   for (int64_t r = run ? int64_t(blockIdx.x) : rows; r < rows; r += gridDim.x) {
     int i = 0;
@@ -419,7 +437,7 @@ __global__ void __launch_bounds__(kThreads) moe_dispatch_tokens_kernel(const Moe
       d.b[j] = 0;
       if (j < p.P) {
         const uint64_t v = m.inv[(m.inv_base[i] + t) * p.P + j];
-        if (uint32_t(v >> 32) == p.epoch) {
+        if (uint32_t(v >> 32) == e) {
           const int64_t k = int64_t(uint32_t(v)) - 1;
           d.b[j] = uint64_t(p.out[j]) + uint64_t(p.jobs[i * p.P + j].dst_off) +
                    uint64_t(k) * uint64_t(m.row_bytes);
@@ -450,15 +468,18 @@ __global__ void __launch_bounds__(kThreads) moe_dispatch_tokens_kernel(const Moe
     for (int q = 0; q < kMaxRanks; ++q) s.a[q] = a;
     atom::tile<atom::CopyOp, kU, kNT, true, false>(s, d, 0, m.row_bytes, true);
   }
-  if (p.sync) snac::exit_notify(p);
+  snac::exit_notify(p, e);
 }
 
 // Combine, first pass: for every entry (i, j, k) the slot (token, j) of
 // rank i's table gets (epoch, k + 1).  Entries of earlier launches carry an
 // older epoch, so the table is never cleared; a slot already holding this
-// launch's epoch is a token twice in one group, which is reported.
+// launch's epoch is a token twice in one group, which is reported.  The
+// pass does not count its exit: the kernel after it reads the same epoch
+// and advances it.
 __global__ void __launch_bounds__(kThreads) moe_inverse_kernel(const MoePlan m) {
   const LaunchPlan &p = m.base;
+  const uint32_t epoch = snac::launch_epoch(p);
   const int64_t total = m.ent_base[p.P];
   for (int64_t e = int64_t(blockIdx.x) * kThreads + threadIdx.x; e < total;
        e += int64_t(gridDim.x) * kThreads) {
@@ -475,10 +496,10 @@ __global__ void __launch_bounds__(kThreads) moe_inverse_kernel(const MoePlan m) 
       flag_bad_arg(p);
       continue;
     }
-    const uint64_t v = (uint64_t(p.epoch) << 32) | uint64_t(k + 1);
+    const uint64_t v = (uint64_t(epoch) << 32) | uint64_t(k + 1);
     const uint64_t old = __hip_atomic_exchange(&m.inv[(m.inv_base[i] + tok) * p.P + j], v,
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (uint32_t(old >> 32) == p.epoch) flag_bad_arg(p);
+    if (uint32_t(old >> 32) == epoch) flag_bad_arg(p);
   }
 }
 
@@ -491,7 +512,8 @@ template <int kU, bool kNT>
 __global__ void __launch_bounds__(kThreads) moe_combine_kernel(const MoePlan m) {
 #pragma clang fp contract(off)
   const LaunchPlan &p = m.base;
-  const bool run = !p.sync || snac::entry(p);
+  const uint32_t e = snac::launch_epoch(p);
+  const bool run = !p.sync || snac::entry(p, e);
   const int64_t rows = m.inv_base[p.P];
   const uint32_t nunits = uint32_t(m.row_bytes >> 4);
   for (int64_t r = run ? int64_t(blockIdx.x) : rows; r < rows; r += gridDim.x) {
@@ -510,7 +532,7 @@ __global__ void __launch_bounds__(kThreads) moe_combine_kernel(const MoePlan m) 
       wt[j] = 0.0f;
       if (j < p.P) {
         const uint64_t v = m.inv[(m.inv_base[i] + t) * p.P + j];
-        if (uint32_t(v >> 32) == p.epoch) {
+        if (uint32_t(v >> 32) == e) {
           const int64_t k = int64_t(uint32_t(v)) - 1;
           const Job jb = p.jobs[i * p.P + j];
           on[j] = true;
@@ -555,7 +577,7 @@ __global__ void __launch_bounds__(kThreads) moe_combine_kernel(const MoePlan m) 
       }
     }
   }
-  if (p.sync) snac::exit_notify(p);
+  snac::exit_notify(p, e);
 }
 
 // ---- Ulysses strided exchange -----------------------------------------------
@@ -587,7 +609,12 @@ template <int kUnit, int kU, bool kNTS = true>
 __global__ void __launch_bounds__(kThreads) strided_kernel(const StridedPlan sp) {
   typedef typename UnitOf<kUnit>::T T;
   const LaunchPlan &p = sp.base;
-  const bool run = !p.sync || snac::entry(p);
+  uint32_t e = 0;
+  bool run = true;
+  if (p.sync) {
+    e = snac::launch_epoch(p);
+    run = snac::entry(p, e);
+  }
   const uint32_t per_row = uint32_t(sp.row_bytes / kUnit);
   const int64_t per_tile = p.chunk_bytes / kUnit;
   int t = run ? int(blockIdx.x) : p.total_tiles;
@@ -640,7 +667,7 @@ __global__ void __launch_bounds__(kThreads) strided_kernel(const StridedPlan sp)
       atom::drain_vm();
     }
   }
-  if (p.sync) snac::exit_notify(p);
+  if (p.sync) snac::exit_notify(p, e);
 }
 
 // ---- calibration copy ------------------------------------------------------

@@ -19,22 +19,25 @@ constexpr int kThreads = 256;           // 4 wavefronts of 64
 constexpr int kFlagStride = 32;          // u32 words between flags (128 bytes)
 // The exit count of a launch is spread over this many counters (workgroup b
 // counts on b % kExitSlots): one counter taking an atomic add from each of
-// ~1000 workgroups serialises them, measured at ~18 us per launch.
+// ~1000 workgroups serialises them, measured at ~18 us per launch.  The
+// workgroup that completes a counter then adds one to a second-level
+// counter, and the one that completes that is the launch's last.
 constexpr int kExitSlots = 32;
 
-// Flag block layout (u32 words, each flag on its own 128-byte line).
+// Flag block of one stream's workspace (u32 words, each flag on its own
+// 128-byte line).  The block starts zeroed.
 enum FlagWord : int {
-  kFlagEntry = 0,                                            // kMaxRanks entry epochs
-  kFlagExit = kMaxRanks * kFlagStride,                       // 2 x kExitSlots exit counters
-  kFlagStatus = (kMaxRanks + 2 * kExitSlots) * kFlagStride,  // sticky device status bits
-  kFlagAbort = (kMaxRanks + 2 * kExitSlots + 1) * kFlagStride,  // epoch of an aborted launch
-  kFlagWords = (kMaxRanks + 2 * kExitSlots + 2) * kFlagStride,
+  kFlagEntry = 0,                                         // kMaxRanks entry epochs
+  kFlagExit = kMaxRanks * kFlagStride,                    // kExitSlots exit counters
+  kFlagExitTop = (kMaxRanks + kExitSlots) * kFlagStride,  // completed exit counters
+  kFlagEpoch = (kMaxRanks + kExitSlots + 1) * kFlagStride,   // epoch of the next launch, minus one
+  kFlagStatus = (kMaxRanks + kExitSlots + 2) * kFlagStride,  // sticky device status bits
+  kFlagAbort = (kMaxRanks + kExitSlots + 3) * kFlagStride,   // epoch of an aborted launch
+  kFlagWords = (kMaxRanks + kExitSlots + 4) * kFlagStride,
 };
 
-// Word of exit counter `slot` of epoch parity `parity`.
-constexpr int exit_word(uint32_t parity, int slot) {
-  return kFlagExit + (int(parity) * kExitSlots + slot) * kFlagStride;
-}
+// Word of exit counter `slot`.
+constexpr int exit_word(int slot) { return kFlagExit + slot * kFlagStride; }
 constexpr uint32_t kStatusTimeout = 1u;
 constexpr uint32_t kStatusBadArg = 2u;   // a device-side argument check failed (MoE indices)
 
@@ -61,19 +64,18 @@ struct StagedJob {
 struct LaunchPlan {
   const char *in[kMaxRanks];
   char *out[kMaxRanks];
-  uint32_t *flags;          // kFlagWords u32 words
+  uint32_t *flags;          // the stream's flag block (kFlagWords u32 words), or null for a
+                            // launch that uses no flag (zero staging without the handshake)
   int32_t P;
   int32_t njobs;
   int32_t total_tiles;
-  uint32_t epoch;           // increases by one per launch on a device
+  int32_t sync;             // 1: entry / exit notify (the full per-rank handshake)
   int64_t chunk_bytes;      // bytes per tile (multiple of 4096)
   uint64_t watchdog_ticks;  // bound of every spin wait, in wall-clock ticks
-  int32_t sync;             // 1: entry/exit notify flags on
   int32_t nt_any_phase;     // 1: nontemporal loads even for sources off the line phase
   int32_t wide_max;         // tiles up to this many bytes that would take a row body
                             // take one wide element pass instead (0: never)
   int32_t tile_begin[kMaxJobs + 1];
-  uint32_t exit_expect[kExitSlots];  // exit counters after the previous launch (sync)
   Job jobs[kMaxJobs];
 };
 

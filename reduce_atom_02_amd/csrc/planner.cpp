@@ -286,8 +286,8 @@ purlin_status derive_cached(purlin_naming in_naming, purlin_naming out_naming, p
   return PURLIN_OK;
 }
 
-void launch_jobs(const Derived &d, char *const *out, std::vector<Job> *jobs,
-                 std::vector<int> *owner) {
+purlin_status launch_jobs(const Derived &d, char *const *out, std::vector<Job> *jobs,
+                          std::vector<int> *owner) {
   jobs->clear();
   owner->clear();
   for (size_t k = 0; k < d.jobs.size(); ++k) {
@@ -310,6 +310,16 @@ void launch_jobs(const Derived &d, char *const *out, std::vector<Job> *jobs,
       }
     }
   }
+  // A launch plan holds kMaxJobs jobs.  The seven collectives stay within it
+  // (at most P * P after the split); a sum of P partitions broadcast to every
+  // rank (by_index -> by_index) with outputs off each other's 16-byte phase
+  // would need P^3.
+  if (jobs->size() > size_t(kMaxJobs)) {
+    jobs->clear();
+    owner->clear();
+    return PURLIN_ERR_UNSUPPORTED;
+  }
+  return PURLIN_OK;
 }
 
 }  // namespace purlin

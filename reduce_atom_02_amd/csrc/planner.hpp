@@ -49,8 +49,9 @@ purlin_status derive_cached(purlin_naming in_naming, purlin_naming out_naming, p
 
 // The jobs of one launch: broadcast jobs whose destinations are not all
 // congruent modulo 16 bytes are split into one job per destination.
-void launch_jobs(const Derived &d, char *const *out, std::vector<Job> *jobs,
-                 std::vector<int> *owner);
+// UNSUPPORTED (and no jobs) when the split would exceed kMaxJobs.
+purlin_status launch_jobs(const Derived &d, char *const *out, std::vector<Job> *jobs,
+                          std::vector<int> *owner);
 
 int name_count(purlin_naming n, int P);
 

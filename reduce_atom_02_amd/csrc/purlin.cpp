@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <vector>
 
 #include "kernels.hpp"
@@ -22,19 +23,31 @@ constexpr int kMaxLanes = 32;
 constexpr int kOwnerTeam = 8;
 constexpr int kMaxTeam = 8;
 
-struct DeviceState {
-  bool ready = false;
-  int cus = 0;
-  uint64_t wall_khz = 0;
+// Library workspace of one stream: the flag block (entry flags, exit
+// counters, epoch, status, abort) and, when a call needs them, the staging
+// rings with their slot flags and the MoE inverse table.  Calls on one
+// stream run one after another (stream order), so they may share it; calls
+// on different streams use different workspaces and never wait for each
+// other.
+struct StreamCtx {
+  hipStream_t stream = nullptr;
   uint32_t *flags = nullptr;
   char *ring = nullptr;
   int64_t ring_bytes = 0;
   uint64_t *slot_flags = nullptr;
   int64_t slot_flag_bytes = 0;
-  uint64_t *inv = nullptr;     // MoE combine: (token, destination rank) -> tagged entry
+  uint64_t *inv = nullptr;     // MoE: (token, destination rank) -> tagged entry
   int64_t inv_bytes = 0;
-  uint32_t epoch = 0;
-  uint32_t exit_total[2][kExitSlots] = {};  // per parity and slot, all launches so far
+};
+
+struct DeviceState {
+  bool ready = false;
+  int cus = 0;
+  uint64_t wall_khz = 0;
+  std::vector<std::unique_ptr<StreamCtx>> ctx;
+  // Outgrown workspace: launches enqueued earlier, or HIP graphs captured
+  // earlier, may still use it, so it is freed only by purlin_release.
+  std::vector<void *> retired;
   int occ[3][2][2][3][2][2][2][2] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
 };
 
@@ -116,18 +129,61 @@ purlin_status device_state(DeviceState **out) {
     s.wall_khz = uint64_t(khz > 0 ? khz : 100000);
     s.ready = true;
   }
-  if (!s.flags) {
-    void *f = nullptr;
-    if (hipMalloc(&f, kFlagWords * sizeof(uint32_t)) != hipSuccess) return PURLIN_ERR_NO_MEMORY;
-    if (hipMemset(f, 0, kFlagWords * sizeof(uint32_t)) != hipSuccess) {
-      (void)hipFree(f);
-      return PURLIN_ERR_HIP;
-    }
-    s.flags = static_cast<uint32_t *>(f);
-    for (auto &par : s.exit_total)
-      for (uint32_t &v : par) v = 0;
-  }
   *out = &s;
+  return PURLIN_OK;
+}
+
+// Nothing is allocated or cleared on a stream that is being captured into a
+// HIP graph: a call that would need that returns UNSUPPORTED.
+purlin_status refuse_if_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return PURLIN_ERR_HIP;
+  return cs == hipStreamCaptureStatusNone ? PURLIN_OK : PURLIN_ERR_UNSUPPORTED;
+}
+
+StreamCtx *find_ctx(DeviceState &ds, hipStream_t stream) {
+  for (auto &c : ds.ctx)
+    if (c->stream == stream) return c.get();
+  return nullptr;
+}
+
+// The stream's workspace, created on its first call that needs one: the flag
+// block is allocated and cleared in stream order (no device synchronization).
+purlin_status stream_ctx(DeviceState &ds, hipStream_t stream, StreamCtx **out) {
+  if ((*out = find_ctx(ds, stream))) return PURLIN_OK;
+  purlin_status st = refuse_if_capturing(stream);
+  if (st != PURLIN_OK) return st;
+  void *f = nullptr;
+  const size_t bytes = size_t(kFlagWords) * sizeof(uint32_t);
+  if (hipMalloc(&f, bytes) != hipSuccess) return PURLIN_ERR_NO_MEMORY;
+  if (hipMemsetAsync(f, 0, bytes, stream) != hipSuccess) {
+    ds.retired.push_back(f);
+    return PURLIN_ERR_HIP;
+  }
+  auto c = std::make_unique<StreamCtx>();
+  c->stream = stream;
+  c->flags = static_cast<uint32_t *>(f);
+  ds.ctx.push_back(std::move(c));
+  *out = ds.ctx.back().get();
+  return PURLIN_OK;
+}
+
+// Grow a workspace buffer to `want` bytes: a new allocation (cleared in
+// stream order when `zero`), the old one retired.
+purlin_status grow(DeviceState &ds, hipStream_t stream, void **buf, int64_t *have, int64_t want,
+                   bool zero) {
+  if (want <= *have) return PURLIN_OK;
+  purlin_status st = refuse_if_capturing(stream);
+  if (st != PURLIN_OK) return st;
+  void *b = nullptr;
+  if (hipMalloc(&b, size_t(want)) != hipSuccess) return PURLIN_ERR_NO_MEMORY;
+  if (zero && hipMemsetAsync(b, 0, size_t(want), stream) != hipSuccess) {
+    ds.retired.push_back(b);
+    return PURLIN_ERR_HIP;
+  }
+  if (*buf) ds.retired.push_back(*buf);
+  *buf = b;
+  *have = want;
   return PURLIN_OK;
 }
 
@@ -145,52 +201,18 @@ int occupancy(DeviceState &s, KernelKind kind, bool staged, bool nt, int unroll_
   return o;
 }
 
-purlin_status ensure_staging(DeviceState &s, int64_t ring_bytes, int64_t flag_bytes) {
-  if (ring_bytes <= s.ring_bytes && flag_bytes <= s.slot_flag_bytes) return PURLIN_OK;
-  // A previous launch may still read the old ring: finish all work first.
-  if (hipDeviceSynchronize() != hipSuccess) return PURLIN_ERR_HIP;
-  if (ring_bytes > s.ring_bytes) {
-    if (s.ring) (void)hipFree(s.ring);
-    s.ring = nullptr;
-    s.ring_bytes = 0;
-    void *r = nullptr;
-    if (hipMalloc(&r, size_t(ring_bytes)) != hipSuccess) return PURLIN_ERR_NO_MEMORY;
-    s.ring = static_cast<char *>(r);
-    s.ring_bytes = ring_bytes;
-  }
-  if (flag_bytes > s.slot_flag_bytes) {
-    if (s.slot_flags) (void)hipFree(s.slot_flags);
-    s.slot_flags = nullptr;
-    s.slot_flag_bytes = 0;
-    void *f = nullptr;
-    if (hipMalloc(&f, size_t(flag_bytes)) != hipSuccess) return PURLIN_ERR_NO_MEMORY;
-    if (hipMemset(f, 0, size_t(flag_bytes)) != hipSuccess) {
-      (void)hipFree(f);
-      return PURLIN_ERR_HIP;
-    }
-    s.slot_flags = static_cast<uint64_t *>(f);
-    s.slot_flag_bytes = flag_bytes;
-  }
-  return PURLIN_OK;
+purlin_status ensure_staging(DeviceState &ds, StreamCtx &c, int64_t ring_bytes, int64_t flag_bytes) {
+  purlin_status st = grow(ds, c.stream, reinterpret_cast<void **>(&c.ring), &c.ring_bytes,
+                          ring_bytes, false);
+  if (st != PURLIN_OK) return st;
+  return grow(ds, c.stream, reinterpret_cast<void **>(&c.slot_flags), &c.slot_flag_bytes,
+              flag_bytes, true);
 }
 
-// The MoE combine's inverse table, zeroed when (re)allocated; its entries
-// carry the launch epoch, so it is never cleared again.
-purlin_status ensure_inverse(DeviceState &s, int64_t bytes) {
-  if (bytes <= s.inv_bytes) return PURLIN_OK;
-  if (hipDeviceSynchronize() != hipSuccess) return PURLIN_ERR_HIP;  // a launch may still use it
-  if (s.inv) (void)hipFree(s.inv);
-  s.inv = nullptr;
-  s.inv_bytes = 0;
-  void *f = nullptr;
-  if (hipMalloc(&f, size_t(bytes)) != hipSuccess) return PURLIN_ERR_NO_MEMORY;
-  if (hipMemset(f, 0, size_t(bytes)) != hipSuccess) {
-    (void)hipFree(f);
-    return PURLIN_ERR_HIP;
-  }
-  s.inv = static_cast<uint64_t *>(f);
-  s.inv_bytes = bytes;
-  return PURLIN_OK;
+// The MoE inverse table, cleared when (re)allocated; its entries carry the
+// launch epoch, so it is never cleared again.
+purlin_status ensure_inverse(DeviceState &ds, StreamCtx &c, int64_t bytes) {
+  return grow(ds, c.stream, reinterpret_cast<void **>(&c.inv), &c.inv_bytes, bytes, true);
 }
 
 KernelKind kind_of(purlin_op op, purlin_dtype dtype) {
@@ -335,22 +357,15 @@ purlin_status moe_plan(void *const *rowsrc, void *const *rowdst, int P, int64_t 
   return PURLIN_OK;
 }
 
-// The launch-wide fields of an MoE or strided plan: flags, epoch, watchdog
-// and handshake.
-void side_launch_fields(DeviceState &ds, LaunchPlan &lp, const purlin_policy &pol) {
-  if (++ds.epoch == 0) ds.epoch = 1;
-  lp.flags = ds.flags;
-  lp.epoch = ds.epoch;
+// The launch-wide fields: flag block, watchdog and handshake.  The
+// handshake (entry / exit notify) is off unless the policy asks for it:
+// calls on one stream are already ordered by the stream.
+void launch_fields(const DeviceState &ds, LaunchPlan &lp, const purlin_policy &pol,
+                   uint32_t *flags) {
+  lp.flags = flags;
   const int64_t wd_ns = pol.watchdog_ns ? pol.watchdog_ns : kDefaultWatchdogNs;
   lp.watchdog_ticks = uint64_t(wd_ns) * ds.wall_khz / 1000000u + 1;
-  lp.sync = pol.sync == 2 ? 0 : 1;
-  for (int k = 0; k < kExitSlots; ++k) lp.exit_expect[k] = ds.exit_total[(ds.epoch - 1u) & 1u][k];
-}
-
-void side_count_exit(DeviceState &ds, const LaunchPlan &lp, int grid) {
-  if (!lp.sync) return;
-  for (int k = 0; k < kExitSlots; ++k)
-    ds.exit_total[lp.epoch & 1u][k] += uint32_t(grid / kExitSlots + (k < grid % kExitSlots ? 1 : 0));
+  lp.sync = pol.sync == 1 ? 1 : 0;
 }
 
 // Divisor d of the strided kernel's row lookup: floor(u / d) = (u * m) >> s
@@ -500,6 +515,12 @@ purlin_status purlin_plan_describe(const purlin_layout *in, const purlin_layout 
   if (s != PURLIN_OK) return s;
   s = check_pointers(*d, in->bufs, out->bufs);
   if (s != PURLIN_OK) return s;
+  if (!d->jobs.empty()) {
+    std::vector<Job> jobs;
+    std::vector<int> owners;
+    s = launch_jobs(*d, reinterpret_cast<char *const *>(out->bufs), &jobs, &owners);
+    if (s != PURLIN_OK) return s;
+  }
   const int64_t n = int64_t(d->segs.size());
   if (segs) {
     const int64_t m = std::min<int64_t>(*n_segs, n);
@@ -526,13 +547,21 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     ptrs[r] = in->bufs[r];
     ptrs[kMaxRanks + r] = out->bufs[r];
   }
-  if (d->id != last_id || std::memcmp(ptrs, last_ptrs, sizeof(ptrs)) != 0) {
+  const bool same_call = d->id == last_id && std::memcmp(ptrs, last_ptrs, sizeof(ptrs)) == 0;
+  if (!same_call) {
     st = check_pointers(*d, in->bufs, out->bufs);
     if (st != PURLIN_OK) return st;
+  }
+  if (d->jobs.empty()) return PURLIN_OK;  // every partition is empty
+
+  std::vector<Job> jobs;
+  std::vector<int> owners;
+  st = launch_jobs(*d, reinterpret_cast<char *const *>(out->bufs), &jobs, &owners);
+  if (st != PURLIN_OK) return st;
+  if (!same_call) {
     last_id = d->id;
     std::memcpy(last_ptrs, ptrs, sizeof(ptrs));
   }
-  if (d->jobs.empty()) return PURLIN_OK;  // every partition is empty
 
   DeviceState *ds = nullptr;
   st = device_state(&ds);
@@ -540,10 +569,6 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
   const purlin_policy pol = effective_policy();
   const KernelKind kind = kind_of(op, dtype);
   const bool nt = nt_env(true);
-
-  std::vector<Job> jobs;
-  std::vector<int> owners;
-  launch_jobs(*d, reinterpret_cast<char *const *>(out->bufs), &jobs, &owners);
 
   const bool staged = pol.zero_staging == PURLIN_STAGING_STAGED;
   bool broadcast = false;
@@ -593,18 +618,21 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
   const int capacity =
       ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows, one, wide, bcast);
 
-  if (++ds->epoch == 0) ds->epoch = 1;  // epoch 0 would match freshly cleared flags
-  const int64_t wd_ns = pol.watchdog_ns ? pol.watchdog_ns : kDefaultWatchdogNs;
+  // The stream's flag block: for the staged kernel and for the handshake;
+  // a zero-staging launch without the handshake touches no flag at all.
+  StreamCtx *ctx = nullptr;
+  if (staged || pol.sync == 1) {
+    st = stream_ctx(*ds, stream, &ctx);
+    if (st != PURLIN_OK) return st;
+  }
 
   LaunchPlan lp{};
   for (int r = 0; r < kMaxRanks; ++r) {
     lp.in[r] = r < P ? static_cast<const char *>(in->bufs[r]) : nullptr;
     lp.out[r] = r < P ? static_cast<char *>(out->bufs[r]) : nullptr;
   }
-  lp.flags = ds->flags;
   lp.P = P;
-  lp.epoch = ds->epoch;
-  lp.watchdog_ticks = uint64_t(wd_ns) * ds->wall_khz / 1000000u + 1;
+  launch_fields(*ds, lp, pol, ctx ? ctx->flags : nullptr);
 
   purlin_launch_info info{};
   info.threads = kThreads;
@@ -620,7 +648,6 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     lp.chunk_bytes = chunk;
     fill_tiles(lp, jobs, chunk);
     const int grid = int(std::max<int64_t>(1, std::min<int64_t>(lp.total_tiles, want_grid)));
-    lp.sync = pol.sync == 2 ? 0 : 1;
     // Nontemporal loads pay off for sources off the destination's line
     // phase too (variable-length partitions), measured at 16 MiB - 1 GiB.
     lp.nt_any_phase = env_i64("PURLIN_NT_ANY_PHASE", 1) ? 1 : 0;
@@ -629,14 +656,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     // body (ReduceScatterV at 8 - 16 KiB per rank: 8.9 us against 10.3 us);
     // from 1 MiB per rank on, the row body is faster.
     lp.wide_max = (wide && small && chunk <= 4096) ? int32_t(chunk + 128) : 0;
-    for (int k = 0; k < kExitSlots; ++k) lp.exit_expect[k] = ds->exit_total[(ds->epoch - 1u) & 1u][k];
     err = launch_zs(lp, kind, nt, unroll_sel, rows, one, wide, bcast, grid, stream);
-    if (err == hipSuccess && lp.sync) {
-      // workgroup b counts on slot b % kExitSlots
-      for (int k = 0; k < kExitSlots; ++k)
-        ds->exit_total[ds->epoch & 1u][k] +=
-            uint32_t(grid / kExitSlots + (k < grid % kExitSlots ? 1 : 0));
-    }
     info.grid = grid;
     info.zero_staging = 1;
     info.rows = rows ? 1 : 0;
@@ -697,19 +717,11 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
     sp.total_roles = role;
     const int64_t ring_bytes = std::max<int64_t>(1, int64_t(ring) * sp.depth * sp.slot_stride);
     const int64_t flag_bytes = std::max<int64_t>(256, int64_t(ring) * sp.depth * 256);
-    st = ensure_staging(*ds, ring_bytes, flag_bytes);
+    st = ensure_staging(*ds, *ctx, ring_bytes, flag_bytes);
     if (st != PURLIN_OK) return st;
-    sp.ring = ds->ring;
-    sp.slot_flags = ds->slot_flags;
-    sp.base.sync = pol.sync == 2 ? 0 : 1;
-    for (int k = 0; k < kExitSlots; ++k)
-      sp.base.exit_expect[k] = ds->exit_total[(ds->epoch - 1u) & 1u][k];
+    sp.ring = ctx->ring;
+    sp.slot_flags = ctx->slot_flags;
     err = launch_staged(sp, kind, nt, stream);
-    if (err == hipSuccess && sp.base.sync) {
-      const int g = sp.total_roles;
-      for (int k = 0; k < kExitSlots; ++k)
-        ds->exit_total[ds->epoch & 1u][k] += uint32_t(g / kExitSlots + (k < g % kExitSlots ? 1 : 0));
-    }
     info.grid = sp.total_roles;
     info.zero_staging = 0;
     info.rows = 1;
@@ -735,7 +747,10 @@ purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t
   DeviceState *ds = nullptr;
   st = device_state(&ds);
   if (st != PURLIN_OK) return st;
-  side_launch_fields(*ds, m.base, effective_policy());
+  StreamCtx *ctx = nullptr;  // the status word for index errors, epochs, the table
+  st = stream_ctx(*ds, stream, &ctx);
+  if (st != PURLIN_OK) return st;
+  launch_fields(*ds, m.base, effective_policy(), ctx->flags);
   bool rows = (row_bytes & 15) != 0;
   for (int r = 0; r < P; ++r)
     rows |= ((uintptr_t(x[r]) | uintptr_t(y[r])) & 15) != 0;
@@ -745,9 +760,9 @@ purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t
   if (by_token) {
     // each token row read once and written to all its ranks: the (token,
     // rank) -> entry table first
-    st = ensure_inverse(*ds, m.inv_base[P] * P * int64_t(sizeof(uint64_t)));
+    st = ensure_inverse(*ds, *ctx, m.inv_base[P] * P * int64_t(sizeof(uint64_t)));
     if (st != PURLIN_OK) return st;
-    m.inv = ds->inv;
+    m.inv = ctx->inv;
     const int g0 = moe_grid(*ds, MoeKernel::kInverse, false, (total + kThreads - 1) / kThreads,
                             int64_t(ds->cus) * 8);
     if (launch_moe(m, MoeKernel::kInverse, false, g0, stream) != hipSuccess) return PURLIN_ERR_HIP;
@@ -762,7 +777,6 @@ purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t
     grid = moe_grid(*ds, MoeKernel::kDispatch, rows, total, int64_t(ds->cus) * 4);
     if (launch_moe(m, MoeKernel::kDispatch, rows, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
   }
-  side_count_exit(*ds, m.base, grid);
   purlin_launch_info info{};
   info.grid = grid;
   info.threads = kThreads;
@@ -798,10 +812,13 @@ purlin_status purlin_moe_combine(void *const *y, void *const *out, int P, int64_
   DeviceState *ds = nullptr;
   st = device_state(&ds);
   if (st != PURLIN_OK) return st;
-  st = ensure_inverse(*ds, out_rows * P * int64_t(sizeof(uint64_t)));
+  StreamCtx *ctx = nullptr;
+  st = stream_ctx(*ds, stream, &ctx);
   if (st != PURLIN_OK) return st;
-  m.inv = ds->inv;
-  side_launch_fields(*ds, m.base, effective_policy());
+  st = ensure_inverse(*ds, *ctx, out_rows * P * int64_t(sizeof(uint64_t)));
+  if (st != PURLIN_OK) return st;
+  m.inv = ctx->inv;
+  launch_fields(*ds, m.base, effective_policy(), ctx->flags);
   m.base.chunk_bytes = row_bytes;
   if (total > 0) {
     const int g0 = moe_grid(*ds, MoeKernel::kInverse, false, (total + kThreads - 1) / kThreads,
@@ -810,7 +827,6 @@ purlin_status purlin_moe_combine(void *const *y, void *const *out, int P, int64_
   }
   const int grid = moe_grid(*ds, MoeKernel::kCombine, false, out_rows, int64_t(ds->cus) * 4);
   if (launch_moe(m, MoeKernel::kCombine, false, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
-  side_count_exit(*ds, m.base, grid);
   purlin_launch_info info{};
   info.grid = grid;
   info.threads = kThreads;
@@ -838,7 +854,12 @@ purlin_status purlin_ulysses(void *const *in, void *const *out, int P, const int
   st = device_state(&ds);
   if (st != PURLIN_OK) return st;
   const purlin_policy pol = effective_policy();
-  side_launch_fields(*ds, sp.base, pol);
+  StreamCtx *ctx = nullptr;
+  if (pol.sync == 1) {
+    st = stream_ctx(*ds, stream, &ctx);
+    if (st != PURLIN_OK) return st;
+  }
+  launch_fields(*ds, sp.base, pol, ctx ? ctx->flags : nullptr);
   // four workgroups per CU (two or three measured within 1% at the
   // Qwen-Image and 64 MiB shapes), 32 KiB tiles, smaller tiles for small
   // exchanges
@@ -865,7 +886,6 @@ purlin_status purlin_ulysses(void *const *in, void *const *out, int P, const int
   if (strided_resident_per_cu(unit, plain, &b) != hipSuccess || b < 1) b = 1;
   const int grid = int(std::max<int64_t>(1, std::min<int64_t>({t, cap, int64_t(ds->cus) * b})));
   if (launch_strided(sp, unit, plain, grid, stream) != hipSuccess) return PURLIN_ERR_HIP;
-  side_count_exit(*ds, sp.base, grid);
   purlin_launch_info info{};
   info.grid = grid;
   info.threads = kThreads;
@@ -887,9 +907,11 @@ purlin_status purlin_check(hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return PURLIN_ERR_HIP;
   auto &all = devices();
-  if (int(all.size()) <= dev || !all[dev].flags) return PURLIN_OK;
+  if (int(all.size()) <= dev) return PURLIN_OK;
+  StreamCtx *c = find_ctx(all[dev], stream);
+  if (!c) return PURLIN_OK;  // no call on this stream used a flag
   uint32_t status = 0;
-  uint32_t *word = all[dev].flags + kFlagStatus;
+  uint32_t *word = c->flags + kFlagStatus;
   if (hipMemcpy(&status, word, sizeof(status), hipMemcpyDeviceToHost) != hipSuccess)
     return PURLIN_ERR_HIP;
   if (status == 0) return PURLIN_OK;
@@ -942,18 +964,17 @@ void purlin_release(void) {
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
   for (size_t dev = 0; dev < all.size(); ++dev) {
     DeviceState &s = all[dev];
-    if (!s.flags && !s.ring && !s.slot_flags && !s.inv) continue;
+    if (s.ctx.empty() && s.retired.empty()) continue;
     if (hipSetDevice(int(dev)) != hipSuccess) continue;
     (void)hipDeviceSynchronize();
-    if (s.flags) (void)hipFree(s.flags);
-    if (s.ring) (void)hipFree(s.ring);
-    if (s.slot_flags) (void)hipFree(s.slot_flags);
-    if (s.inv) (void)hipFree(s.inv);
-    s.flags = nullptr;
-    s.ring = nullptr;
-    s.slot_flags = nullptr;
-    s.inv = nullptr;
-    s.ring_bytes = s.slot_flag_bytes = s.inv_bytes = 0;
+    for (auto &c : s.ctx) {
+      for (void *b : {static_cast<void *>(c->flags), static_cast<void *>(c->ring),
+                      static_cast<void *>(c->slot_flags), static_cast<void *>(c->inv)})
+        if (b) (void)hipFree(b);
+    }
+    for (void *b : s.retired) (void)hipFree(b);
+    s.ctx.clear();
+    s.retired.clear();
   }
   if (have_cur) (void)hipSetDevice(cur);
 }

@@ -19,6 +19,7 @@ __all__ = [
     "all_reduce", "reduce_scatter", "all_gather", "all_to_all", "check",
     "set_policy", "get_policy", "plan_describe", "last_launch", "stream_copy", "stream_pattern",
     "moe_dispatch", "moe_combine", "ulysses", "release", "exported_symbols",
+    "name_count", "extents", "check_tensors",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpurlin.so")
@@ -179,8 +180,9 @@ def _cached(key, make):
     return v
 
 
-def _layout(naming, bufs):
-    ptrs = tuple(map(_ptr, bufs))
+def _layout(naming, bufs, ptrs=None):
+    if ptrs is None:
+        ptrs = tuple(map(_ptr, bufs))
 
     def make():
         arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
@@ -197,6 +199,97 @@ def _i64(values):
                    lambda: (ctypes.c_int64 * max(1, len(vals)))(*map(int, vals)))
 
 
+_TORCH_DTYPES = {"torch.float32": "f32", "torch.bfloat16": "bf16"}
+_ESZ = {"f32": 4, "bf16": 2}
+
+
+def name_count(naming, P):
+    """Names of a naming at P ranks (the length of its counts array)."""
+    return 1 if naming == "whole" else (P if naming in ("by_rank", "by_index") else P * P)
+
+
+def extents(naming, P, counts, displs_side=None):
+    """Elements each rank's buffer must hold under `naming`: the end of its
+    last non-empty partition (counts and displacements indexed by name, as
+    in include/purlin.h; displs_side None means packed in index order)."""
+    ext = []
+    for r in range(P):
+        if naming == "whole":
+            names = (0,)
+        elif naming == "by_rank":
+            names = (r,)
+        elif naming == "by_index":
+            names = range(P)
+        elif naming == "by_rank_index":
+            names = [r * P + q for q in range(P)]
+        else:
+            names = [q * P + r for q in range(P)]
+        end = packed = 0
+        for nm in names:
+            c = int(counts[nm])
+            off = int(displs_side[nm]) if displs_side is not None else packed
+            packed += c
+            if c > 0:
+                end = max(end, off + c)
+        ext.append(end)
+    return ext
+
+
+def check_tensors(bufs, need, dt, op, what, device=None):
+    """Reject, before any GPU work, a tensor the library would misread:
+    not on the GPU `device` (None skips that check), not contiguous, of
+    another element type than the others or than `dt`, or smaller than the
+    `need` elements its rank's partitions reach.  Raw addresses (ints) and
+    None pass unchecked.  Raises ValueError."""
+    tdtype = None
+    for r, t in enumerate(bufs):
+        if t is None or isinstance(t, int):
+            continue
+        if device is not None and (not t.is_cuda or t.get_device() != device):
+            raise ValueError("%s %d is not on the current GPU (device %s)" % (what, r, t.device))
+        if not t.is_contiguous():
+            raise ValueError("%s %d is not contiguous" % (what, r))
+        if tdtype is None:
+            tdtype = t.dtype
+        elif t.dtype != tdtype:
+            raise ValueError("%s %d has dtype %s, another buffer %s" % (what, r, t.dtype, tdtype))
+        if t.element_size() != _ESZ[dt] or (op == "sum" and _TORCH_DTYPES.get(str(t.dtype)) != dt):
+            raise ValueError("%s %d has dtype %s, the collective %s" % (what, r, t.dtype, dt))
+        if t.numel() < need[r]:
+            raise ValueError("%s %d holds %d elements, its partitions reach %d"
+                             % (what, r, t.numel(), need[r]))
+
+
+_CHECKED = {}
+
+
+def _validate(ins, outs, pin, pout, in_naming, out_naming, op, dt, counts, displs):
+    """The binding's checks of one call (cached by buffers and plan); pin and
+    pout are the buffers' addresses."""
+    P = len(ins)
+    key = (in_naming, out_naming, op, dt, P, tuple(counts),
+           None if displs is None else tuple(displs), pin, pout,
+           tuple(None if t is None or isinstance(t, int) else (t.numel(), t.dtype)
+                 for t in itertools.chain(ins, outs)))
+    if key in _CHECKED:
+        return
+    nn = name_count(in_naming, P)
+    if len(counts) != nn:
+        raise ValueError("%s at P=%d takes %d counts, got %d" % (in_naming, P, nn, len(counts)))
+    if displs is not None and len(displs) != 2 * nn:
+        raise ValueError("displs takes %d entries, got %d" % (2 * nn, len(displs)))
+    if name_count(out_naming, P) == nn:
+        import torch
+        dev = torch.cuda.current_device() if torch.cuda.is_available() else -1
+        din = None if displs is None else displs[:nn]
+        dout = None if displs is None else displs[nn:]
+        check_tensors(ins, extents(in_naming, P, counts, din), dt, op, "input", dev)
+        check_tensors(outs, extents(out_naming, P, counts, dout), dt, op, "output", dev)
+    if len(_CHECKED) >= _CACHE_MAX:
+        _CHECKED.clear()
+    _CHECKED[key] = True
+
+
 def collective(ins, outs, in_naming, out_naming, op, counts, displs=None, dtype=None,
                stream=None):
     """Enqueue one collective on ``stream`` (torch's current stream by default).
@@ -204,13 +297,18 @@ def collective(ins, outs, in_naming, out_naming, op, counts, displs=None, dtype=
     ins, outs: P torch tensors or device addresses, one per rank.
     counts: one element count per name (see include/purlin.h).
     displs: None (packed) or input offsets then output offsets, by name.
+    Tensors are checked before the call (on the current GPU, contiguous, one
+    element type, large enough for their partitions): ValueError otherwise.
     """
     P = len(ins)
     if len(outs) != P:
         raise ValueError("need as many output buffers as input buffers")
     dt = _dtype_of(itertools.chain(ins, outs), dtype)
-    lin, keep_in = _layout(in_naming, ins)
-    lout, keep_out = _layout(out_naming, outs)
+    pin = tuple(map(_ptr, ins))
+    pout = tuple(map(_ptr, outs))
+    _validate(ins, outs, pin, pout, in_naming, out_naming, op, dt, counts, displs)
+    lin, keep_in = _layout(in_naming, ins, pin)
+    lout, keep_out = _layout(out_naming, outs, pout)
     c = _i64(counts)
     d = _i64(displs)
     status = _lib.purlin_collective(ctypes.byref(lin), ctypes.byref(lout), OPS[op], DTYPES[dt], P,

@@ -23,11 +23,18 @@
 // a wall-clock watchdog; on expiry it sets the status word and the launch's
 // abort epoch, and every other wait of that launch then gives up.
 //
-// Launches also run the zero-staging handshake: announcer r waits for the
-// exit counters of the previous launch (spread over several counters, each
-// workgroup adds 1 to counter b % S) and publishes entry[r] = epoch; every
-// workgroup waits for all entry flags before it starts and adds itself to
-// its exit counter when it is done.
+// The launch epoch lives in shared memory, as on the device: every workgroup
+// reads the epoch word when it starts (epoch = word + 1), and the last
+// workgroup to count itself out advances it.  The exit count is spread over
+// several counters (workgroup b adds 1 to counter b % S); the workgroup that
+// completes a counter resets it and adds 1 to a second-level counter, and
+// the one completing that resets it and stores the next epoch.  Launches run
+// one after another (stream order), and the host checks that every launch
+// advanced the epoch by exactly one.  Launches also run the handshake:
+// announcer r publishes entry[r] = epoch, and every workgroup waits for all
+// entry flags before it starts.  Workgroups are numbered as in the kernel:
+// per piece and lane the stagers, then the owners, then the scatter
+// consumers.
 //
 // Memory orders: a notify that publishes data is a release and its wait an
 // acquire, as on the GPU.  The GPU's "done reading" notifies (credits, exit
@@ -46,7 +53,10 @@
 // owner notifies its scatter ring before writing the slot, 3 a scatter
 // consumer returns its credit before copying the slot, 4 a scatter consumer
 // waits for the first owner of the team only, 5 a stager waits for one
-// owner's credit per round instead of the team's.
+// owner's credit per round instead of the team's, 6 the workgroup completing
+// an exit counter does not reset it (the next launch's count never
+// completes, so the epoch stops advancing and the flags of two launches
+// carry one epoch).
 // Exit status 0: every launch correct, or with withholding: the withheld
 // launch ended in TIMEOUT, every thread returned, and the launches after it
 // are correct again.
@@ -84,8 +94,9 @@ struct Model {
   std::vector<Flag> ready, credit;
   std::vector<Flag> team_ready;  // scatter slots: one ready word per owner of the team
   Flag entry[64];
-  Flag exits[2][kExitSlots];
-  uint64_t exit_total[2][kExitSlots] = {};
+  Flag exits[kExitSlots];
+  Flag exit_top;
+  std::atomic<uint32_t> epoch_word{0};
   std::atomic<uint32_t> status{0};
   std::atomic<uint32_t> abort_epoch{0};
   int withhold_launch = -1, withhold_chunk = -1;
@@ -214,20 +225,26 @@ struct Model {
     }
   }
 
-  // zero-staging handshake of one workgroup b of a grid of G
+  // the launch epoch a workgroup reads when it starts
+  uint32_t launch_epoch() const { return epoch_word.load(std::memory_order_acquire) + 1u; }
+  // handshake of one workgroup b of a grid of G
   bool entry_wait(int b, int G, uint32_t e, std::mt19937 &rng) {
-    if (b < P) {
-      const uint32_t prev = (e - 1u) & 1u;
-      for (int s = 0; s < kExitSlots; ++s)
-        if (!wait_geq(exits[prev][s].v, exit_total[prev][s], e, rng)) return false;
-      for (int r = b; r < P; r += G) entry[r].v.store(e, std::memory_order_release);
-    }
+    for (int r = b; r < P; r += G) entry[r].v.store(e, std::memory_order_release);
     for (int r = 0; r < P; ++r)
       if (!wait_geq(entry[r].v, e, e, rng)) return false;
     return true;
   }
-  void exit_notify(int b, uint32_t e) {
-    exits[e & 1u][b % kExitSlots].v.fetch_add(1, std::memory_order_release);
+  void exit_notify(int b, int G, uint32_t e) {
+    const int s = b % kExitSlots;
+    const uint64_t want = uint64_t(G / kExitSlots + (s < G % kExitSlots ? 1 : 0));
+    const uint64_t nslots = uint64_t(G < kExitSlots ? G : kExitSlots);
+    if (exits[s].v.fetch_add(1, std::memory_order_acq_rel) + 1 == want) {
+      if (mutation != 6) exits[s].v.store(0, std::memory_order_relaxed);
+      if (exit_top.v.fetch_add(1, std::memory_order_acq_rel) + 1 == nslots) {
+        exit_top.v.store(0, std::memory_order_relaxed);
+        epoch_word.store(e == 0xffffffffu ? 0u : e, std::memory_order_release);
+      }
+    }
   }
 };
 
@@ -270,14 +287,19 @@ int main(int argc, char **argv) {
 
   std::mt19937 rng(seed);
   int bad = 0;
-  uint32_t epoch = 0;
+  uint32_t last_epoch = 0;
   for (int launch = 0; launch < launches; ++launch) {
-    ++epoch;
+    const uint32_t before = M.launch_epoch();
+    if (before != last_epoch + 1) {
+      std::fprintf(stderr, "launch %d: epoch %u after %u\n", launch, before, last_epoch);
+      ++bad;
+    }
+    last_epoch = before;
     for (int r = 0; r < M.P; ++r)
       for (int x = 0; x < N; ++x) M.in[r][x] = int64_t(rng() % 1000003) - 500000 + launch;
     for (auto &o : M.out) std::fill(o.begin(), o.end(), int64_t(-1));
-    // one workgroup per role, as in the kernel: per piece and lane T owners,
-    // P-1 stagers and P-1 scatter consumers
+    // one workgroup per role, as in the kernel: per piece and lane P-1
+    // stagers, T owners and P-1 scatter consumers
     std::vector<std::thread> th;
     const int roles = M.T + 2 * (M.P - 1);
     int G = M.P * M.L * roles;
@@ -286,18 +308,22 @@ int main(int argc, char **argv) {
       for (int lane = 0; lane < M.L; ++lane)
         for (int role = 0; role < roles; ++role, ++b) {
           const unsigned s = unsigned(rng());
-          th.emplace_back([&M, piece, lane, role, b, G, epoch, launch, s] {
+          th.emplace_back([&M, piece, lane, role, b, G, launch, s] {
             std::mt19937 r(s);
+            const uint32_t epoch = M.launch_epoch();
             if (M.entry_wait(b, G, epoch, r)) {
-              if (role < M.T) M.owner(piece, lane, role, epoch, s);
-              else if (role < M.T + M.P - 1) M.stager(piece, lane, role - M.T, epoch, launch, s);
+              if (role < M.P - 1) M.stager(piece, lane, role, epoch, launch, s);
+              else if (role < M.P - 1 + M.T) M.owner(piece, lane, role - (M.P - 1), epoch, s);
               else M.scatter(piece, lane, role - M.T - (M.P - 1), epoch, s);
             }
-            M.exit_notify(b, epoch);
+            M.exit_notify(b, G, epoch);
           });
         }
     for (auto &t : th) t.join();
-    for (int w = 0; w < G; ++w) M.exit_total[epoch & 1u][w % kExitSlots] += 1;
+    if (M.launch_epoch() != last_epoch + 1) {
+      std::fprintf(stderr, "launch %d: the epoch did not advance\n", launch);
+      ++bad;
+    }
     const bool timed_out = (M.status.load() & 1u) != 0;
     if (launch == M.withhold_launch) {
       if (!timed_out) {

@@ -239,3 +239,72 @@ def test_ulysses_argument_checks(purlin):
     assert uly([4, 4], out_=V(A_OUT, A_OUT + 1024)) == 1                # outputs overlap
     assert uly([1 << 41, 4]) == 1                                       # too many tokens
     assert uly([0, 0], in_=V(0, 0), out_=V(0, 0)) == 0                  # nothing to move
+
+
+@pytest.mark.parametrize("P", [5, 6, 7, 8])
+def test_job_bound_after_the_broadcast_split(purlin, P):
+    """A sum of P partitions broadcast to every rank (by_index -> by_index)
+    derives P * P pieces; outputs off each other's 16-byte phase would split
+    each into P single-destination jobs, past the 64 a launch plan holds:
+    refused as UNSUPPORTED before any HIP call (describe and collective)."""
+    counts = [40] * P
+    outs = [A_OUT + r * (1 << 30) + 2 * r for r in range(P)]   # phases 0, 2, 4, ... bytes
+    assert st(purlin, "by_index", "by_index", "sum", "bf16", counts, P=P,
+              ins=bufs(P, A_IN), outs=outs) == "UNSUPPORTED"
+    with pytest.raises(purlin.PurlinError) as e:
+        purlin.collective(bufs(P, A_IN), outs, "by_index", "by_index", "sum", counts, dtype="bf16",
+                          stream=0)
+    assert e.value.status == "UNSUPPORTED"
+    # congruent outputs keep the broadcast jobs: within the bound
+    assert st(purlin, "by_index", "by_index", "sum", "bf16", counts, P=P,
+              ins=bufs(P, A_IN), outs=bufs(P, A_OUT)) == "OK"
+    # the same split of a single sum (AllReduce) stays at P * P jobs
+    assert st(purlin, "whole", "whole", "sum", "bf16", [40 * P], P=P, ins=bufs(P, A_IN),
+              outs=outs) == "OK"
+
+
+def test_binding_rejects_tensors_it_would_misread(purlin):
+    """The Python binding checks tensors before the C call: CPU tensors, a
+    dtype mismatch, non-contiguous views and buffers shorter than their
+    partitions raise ValueError (no GPU work is started)."""
+    import torch
+    P = 8
+    x = [torch.zeros(8, dtype=torch.bfloat16) for _ in range(P)]
+    y = [torch.zeros(64, dtype=torch.bfloat16) for _ in range(P)]
+    with pytest.raises(ValueError, match="not on the current GPU"):
+        purlin.all_gather(x, y)
+    # the extents each rank's buffer must reach
+    assert purlin.extents("by_rank", P, [8] * P) == [8] * P
+    assert purlin.extents("by_index", P, [8] * P) == [64] * P
+    assert purlin.extents("by_index", 2, [3, 0], [10, 40]) == [13, 13]
+    assert purlin.extents("by_rank_index", 2, [1, 2, 3, 4]) == [3, 7]
+    assert purlin.extents("by_index_rank", 2, [1, 2, 3, 4]) == [4, 6]
+    assert purlin.extents("whole", 3, [5], [2]) == [7, 7, 7]
+    # tensor checks, device check skipped (no GPU here)
+    need = [64] * P
+    purlin.check_tensors(y, need, "bf16", "copy", "output")
+    short = list(y)
+    short[3] = torch.zeros(63, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="output 3 holds 63 elements"):
+        purlin.check_tensors(short, need, "bf16", "copy", "output")
+    mixed = list(y)
+    mixed[5] = torch.zeros(64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="dtype"):
+        purlin.check_tensors(mixed, need, "bf16", "copy", "output")
+    with pytest.raises(ValueError, match="dtype"):
+        purlin.check_tensors([torch.zeros(64, dtype=torch.float16)] * P, need, "bf16", "sum", "input")
+    with pytest.raises(ValueError, match="dtype"):
+        purlin.check_tensors(y, [16] * P, "f32", "copy", "input")
+    strided = list(y)
+    strided[0] = torch.zeros(128, dtype=torch.bfloat16)[::2]
+    with pytest.raises(ValueError, match="not contiguous"):
+        purlin.check_tensors(strided, need, "bf16", "copy", "output")
+    # raw addresses and None pass unchecked
+    purlin.check_tensors([A_IN, None] + y[2:], need, "bf16", "copy", "output")
+    # a counts array of the wrong length never reaches the library
+    with pytest.raises(ValueError, match="counts"):
+        purlin.collective(bufs(P, A_IN), bufs(P, A_OUT), "by_rank", "by_index", "copy", [8] * 7,
+                          dtype="bf16")
+    with pytest.raises(ValueError, match="displs"):
+        purlin.collective(bufs(P, A_IN), bufs(P, A_OUT), "by_rank", "by_index", "copy", [8] * 8,
+                          [0] * 8, dtype="bf16")

@@ -47,8 +47,10 @@ def full_check(purlin, name, dtype, counts, ins, outs, displs=None):
     in_n, out_n, op = oracle.COLLECTIVES[name]
     want = oracle.collective(in_n, out_n, op, dtype, P, counts, displs, ins, outs)
     got = run_collective(purlin, in_n, out_n, op, dtype, P, counts, displs, ins, outs)
+    inexact = 0
     for j in range(P):
-        compare("%s rank %d" % (name, j), got[j], want[j], dtype, op)
+        inexact += compare("%s rank %d" % (name, j), got[j], want[j], dtype, op)
+    assert inexact == 0, "%s: %d bf16 sums one step off the oracle" % (name, inexact)
 
 
 # --------------------------------------------------------------- small configs
@@ -170,7 +172,8 @@ def _sampled_sum_check(name, counts, ins, outs, rng, samples=4096):
             want = oracle.collective("whole", "whole", "sum", "bf16", P, [m], None, cols,
                                      [np.zeros(m, np.uint16) for _ in range(P)])[0]
             got = to_host(outs[j][off:off + c][pos], "bf16")
-            compare("%s rank %d sampled" % (name, j), got, want, "bf16", "sum")
+            inexact = compare("%s rank %d sampled" % (name, j), got, want, "bf16", "sum")
+            assert inexact == 0, "%s rank %d: %d sampled sums one step off" % (name, j, inexact)
 
 
 @pytest.mark.parametrize("variant", ["zs", "staged"])

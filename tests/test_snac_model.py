@@ -3,10 +3,12 @@ under ThreadSanitizer (tests/snac_model/snac_model.cpp).
 
 Threads play the kernel's workgroups (owners, alone or as a team that splits
 each chunk, stagers, scatter consumers, announcers) over std::atomic flags with random delays; several launches
-reuse the rings and flags with new epochs.  Checked: every output equals the
-rank-order sum, no data race on ring slots or outputs, a withheld notify ends
-in TIMEOUT with every thread returned (and the next launch is right again),
-and each of three planted protocol mistakes is caught.
+reuse the rings and flags with new epochs, read from the shared epoch word
+and advanced by each launch's last exit.  Checked: every output equals the
+rank-order sum, every launch advances the epoch by one, no data race on ring
+slots or outputs, a withheld notify ends in TIMEOUT with every thread
+returned (and the next launch is right again), and each planted protocol
+mistake is caught.
 """
 import os
 import shutil
@@ -72,7 +74,7 @@ def test_withheld_notify_with_an_owner_team(model):
     assert r.returncode == 0, r.stdout + r.stderr
 
 
-@pytest.mark.parametrize("mutation", [1, 2, 3])
+@pytest.mark.parametrize("mutation", [1, 2, 3, 6])
 def test_planted_protocol_mistakes_are_caught(model, mutation):
     env = dict(ENV, SNAC_MUTATION=str(mutation))
     r = run(model, 4, 2, 1, 12, 32, 3, 7, env=env)
