@@ -217,6 +217,9 @@ def test_capture_needing_new_workspace_is_refused(purlin):
     P = 8
     rng = np.random.default_rng(57)
     c = Case("reducescatter", P, "f32", [3000] * P, rng)
+    # torch hands out streams from a pool, so the capture stream may have
+    # served earlier calls: drop every stream's workspace first
+    purlin.release()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     statuses = []
