@@ -186,6 +186,32 @@ PURLIN_API purlin_status purlin_collective(const purlin_layout *in, const purlin
                                 const int64_t *counts, const int64_t *displs,
                                 hipStream_t stream);
 
+/*
+ * purlin_collective for callers that cannot allocate device memory on the
+ * call path: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, semantics and synchronous errors
+ * as purlin_collective; it calls no hipMalloc, hipFree or other allocating
+ * routine.  Instead of its stream's workspace it uses one fixed array in
+ * device memory per GPU, held from the first call on that GPU until the
+ * process ends: a 8 KiB flag block, 256 KiB of staging slot flags (1024
+ * slots) and 32 MiB of staging rings.  The first call on a device looks up
+ * the array's address (make it outside graph capture).  A staged plan is
+ * shrunk to fit the array (depth down to 2, fewer pipelines, chunks down to
+ * 4 KiB, as far as the policy leaves them open); when the policy fixes a
+ * plan larger than the array the call returns PURLIN_ERR_NO_MEMORY and
+ * enqueues nothing.  Zero staging without the handshake uses none of the
+ * array.  Every call on a GPU shares that GPU's array: calls whose
+ * execution overlaps on one GPU (on different streams, or a graph replayed
+ * beside an eager call) race and are not supported; calls in one stream's
+ * order are.  A device-side timeout of such a call is reported by
+ * purlin_check on any stream of that device.
+ */
+PURLIN_API purlin_status purlin_collective_noalloc(const purlin_layout *in,
+                                                   const purlin_layout *out, purlin_op op,
+                                                   purlin_dtype dtype, int P,
+                                                   const int64_t *counts, const int64_t *displs,
+                                                   hipStream_t stream);
+
 /* Synchronize `stream`, then read and clear that stream's device status
  * word (current device): PURLIN_ERR_TIMEOUT if any wait of a call on the
  * stream expired since the last check, else PURLIN_ERR_INVALID_ARG if a

@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libpurlin.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kernels.hip", "planner.cpp", "purlin.cpp"]
+SOURCES = ["kernels.hip", "noalloc.hip", "planner.cpp", "purlin.cpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",

@@ -10,6 +10,7 @@
 #include <memory>
 #include <vector>
 
+#include "collective.hpp"
 #include "kernels.hpp"
 #include "planner.hpp"
 
@@ -469,6 +470,246 @@ int moe_grid(DeviceState &ds, MoeKernel which, bool rows, int64_t work, int64_t 
 }
 
 }  // namespace
+
+purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out, purlin_op op,
+                              purlin_dtype dtype, int P, const int64_t *counts,
+                              const int64_t *displs, hipStream_t stream, FixedWorkspaceFn fixed_fn) {
+  if (!in || !out || !in->bufs || !out->bufs) return PURLIN_ERR_INVALID_ARG;
+  const Derived *d = nullptr;
+  purlin_status st = derive_cached(in->naming, out->naming, op, dtype, P, counts, displs, &d);
+  if (st != PURLIN_OK) return st;
+  // The overlap checks sort every partition; skip them when the plan and the
+  // buffers are those of the previous successful call.
+  static uint64_t last_id = 0;
+  static void *last_ptrs[2 * kMaxRanks];
+  void *ptrs[2 * kMaxRanks] = {};
+  for (int r = 0; r < P; ++r) {
+    ptrs[r] = in->bufs[r];
+    ptrs[kMaxRanks + r] = out->bufs[r];
+  }
+  const bool same_call = d->id == last_id && std::memcmp(ptrs, last_ptrs, sizeof(ptrs)) == 0;
+  if (!same_call) {
+    st = check_pointers(*d, in->bufs, out->bufs);
+    if (st != PURLIN_OK) return st;
+  }
+  if (d->jobs.empty()) return PURLIN_OK;  // every partition is empty
+
+  std::vector<Job> jobs;
+  std::vector<int> owners;
+  st = launch_jobs(*d, reinterpret_cast<char *const *>(out->bufs), &jobs, &owners);
+  if (st != PURLIN_OK) return st;
+  if (!same_call) {
+    last_id = d->id;
+    std::memcpy(last_ptrs, ptrs, sizeof(ptrs));
+  }
+  FixedWorkspace fixed_ws{};
+  const FixedWorkspace *fixed = nullptr;
+  if (fixed_fn) {
+    st = fixed_fn(&fixed_ws);
+    if (st != PURLIN_OK) return st;
+    fixed = &fixed_ws;
+  }
+
+  DeviceState *ds = nullptr;
+  st = device_state(&ds);
+  if (st != PURLIN_OK) return st;
+  const purlin_policy pol = effective_policy();
+  const KernelKind kind = kind_of(op, dtype);
+  const bool nt = nt_env(true);
+
+  const bool staged = pol.zero_staging == PURLIN_STAGING_STAGED;
+  bool broadcast = false;
+  int64_t job_bytes = 0;
+  for (const Job &jb : jobs) {
+    job_bytes += jb.nbytes;
+    broadcast |= jb.dst < 0;
+  }
+  const AutoPolicy ap = auto_policy(kind, broadcast, job_bytes);
+  int unroll_sel = unroll_env();
+  if (unroll_sel < 0 || unroll_sel > 2) unroll_sel = ap.unroll_sel;
+  // Whether some job has a source off its destinations' 16-byte phase and
+  // so needs the kernel with the row bodies.  (Broadcast destinations are
+  // congruent modulo 16 once launch_jobs has split the others.)
+  bool rows = false;
+  for (const Job &jb : jobs) {
+    const uint64_t d0 = uint64_t(reinterpret_cast<uintptr_t>(out->bufs[jb.dst < 0 ? 0 : jb.dst])) +
+                        uint64_t(jb.dst_off);
+    for (int i = jb.src < 0 ? 0 : jb.src; i < (jb.src < 0 ? P : jb.src + 1); ++i) {
+      const uint64_t a = uint64_t(reinterpret_cast<uintptr_t>(in->bufs[i])) + uint64_t(jb.src_off);
+      rows |= ((a - d0) & 15u) != 0;
+    }
+  }
+  // every job writes one destination rank (no broadcast): the build whose
+  // destination loops fold to a single store
+  bool single_dst = true;
+  for (const Job &jb : jobs) single_dst &= jb.dst >= 0;
+  const bool one = !staged && one_build(kind, nt, rows, single_dst);
+  // The build with the wide element pass (for small misaligned single-
+  // destination tiles, taken in the latency regime only: at most 512 KiB of
+  // jobs).  Larger reductions run the build without it, whose row bodies
+  // keep a workgroup per CU more (ReduceScatterV 4-11% faster at 2-8 MiB per
+  // rank, 2% at 16).  Copies run the wide build at every size: its row body
+  // measured 2-3% faster on AllToAllV at 8 MiB - 1 GiB per rank (paired on
+  // the same buffers; the pass itself is not taken there, so this is the
+  // compiled code, not the pass).
+  const bool small = job_bytes <= (int64_t(512) << 10);
+  const bool wide = !staged && rows && (small || kind == KernelKind::kCopy);
+  // Copy broadcasts of 16 MiB of jobs or more store plainly: AllGather 5-8%,
+  // AllGatherV 4-8% faster at 64 MiB - 1 GiB per rank than with nontemporal
+  // stores (paired on the same buffers, both orders).  Nontemporal stores
+  // stay for smaller broadcasts (AllGather 6% faster with them at 4 MiB),
+  // for AllReduce's broadcast sums (2-4% faster with them at 64 MiB -
+  // 1 GiB) and for single-destination copies (AllToAllV 3-5%).
+  const bool bcast = !staged && broadcast && kind == KernelKind::kCopy &&
+                     job_bytes >= (int64_t(16) << 20) && env_i64("PURLIN_BCAST_PLAIN", 1) != 0;
+  const int capacity =
+      ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows, one, wide, bcast);
+
+  // The stream's flag block: for the staged kernel and for the handshake;
+  // a zero-staging launch without the handshake touches no flag at all.
+  StreamCtx *ctx = nullptr;
+  uint32_t *flags = nullptr;
+  if (fixed && (staged || pol.sync == 1)) {
+    flags = fixed->flags;
+  } else if (staged || pol.sync == 1) {
+    st = stream_ctx(*ds, stream, &ctx);
+    if (st != PURLIN_OK) return st;
+    flags = ctx->flags;
+  }
+
+  LaunchPlan lp{};
+  for (int r = 0; r < kMaxRanks; ++r) {
+    lp.in[r] = r < P ? static_cast<const char *>(in->bufs[r]) : nullptr;
+    lp.out[r] = r < P ? static_cast<char *>(out->bufs[r]) : nullptr;
+  }
+  lp.P = P;
+  launch_fields(*ds, lp, pol, flags);
+
+  purlin_launch_info info{};
+  info.threads = kThreads;
+  info.bytes_min = d->bytes_min;
+  info.njobs = int32_t(jobs.size());
+
+  hipError_t err;
+  if (!staged) {
+    const int64_t want_grid = std::min<int64_t>(
+        capacity, pol.wgs_per_rank ? int64_t(P) * pol.wgs_per_rank : int64_t(ap.grid));
+    const int64_t chunk =
+        pol.chunk_bytes ? pol.chunk_bytes : fit_chunk(ap.chunk, job_bytes, want_grid);
+    lp.chunk_bytes = chunk;
+    fill_tiles(lp, jobs, chunk);
+    const int grid = int(std::max<int64_t>(1, std::min<int64_t>(lp.total_tiles, want_grid)));
+    // Nontemporal loads pay off for sources off the destination's line
+    // phase too (variable-length partitions), measured at 16 MiB - 1 GiB.
+    lp.nt_any_phase = env_i64("PURLIN_NT_ANY_PHASE", 1) ? 1 : 0;
+    // Latency regime (the wide build, 4 KiB tiles): small misaligned
+    // single-destination tiles take one wide element pass instead of a row
+    // body (ReduceScatterV at 8 - 16 KiB per rank: 8.9 us against 10.3 us);
+    // from 1 MiB per rank on, the row body is faster.
+    lp.wide_max = (wide && small && chunk <= 4096) ? int32_t(chunk + 128) : 0;
+    err = launch_zs(lp, kind, nt, unroll_sel, rows, one, wide, bcast, grid, stream);
+    info.grid = grid;
+    info.zero_staging = 1;
+    info.rows = rows ? 1 : 0;
+    info.one = one ? 1 : 0;
+    info.plain_stores = bcast ? 1 : 0;
+    info.chunk_bytes = chunk;
+    info.tiles = lp.total_tiles;
+    info.sync = lp.sync;
+  } else {
+    StagedPlan sp{};
+    sp.base = lp;
+    sp.withhold = pol.test_withhold;
+    // Staged chunks are long: every handoff costs an L2 writeback (release)
+    // and an invalidate (acquire) on the XCDs involved.  About eight chunks
+    // per job, between 64 KiB and 1 MiB.
+    int64_t max_job = 0;
+    for (const Job &jb : jobs) max_job = std::max(max_job, jb.nbytes);
+    int64_t chunk = pol.chunk_bytes;
+    if (!chunk) {
+      chunk = int64_t(64) << 10;
+      while (chunk < (int64_t(1) << 20) && chunk * 8 < max_job) chunk *= 2;
+    }
+    int depth = pol.depth ? pol.depth : 4;
+    // roles per lane of each job
+    const int owner_team = int(std::min<int64_t>(kMaxTeam, std::max<int64_t>(1, env_i64("PURLIN_OWNER_TEAM", kOwnerTeam))));
+    int roles_per_lane = 0;
+    std::vector<StagedJob> sj(jobs.size());
+    for (size_t k = 0; k < jobs.size(); ++k) {
+      const Job &jb = jobs[k];
+      const int owner = jb.dst >= 0 ? jb.dst : (jb.src >= 0 ? jb.src : owners[k]);
+      sj[k].owner = int16_t(owner);
+      sj[k].n_stage = int16_t(jb.src < 0 ? P - 1 : (jb.src != owner ? 1 : 0));
+      sj[k].n_scatter = int16_t(jb.dst < 0 ? P - 1 : 0);
+      // A reduction's owner reads every source of a chunk while a stager
+      // copies one: a team of owners, each combining a slice of the chunk,
+      // keeps pace with the stagers.
+      sj[k].team = int16_t(kind != KernelKind::kCopy && sj[k].n_stage > 0 ? owner_team : 1);
+      roles_per_lane += sj[k].team + sj[k].n_stage + sj[k].n_scatter;
+    }
+    if (roles_per_lane > capacity) return PURLIN_ERR_UNSUPPORTED;  // cannot be co-resident
+    int lane_cap = pol.wgs_per_rank ? pol.wgs_per_rank : capacity / std::max(1, roles_per_lane);
+    int64_t ring_bytes = 0, flag_bytes = 0;
+    // Lay out tiles, lanes, roles and rings for (chunk, depth, lane_cap).
+    auto layout = [&]() {
+      sp.base.chunk_bytes = chunk;
+      fill_tiles(sp.base, jobs, chunk);
+      sp.depth = depth;
+      sp.slot_stride = chunk + 256;
+      int max_tiles = 1;
+      for (size_t k = 0; k < jobs.size(); ++k)
+        max_tiles = std::max(max_tiles, sp.base.tile_begin[k + 1] - sp.base.tile_begin[k]);
+      int lanes = std::max(1, std::min({lane_cap, kMaxLanes, max_tiles}));
+      while (lanes > 1 && lanes * roles_per_lane > capacity) --lanes;
+      sp.lanes = lanes;
+      int role = 0, ring = 0;
+      for (size_t k = 0; k < jobs.size(); ++k) {
+        sj[k].role_begin = role;
+        sj[k].ring_begin = ring;
+        role += (sj[k].team + sj[k].n_stage + sj[k].n_scatter) * lanes;
+        ring += (sj[k].n_stage + (sj[k].n_scatter > 0 ? 1 : 0)) * lanes;
+        sp.sj[k] = sj[k];
+      }
+      for (size_t k = jobs.size(); k < size_t(kMaxJobs); ++k) sp.sj[k].role_begin = role;
+      sp.total_roles = role;
+      ring_bytes = std::max<int64_t>(1, int64_t(ring) * sp.depth * sp.slot_stride);
+      flag_bytes = std::max<int64_t>(256, int64_t(ring) * sp.depth * 256);
+    };
+    layout();
+    if (fixed) {
+      // The fixed scratch: shrink what the policy leaves open until the rings
+      // fit (depth down to 2, which the pipeline sweep measured as fast as
+      // deeper rings, then fewer lanes, then shorter chunks).
+      while (ring_bytes > fixed->ring_bytes || flag_bytes > fixed->slot_flag_bytes) {
+        if (!pol.depth && depth > 2) --depth;
+        else if (!pol.wgs_per_rank && sp.lanes > 1) lane_cap = sp.lanes / 2;
+        else if (!pol.chunk_bytes && chunk > 4096) chunk /= 2;
+        else return PURLIN_ERR_NO_MEMORY;  // the policy fixes a plan too large for the scratch
+        layout();
+      }
+      sp.ring = fixed->ring;
+      sp.slot_flags = fixed->slot_flags;
+    } else {
+      st = ensure_staging(*ds, *ctx, ring_bytes, flag_bytes);
+      if (st != PURLIN_OK) return st;
+      sp.ring = ctx->ring;
+      sp.slot_flags = ctx->slot_flags;
+    }
+    err = launch_staged(sp, kind, nt, stream);
+    info.grid = sp.total_roles;
+    info.zero_staging = 0;
+    info.rows = 1;
+    info.depth = sp.depth;
+    info.chunk_bytes = sp.base.chunk_bytes;
+    info.tiles = sp.base.total_tiles;
+    info.sync = sp.base.sync;
+  }
+  if (err != hipSuccess) return PURLIN_ERR_HIP;
+  g_last = info;
+  g_have_last = true;
+  return PURLIN_OK;
+}
+
 }  // namespace purlin
 
 using namespace purlin;
@@ -534,206 +775,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
                                 purlin_op op, purlin_dtype dtype, int P,
                                 const int64_t *counts, const int64_t *displs,
                                 hipStream_t stream) {
-  if (!in || !out || !in->bufs || !out->bufs) return PURLIN_ERR_INVALID_ARG;
-  const Derived *d = nullptr;
-  purlin_status st = derive_cached(in->naming, out->naming, op, dtype, P, counts, displs, &d);
-  if (st != PURLIN_OK) return st;
-  // The overlap checks sort every partition; skip them when the plan and the
-  // buffers are those of the previous successful call.
-  static uint64_t last_id = 0;
-  static void *last_ptrs[2 * kMaxRanks];
-  void *ptrs[2 * kMaxRanks] = {};
-  for (int r = 0; r < P; ++r) {
-    ptrs[r] = in->bufs[r];
-    ptrs[kMaxRanks + r] = out->bufs[r];
-  }
-  const bool same_call = d->id == last_id && std::memcmp(ptrs, last_ptrs, sizeof(ptrs)) == 0;
-  if (!same_call) {
-    st = check_pointers(*d, in->bufs, out->bufs);
-    if (st != PURLIN_OK) return st;
-  }
-  if (d->jobs.empty()) return PURLIN_OK;  // every partition is empty
-
-  std::vector<Job> jobs;
-  std::vector<int> owners;
-  st = launch_jobs(*d, reinterpret_cast<char *const *>(out->bufs), &jobs, &owners);
-  if (st != PURLIN_OK) return st;
-  if (!same_call) {
-    last_id = d->id;
-    std::memcpy(last_ptrs, ptrs, sizeof(ptrs));
-  }
-
-  DeviceState *ds = nullptr;
-  st = device_state(&ds);
-  if (st != PURLIN_OK) return st;
-  const purlin_policy pol = effective_policy();
-  const KernelKind kind = kind_of(op, dtype);
-  const bool nt = nt_env(true);
-
-  const bool staged = pol.zero_staging == PURLIN_STAGING_STAGED;
-  bool broadcast = false;
-  int64_t job_bytes = 0;
-  for (const Job &jb : jobs) {
-    job_bytes += jb.nbytes;
-    broadcast |= jb.dst < 0;
-  }
-  const AutoPolicy ap = auto_policy(kind, broadcast, job_bytes);
-  int unroll_sel = unroll_env();
-  if (unroll_sel < 0 || unroll_sel > 2) unroll_sel = ap.unroll_sel;
-  // Whether some job has a source off its destinations' 16-byte phase and
-  // so needs the kernel with the row bodies.  (Broadcast destinations are
-  // congruent modulo 16 once launch_jobs has split the others.)
-  bool rows = false;
-  for (const Job &jb : jobs) {
-    const uint64_t d0 = uint64_t(reinterpret_cast<uintptr_t>(out->bufs[jb.dst < 0 ? 0 : jb.dst])) +
-                        uint64_t(jb.dst_off);
-    for (int i = jb.src < 0 ? 0 : jb.src; i < (jb.src < 0 ? P : jb.src + 1); ++i) {
-      const uint64_t a = uint64_t(reinterpret_cast<uintptr_t>(in->bufs[i])) + uint64_t(jb.src_off);
-      rows |= ((a - d0) & 15u) != 0;
-    }
-  }
-  // every job writes one destination rank (no broadcast): the build whose
-  // destination loops fold to a single store
-  bool single_dst = true;
-  for (const Job &jb : jobs) single_dst &= jb.dst >= 0;
-  const bool one = !staged && one_build(kind, nt, rows, single_dst);
-  // The build with the wide element pass (for small misaligned single-
-  // destination tiles, taken in the latency regime only: at most 512 KiB of
-  // jobs).  Larger reductions run the build without it, whose row bodies
-  // keep a workgroup per CU more (ReduceScatterV 4-11% faster at 2-8 MiB per
-  // rank, 2% at 16).  Copies run the wide build at every size: its row body
-  // measured 2-3% faster on AllToAllV at 8 MiB - 1 GiB per rank (paired on
-  // the same buffers; the pass itself is not taken there, so this is the
-  // compiled code, not the pass).
-  const bool small = job_bytes <= (int64_t(512) << 10);
-  const bool wide = !staged && rows && (small || kind == KernelKind::kCopy);
-  // Copy broadcasts of 16 MiB of jobs or more store plainly: AllGather 5-8%,
-  // AllGatherV 4-8% faster at 64 MiB - 1 GiB per rank than with nontemporal
-  // stores (paired on the same buffers, both orders).  Nontemporal stores
-  // stay for smaller broadcasts (AllGather 6% faster with them at 4 MiB),
-  // for AllReduce's broadcast sums (2-4% faster with them at 64 MiB -
-  // 1 GiB) and for single-destination copies (AllToAllV 3-5%).
-  const bool bcast = !staged && broadcast && kind == KernelKind::kCopy &&
-                     job_bytes >= (int64_t(16) << 20) && env_i64("PURLIN_BCAST_PLAIN", 1) != 0;
-  const int capacity =
-      ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows, one, wide, bcast);
-
-  // The stream's flag block: for the staged kernel and for the handshake;
-  // a zero-staging launch without the handshake touches no flag at all.
-  StreamCtx *ctx = nullptr;
-  if (staged || pol.sync == 1) {
-    st = stream_ctx(*ds, stream, &ctx);
-    if (st != PURLIN_OK) return st;
-  }
-
-  LaunchPlan lp{};
-  for (int r = 0; r < kMaxRanks; ++r) {
-    lp.in[r] = r < P ? static_cast<const char *>(in->bufs[r]) : nullptr;
-    lp.out[r] = r < P ? static_cast<char *>(out->bufs[r]) : nullptr;
-  }
-  lp.P = P;
-  launch_fields(*ds, lp, pol, ctx ? ctx->flags : nullptr);
-
-  purlin_launch_info info{};
-  info.threads = kThreads;
-  info.bytes_min = d->bytes_min;
-  info.njobs = int32_t(jobs.size());
-
-  hipError_t err;
-  if (!staged) {
-    const int64_t want_grid = std::min<int64_t>(
-        capacity, pol.wgs_per_rank ? int64_t(P) * pol.wgs_per_rank : int64_t(ap.grid));
-    const int64_t chunk =
-        pol.chunk_bytes ? pol.chunk_bytes : fit_chunk(ap.chunk, job_bytes, want_grid);
-    lp.chunk_bytes = chunk;
-    fill_tiles(lp, jobs, chunk);
-    const int grid = int(std::max<int64_t>(1, std::min<int64_t>(lp.total_tiles, want_grid)));
-    // Nontemporal loads pay off for sources off the destination's line
-    // phase too (variable-length partitions), measured at 16 MiB - 1 GiB.
-    lp.nt_any_phase = env_i64("PURLIN_NT_ANY_PHASE", 1) ? 1 : 0;
-    // Latency regime (the wide build, 4 KiB tiles): small misaligned
-    // single-destination tiles take one wide element pass instead of a row
-    // body (ReduceScatterV at 8 - 16 KiB per rank: 8.9 us against 10.3 us);
-    // from 1 MiB per rank on, the row body is faster.
-    lp.wide_max = (wide && small && chunk <= 4096) ? int32_t(chunk + 128) : 0;
-    err = launch_zs(lp, kind, nt, unroll_sel, rows, one, wide, bcast, grid, stream);
-    info.grid = grid;
-    info.zero_staging = 1;
-    info.rows = rows ? 1 : 0;
-    info.one = one ? 1 : 0;
-    info.plain_stores = bcast ? 1 : 0;
-    info.chunk_bytes = chunk;
-    info.tiles = lp.total_tiles;
-    info.sync = lp.sync;
-  } else {
-    StagedPlan sp{};
-    sp.base = lp;
-    // Staged chunks are long: every handoff costs an L2 writeback (release)
-    // and an invalidate (acquire) on the XCDs involved.  About eight chunks
-    // per job, between 64 KiB and 1 MiB.
-    int64_t max_job = 0;
-    for (const Job &jb : jobs) max_job = std::max(max_job, jb.nbytes);
-    int64_t chunk = pol.chunk_bytes;
-    if (!chunk) {
-      chunk = int64_t(64) << 10;
-      while (chunk < (int64_t(1) << 20) && chunk * 8 < max_job) chunk *= 2;
-    }
-    sp.base.chunk_bytes = chunk;
-    fill_tiles(sp.base, jobs, chunk);
-    sp.depth = pol.depth ? pol.depth : 4;
-    sp.slot_stride = chunk + 256;
-    sp.withhold = pol.test_withhold;
-    // roles and rings per lane
-    const int owner_team = int(std::min<int64_t>(kMaxTeam, std::max<int64_t>(1, env_i64("PURLIN_OWNER_TEAM", kOwnerTeam))));
-    int roles_per_lane = 0, max_tiles = 1;
-    std::vector<StagedJob> sj(jobs.size());
-    for (size_t k = 0; k < jobs.size(); ++k) {
-      const Job &jb = jobs[k];
-      const int owner = jb.dst >= 0 ? jb.dst : (jb.src >= 0 ? jb.src : owners[k]);
-      sj[k].owner = int16_t(owner);
-      sj[k].n_stage = int16_t(jb.src < 0 ? P - 1 : (jb.src != owner ? 1 : 0));
-      sj[k].n_scatter = int16_t(jb.dst < 0 ? P - 1 : 0);
-      // A reduction's owner reads every source of a chunk while a stager
-      // copies one: a team of owners, each combining a slice of the chunk,
-      // keeps pace with the stagers.
-      sj[k].team = int16_t(kind != KernelKind::kCopy && sj[k].n_stage > 0 ? owner_team : 1);
-      roles_per_lane += sj[k].team + sj[k].n_stage + sj[k].n_scatter;
-      max_tiles = std::max(max_tiles, sp.base.tile_begin[k + 1] - sp.base.tile_begin[k]);
-    }
-    int lanes = pol.wgs_per_rank ? pol.wgs_per_rank : capacity / std::max(1, roles_per_lane);
-    lanes = std::max(1, std::min({lanes, kMaxLanes, max_tiles}));
-    while (lanes > 1 && lanes * roles_per_lane > capacity) --lanes;
-    if (roles_per_lane > capacity) return PURLIN_ERR_UNSUPPORTED;  // cannot be co-resident
-    sp.lanes = lanes;
-    int role = 0, ring = 0;
-    for (size_t k = 0; k < jobs.size(); ++k) {
-      sj[k].role_begin = role;
-      sj[k].ring_begin = ring;
-      role += (sj[k].team + sj[k].n_stage + sj[k].n_scatter) * lanes;
-      ring += (sj[k].n_stage + (sj[k].n_scatter > 0 ? 1 : 0)) * lanes;
-      sp.sj[k] = sj[k];
-    }
-    for (size_t k = jobs.size(); k < size_t(kMaxJobs); ++k) sp.sj[k].role_begin = role;
-    sp.total_roles = role;
-    const int64_t ring_bytes = std::max<int64_t>(1, int64_t(ring) * sp.depth * sp.slot_stride);
-    const int64_t flag_bytes = std::max<int64_t>(256, int64_t(ring) * sp.depth * 256);
-    st = ensure_staging(*ds, *ctx, ring_bytes, flag_bytes);
-    if (st != PURLIN_OK) return st;
-    sp.ring = ctx->ring;
-    sp.slot_flags = ctx->slot_flags;
-    err = launch_staged(sp, kind, nt, stream);
-    info.grid = sp.total_roles;
-    info.zero_staging = 0;
-    info.rows = 1;
-    info.depth = sp.depth;
-    info.chunk_bytes = chunk;
-    info.tiles = sp.base.total_tiles;
-    info.sync = sp.base.sync;
-  }
-  if (err != hipSuccess) return PURLIN_ERR_HIP;
-  g_last = info;
-  g_have_last = true;
-  return PURLIN_OK;
+  return collective_impl(in, out, op, dtype, P, counts, displs, stream, nullptr);
 }
 
 purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t row_bytes,
@@ -907,15 +949,19 @@ purlin_status purlin_check(hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return PURLIN_ERR_HIP;
   auto &all = devices();
-  if (int(all.size()) <= dev) return PURLIN_OK;
-  StreamCtx *c = find_ctx(all[dev], stream);
-  if (!c) return PURLIN_OK;  // no call on this stream used a flag
+  // the stream's flag block, and the fixed scratch's (no-allocation calls)
+  uint32_t *words[2] = {nullptr, scratch_status_word()};
+  if (int(all.size()) > dev)
+    if (StreamCtx *c = find_ctx(all[dev], stream)) words[0] = c->flags + kFlagStatus;
   uint32_t status = 0;
-  uint32_t *word = c->flags + kFlagStatus;
-  if (hipMemcpy(&status, word, sizeof(status), hipMemcpyDeviceToHost) != hipSuccess)
-    return PURLIN_ERR_HIP;
+  for (uint32_t *word : words) {
+    if (!word) continue;
+    uint32_t v = 0;
+    if (hipMemcpy(&v, word, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return PURLIN_ERR_HIP;
+    if (v && hipMemset(word, 0, sizeof(uint32_t)) != hipSuccess) return PURLIN_ERR_HIP;
+    status |= v;
+  }
   if (status == 0) return PURLIN_OK;
-  if (hipMemset(word, 0, sizeof(uint32_t)) != hipSuccess) return PURLIN_ERR_HIP;
   if (status & kStatusTimeout) return PURLIN_ERR_TIMEOUT;
   return (status & kStatusBadArg) ? PURLIN_ERR_INVALID_ARG : PURLIN_ERR_HIP;
 }

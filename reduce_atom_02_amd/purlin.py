@@ -17,7 +17,8 @@ import os
 __all__ = [
     "LIB_PATH", "NAMINGS", "OPS", "DTYPES", "STATUS", "PurlinError", "collective",
     "all_reduce", "reduce_scatter", "all_gather", "all_to_all", "check",
-    "set_policy", "get_policy", "plan_describe", "last_launch", "stream_copy", "stream_pattern",
+    "collective_noalloc", "set_policy", "get_policy", "plan_describe", "last_launch",
+    "stream_copy", "stream_pattern",
     "moe_dispatch", "moe_combine", "ulysses", "release", "exported_symbols",
     "name_count", "extents", "check_tensors",
 ]
@@ -80,6 +81,8 @@ def _load():
     lib.purlin_collective.argtypes = [P_LAYOUT, P_LAYOUT, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       P_I64, P_I64, ctypes.c_void_p]
     lib.purlin_collective.restype = ctypes.c_int
+    lib.purlin_collective_noalloc.argtypes = lib.purlin_collective.argtypes
+    lib.purlin_collective_noalloc.restype = ctypes.c_int
     lib.purlin_check.argtypes = [ctypes.c_void_p]
     lib.purlin_check.restype = ctypes.c_int
     lib.purlin_set_policy.argtypes = [ctypes.POINTER(Policy)]
@@ -121,7 +124,7 @@ _lib = _load()
 
 def exported_symbols():
     """Names of the C ABI functions the loaded library resolves."""
-    names = ["purlin_collective", "purlin_check", "purlin_set_policy", "purlin_get_policy",
+    names = ["purlin_collective", "purlin_collective_noalloc", "purlin_check", "purlin_set_policy", "purlin_get_policy",
              "purlin_plan_describe", "purlin_last_launch", "purlin_stream_copy",
              "purlin_stream_pattern", "purlin_moe_dispatch", "purlin_moe_combine",
              "purlin_ulysses", "purlin_strerror", "purlin_release"]
@@ -291,12 +294,14 @@ def _validate(ins, outs, pin, pout, in_naming, out_naming, op, dt, counts, displ
 
 
 def collective(ins, outs, in_naming, out_naming, op, counts, displs=None, dtype=None,
-               stream=None):
+               stream=None, noalloc=False):
     """Enqueue one collective on ``stream`` (torch's current stream by default).
 
     ins, outs: P torch tensors or device addresses, one per rank.
     counts: one element count per name (see include/purlin.h).
     displs: None (packed) or input offsets then output offsets, by name.
+    noalloc: run purlin_collective_noalloc (the library's fixed scratch
+    array instead of the stream's workspace; nothing is allocated).
     Tensors are checked before the call (on the current GPU, contiguous, one
     element type, large enough for their partitions): ValueError otherwise.
     """
@@ -311,9 +316,16 @@ def collective(ins, outs, in_naming, out_naming, op, counts, displs=None, dtype=
     lout, keep_out = _layout(out_naming, outs, pout)
     c = _i64(counts)
     d = _i64(displs)
-    status = _lib.purlin_collective(ctypes.byref(lin), ctypes.byref(lout), OPS[op], DTYPES[dt], P,
-                                    c, d, ctypes.c_void_p(_stream(stream)))
-    _raise(status, "purlin_collective")
+    fn = _lib.purlin_collective_noalloc if noalloc else _lib.purlin_collective
+    status = fn(ctypes.byref(lin), ctypes.byref(lout), OPS[op], DTYPES[dt], P, c, d,
+                ctypes.c_void_p(_stream(stream)))
+    _raise(status, "purlin_collective_noalloc" if noalloc else "purlin_collective")
+
+
+def collective_noalloc(ins, outs, in_naming, out_naming, op, counts, displs=None, dtype=None,
+                       stream=None):
+    """collective() through purlin_collective_noalloc (see include/purlin.h)."""
+    collective(ins, outs, in_naming, out_naming, op, counts, displs, dtype, stream, noalloc=True)
 
 
 def _numel(t):

@@ -1,0 +1,150 @@
+"""purlin_collective_noalloc against purlin_collective (needs a GPU).
+
+The no-allocation entry point runs the same kernels on the library's fixed
+scratch array instead of the stream's workspace.  For each policy (zero
+staging, zero staging with the handshake, staged) and collective it makes
+two calls in a row, the second with a smaller input, and each output must
+equal, element for element, what purlin_collective writes for the same
+inputs (and the oracle's result).  Also: a staged plan the policy fixes too
+large for the array is refused with NO_MEMORY, and a staged call captured
+into a HIP graph on a stream without workspace runs (where
+purlin_collective has to refuse it) and replays correctly.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import pins
+from gpu_util import compare, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def purlin():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from reduce_atom_02_amd import purlin as p
+    return p
+
+
+@pytest.fixture(autouse=True)
+def _policy(purlin):
+    purlin.set_policy(reset=True)
+    yield
+    purlin.set_policy(reset=True)
+
+
+POLICIES = {
+    "zs": dict(zero_staging="zs"),
+    "zs_sync": dict(zero_staging="zs", sync=True),
+    "staged": dict(zero_staging="staged"),
+}
+
+
+def _run(purlin, name, dtype, counts, ins, outs, noalloc, shifts):
+    """One call on fresh device buffers; the P outputs as bit patterns."""
+    in_n, out_n, op = oracle.COLLECTIVES[name]
+    P = len(ins)
+    keep, din, dout = [], [], []
+    for r in range(P):
+        b, v = to_device(ins[r], dtype, shifts[r])
+        keep.append(b)
+        din.append(v)
+        b, v = to_device(outs[r], dtype)
+        keep.append(b)
+        dout.append(v)
+    purlin.collective(din, dout, in_n, out_n, op, counts, dtype=dtype, noalloc=noalloc)
+    purlin.check()
+    return [to_host(v, dtype) for v in dout]
+
+
+@pytest.mark.parametrize("policy", list(POLICIES))
+@pytest.mark.parametrize("name", ["allreduce", "reducescatter", "allgather", "alltoall"])
+def test_noalloc_matches_purlin_collective(purlin, name, policy):
+    P = 8
+    print("case noalloc", name, policy, flush=True)
+    rng = np.random.default_rng([71, len(name), len(policy)])
+    nparts = P * P if name == "alltoall" else P
+    dtype = "bf16" if name != "reducescatter" else "f32"
+    in_n, out_n, op = oracle.COLLECTIVES[name]
+    # two calls in a row, the second with a smaller input
+    for scale in (200000 if name != "alltoall" else 40000, 9000 if name != "alltoall" else 1500):
+        sizes = [int(v) | 1 for v in rng.integers(scale // 2, scale, nparts)]
+        counts = pins.counts_for(name, P, sizes)
+        ins, outs = pins.make_case(name, P, counts, dtype, rng, None, sentinel=0x4D4D)
+        shifts = [(3 * r) % 4 for r in range(P)]
+        purlin.set_policy(**POLICIES[policy])
+        got = _run(purlin, name, dtype, counts, ins, outs, True, shifts)
+        info = purlin.last_launch()
+        assert info["zero_staging"] == (0 if policy == "staged" else 1), info
+        ref = _run(purlin, name, dtype, counts, ins, outs, False, shifts)
+        want = oracle.collective(in_n, out_n, op, dtype, P, counts, None, ins, outs)
+        for j in range(P):
+            assert np.array_equal(got[j], ref[j]), (name, policy, scale, j)
+            inexact = compare("%s rank %d" % (name, j), got[j], want[j], dtype, op)
+            assert inexact == 0
+
+
+def test_noalloc_refuses_a_fixed_plan_too_large(purlin):
+    """A staged plan whose chunk and depth the policy fixes beyond the 32 MiB
+    of rings: NO_MEMORY, nothing enqueued (the outputs keep their values);
+    the same call with those fields open is shrunk to fit and runs."""
+    import torch
+    P = 8
+    n = 4 << 20
+    ins = [torch.ones(n, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    outs = [torch.full((n,), 5.0, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    purlin.set_policy(zero_staging="staged", chunk_bytes=1 << 20, depth=8, wgs_per_rank=4)
+    with pytest.raises(purlin.PurlinError) as e:
+        purlin.collective_noalloc(ins, outs, "whole", "whole", "sum", [n])
+    assert e.value.status == "NO_MEMORY"
+    torch.cuda.synchronize()
+    assert all(bool((o == 5.0).all()) for o in outs)
+    purlin.set_policy(zero_staging="staged")
+    purlin.collective_noalloc(ins, outs, "whole", "whole", "sum", [n])
+    purlin.check()
+    assert all(bool((o == 8.0).all()) for o in outs)
+
+
+def test_noalloc_staged_under_graph_capture(purlin):
+    """A staged call captured on a fresh stream: purlin_collective has no
+    workspace there and refuses, the no-allocation entry point runs from its
+    fixed array; four replays with new inputs match the oracle."""
+    import torch
+    P = 8
+    rng = np.random.default_rng(73)
+    counts = pins.counts_for("reducescatter", P, [20001 + 2 * r for r in range(P)])
+    ins, outs = pins.make_case("reducescatter", P, counts, "f32", rng, None, sentinel=0x1F1F)
+    din = [to_device(x, "f32")[1] for x in ins]
+    dout = [to_device(y, "f32")[1] for y in outs]
+    purlin.set_policy(zero_staging="staged", chunk_bytes=16384)
+    purlin.collective_noalloc(din, dout, "by_index", "by_rank", "sum", counts)   # eager first
+    purlin.check()
+    # torch hands out streams from a pool, so the capture stream may have
+    # served earlier calls: drop every stream's workspace first
+    purlin.release()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    refused = []
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        try:
+            purlin.collective(din, dout, "by_index", "by_rank", "sum", counts)
+        except purlin.PurlinError as e:
+            refused.append(e.status)
+        purlin.collective_noalloc(din, dout, "by_index", "by_rank", "sum", counts)
+    assert refused == ["UNSUPPORTED"]
+    for rep in range(4):
+        ins, outs = pins.make_case("reducescatter", P, counts, "f32", rng, None, sentinel=0x1F1F)
+        for r in range(P):
+            din[r].copy_(to_device(ins[r], "f32")[1])
+            dout[r].copy_(to_device(outs[r], "f32")[1])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        purlin.check(s)
+        want = oracle.collective("by_index", "by_rank", "sum", "f32", P, counts, None, ins, outs)
+        for j in range(P):
+            compare("replay %d rank %d" % (rep, j), to_host(dout[j], "f32"), want[j], "f32", "sum")
+    del g
