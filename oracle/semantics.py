@@ -2,9 +2,9 @@
 
 Purlin specifies a collective as a naming of an input layout, a naming of an
 output layout, and a copy or a reduction (Purlin, abstract).  The layouts
-"describe the required results independently of any transfer mechanism"
-(Purlin, Figure 4 caption), so this module computes exactly that definition
-and models none of the orchestration (SNAC) or the datapath (Atom).
+fix the result without saying how bytes move (Purlin, Figure 4 caption), so
+this module computes exactly that definition and models none of the
+orchestration (SNAC) or the datapath (Atom).
 
 Definition (Purlin, abstract and Figure 4; the readings are listed below):
 

@@ -53,10 +53,10 @@ __device__ __forceinline__ void tile_bounds(uint64_t ref, int64_t n, int64_t C, 
 }
 
 // ---- zero staging --------------------------------------------------------
-// Purlin-ZS omits staging (Figure 10 caption): every workgroup reads the
-// inputs of all ranks directly and writes each result unit straight from
-// registers to every destination (Figure 6: the reduced chunk of piece k
-// reaches all ranks without a second pass).  Tiles are dealt to a resident
+// The zero-staging variant has no staging step (Figure 10 caption): every
+// workgroup reads the inputs of all ranks directly and writes each result
+// unit straight from registers to every destination (Figure 6: the reduced
+// chunk of piece k reaches all ranks without a second pass).  Tiles are dealt to a resident
 // grid in grid-stride order; the tile list holds the share of rank 0, then
 // rank 1, and so on.
 // kWide: the build for the latency regime, whose small misaligned tiles may
