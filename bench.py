@@ -561,6 +561,117 @@ def ulysses_bench(purlin, steps, warmup, dev):
     return {"ulysses": res, "P": P, "steps": steps, "dtype": "bf16", "data": "synthetic"}
 
 
+def engine_bench(purlin, T, steps, dev):
+    """The copy collectives on the DMA copy engines (no kernel) against the
+    shader kernels, at T bytes per rank: p50 of `steps` calls each (a 1 GiB
+    fill between calls, outside the events, so inputs come from HBM), and
+    what a compute-bound kernel on another stream keeps of its throughput
+    beside each: a bf16 GEMM [8192 x 8192] x [8192 x 8192] (hipBLASLt through
+    torch), timed alone and while the collective runs back to back on its
+    own stream for longer than the GEMMs; the collective's throughput beside
+    the GEMM is reported too."""
+    import torch
+    import workloads
+    names = ["allgather", "alltoall", "allgatherv", "alltoallv"]
+    shapes = collective_shapes(T)
+    n = T // ESZ
+    ins = [workloads.device_values(n, "normal", "bf16", 3, r, dev) for r in range(P)]
+    out_len = max(max(shapes[nm]["outs"]) for nm in names)
+    outs = [torch.empty(out_len, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    sx, sc = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def call(name, stream):
+        s = shapes[name]
+        in_n, out_n, op = SPECS[name]
+        purlin.collective([ins[r][:s["ins"][r]] for r in range(P)],
+                          [outs[r][:s["outs"][r]] for r in range(P)],
+                          in_n, out_n, op, s["counts"], stream=stream)
+
+    def p50(fn, stream, reps):
+        fn()
+        ev = []
+        for _ in range(reps):
+            with torch.cuda.stream(stream):
+                flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+        return ts[len(ts) // 2]
+
+    res = {}
+    for name in names:
+        row = {}
+        for engine in ("shader", "copy"):
+            purlin.set_policy(engine=engine)
+            t = p50(lambda: call(name, sx), sx, steps)
+            info = purlin.last_launch()
+            row[engine] = {"p50_us": round(t * 1e6, 1), "algbw_GBps": round(T / t / 1e9, 1),
+                           "hbm_frac": round(shapes[name]["bmin"] / t / HBM_PEAK, 4),
+                           "kernel_grid": info["grid"], "engine_copies": info["engine_copies"]}
+        res[name] = row
+        print("%s done" % name, flush=True)
+    purlin.set_policy(reset=True)
+
+    # a compute-bound kernel beside the collective
+    m = 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    a = torch.randn(m, m, dtype=torch.bfloat16, device=dev, generator=g)
+    b = torch.randn(m, m, dtype=torch.bfloat16, device=dev, generator=g)
+    c = torch.empty(m, m, dtype=torch.bfloat16, device=dev)
+    n_gemm = 40
+    flops = 2.0 * m * m * m * n_gemm
+
+    def gemms():
+        with torch.cuda.stream(sc):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(sc)
+            for _ in range(n_gemm):
+                torch.matmul(a, b, out=c)
+            e1.record(sc)
+        return e0, e1
+
+    torch.cuda.synchronize()
+    gemms()
+    torch.cuda.synchronize()
+    e0, e1 = gemms()
+    torch.cuda.synchronize()
+    t_alone = e0.elapsed_time(e1) * 1e-3
+    beside = {"gemm_alone_TFLOPs": round(flops / t_alone / 1e12, 1), "gemm": "bf16 %dx%dx%d x%d"
+              % (m, m, m, n_gemm)}
+    name = "alltoall"
+    for engine in ("shader", "copy"):
+        purlin.set_policy(engine=engine)
+        t_one = res[name][engine]["p50_us"] * 1e-6
+        reps = max(4, int(1.5 * t_alone / t_one) + 1)
+        torch.cuda.synchronize()
+        x0 = torch.cuda.Event(enable_timing=True)
+        x1 = torch.cuda.Event(enable_timing=True)
+        x0.record(sx)
+        for _ in range(reps):
+            call(name, sx)
+        x1.record(sx)
+        g0, g1 = gemms()
+        torch.cuda.synchronize()
+        purlin.check(sx)
+        t_g = g0.elapsed_time(g1) * 1e-3
+        t_x = x0.elapsed_time(x1) * 1e-3 / reps
+        beside[engine] = {"gemm_TFLOPs_beside": round(flops / t_g / 1e12, 1),
+                          "gemm_kept_frac": round(t_alone / t_g, 3),
+                          "alltoall_calls": reps,
+                          "alltoall_algbw_GBps_beside_gemm": round(T / t_x / 1e9, 1)}
+    purlin.set_policy(reset=True)
+    return {"engines": res, "beside_gemm": beside, "T_bytes_per_rank": T, "P": P,
+            "dtype": "bf16", "steps": steps, "data": "synthetic"}
+
+
 def pipeline_sweep(purlin, T, names, path, dev):
     """Staged SNAC pipeline against zero staging, in the shape of the pages'
     pipelining figure (a 256 MiB one-sided transfer; pipeline depth 1-8;
@@ -660,6 +771,9 @@ def main():
                          "8->1, 8->8 streams of --size bytes) with cold caches")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the pattern-ceiling measurement after the timed steps")
+    ap.add_argument("--engines", action="store_true",
+                    help="time the copy collectives on the DMA copy engines against the shader "
+                         "kernels at --size bytes per rank, and a bf16 GEMM beside each")
     ap.add_argument("--moe", action="store_true",
                     help="time MoE dispatch / combine at 4096 x 7168 bf16 per rank, top-8 of 256")
     ap.add_argument("--ulysses", action="store_true",
@@ -695,6 +809,9 @@ def main():
     T = args.size
     if args.calibrate_copy:
         calibrate_copy(purlin, T, args.steps, args.warmup, dev)
+        return
+    if args.engines:
+        print(json.dumps(engine_bench(purlin, T, args.steps, dev)), flush=True)
         return
     if args.moe:
         print(json.dumps(moe_bench(purlin, args.steps, args.warmup, dev)), flush=True)

@@ -98,6 +98,18 @@ typedef enum {
   PURLIN_STAGING_STAGED = 2 /* producers stage chunks in a ring, notify, consumers consume */
 } purlin_staging;
 
+/* Datapath of copy collectives (copy engines: the copy-engine AllGather of the
+ * Figure 10 caption, which launches no kernel, and the Figure 3 caption's
+ * point that copies need not occupy compute units). */
+typedef enum {
+  PURLIN_ENGINE_AUTO = 0,   /* shader kernels (the Atom) */
+  PURLIN_ENGINE_SHADER = 1, /* shader kernels (the Atom) */
+  PURLIN_ENGINE_COPY = 2    /* COPY collectives as stream-ordered transfers on the DMA copy
+                               engines (hipMemcpyDeviceToDeviceNoCU), one per (output
+                               partition, destination rank): no kernel, no compute unit.
+                               SUM collectives still run on the shader kernels. */
+} purlin_engine;
+
 /* Execution policy ("codesign policies tune execution", Figure 1 caption).
  * A zero field means "automatic".  It never changes a result, only speed. */
 typedef struct {
@@ -110,7 +122,7 @@ typedef struct {
   int64_t watchdog_ns;   /* bound of every device spin wait */
   int32_t test_withhold; /* test only: k > 0 withholds the k-th ready notify
                             of staging channel 0, to exercise the watchdog */
-  int32_t reserved;
+  int32_t engine;        /* purlin_engine */
 } purlin_policy;
 
 /* One (output partition, matching input partition) pair of a plan. */
@@ -139,6 +151,8 @@ typedef struct {
   int32_t plain_stores;  /* 1 if the build with plain (not nontemporal) body stores ran:
                             copy broadcasts of 16 MiB of jobs or more, Ulysses exchanges of
                             at most 128 MiB each way */
+  int32_t engine_copies; /* copy-engine transfers enqueued (PURLIN_ENGINE_COPY; grid is then
+                            0: no kernel ran), 0 for kernel launches */
 } purlin_launch_info;
 
 /*

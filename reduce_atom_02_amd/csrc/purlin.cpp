@@ -81,6 +81,7 @@ bool policy_valid(const purlin_policy &p) {
   if (p.zero_staging < 0 || p.zero_staging > 2) return false;
   if (p.sync < 0 || p.sync > 2) return false;
   if (p.watchdog_ns < 0 || p.test_withhold < 0) return false;
+  if (p.engine < PURLIN_ENGINE_AUTO || p.engine > PURLIN_ENGINE_COPY) return false;
   return true;
 }
 
@@ -95,6 +96,7 @@ purlin_policy effective_policy() {
   const int64_t sy = env_i64("PURLIN_SYNC", -1);
   p.sync = sy < 0 ? 0 : (sy ? 1 : 2);
   p.watchdog_ns = env_i64("PURLIN_WATCHDOG_NS", 0);
+  p.engine = int32_t(env_i64("PURLIN_ENGINE", 0));
   if (!policy_valid(p)) p = purlin_policy{};
   if (g_user_policy_set) {
     const purlin_policy &u = user_policy();
@@ -104,6 +106,7 @@ purlin_policy effective_policy() {
     if (u.zero_staging) p.zero_staging = u.zero_staging;
     if (u.sync) p.sync = u.sync;
     if (u.watchdog_ns) p.watchdog_ns = u.watchdog_ns;
+    if (u.engine) p.engine = u.engine;
     p.test_withhold = u.test_withhold;
   }
   return p;
@@ -510,10 +513,31 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     fixed = &fixed_ws;
   }
 
+  const purlin_policy pol = effective_policy();
+  if (op == PURLIN_OP_COPY && pol.engine == PURLIN_ENGINE_COPY) {
+    // The copy engines: one stream-ordered DMA transfer per (job,
+    // destination rank), no kernel and no compute unit.
+    purlin_launch_info info{};
+    info.bytes_min = d->bytes_min;
+    info.njobs = int32_t(jobs.size());
+    for (const Job &jb : jobs) {
+      const char *src = static_cast<const char *>(in->bufs[jb.src]) + jb.src_off;
+      for (int r = jb.dst < 0 ? 0 : jb.dst; r < (jb.dst < 0 ? P : jb.dst + 1); ++r) {
+        char *dst = static_cast<char *>(out->bufs[r]) + jb.dst_off;
+        if (hipMemcpyAsync(dst, src, size_t(jb.nbytes), hipMemcpyDeviceToDeviceNoCU, stream) !=
+            hipSuccess)
+          return PURLIN_ERR_HIP;
+        ++info.engine_copies;
+      }
+    }
+    info.tiles = info.engine_copies;
+    g_last = info;
+    g_have_last = true;
+    return PURLIN_OK;
+  }
   DeviceState *ds = nullptr;
   st = device_state(&ds);
   if (st != PURLIN_OK) return st;
-  const purlin_policy pol = effective_policy();
   const KernelKind kind = kind_of(op, dtype);
   const bool nt = nt_env(true);
 

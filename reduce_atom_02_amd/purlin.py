@@ -30,6 +30,7 @@ OPS = {"copy": 0, "sum": 1}
 DTYPES = {"f32": 0, "bf16": 1}
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "NO_MEMORY", 4: "HIP", 5: "TIMEOUT"}
 STAGING = {"auto": 0, "zs": 1, "staged": 2}
+ENGINES = {"auto": 0, "shader": 1, "copy": 2}
 
 COLLECTIVES = {
     "allreduce": ("whole", "whole", "sum"),
@@ -53,7 +54,7 @@ class Policy(ctypes.Structure):
     _fields_ = [("chunk_bytes", ctypes.c_int64), ("depth", ctypes.c_int32),
                 ("wgs_per_rank", ctypes.c_int32), ("zero_staging", ctypes.c_int32),
                 ("sync", ctypes.c_int32), ("watchdog_ns", ctypes.c_int64),
-                ("test_withhold", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("test_withhold", ctypes.c_int32), ("engine", ctypes.c_int32)]
 
 
 class Segment(ctypes.Structure):
@@ -68,7 +69,8 @@ class LaunchInfo(ctypes.Structure):
                 ("chunk_bytes", ctypes.c_int64), ("tiles", ctypes.c_int64),
                 ("bytes_min", ctypes.c_int64), ("njobs", ctypes.c_int32),
                 ("sync", ctypes.c_int32), ("rows", ctypes.c_int32), ("unit", ctypes.c_int32),
-                ("one", ctypes.c_int32), ("plain_stores", ctypes.c_int32)]
+                ("one", ctypes.c_int32), ("plain_stores", ctypes.c_int32),
+                ("engine_copies", ctypes.c_int32)]
 
 
 def _load():
@@ -368,12 +370,15 @@ def check(stream=None):
 
 
 def set_policy(chunk_bytes=0, depth=0, wgs_per_rank=0, zero_staging="auto", sync=None,
-               watchdog_ns=0, test_withhold=0, reset=False):
+               watchdog_ns=0, test_withhold=0, engine="auto", reset=False):
+    """engine: "auto" / "shader" (the Atom kernels) or "copy" (copy collectives
+    on the DMA copy engines, no kernel)."""
     if reset:
         _raise(_lib.purlin_set_policy(None), "purlin_set_policy")
         return
     p = Policy(chunk_bytes, depth, wgs_per_rank, STAGING[zero_staging],
-               0 if sync is None else (1 if sync else 2), watchdog_ns, test_withhold, 0)
+               0 if sync is None else (1 if sync else 2), watchdog_ns, test_withhold,
+               ENGINES[engine])
     _raise(_lib.purlin_set_policy(ctypes.byref(p)), "purlin_set_policy")
 
 
