@@ -117,24 +117,30 @@ def kernel_of(name, rows, one, plain=False):
                                       "one" if one else "general", ",plain" if plain else "")
 
 
-def cpu_baseline(T_sample, names):
+def cpu_baseline(T_sample, names, reps=5):
     """The oracle, as it stands, on the host cores: seven collectives at
-    T_sample bytes per rank, same seeds; generation is not timed."""
+    T_sample bytes per rank, same seeds, the p50 of `reps` calls each;
+    generation is not timed."""
     import numpy as np
     import oracle
     import workloads
     shapes = collective_shapes(T_sample)
     n = T_sample // ESZ
     ins = [workloads.host_values(n, "normal", "bf16", 3, r) for r in range(P)]
-    total_T, total_t = 0, 0.0
+    total_T, total_t, spent = 0, 0.0, 0.0
     for name in names:
         s = shapes[name]
         in_n, out_n, op = SPECS[name]
         xs = [ins[r][:s["ins"][r]] for r in range(P)]
-        ys = [np.zeros(s["outs"][r], np.uint16) for r in range(P)]
-        t0 = time.perf_counter()
-        oracle.collective(in_n, out_n, op, "bf16", P, s["counts"], None, xs, ys)
-        total_t += time.perf_counter() - t0
+        ts = []
+        for _ in range(reps):
+            ys = [np.zeros(s["outs"][r], np.uint16) for r in range(P)]
+            t0 = time.perf_counter()
+            oracle.collective(in_n, out_n, op, "bf16", P, s["counts"], None, xs, ys)
+            ts.append(time.perf_counter() - t0)
+        ts.sort()
+        total_t += ts[len(ts) // 2]
+        spent += sum(ts)
         total_T += s["T"]
     model = "unknown"
     try:
@@ -145,20 +151,39 @@ def cpu_baseline(T_sample, names):
     return {"value": round(total_T / total_t / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": "the same seven collectives, bf16, P=8, at %d MiB per rank instead of "
-                      "%s; numpy oracle single-threaded; %.1f s of oracle time; host: %d CPUs, "
-                      "%d in this process's affinity, %s"
-                      % (T_sample >> 20, "the timed size", total_t, os.cpu_count() or 0,
+                      "the timed size; the p50 of %d calls each (sum of T over the sum of the "
+                      "p50s); numpy oracle single-threaded; %.1f s of oracle time; host: %d "
+                      "CPUs, %d in this process's affinity, %s"
+                      % (T_sample >> 20, reps, spent, os.cpu_count() or 0,
                          len(os.sched_getaffinity(0)), model)}
 
 
-def ceilings(purlin, T, steps, dev):
-    """HBM ceiling of each collective's access pattern: n read streams and m
-    write streams, 16-byte nontemporal accesses over 16 KiB tiles, no
-    planning or flags (purlin_stream_pattern), the best of three grid sizes;
-    a 1 GiB fill between calls (cold caches).  1->1 over P*T bytes is
-    AllToAll's pattern and footprint, 1->8 of T bytes AllGather's, 8->1
-    ReduceScatter's, 8->8 AllReduce's.  Also hipMemcpyAsync device to device
-    (torch's copy_) over the P*T bytes, as a context figure."""
+# The collectives' bare access patterns: label, sources, destinations,
+# bytes per stream as a multiple of T, the collectives the pattern bounds.
+# 1->1 over P*T is AllToAll's pattern and footprint, 1->8 of T AllGather's,
+# 8->1 ReduceScatter's, 8->8 AllReduce's; read-only and write-only streams
+# bound every mix of the two.
+PATTERNS = [
+    ("1->1", 1, 1, P, ("alltoall", "alltoallv")),
+    ("1->8", 1, 8, 1, ("allgather", "allgatherv")),
+    ("8->1", 8, 1, 1, ("reducescatter", "reducescatterv")),
+    ("8->8", 8, 8, 1, ("allreduce",)),
+    ("read-only x8", 8, 0, 1, ()),
+    ("write-only x8", 0, 8, 1, ()),
+]
+ACCESS = {(True, True): "nt/nt", (True, False): "nt/plain", (False, True): "plain/nt",
+          (False, False): "plain/plain"}
+
+
+def ceilings(purlin, T, reps, dev, full=False, path=None):
+    """HBM ceiling of each collective's access pattern (purlin_stream_pattern:
+    n read streams, m write streams, no planning or flags), the best over a
+    sweep of nontemporal or plain loads x nontemporal or plain stores x tile
+    (16 KiB - 1 MiB) x grid x unroll (full=True: 4 x 4 x 4 grids x 3
+    unrolls; else 4 x 2 x 2 x 1), p50 of `reps` cold calls per point (a 1 GiB
+    fill between calls, outside the events).  Also hipMemcpyAsync device to
+    device (torch's copy_) over P*T bytes, as a context figure.  Every point
+    goes to `path` (JSONL) when given."""
     import torch
     big_src = torch.ones(P * T // 4, dtype=torch.float32, device=dev)
     big_dst = torch.empty(P * T // 4, dtype=torch.float32, device=dev)
@@ -170,7 +195,7 @@ def ceilings(purlin, T, steps, dev):
     def p50_of(fn):
         fn()
         ev = []
-        for _ in range(steps):
+        for _ in range(reps):
             flush.fill_(1.0)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -182,20 +207,170 @@ def ceilings(purlin, T, steps, dev):
         ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
         return ts[len(ts) // 2]
 
+    tiles = (16 << 10, 64 << 10, 256 << 10, 1 << 20) if full else (16 << 10, 256 << 10)
+    grids = (256, 512, 1024, 2048) if full else (512, 1024)
     out = {}
-    for nr, nw, nbytes, label in ((1, 1, P * T, "1->1 (alltoall)"),
-                                  (1, 8, T, "1->8 (allgather)"),
-                                  (8, 1, T, "8->1 (reducescatter)"),
-                                  (8, 8, T, "8->8 (allreduce)")):
-        s_, d_ = ([big_src], [big_dst]) if nr == 1 and nw == 1 else (srcs[:nr], dsts[:nw])
-        best = min(p50_of(lambda: purlin.stream_pattern(s_, d_, nbytes, grid=g, stream=stream))
-                   for g in (512, 1024, 2048))
-        out[label] = round((nr + nw) * nbytes / best / HBM_PEAK, 4)
+    f = open(path, "w") if path else None
+    for label, nr, nw, mult, bounds in PATTERNS:
+        nbytes = mult * T
+        if nr <= 1 and nw <= 1:
+            s_, d_ = ([big_src] if nr else []), ([big_dst] if nw else [])
+        else:
+            s_, d_ = srcs[:nr], dsts[:nw]
+        unrolls = ((2, 4, 8) if nr < 8 else (2, 4)) if full else (4,)
+        best = None
+        for (ntl, nts) in ACCESS:
+            if nr == 0 and not ntl or nw == 0 and not nts:
+                continue                       # the unused side: one setting
+            for tile in tiles:
+                for g in grids:
+                    for u in unrolls:
+                        t = p50_of(lambda: purlin.stream_pattern(
+                            s_, d_, nbytes, grid=g, tile_bytes=tile, unroll=u, nt_loads=ntl,
+                            nt_stores=nts, stream=stream))
+                        frac = (nr + nw) * nbytes / t / HBM_PEAK
+                        point = {"pattern": label, "access": ACCESS[(ntl, nts)], "tile": tile,
+                                 "grid": g, "unroll": u, "p50_us": round(t * 1e6, 1),
+                                 "hbm_frac": round(frac, 4), "bytes": (nr + nw) * nbytes}
+                        if f:
+                            f.write(json.dumps(point) + "\n")
+                            f.flush()
+                        if best is None or frac > best["hbm_frac"]:
+                            best = dict(point, hbm_frac=round(frac, 4))
+        out[label] = {"hbm_frac": best["hbm_frac"], "access": best["access"],
+                      "tile": best["tile"], "grid": best["grid"], "unroll": best["unroll"],
+                      "bounds": list(bounds)}
+        print("ceiling %s done" % label, flush=True)
     t = p50_of(lambda: big_dst.copy_(big_src))
-    out["hipMemcpyAsync D2D"] = round(2 * P * T / t / HBM_PEAK, 4)
+    out["hipMemcpyAsync D2D"] = {"hbm_frac": round(2 * P * T / t / HBM_PEAK, 4)}
+    if f:
+        f.close()
     del srcs, dsts, big_src, big_dst, flush
     torch.cuda.empty_cache()
     return out
+
+
+def latency_block(purlin, dev, ins):
+    """Device p50 latency of each collective at 1 KiB, 64 KiB and 512 KiB
+    per rank (warm, 200 timed calls queued behind a spin kernel so that the
+    events bracket GPU work only) and at 1 MiB (cold: a 1 GiB fill between
+    calls, 50 calls), the fp32 AllReduce of 1 MiB per rank (values 2U - 1)
+    and the TP8 AllReduce of [t x 7168] bf16 activations for t = 1, 64, 256
+    (warm, queued), and the empty-kernel floor timed the same way.  Inputs
+    are prefixes of the bench's resident buffers; 20 warm-up calls per
+    point; P = 8, zero staging, default policy."""
+    import torch
+    import workloads
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    outs = [torch.empty(256 * 7168, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    empty = torch.empty(1, device=dev)
+
+    def timed(fn, reps, cold):
+        for _ in range(20):
+            fn()
+        ev = []
+        for k in range(reps):
+            if not cold and k % 200 == 0:
+                torch.cuda.synchronize()
+                torch.cuda._sleep(20_000_000)     # ~10 ms: covers 200 enqueues
+            if cold:
+                flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+        return round(ts[len(ts) // 2] * 1e6, 2)
+
+    res = {"empty_kernel_p50_us": timed(lambda: empty.add_(0), 200, False), "collectives": {}}
+    for T in (1 << 10, 64 << 10, 512 << 10, 1 << 20):
+        shapes = collective_shapes(T)
+        row = {}
+        for name, s in shapes.items():
+            in_n, out_n, op = SPECS[name]
+            xi = [ins[r][:s["ins"][r]] for r in range(P)]
+            yo = [outs[r][:s["outs"][r]] for r in range(P)]
+            row[name] = timed(lambda: purlin.collective(xi, yo, in_n, out_n, op, s["counts"],
+                                                        stream=stream), 50 if T >= 1 << 20 else 200,
+                              T >= 1 << 20)
+        res["collectives"]["%d_KiB" % (T >> 10)] = row
+    purlin.check(stream)
+    n = 262144
+    xf = [workloads.device_values(n, "uniform", "f32", 0, r, dev) for r in range(P)]
+    yf = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(P)]
+    res["allreduce_f32_1MiB_warm_p50_us"] = timed(
+        lambda: purlin.collective(xf, yf, "whole", "whole", "sum", [n], stream=stream), 200, False)
+    res["allreduce_f32_1MiB_cold_p50_us"] = timed(
+        lambda: purlin.collective(xf, yf, "whole", "whole", "sum", [n], stream=stream), 50, True)
+    for t in (1, 64, 256):
+        m = t * 7168
+        xi = [ins[r][:m] for r in range(P)]
+        yo = [outs[r][:m] for r in range(P)]
+        res["tp8_allreduce_bf16_%dx7168_p50_us" % t] = timed(
+            lambda: purlin.collective(xi, yo, "whole", "whole", "sum", [m], stream=stream), 200,
+            False)
+    purlin.check(stream)
+    del flush, outs, xf, yf
+    return res
+
+
+def placement_spread(purlin, T, names, steps, dev, first):
+    """The step on two more sets of freshly allocated rank buffers (held at
+    the same time as the first, so every set has its own physical pages):
+    `steps` timed steps per set after one warm-up step.  Returns the B_min
+    fraction of the whole step and of each collective per set, the first
+    set's (`first`, from the timed run) included, with min / median / max."""
+    import torch
+    import workloads
+    shapes = collective_shapes(T)
+    stream = torch.cuda.current_stream()
+    sets = [first]
+    keep = []
+    for k in range(2):
+        n = T // ESZ
+        ins = [workloads.device_values(n, "normal", "bf16", 3, r, dev) for r in range(P)]
+        out_len = max(max(s["outs"]) for s in shapes.values())
+        outs = [torch.empty(out_len, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+        keep.append((ins, outs))
+        per = {}
+        total_b, total_t = 0, 0.0
+        for name in names:
+            s = shapes[name]
+            in_n, out_n, op = SPECS[name]
+            xi = [ins[r][:s["ins"][r]] for r in range(P)]
+            yo = [outs[r][:s["outs"][r]] for r in range(P)]
+            purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
+            ev = []
+            for _ in range(steps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
+                e1.record(stream)
+                ev.append((e0, e1))
+            torch.cuda.synchronize()
+            ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+            p50 = ts[len(ts) // 2]
+            per[name] = round(s["bmin"] / p50 / HBM_PEAK, 4)
+            total_b += s["bmin"]
+            total_t += p50
+        purlin.check(stream)
+        sets.append({"hbm_frac": round(total_b / total_t / HBM_PEAK, 4), "collectives": per})
+    del keep
+    torch.cuda.empty_cache()
+
+    def spread(vals):
+        v = sorted(vals)
+        return {"min": v[0], "median": v[len(v) // 2], "max": v[-1]}
+
+    return {"sets": len(sets), "steps_per_set": steps,
+            "step_hbm_frac": spread([x["hbm_frac"] for x in sets]),
+            "collectives": {n_: spread([x["collectives"][n_] for x in sets]) for n_ in names},
+            "per_set": sets}
 
 
 def calibrate_copy(purlin, T, steps, warmup, dev):
@@ -761,16 +936,19 @@ def main():
     ap.add_argument("--size", type=int, default=1 << 30, help="T, bytes per rank")
     ap.add_argument("--variant", choices=["zs", "staged"], default="zs")
     ap.add_argument("--only", default="", help="comma-separated subset of collectives")
-    ap.add_argument("--cpu-sample", type=int, default=256 << 20,
+    ap.add_argument("--cpu-sample", type=int, default=64 << 20,
                     help="T of the oracle sample, bytes per rank (0 skips it)")
     ap.add_argument("--sweep", default="",
                     help="write p50 latency / algorithm bandwidth of every collective over "
                          "T = 1 KiB .. --size to this JSONL file instead of the step benchmark")
-    ap.add_argument("--ceilings", action="store_true",
-                    help="time the bare read/write patterns of the collectives (1->1, 1->8, "
-                         "8->1, 8->8 streams of --size bytes) with cold caches")
+    ap.add_argument("--ceilings", default="",
+                    help="sweep the bare read/write patterns of the collectives (1->1, 1->8, "
+                         "8->1, 8->8, read-only, write-only; loads / stores nontemporal or "
+                         "plain x tile x grid x unroll) at --size bytes, cold, every point to "
+                         "this JSONL file")
     ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip the pattern-ceiling measurement after the timed steps")
+                    help="skip the pattern ceilings, the latency block and the placement "
+                         "spread after the timed steps")
     ap.add_argument("--engines", action="store_true",
                     help="time the copy collectives on the DMA copy engines against the shader "
                          "kernels at --size bytes per rank, and a bf16 GEMM beside each")
@@ -830,7 +1008,8 @@ def main():
         sweep(purlin, T, args.variant, args.sweep, dev)
         return
     if args.ceilings:
-        print(json.dumps({"ceilings_hbm_frac": ceilings(purlin, T, args.steps, dev),
+        print(json.dumps({"ceilings_hbm_frac": ceilings(purlin, T, args.steps, dev, full=True,
+                                                        path=args.ceilings),
                           "T_bytes_per_stream": T, "cold": True}), flush=True)
         return
     names = [n for n in SPECS if not args.only or n in args.only.split(",")]
@@ -905,11 +1084,24 @@ def main():
     total_bmin = sum(shapes[n_]["bmin"] for n_ in names) * args.steps
     value = total_T / elapsed / 1e9
     cpu = cpu_baseline(min(args.cpu_sample, T), names) if args.cpu_sample else None
+    # after the timed region: the latency half of the metric (device p50 at
+    # small sizes), the step on two more allocation sets, and what HBM
+    # sustains for each collective's bare access pattern at this size
+    latency = placement = pattern = None
+    if not args.no_ceilings:
+        latency = latency_block(purlin, dev, ins)
+        first = {"hbm_frac": round(sum(shapes[n_]["bmin"] for n_ in names) /
+                                   sum(per[n_]["p50_us"] * 1e-6 for n_ in names) / HBM_PEAK, 4),
+                 "collectives": {n_: per[n_]["hbm_frac"] for n_ in names}}
+        placement = placement_spread(purlin, T, names, 5, dev, first)
     del ins, outs
     torch.cuda.empty_cache()
-    # context, after the timed region: what HBM sustains for each collective's
-    # bare read/write pattern at this size (cold caches)
-    pattern = ceilings(purlin, T, 5, dev) if not args.no_ceilings else None
+    if not args.no_ceilings:
+        pattern = ceilings(purlin, T, 3, dev)
+        for label, c in pattern.items():
+            for n_ in c.get("bounds", ()):
+                if n_ in per:
+                    per[n_]["frac_of_pattern_ceiling"] = round(per[n_]["hbm_frac"] / c["hbm_frac"], 4)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -937,7 +1129,9 @@ def main():
                      "avg_launch_us": round(dom["time"] / dom["launches"] * 1e6, 2),
                      "bytes_per_launch": dom["bytes"] // dom["launches"]},
         "cpu_baseline": cpu,
-        "pattern_ceilings_hbm_frac": pattern,
+        "latency_p50_us": latency,
+        "placement": placement,
+        "pattern_ceilings": pattern,
         "collectives": per,
     }
     print(json.dumps(out), flush=True)

@@ -348,14 +348,19 @@ PURLIN_API purlin_status purlin_stream_copy(void *dst, const void *src, int64_t 
 /* Measurement: the bare memory pattern of a collective, as a ceiling.  Each
  * 16-byte unit u < bytes/16 is read from n_src sources (added as integers)
  * and the result written to n_dst destinations, at the same offset in every
- * buffer; n_src and n_dst in {1, 8}, all pointers 16-byte aligned and every
- * destination disjoint from every source.  `grid` workgroups (0: four per
- * CU, at most 65536) walk 16 KiB tiles in grid-stride order with 16-byte
- * nontemporal accesses, as the collectives do, with no planning or flags.
- * Asynchronous on `stream`. */
+ * buffer; n_src and n_dst in {0, 1, 8}, not both 0 (n_src 0: write-only, a
+ * pattern of the unit index; n_dst 0: read-only), all pointers 16-byte
+ * aligned and every destination disjoint from every source.  `grid`
+ * workgroups (0: four per CU, at most 65536) walk tiles of tile_bytes (0:
+ * 16 KiB; a multiple of 16) in grid-stride order, `unroll` 16-byte units
+ * per lane in flight (0: 4; else 2, 4 or 8; eight sources take at most 4),
+ * with no planning or flags, as
+ * the collectives walk theirs.  access bit 0: nontemporal loads, bit 1:
+ * nontemporal stores.  INVALID_ARG otherwise.  Asynchronous on `stream`. */
 PURLIN_API purlin_status purlin_stream_pattern(const void *const *srcs, int n_src,
                                                void *const *dsts, int n_dst, int64_t bytes,
-                                               int grid, hipStream_t stream);
+                                               int grid, int64_t tile_bytes, int unroll,
+                                               int access, hipStream_t stream);
 
 /* Static text for a status code. */
 PURLIN_API const char *purlin_strerror(purlin_status s);

@@ -9,6 +9,11 @@
 
 namespace purlin {
 
+// Where a read-only pattern's folded loads go, so that they are not dead:
+// written only when the fold hits one value.  External linkage: a global
+// no code could read would let the compiler drop the store and every load.
+__device__ atom::u32x4 g_pattern_sink;
+
 namespace {
 
 __device__ __forceinline__ void job_srcs(const LaunchPlan &p, const Job &jb, atom::Srcs &s) {
@@ -694,61 +699,119 @@ __global__ void __launch_bounds__(kThreads) stream_copy_kernel(atom::u32x4 *dst,
   }
 }
 
-// Bare pattern of a collective (ceiling measurement): kR sources added as
-// integers, written to kW destinations, same offset everywhere.  Walks
-// 16 KiB tiles in grid-stride order, as the collectives do.
+// Bare access pattern of a collective (ceiling measurement): kR sources
+// (0: write-only) added as integers, written to kW destinations (0:
+// read-only), the same offset everywhere, with no planning or flags.  Tiles
+// of `tile16` units are dealt in grid-stride order as the collectives deal
+// theirs; full passes of kU units per lane are unguarded, the tile's last
+// pass is guarded.  kNTL / kNTS: nontemporal loads / stores.
 struct PatternPtrs {
   const atom::u32x4 *src[kMaxRanks];
   atom::u32x4 *dst[kMaxRanks];
 };
 
-template <int kR, int kW, int kU>
-__global__ void __launch_bounds__(kThreads) pattern_kernel(PatternPtrs p, int64_t n16) {
-  constexpr int64_t kTile = 1024;  // units of 16 bytes; a multiple of kThreads * kU
-  static_assert(kTile % (kThreads * kU) == 0, "tile is whole passes");
-  const int64_t ntiles = (n16 + kTile - 1) / kTile;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    for (int64_t b = t * kTile + threadIdx.x; b < (t + 1) * kTile; b += kThreads * kU) {
-      atom::u32x4 v[kU][kR];
+
+// One pass of kU units per lane from unit b (this lane's first); with
+// kGuard, units at or past `end` are neither loaded (clamped) nor stored.
+template <int kR, int kW, int kU, bool kNTL, bool kNTS, bool kGuard>
+__device__ __forceinline__ void pattern_pass(const PatternPtrs &p, int64_t b, int64_t end,
+                                             atom::u32x4 &acc) {
+  atom::u32x4 v[kU][kR > 0 ? kR : 1];
 #pragma unroll
-      for (int k = 0; k < kU; ++k) {
-        int64_t i = b + int64_t(k) * kThreads;
-        if (i >= n16) i = n16 - 1;
+  for (int k = 0; k < kU; ++k) {
+    int64_t i = b + int64_t(k) * kThreads;
+    if (kGuard && i >= end) i = end - 1;
 #pragma unroll
-        for (int r = 0; r < kR; ++r) v[k][r] = atom::ld16<true>(uint64_t(p.src[r] + i));
-      }
+    for (int r = 0; r < kR; ++r) v[k][r] = atom::ld16<kNTL>(uint64_t(p.src[r] + i));
+  }
 #pragma unroll
-      for (int k = 0; k < kU; ++k) {
-        const int64_t i = b + int64_t(k) * kThreads;
-        atom::u32x4 a = v[k][0];
+  for (int k = 0; k < kU; ++k) {
+    const int64_t i = b + int64_t(k) * kThreads;
+    atom::u32x4 a;
+    if constexpr (kR == 0) {
+      a = atom::u32x4{uint32_t(i), uint32_t(i >> 32), 0x5a5a5a5au, 0xa5a5a5a5u};
+    } else {
+      a = v[k][0];
 #pragma unroll
-        for (int r = 1; r < kR; ++r) a += v[k][r];
-        if (i < n16) {
+      for (int r = 1; r < kR; ++r) a += v[k][r];
+    }
+    if constexpr (kW == 0) {
+      acc ^= a;
+    } else if (!kGuard || i < end) {
 #pragma unroll
-          for (int w = 0; w < kW; ++w) atom::st16<true>(uint64_t(p.dst[w] + i), a);
-        }
-      }
+      for (int w = 0; w < kW; ++w) atom::st16<kNTS>(uint64_t(p.dst[w] + i), a);
     }
   }
+}
+
+template <int kR, int kW, int kU, bool kNTL, bool kNTS>
+__global__ void __launch_bounds__(kThreads) pattern_kernel(PatternPtrs p, int64_t n16, int64_t tile16) {
+  constexpr int64_t kPass = int64_t(kThreads) * kU;
+  const int64_t ntiles = (n16 + tile16 - 1) / tile16;
+  atom::u32x4 acc{0u, 0u, 0u, 0u};
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t end = (t + 1) * tile16 < n16 ? (t + 1) * tile16 : n16;
+    int64_t b = t * tile16;
+    // full passes: every unit lies inside the tile, no guard
+    for (; b + kPass <= end; b += kPass)
+      pattern_pass<kR, kW, kU, kNTL, kNTS, false>(p, b + threadIdx.x, end, acc);
+    if (b < end) {
+      pattern_pass<kR, kW, kU, kNTL, kNTS, true>(p, b + threadIdx.x, end, acc);
+      atom::drain_vm();
+    }
+  }
+  if constexpr (kW == 0)
+    if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u) g_pattern_sink = acc;
+}
+
+template <int kR, int kW, int kU>
+const void *pattern_fn_u(bool ntl, bool nts) {
+  if (ntl) return nts ? reinterpret_cast<const void *>(&pattern_kernel<kR, kW, kU, true, true>)
+                      : reinterpret_cast<const void *>(&pattern_kernel<kR, kW, kU, true, false>);
+  return nts ? reinterpret_cast<const void *>(&pattern_kernel<kR, kW, kU, false, true>)
+             : reinterpret_cast<const void *>(&pattern_kernel<kR, kW, kU, false, false>);
+}
+
+// Eight sources keep at most four units per lane in flight (eight would
+// hold 256 VGPRs of loads and spill).
+template <int kR, int kW>
+const void *pattern_fn_rw(int unroll, bool ntl, bool nts) {
+  switch (unroll) {
+    case 2: return pattern_fn_u<kR, kW, 2>(ntl, nts);
+    case 8:
+      if constexpr (kR < 8) return pattern_fn_u<kR, kW, 8>(ntl, nts);
+      else return pattern_fn_u<kR, kW, 4>(ntl, nts);
+    default: return pattern_fn_u<kR, kW, 4>(ntl, nts);
+  }
+}
+
+const void *pattern_fn(int n_src, int n_dst, int unroll, bool ntl, bool nts) {
+  if (n_src == 0 && n_dst == 1) return pattern_fn_rw<0, 1>(unroll, ntl, nts);
+  if (n_src == 0 && n_dst == 8) return pattern_fn_rw<0, 8>(unroll, ntl, nts);
+  if (n_src == 1 && n_dst == 0) return pattern_fn_rw<1, 0>(unroll, ntl, nts);
+  if (n_src == 8 && n_dst == 0) return pattern_fn_rw<8, 0>(unroll, ntl, nts);
+  if (n_src == 1 && n_dst == 1) return pattern_fn_rw<1, 1>(unroll, ntl, nts);
+  if (n_src == 1 && n_dst == 8) return pattern_fn_rw<1, 8>(unroll, ntl, nts);
+  if (n_src == 8 && n_dst == 1) return pattern_fn_rw<8, 1>(unroll, ntl, nts);
+  if (n_src == 8 && n_dst == 8) return pattern_fn_rw<8, 8>(unroll, ntl, nts);
+  return nullptr;
 }
 
 }  // namespace
 
 hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts, int n_dst,
-                          int64_t bytes, int grid, hipStream_t stream) {
+                          int64_t bytes, int grid, int64_t tile_bytes, int unroll, bool ntl,
+                          bool nts, hipStream_t stream) {
   PatternPtrs p{};
   for (int r = 0; r < kMaxRanks; ++r) {
-    p.src[r] = static_cast<const atom::u32x4 *>(srcs[r < n_src ? r : 0]);
-    p.dst[r] = static_cast<atom::u32x4 *>(dsts[r < n_dst ? r : 0]);
+    p.src[r] = n_src ? static_cast<const atom::u32x4 *>(srcs[r < n_src ? r : 0]) : nullptr;
+    p.dst[r] = n_dst ? static_cast<atom::u32x4 *>(dsts[r < n_dst ? r : 0]) : nullptr;
   }
-  const int64_t n16 = bytes / 16;
-  void *args[] = {&p, const_cast<int64_t *>(&n16)};
-  const void *fn = nullptr;
-  if (n_src == 1 && n_dst == 1) fn = reinterpret_cast<const void *>(&pattern_kernel<1, 1, 4>);
-  else if (n_src == 1 && n_dst == 8) fn = reinterpret_cast<const void *>(&pattern_kernel<1, 8, 4>);
-  else if (n_src == 8 && n_dst == 1) fn = reinterpret_cast<const void *>(&pattern_kernel<8, 1, 2>);
-  else if (n_src == 8 && n_dst == 8) fn = reinterpret_cast<const void *>(&pattern_kernel<8, 8, 2>);
-  else return hipErrorInvalidValue;
+  int64_t n16 = bytes / 16;
+  int64_t tile16 = tile_bytes / 16;
+  const void *fn = pattern_fn(n_src, n_dst, unroll, ntl, nts);
+  if (!fn) return hipErrorInvalidValue;
+  void *args[] = {&p, &n16, &tile16};
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
 }
 

@@ -27,8 +27,12 @@ int unroll_of(KernelKind kind, int unroll_sel);
 bool one_build(KernelKind kind, bool nt, bool rows, bool single_dst);
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,
                               hipStream_t stream);
+// The bare access pattern of a collective (n_src, n_dst in {0, 1, 8}, not
+// both 0): `tile_bytes` per tile (a multiple of 16), `unroll` units per lane
+// in flight (2, 4 or 8), nontemporal loads (ntl) and stores (nts).
 hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts, int n_dst,
-                          int64_t bytes, int grid, hipStream_t stream);
+                          int64_t bytes, int grid, int64_t tile_bytes, int unroll, bool ntl,
+                          bool nts, hipStream_t stream);
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
                                bool one, bool wide, bool bcast, int *blocks);
 

@@ -1010,9 +1010,13 @@ purlin_status purlin_stream_copy(void *dst, const void *src, int64_t bytes, hipS
 }
 
 purlin_status purlin_stream_pattern(const void *const *srcs, int n_src, void *const *dsts,
-                                    int n_dst, int64_t bytes, int grid, hipStream_t stream) {
-  if (!srcs || !dsts || (n_src != 1 && n_src != 8) || (n_dst != 1 && n_dst != 8) ||
-      bytes < 0 || (bytes & 15) || grid < 0 || grid > 65536)
+                                    int n_dst, int64_t bytes, int grid, int64_t tile_bytes,
+                                    int unroll, int access, hipStream_t stream) {
+  const bool ok_n = (n_src == 0 || n_src == 1 || n_src == 8) && (n_dst == 0 || n_dst == 1 || n_dst == 8) &&
+                    (n_src + n_dst) > 0;
+  if (!ok_n || (n_src && !srcs) || (n_dst && !dsts) || bytes < 0 || (bytes & 15) || grid < 0 ||
+      grid > 65536 || tile_bytes < 0 || (tile_bytes & 15) ||
+      (unroll != 0 && unroll != 2 && unroll != 4 && unroll != 8) || access < 0 || access > 3)
     return PURLIN_ERR_INVALID_ARG;
   for (int r = 0; r < n_src; ++r)
     if (!srcs[r] || (uintptr_t(srcs[r]) & 15)) return PURLIN_ERR_INVALID_ARG;
@@ -1022,8 +1026,9 @@ purlin_status purlin_stream_pattern(const void *const *srcs, int n_src, void *co
   DeviceState *ds = nullptr;
   purlin_status st = device_state(&ds);
   if (st != PURLIN_OK) return st;
-  return launch_pattern(srcs, n_src, dsts, n_dst, bytes, grid ? grid : ds->cus * 4, stream) ==
-                 hipSuccess
+  return launch_pattern(srcs, n_src, dsts, n_dst, bytes, grid ? grid : ds->cus * 4,
+                        tile_bytes ? tile_bytes : int64_t(16) << 10, unroll ? unroll : 4,
+                        (access & 1) != 0, (access & 2) != 0, stream) == hipSuccess
              ? PURLIN_OK
              : PURLIN_ERR_HIP;
 }

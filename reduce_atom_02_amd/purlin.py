@@ -102,7 +102,8 @@ def _load():
     lib.purlin_stream_copy.restype = ctypes.c_int
     lib.purlin_stream_pattern.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
-                                          ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+                                          ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     P_VP = ctypes.POINTER(ctypes.c_void_p)
     lib.purlin_moe_dispatch.argtypes = [P_VP, P_VP, ctypes.c_int, ctypes.c_int64, P_VP, P_I64,
                                         P_I64, ctypes.c_int, ctypes.c_void_p]
@@ -430,12 +431,16 @@ def stream_copy(dst, src, nbytes, stream=None):
            "purlin_stream_copy")
 
 
-def stream_pattern(srcs, dsts, nbytes, grid=0, stream=None):
-    """Bare read/write pattern of a collective (ceiling measurement); grid 0
-    is four workgroups per CU."""
-    sa = (ctypes.c_void_p * len(srcs))(*[_ptr(x) for x in srcs])
+def stream_pattern(srcs, dsts, nbytes, grid=0, tile_bytes=0, unroll=0, nt_loads=True,
+                   nt_stores=True, stream=None):
+    """Bare read/write pattern of a collective (ceiling measurement): srcs
+    and dsts hold 0, 1 or 8 buffers each; grid 0 is four workgroups per CU,
+    tile_bytes 0 is 16 KiB, unroll 0 is 4 units per lane."""
+    sa = (ctypes.c_void_p * max(1, len(srcs)))(*[_ptr(x) for x in srcs])
     da = (ctypes.c_void_p * max(1, len(dsts)))(*[_ptr(x) for x in dsts])
+    access = (1 if nt_loads else 0) | (2 if nt_stores else 0)
     _raise(_lib.purlin_stream_pattern(sa, len(srcs), da, len(dsts), int(nbytes), int(grid),
+                                      int(tile_bytes), int(unroll), access,
                                       ctypes.c_void_p(_stream(stream))), "purlin_stream_pattern")
 
 
