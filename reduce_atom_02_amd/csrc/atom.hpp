@@ -61,6 +61,25 @@ __device__ __forceinline__ void st16(uint64_t addr, u32x4 v) {
   else *p = v;
 }
 
+// A 16-byte store to an address that is only 2-byte aligned: one
+// global_store_dwordx4 (gfx950 under the HSA runtime serves misaligned
+// global accesses; the compiler emits this form for any 2-byte-aligned
+// 16-byte access).  The memory system splits it at 16-byte boundaries.
+typedef u32x4 u32x4_a2 __attribute__((aligned(2)));
+template <bool kNT>
+__device__ __forceinline__ void st16u(uint64_t addr, u32x4 v) {
+  gptr<u32x4_a2> p = gp<u32x4_a2>(addr);
+  if constexpr (kNT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// kUS: the destination is off the 16-byte grid (misaligned stores).
+template <bool kNT, bool kUS>
+__device__ __forceinline__ void st16x(uint64_t addr, u32x4 v) {
+  if constexpr (kUS) st16u<kNT>(addr, v);
+  else st16<kNT>(addr, v);
+}
+
 // The 16 bytes that start `sh` bytes into the 32-byte pair (lo, hi);
 // sh in [0, 16) is the same for every lane.
 __device__ __forceinline__ u32x4 funnel(u32x4 lo, u32x4 hi, uint32_t sh) {
@@ -89,14 +108,21 @@ __device__ __forceinline__ void drain_vm() { __builtin_amdgcn_s_waitcnt(0x0F70);
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// IEEE round to nearest, ties to even, of fp32 to bf16.  Overflow carries
-// into the exponent and gives inf; a NaN keeps its sign and top payload bits
-// and gets the quiet bit, so it can never round to inf.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rounded;
+// IEEE round to nearest, ties to even, of two fp32 values to bf16 (lo in
+// the low half, hi in the high half), with gfx950's one packed conversion
+// instruction (v_cvt_pk_bf16_f32) instead of six integer operations per
+// value.  Its results were compared on the device with the integer rule
+// (add 0x7fff plus the lowest kept bit, keep the top half) for every one of
+// the 2^32 fp32 patterns: identical for every non-NaN input (subnormals,
+// ties, overflow to inf, signed zeros), and every NaN input gives a NaN.  A
+// NaN result of a sum may carry any payload (IEEE leaves it open).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t bf16_rne(float f) { return bf16x2_rne(f, 0.0f) & 0xffffu; }
 
 // ---- element operations (head and tail of a tile, < 16 bytes) -------------
 
@@ -286,10 +312,10 @@ __device__ __forceinline__ u32x4 fold_bf16(const u32x4 *x, int n) {
     }
   }
   u32x4 o;
-  o.x = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
-  o.y = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
-  o.z = bf16_rne(a[4]) | (bf16_rne(a[5]) << 16);
-  o.w = bf16_rne(a[6]) | (bf16_rne(a[7]) << 16);
+  o.x = bf16x2_rne(a[0], a[1]);
+  o.y = bf16x2_rne(a[2], a[3]);
+  o.z = bf16x2_rne(a[4], a[5]);
+  o.w = bf16x2_rne(a[6], a[7]);
   return o;
 }
 
@@ -297,7 +323,7 @@ __device__ __forceinline__ u32x4 fold_bf16(const u32x4 *x, int n) {
 // stored.  kGuard = false for passes that lie wholly inside the tile: then
 // the pass is straight-line code, so the compiler keeps every load in
 // flight until its data is needed instead of draining at guard branches.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard>
+template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard, bool kUS = false>
 __device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const uint64_t *db,
                                              int nd, uint32_t nunits, uint32_t u0) {
   constexpr int kS = Op::kSum ? kMaxRanks : 1;
@@ -324,7 +350,7 @@ __device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const u
       const uint64_t o = uint64_t(u * 16u);
 #pragma unroll
       for (int j = 0; j < kMaxRanks + 1; ++j)
-        if (j < nd) st16<kNTS>(db[j] + o, v);
+        if (j < nd) st16x<kNTS, kUS>(db[j] + o, v);
     }
   }
 }
@@ -335,7 +361,10 @@ __device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const u
 // uniform 64-bit base per buffer plus one 32-bit lane offset shared by all
 // buffers, so the loads use the scalar-base form and the sources cost no
 // per-lane address registers.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kOne = false>
+// kUS: the destinations are off the 16-byte grid (every source on one
+// 16-byte phase, the destinations on another): units follow the sources and
+// every store is a misaligned 16-byte store.
+template <class Op, int kU, bool kNTL, bool kNTS, bool kOne = false, bool kUS = false>
 __device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const uint64_t *db,
                                              int nd, uint32_t nunits) {
   constexpr uint32_t kPass = uint32_t(kThreads) * kU;
@@ -355,18 +384,18 @@ __device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const u
           x[k] = ld16<kNTL>(sa[0] + uint64_t((u0 + uint32_t(k) * kThreads + tid) * 16u));
 #pragma unroll
         for (int k = 0; k < kU; ++k)
-          st16<kNTS>(db[0] + uint64_t((u0 + uint32_t(k) * kThreads + tid) * 16u), x[k]);
+          st16x<kNTS, kUS>(db[0] + uint64_t((u0 + uint32_t(k) * kThreads + tid) * 16u), x[k]);
       }
       if (u0 < nunits) {
-        pass_aligned<Op, kU, kNTL, kNTS, true>(sa, ns, db, nd, nunits, u0);
+        pass_aligned<Op, kU, kNTL, kNTS, true, kUS>(sa, ns, db, nd, nunits, u0);
         drain_vm();
       }
       return;
     }
   }
   for (; u0 + kPass <= nunits; u0 += kPass)
-    pass_aligned<Op, kU, kNTL, kNTS, false>(sa, ns, db, nd, nunits, u0);
-  if (u0 < nunits) pass_aligned<Op, kU, kNTL, kNTS, true>(sa, ns, db, nd, nunits, u0);
+    pass_aligned<Op, kU, kNTL, kNTS, false, kUS>(sa, ns, db, nd, nunits, u0);
+  if (u0 < nunits) pass_aligned<Op, kU, kNTL, kNTS, true, kUS>(sa, ns, db, nd, nunits, u0);
 }
 
 // Lane l receives lane l + 1's value (lane 63: unspecified).  kDpp: a DPP
@@ -570,8 +599,20 @@ __device__ __forceinline__ bool src_rows(const Srcs &s, const Dsts &d) {
 // with no head pass.  With e = (dst - src0) mod 128 the boundary sits where
 // the destination is at ceil16(e) mod 128, and src0 there is < 16 bytes
 // past a line start.
+// Whether a job's tiles take source-aligned units with misaligned stores
+// (the launch allows it, every source sits on one 16-byte phase and the
+// destinations on another).
+__device__ __forceinline__ bool shifted_stores(const Srcs &s, const Dsts &d, bool allow) {
+  if (!allow) return false;
+  uint32_t spread = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxRanks; ++i) spread |= uint32_t(s.a[i] - s.a[0]) & 15u;
+  return spread == 0 && (uint32_t(d.b[0] - s.a[0]) & 15u) != 0;
+}
+
 template <class Op>
-__device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
+__device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d, bool shift_stores = false) {
+  if (shifted_stores(s, d, shift_stores)) return s.a[0];
   if (!src_rows<Op>(s, d)) return d.b[0];
   const uint32_t e = uint32_t(d.b[0] - s.a[0]) & 127u;
   return d.b[0] - uint64_t((e + 15u) & 112u);
@@ -602,11 +643,34 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d) {
 template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true, bool kOne = false,
           bool kWide = false, bool kNTS = kNT>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
-                                     bool nt_any_phase = false, int64_t wide_max = 0) {
+                                     bool nt_any_phase = false, int64_t wide_max = 0,
+                                     bool shift_stores = false) {
   if (x1 <= x0) return;
   if (x1 - x0 <= int64_t(kThreads) * Op::kElem) {
     elements<Op>(s, d, x0, x1);
     return;
+  }
+  if constexpr (kRows) {
+    if (shifted_stores(s, d, shift_stores)) {
+      // Every source on one 16-byte phase, the destinations on another:
+      // units follow the sources (the loads are the aligned body's, with no
+      // realignment in registers) and the stores are misaligned.  Head and
+      // tail (< 16 bytes each) are element passes.
+      const int64_t xs =
+          x0 + int64_t((16u - uint32_t((s.a[0] + uint64_t(x0)) & 15u)) & 15u);
+      const uint32_t n16 = uint32_t((x1 - xs) >> 4);
+      const int64_t xe = xs + int64_t(n16) * 16;
+      elements<Op>(s, d, x0, xs);
+      elements<Op>(s, d, xe, x1, kThreads - 64);
+      uint64_t sa[kMaxRanks], db[kMaxRanks + 1];
+#pragma unroll
+      for (int i = 0; i < kMaxRanks; ++i) sa[i] = s.a[i] + uint64_t(xs);
+#pragma unroll
+      for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(xs);
+      if (kNT && nt_any_phase) body_aligned<Op, kU, true, kNTS, kOne, true>(sa, s.n, db, d.n, n16);
+      else body_aligned<Op, kU, false, kNTS, kOne, true>(sa, s.n, db, d.n, n16);
+      return;
+    }
   }
   if constexpr (kRows && kWide) {
     // In the latency regime (the launch sets wide_max), a single-
@@ -651,7 +715,10 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
   const uint32_t nbody = nall - nh;
   // a sum holds eight sources per row, so two rows per wavefront (more
   // measured slower); a copy holds one and takes the tile's unroll
-  constexpr int kUr = Op::kSum ? 2 : kU;
+#ifndef PURLIN_SUM_ROWS
+#define PURLIN_SUM_ROWS 2
+#endif
+  constexpr int kUr = Op::kSum ? PURLIN_SUM_ROWS : kU;
   // The head goes to wavefront 2 when the row body leaves wavefronts 2 and
   // 3 without rows (small tiles, the latency regime), so that no wavefront
   // makes two round trips; otherwise to wavefront 0.

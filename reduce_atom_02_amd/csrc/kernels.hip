@@ -100,10 +100,10 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
     }
     d.b[kMaxRanks] = d.b[0];
     int64_t x0, x1;
-    tile_bounds(atom::line_ref<Op>(s, d), jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
-                p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
+    tile_bounds(atom::line_ref<Op>(s, d, p.shift_stores != 0), jb.nbytes, p.chunk_bytes,
+                t - p.tile_begin[j], p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
     atom::tile<Op, kU, kNTL, true, kRows, kOne, kWide, kNTS>(s, d, x0, x1, p.nt_any_phase != 0,
-                                                  p.wide_max);
+                                                  p.wide_max, p.shift_stores != 0);
   }
   if (p.sync) snac::exit_notify(p, e);
 }
@@ -574,10 +574,10 @@ __global__ void __launch_bounds__(kThreads) moe_combine_kernel(const MoePlan m) 
           }
         }
         atom::u32x4 o;
-        o.x = atom::bf16_rne(a[0]) | (atom::bf16_rne(a[1]) << 16);
-        o.y = atom::bf16_rne(a[2]) | (atom::bf16_rne(a[3]) << 16);
-        o.z = atom::bf16_rne(a[4]) | (atom::bf16_rne(a[5]) << 16);
-        o.w = atom::bf16_rne(a[6]) | (atom::bf16_rne(a[7]) << 16);
+        o.x = atom::bf16x2_rne(a[0], a[1]);
+        o.y = atom::bf16x2_rne(a[2], a[3]);
+        o.z = atom::bf16x2_rne(a[4], a[5]);
+        o.w = atom::bf16x2_rne(a[6], a[7]);
         atom::st16<kNT>(dst + uint64_t(u) * 16u, o);
       }
     }

@@ -75,6 +75,9 @@ struct LaunchPlan {
   int32_t nt_any_phase;     // 1: nontemporal loads even for sources off the line phase
   int32_t wide_max;         // tiles up to this many bytes that would take a row body
                             // take one wide element pass instead (0: never)
+  int32_t shift_stores;     // 1: jobs whose sources share a 16-byte phase off their
+                            // destinations' take source-aligned units, misaligned stores
+  int32_t pad_;
   int32_t tile_begin[kMaxJobs + 1];
   Job jobs[kMaxJobs];
 };

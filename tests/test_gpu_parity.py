@@ -189,14 +189,18 @@ def test_large_unaligned_tiles(purlin, name, dtype, chunk):
     oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, None, shifts, out_shift)
 
 
+@pytest.mark.parametrize("body", ["shifted_stores", "rows"])
 @pytest.mark.parametrize("chunk", [4096, 65536, 0])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_reduce_one_destination_shifted_sources(purlin, dtype, chunk):
+def test_reduce_one_destination_shifted_sources(purlin, dtype, chunk, body, monkeypatch):
     """ReduceScatter whose sources all share one shift off the destination's
-    16-byte phase (as with variable-length partitions): rows aligned to the
-    sources, tiles whose unit counts sit on and around the 512-unit passes."""
+    16-byte phase (as with variable-length partitions), in both tile forms:
+    source-aligned units with misaligned stores (the default for sums) and
+    the realigning row body that follows the sources' lines (folded before
+    the shift); tiles whose unit counts sit on and around the passes."""
     P = 8
-    print("case reduce-shifted", dtype, chunk, flush=True)
+    print("case reduce-shifted", dtype, chunk, body, flush=True)
+    monkeypatch.setenv("PURLIN_SHIFT_STORES", "1" if body == "shifted_stores" else "0")
     esz = 4 if dtype == "f32" else 2
     per = 16 // esz
     rng = np.random.default_rng([23, esz, chunk])
@@ -244,7 +248,7 @@ def test_rows_at_pass_boundaries(purlin, name, dtype, unroll):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("name", ["reducescatter", "alltoall"])
-def test_wide_element_pass_at_its_size_limit(purlin, name, dtype):
+def test_wide_element_pass_at_its_size_limit(purlin, name, dtype, monkeypatch):
     """Small misaligned single-destination tiles in the latency regime (4 KiB
     chunks, under 512 KiB of jobs) take one wide element pass instead of a
     row body when they hold at most 4224 bytes: partitions on both sides of
@@ -262,10 +266,14 @@ def test_wide_element_pass_at_its_size_limit(purlin, name, dtype):
     counts = pins.counts_for(name, P, sizes)
     ins, outs = pins.make_case(name, P, counts, dtype, rng, None, sentinel=0x6B6B)
     purlin.set_policy(zero_staging="zs")
-    for shift in range(1, per):
-        oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, None, [shift] * P, [0] * P)
-        info = purlin.last_launch()
-        assert info["chunk_bytes"] == 4096, info
+    # sums whose sources share one phase take source-aligned units by
+    # default; the wide pass is their form without that
+    for shifted in (("1", "0") if name == "reducescatter" else ("0",)):
+        monkeypatch.setenv("PURLIN_SHIFT_STORES", shifted)
+        for shift in range(1, per):
+            oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, None, [shift] * P, [0] * P)
+            info = purlin.last_launch()
+            assert info["chunk_bytes"] == 4096, info
 
 
 @pytest.mark.parametrize("name", ["alltoall", "allgather", "reducescatter"])
