@@ -398,6 +398,63 @@ __device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const u
   if (u0 < nunits) pass_aligned<Op, kU, kNTL, kNTS, true, kUS>(sa, ns, db, nd, nunits, u0);
 }
 
+// ---- LDS-staged body (experimental build) ----------------------------------
+// Aligned jobs staged through LDS with gfx950's 16-byte global-to-LDS loads.
+// The workgroup's rows (64 units = 1 KiB of each source) go in batches of
+// 4 * kR rows; wavefront w takes rows w, w + 4, ... of a batch, loads every
+// source row of them straight into its own LDS slice (no VGPR holds data in
+// flight), waits once for all of them, reads each lane's units back, folds
+// them (sums) and stores them: per wavefront a burst of loads, then a burst
+// of stores.  The units after the last whole batch take the register
+// passes.  `slice` is this wavefront's kS * kR KiB of LDS.
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+template <class Op, int kR, int kU, bool kNTL, bool kNTS>
+__device__ __forceinline__ void body_lds(const uint64_t *sa, int ns, const uint64_t *db, int nd,
+                                         uint32_t nunits, lds_u32x4 *slice) {
+  constexpr int kS = Op::kSum ? kMaxRanks : 1;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = uint32_t(__builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)));
+  const uint32_t nrows = nunits >> 6;
+  constexpr uint32_t kBatch = 4u * kR;
+  uint32_t r0 = 0;
+  for (; r0 + kBatch <= nrows; r0 += kBatch) {
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const uint64_t off = (uint64_t(r0 + wave + 4u * uint32_t(k)) * 64u + lane) * 16u;
+#pragma unroll
+      for (int i = 0; i < kS; ++i)
+        __builtin_amdgcn_global_load_lds(gp<const void>(sa[i] + off),
+                                         reinterpret_cast<__attribute__((address_space(3))) void *>(
+                                             slice + (k * kS + i) * 64),
+                                         16, 0, kNTL ? 2 : 0);
+    }
+    drain_vm();  // every row of the batch is in LDS
+    u32x4 v[kR];
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      u32x4 x[kS];
+#pragma unroll
+      for (int i = 0; i < kS; ++i) x[i] = slice[(k * kS + i) * 64 + int(lane)];
+      if constexpr (!Op::kSum) v[k] = x[0];
+      else if constexpr (Op::kElem == 4) v[k] = fold_f32(x, ns);
+      else v[k] = fold_bf16(x, ns);
+    }
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const uint64_t off = (uint64_t(r0 + wave + 4u * uint32_t(k)) * 64u + lane) * 16u;
+#pragma unroll
+      for (int j = 0; j < kMaxRanks + 1; ++j)
+        if (j < nd) st16<kNTS>(db[j] + off, v[k]);
+    }
+  }
+  constexpr uint32_t kPass = uint32_t(kThreads) * kU;
+  uint32_t u0 = r0 * 64u;
+  for (; u0 + kPass <= nunits; u0 += kPass)
+    pass_aligned<Op, kU, kNTL, kNTS, false>(sa, ns, db, nd, nunits, u0);
+  if (u0 < nunits) pass_aligned<Op, kU, kNTL, kNTS, true>(sa, ns, db, nd, nunits, u0);
+}
+
 // Lane l receives lane l + 1's value (lane 63: unspecified).  kDpp: a DPP
 // wavefront shift (wave_shl:1), a plain VALU move; else __shfl_down, which
 // goes through the LDS crossbar (ds_bpermute).  Copies take the DPP move;
@@ -641,10 +698,10 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d, bool 
 // or when nt_any_phase asks for it (measured faster for misaligned
 // variable-length partitions too).  A tile spans less than 4 GiB.
 template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true, bool kOne = false,
-          bool kWide = false, bool kNTS = kNT>
+          bool kWide = false, bool kNTS = kNT, int kLdsRows = 0>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
                                      bool nt_any_phase = false, int64_t wide_max = 0,
-                                     bool shift_stores = false) {
+                                     bool shift_stores = false, lds_u32x4 *lds_slice = nullptr) {
   if (x1 <= x0) return;
   if (x1 - x0 <= int64_t(kThreads) * Op::kElem) {
     elements<Op>(s, d, x0, x1);
@@ -732,6 +789,11 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
   for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(xh);
   const bool ntl = kNT && (phase == 0 || nt_any_phase);
   if (any == 0) {
+    if constexpr (kLdsRows > 0) {
+      if (ntl) body_lds<Op, kLdsRows, kU, true, kNTS>(sa, s.n, db, d.n, nbody, lds_slice);
+      else body_lds<Op, kLdsRows, kU, false, kNTS>(sa, s.n, db, d.n, nbody, lds_slice);
+      return;
+    }
     if (ntl) body_aligned<Op, kU, true, kNTS, kOne>(sa, s.n, db, d.n, nbody);
     else body_aligned<Op, kU, false, kNTS, kOne>(sa, s.n, db, d.n, nbody);
     return;

@@ -108,6 +108,51 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
   if (p.sync) snac::exit_notify(p, e);
 }
 
+// The zero-staging kernel for launches whose every job is aligned, with the
+// LDS-staged body (kLdsRows rows of 64 units per wavefront and batch): an
+// experimental build, selected with PURLIN_LDS=1.
+template <class Op, int kU, bool kNTS, bool kOne, int kLdsRows>
+__global__ void __launch_bounds__(kThreads) zs_lds_kernel(const LaunchPlan p) {
+  constexpr int kS = Op::kSum ? kMaxRanks : 1;
+  constexpr int kSlice = kS * kLdsRows * 64;  // 16-byte units per wavefront
+  __shared__ atom::u32x4 lds[4 * kSlice];
+  atom::lds_u32x4 *slice =
+      (atom::lds_u32x4 *)(&lds[0]) + int(__builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6))) * kSlice;
+  uint32_t e = 0;
+  bool run = true;
+  if (p.sync) {
+    e = snac::launch_epoch(p);
+    run = snac::entry(p, e);
+  }
+  int t = run ? int(blockIdx.x) : p.total_tiles;
+  int j = t < p.total_tiles ? job_of_tile(p, t) : 0;
+  for (; t < p.total_tiles; t += gridDim.x) {
+    if (t >= p.tile_begin[j + 1]) j = job_of_tile(p, t);
+    const Job jb = p.jobs[j];
+    atom::Srcs s;
+    job_srcs(p, jb, s);
+    atom::Dsts d;
+    if (kOne && jb.dst < 0) continue;
+    if (!kOne && jb.dst < 0) {
+      d.n = p.P;
+#pragma unroll
+      for (int k = 0; k < kMaxRanks; ++k)
+        d.b[k] = uint64_t(p.out[k < p.P ? k : 0]) + uint64_t(jb.dst_off);
+    } else {
+      d.n = 1;
+#pragma unroll
+      for (int k = 0; k < kMaxRanks; ++k) d.b[k] = uint64_t(p.out[jb.dst]) + uint64_t(jb.dst_off);
+    }
+    d.b[kMaxRanks] = d.b[0];
+    int64_t x0, x1;
+    tile_bounds(d.b[0], jb.nbytes, p.chunk_bytes, t - p.tile_begin[j],
+                p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
+    atom::tile<Op, kU, true, true, false, kOne, false, kNTS, kLdsRows>(
+        s, d, x0, x1, p.nt_any_phase != 0, 0, false, slice);
+  }
+  if (p.sync) snac::exit_notify(p, e);
+}
+
 // ---- staged SNAC pipeline --------------------------------------------------
 // Each job runs on `lanes` parallel pipelines; chunk c goes to lane c % lanes.
 // Per lane the job has three kinds of workgroup, numbered in this order (so
@@ -892,6 +937,31 @@ hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_s
   void *args[] = {const_cast<LaunchPlan *>(&p)};
   return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel, rows, one, wide, bcast), dim3(grid),
                          dim3(kThreads), args, 0, stream);
+}
+
+static void *zs_lds_fn(KernelKind kind, bool one, bool bcast) {
+  switch (kind) {
+    case KernelKind::kCopy:
+      if (one) return reinterpret_cast<void *>(&zs_lds_kernel<atom::CopyOp, 4, true, true, 8>);
+      return bcast ? reinterpret_cast<void *>(&zs_lds_kernel<atom::CopyOp, 4, false, false, 8>)
+                   : reinterpret_cast<void *>(&zs_lds_kernel<atom::CopyOp, 4, true, false, 8>);
+    case KernelKind::kSumF32:
+      return one ? reinterpret_cast<void *>(&zs_lds_kernel<atom::SumF32, 1, true, true, 2>)
+                 : reinterpret_cast<void *>(&zs_lds_kernel<atom::SumF32, 1, true, false, 2>);
+    default:
+      return one ? reinterpret_cast<void *>(&zs_lds_kernel<atom::SumBf16, 1, true, true, 2>)
+                 : reinterpret_cast<void *>(&zs_lds_kernel<atom::SumBf16, 1, true, false, 2>);
+  }
+}
+
+hipError_t launch_zs_lds(const LaunchPlan &p, KernelKind kind, bool one, bool bcast, int grid,
+                         hipStream_t stream) {
+  void *args[] = {const_cast<LaunchPlan *>(&p)};
+  return hipLaunchKernel(zs_lds_fn(kind, one, bcast), dim3(grid), dim3(kThreads), args, 0, stream);
+}
+
+hipError_t zs_lds_resident_per_cu(KernelKind kind, bool one, bool bcast, int *blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, zs_lds_fn(kind, one, bcast), kThreads, 0);
 }
 
 hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStream_t stream) {

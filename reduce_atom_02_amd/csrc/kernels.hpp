@@ -21,6 +21,11 @@ enum class KernelKind { kCopy, kSumF32, kSumBf16 };
 hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, bool rows,
                      bool one, bool wide, bool bcast, int grid, hipStream_t stream);
 hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStream_t stream);
+// The zero-staging build with the LDS-staged aligned body (launches whose
+// every job is aligned; one: single-destination jobs; bcast: plain stores).
+hipError_t launch_zs_lds(const LaunchPlan &p, KernelKind kind, bool one, bool bcast, int grid,
+                         hipStream_t stream);
+hipError_t zs_lds_resident_per_cu(KernelKind kind, bool one, bool bcast, int *blocks);
 int unroll_of(KernelKind kind, int unroll_sel);
 // Whether a launch whose jobs all have one destination rank (single_dst) runs
 // the single-destination build (the `one` argument of launch_zs).

@@ -640,7 +640,15 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     // on AllGatherV and 4-11% on AllToAllV.
     const int64_t shift_env = env_i64("PURLIN_SHIFT_STORES", -1);
     lp.shift_stores = (shift_env < 0 ? kind != KernelKind::kCopy : shift_env != 0) ? 1 : 0;
-    err = launch_zs(lp, kind, nt, unroll_sel, rows, one, wide, bcast, grid, stream);
+    const bool lds = !rows && nt && env_i64("PURLIN_LDS", 0) != 0;
+    if (lds) {
+      int b = 0;
+      if (zs_lds_resident_per_cu(kind, single_dst, bcast, &b) != hipSuccess || b < 1) b = 1;
+      const int g = std::min(grid, ds->cus * b);
+      err = launch_zs_lds(lp, kind, single_dst, bcast, g, stream);
+    } else {
+      err = launch_zs(lp, kind, nt, unroll_sel, rows, one, wide, bcast, grid, stream);
+    }
     info.grid = grid;
     info.zero_staging = 1;
     info.rows = rows ? 1 : 0;
