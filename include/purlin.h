@@ -66,7 +66,9 @@ typedef enum {
                                  the call would need new workspace during graph capture */
   PURLIN_ERR_NO_MEMORY = 3,   /* workspace allocation failed */
   PURLIN_ERR_HIP = 4,         /* a HIP call or kernel launch failed */
-  PURLIN_ERR_TIMEOUT = 5      /* a bounded device wait expired (see purlin_check) */
+  PURLIN_ERR_TIMEOUT = 5,     /* a bounded device wait expired (see purlin_check) */
+  PURLIN_ERR_PROTOCOL = 6     /* the protocol-checking build saw a flag, credit or staging-slot
+                                 header other than the protocol allows (see purlin_check) */
 } purlin_status;
 
 typedef enum { PURLIN_OP_COPY = 0, PURLIN_OP_SUM = 1 } purlin_op;
@@ -228,7 +230,11 @@ PURLIN_API purlin_status purlin_collective_noalloc(const purlin_layout *in,
 
 /* Synchronize `stream`, then read and clear that stream's device status
  * word (current device): PURLIN_ERR_TIMEOUT if any wait of a call on the
- * stream expired since the last check, else PURLIN_ERR_INVALID_ARG if a
+ * stream expired since the last check, else PURLIN_ERR_PROTOCOL if the
+ * library was built with PURLIN_DEBUG_PROTOCOL and one of its checks failed
+ * (a staged flag or credit past the value the protocol allows at that
+ * point, or a staging slot whose header or canary is not the one its
+ * producer wrote for that chunk), else PURLIN_ERR_INVALID_ARG if a
  * device-side argument check failed (MoE indices), PURLIN_ERR_HIP if the
  * synchronization failed, else PURLIN_OK.  This call synchronizes. */
 PURLIN_API purlin_status purlin_check(hipStream_t stream);

@@ -1,6 +1,7 @@
 """Build libpurlin.so (HIP for gfx950) in place, next to this file.
 
-    python -m reduce_atom_02_amd.build
+    python -m reduce_atom_02_amd.build            # libpurlin.so
+    python -m reduce_atom_02_amd.build --debug    # libpurlin_debug.so (protocol checks)
 
 Every source under csrc/ is compiled by hipcc into one shared library with
 no dependency other than the HIP runtime.  Packed fp32 instructions are
@@ -26,9 +27,19 @@ FLAGS = [
 ]
 
 
-def build(verbose=False, extra=()):
+DEBUG_LIB = os.path.join(HERE, "libpurlin_debug.so")
+
+
+def build(verbose=False, extra=(), debug=False):
+    """Build libpurlin.so, or with debug=True libpurlin_debug.so: the same
+    library with the staged protocol's checks compiled in
+    (PURLIN_DEBUG_PROTOCOL: exact flag and credit values, slot headers and
+    canaries, reported by purlin_check as PURLIN_ERR_PROTOCOL)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+    lib = DEBUG_LIB if debug else LIB
+    if debug:
+        extra = list(extra) + ["-DPURLIN_DEBUG_PROTOCOL"]
+    tmp = lib + ".tmp"
     cmd = [HIPCC] + FLAGS + list(extra) + ["-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -41,9 +52,9 @@ def build(verbose=False, extra=()):
         lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
         if lines:
             sys.stderr.write("\n".join(lines) + "\n")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, debug="--debug" in sys.argv))

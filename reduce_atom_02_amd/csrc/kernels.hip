@@ -202,6 +202,62 @@ __device__ __forceinline__ uint64_t tag(uint32_t epoch, uint64_t v) {
   return (uint64_t(epoch) << 32) | v;
 }
 
+// ---- protocol checks (built with PURLIN_DEBUG_PROTOCOL) ---------------------
+// A producer writes, after a slot's data and before its ready notify, a
+// header (the launch epoch and the chunk index) and a canary word at byte
+// chunk_bytes + 128 of the slot, past every byte a chunk can occupy (the
+// data starts at most 127 bytes into the slot); a consumer checks both after
+// its wait.  A consumer also checks that the flag it waited for holds exactly
+// the value it waited for, and a producer that its credits are exactly the
+// round's: with the protocol right, no producer can run a round ahead.  A
+// failed check sets the status bit that purlin_check reports as
+// PURLIN_ERR_PROTOCOL.
+#ifdef PURLIN_DEBUG_PROTOCOL
+constexpr bool kCheckProtocol = true;
+#else
+constexpr bool kCheckProtocol = false;
+#endif
+constexpr uint64_t kSlotCanary = 0xc0ffee5a5aa5f00dull;
+
+[[maybe_unused]] __device__ __forceinline__ void flag_protocol(const LaunchPlan &p) {
+  __hip_atomic_fetch_or(&p.flags[kFlagStatus], kStatusProtocol, __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_AGENT);
+}
+
+[[maybe_unused]] __device__ __forceinline__ uint64_t *slot_header(const StagedPlan &sp,
+                                                                   uint64_t slot_data) {
+  return reinterpret_cast<uint64_t *>(slot_data + uint64_t(sp.base.chunk_bytes) + 128u);
+}
+
+// thread 0 of a producer, after its drain and before its ready notify
+__device__ __forceinline__ void write_header(const StagedPlan &sp, uint64_t slot_data, uint32_t e,
+                                             int chunk) {
+  if constexpr (kCheckProtocol) {
+    uint64_t *h = slot_header(sp, slot_data);
+    h[0] = tag(e, uint64_t(chunk) + 1u);
+    h[1] = kSlotCanary;
+    __threadfence();  // the header is visible before the release that follows
+  }
+}
+
+// thread 0 of a consumer, after its wait (and acquire)
+__device__ __forceinline__ void check_header(const StagedPlan &sp, uint64_t slot_data, uint32_t e,
+                                             int chunk) {
+  if constexpr (kCheckProtocol) {
+    const uint64_t *h = slot_header(sp, slot_data);
+    if (__hip_atomic_load(&h[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+            tag(e, uint64_t(chunk) + 1u) ||
+        __hip_atomic_load(&h[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != kSlotCanary)
+      flag_protocol(sp.base);
+  }
+}
+
+// thread 0, after a wait that saw *f reach `target`: it must not be past it
+__device__ __forceinline__ void check_exact(const LaunchPlan &p, const uint64_t *f, uint64_t target) {
+  if constexpr (kCheckProtocol)
+    if (snac::load_rlx(f) != target) flag_protocol(p);
+}
+
 template <class Op, int kU, bool kNTL, bool kNTS>
 __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
   const LaunchPlan &p = sp.base;
@@ -258,6 +314,8 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
           __hip_atomic_store(o.credit, tag(e, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else if (!snac::wait_geq<uint64_t, false>(o.credit, tag(e, round * uint64_t(team)), p, e)) {
           ok = 0;
+        } else {
+          check_exact(p, o.credit, tag(e, round * uint64_t(team)));
         }
       }
       __syncthreads();
@@ -281,6 +339,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       // them and the owner read a stale line.
       snac::drain_workgroup();
       if (threadIdx.x == 0) {
+        write_header(sp, o.data, e, c);
         const bool withhold = sp.withhold > 0 && ring == 0 && m + 1 == sp.withhold;
         if (!withhold) snac::store_rel(o.ready, tag(e, round + 1));
       }
@@ -304,12 +363,21 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
           if (!snac::wait_geq<uint64_t, false>(slot_ref(sp, ring0 + k, slot).ready, tag(e, round + 1), p, e))
             ok = 0;
         if (sj.n_stage > 0 && ok) snac::acquire_fence();
+        if (kCheckProtocol && ok) {
+          for (int k = 0; k < sj.n_stage; ++k) {
+            const SlotRef o = slot_ref(sp, ring0 + k, slot);
+            check_exact(p, o.ready, tag(e, round + 1));
+            check_header(sp, o.data, e, c);
+          }
+        }
         if (sj.n_scatter > 0 && ok) {
           const SlotRef o = slot_ref(sp, ring0 + sj.n_stage, slot);
           if (round == 0) {
             __hip_atomic_store(o.credit, tag(e, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           } else if (!snac::wait_geq<uint64_t, false>(o.credit, tag(e, round * sj.n_scatter), p, e)) {
             ok = 0;
+          } else {
+            check_exact(p, o.credit, tag(e, round * sj.n_scatter));
           }
         }
       }
@@ -371,8 +439,11 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       if (threadIdx.x == 0) {
         for (int k = 0; k < sj.n_stage; ++k)
           snac::add_rlx(slot_ref(sp, ring0 + k, slot).credit, uint64_t(1));
-        if (sj.n_scatter > 0)
+        if (sj.n_scatter > 0) {
+          // the team's last member writes the scatter slot's header
+          if (t + 1 == team) write_header(sp, slot_ref(sp, ring0 + sj.n_stage, slot).data, e, c);
           snac::store_rel(slot_ref(sp, ring0 + sj.n_stage, slot).ready + t, tag(e, round + 1));
+        }
       }
     }
   } else {
@@ -392,6 +463,10 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
         for (int q = 0; q < team && ok; ++q)
           if (!snac::wait_geq<uint64_t, false>(o.ready + q, tag(e, round + 1), p, e)) ok = 0;
         if (ok) snac::acquire_fence();
+        if (kCheckProtocol && ok) {
+          for (int q = 0; q < team; ++q) check_exact(p, o.ready + q, tag(e, round + 1));
+          check_header(sp, o.data, e, c);
+        }
       }
       __syncthreads();
       if (!ok) break;

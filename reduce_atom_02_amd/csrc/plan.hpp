@@ -40,6 +40,7 @@ enum FlagWord : int {
 constexpr int exit_word(int slot) { return kFlagExit + slot * kFlagStride; }
 constexpr uint32_t kStatusTimeout = 1u;
 constexpr uint32_t kStatusBadArg = 2u;   // a device-side argument check failed (MoE indices)
+constexpr uint32_t kStatusProtocol = 4u; // a protocol check of the debug build failed
 
 struct Job {
   int64_t src_off;  // byte offset into in[src] (into every in[i] when src < 0)

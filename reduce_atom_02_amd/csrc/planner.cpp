@@ -29,6 +29,18 @@ struct Part {
 
 bool valid_naming(int n) { return n >= PURLIN_NAME_WHOLE && n <= PURLIN_NAME_BY_INDEX_RANK; }
 
+// Components of a naming's names: () for WHOLE, (r) or (q), (r, q) or (q, r).
+// Names of different lengths never match, even where their numbers in the
+// counts array coincide (P = 1).
+int name_arity(purlin_naming n) {
+  switch (n) {
+    case PURLIN_NAME_WHOLE: return 0;
+    case PURLIN_NAME_BY_RANK:
+    case PURLIN_NAME_BY_INDEX: return 1;
+    default: return 2;
+  }
+}
+
 // Partitions of rank r's buffer under naming n; displs_side may be null (packed).
 int parts_of(purlin_naming n, int r, int P, const int64_t *counts, const int64_t *displs_side,
              Part *out) {
@@ -91,7 +103,8 @@ purlin_status derive(purlin_naming in_naming, purlin_naming out_naming, purlin_o
   if (displs)
     for (int k = 0; k < 2 * std::min(nn, nn_out); ++k)
       if (displs[k] < 0 || displs[k] > kMaxCount) return PURLIN_ERR_INVALID_ARG;
-  if (nn_out != nn) return PURLIN_ERR_UNSUPPORTED;  // no name can match
+  // no name can match
+  if (nn_out != nn || name_arity(in_naming) != name_arity(out_naming)) return PURLIN_ERR_UNSUPPORTED;
 
   const int esz = dtype == PURLIN_F32 ? 4 : 2;
   const int64_t *in_d = displs ? displs : nullptr;

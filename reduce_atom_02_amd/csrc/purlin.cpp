@@ -765,6 +765,7 @@ const char *purlin_strerror(purlin_status s) {
     case PURLIN_ERR_NO_MEMORY: return "out of device memory";
     case PURLIN_ERR_HIP: return "HIP error";
     case PURLIN_ERR_TIMEOUT: return "device wait timed out";
+    case PURLIN_ERR_PROTOCOL: return "protocol check failed";
   }
   return "unknown status";
 }
@@ -1004,6 +1005,7 @@ purlin_status purlin_check(hipStream_t stream) {
   }
   if (status == 0) return PURLIN_OK;
   if (status & kStatusTimeout) return PURLIN_ERR_TIMEOUT;
+  if (status & kStatusProtocol) return PURLIN_ERR_PROTOCOL;
   return (status & kStatusBadArg) ? PURLIN_ERR_INVALID_ARG : PURLIN_ERR_HIP;
 }
 

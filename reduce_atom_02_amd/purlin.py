@@ -23,12 +23,16 @@ __all__ = [
     "name_count", "extents", "check_tensors",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpurlin.so")
+# PURLIN_LIBRARY names another build of the library to load (the tests load
+# libpurlin_debug.so, the build with the protocol checks, this way).
+LIB_PATH = os.environ.get("PURLIN_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpurlin.so")
 
 NAMINGS = {"whole": 0, "by_rank": 1, "by_index": 2, "by_rank_index": 3, "by_index_rank": 4}
 OPS = {"copy": 0, "sum": 1}
 DTYPES = {"f32": 0, "bf16": 1}
-STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "NO_MEMORY", 4: "HIP", 5: "TIMEOUT"}
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "NO_MEMORY", 4: "HIP", 5: "TIMEOUT",
+          6: "PROTOCOL"}
 STAGING = {"auto": 0, "zs": 1, "staged": 2}
 ENGINES = {"auto": 0, "shader": 1, "copy": 2}
 

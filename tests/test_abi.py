@@ -145,6 +145,13 @@ def test_unsupported_triples(purlin):
     assert st(purlin, "by_index", "by_rank", "copy", "bf16", [4] * 8) == "UNSUPPORTED"
     assert st(purlin, "by_rank_index", "by_rank_index", "copy", "bf16", [2] * 64) == "OK"
     assert st(purlin, "by_index", "by_index", "sum", "bf16", [4] * 8) == "OK"
+    # at P = 1 every naming has one name, but names of different lengths
+    # never match: () is not (0), and (0) is not (0, 0)
+    for i_, o_ in (("whole", "by_rank"), ("by_index", "whole"), ("by_rank", "by_rank_index"),
+                   ("by_index_rank", "by_index")):
+        for op in ("copy", "sum"):
+            assert st(purlin, i_, o_, op, "bf16", [4], P=1) == "UNSUPPORTED", (i_, o_, op)
+    assert st(purlin, "by_rank", "by_index", "copy", "bf16", [4], P=1) == "OK"
 
 
 def test_null_layouts(purlin):
@@ -172,6 +179,7 @@ def test_policy_roundtrip_and_validation(purlin):
 
 def test_strerror(purlin):
     assert purlin._lib.purlin_strerror(5) == b"device wait timed out"
+    assert purlin._lib.purlin_strerror(6) == b"protocol check failed"
     assert purlin._lib.purlin_strerror(42) == b"unknown status"
 
 
