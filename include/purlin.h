@@ -155,6 +155,12 @@ typedef struct {
                             at most 128 MiB each way */
   int32_t engine_copies; /* copy-engine transfers enqueued (PURLIN_ENGINE_COPY; grid is then
                             0: no kernel ran), 0 for kernel launches */
+  int32_t shift_stores;  /* zero staging: 1 if jobs whose sources share a 16-byte phase off
+                            their destination's took source-aligned units and misaligned
+                            stores (reductions) */
+  int32_t unaligned_loads; /* zero staging: 1 if jobs with a source off their destinations'
+                              phase took destination-aligned units and misaligned loads
+                              (copy broadcasts of 32 - 512 MiB of jobs) */
 } purlin_launch_info;
 
 /*

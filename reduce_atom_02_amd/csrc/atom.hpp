@@ -73,6 +73,21 @@ __device__ __forceinline__ void st16u(uint64_t addr, u32x4 v) {
   else *p = v;
 }
 
+// A 16-byte load from an address that is only 2-byte aligned (as st16u).
+template <bool kNT>
+__device__ __forceinline__ u32x4 ld16u(uint64_t addr) {
+  gptr<const u32x4_a2> p = gp<const u32x4_a2>(addr);
+  if constexpr (kNT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+// kUL: the source is off the 16-byte grid (misaligned loads).
+template <bool kNT, bool kUL>
+__device__ __forceinline__ u32x4 ld16x(uint64_t addr) {
+  if constexpr (kUL) return ld16u<kNT>(addr);
+  else return ld16<kNT>(addr);
+}
+
 // kUS: the destination is off the 16-byte grid (misaligned stores).
 template <bool kNT, bool kUS>
 __device__ __forceinline__ void st16x(uint64_t addr, u32x4 v) {
@@ -323,7 +338,7 @@ __device__ __forceinline__ u32x4 fold_bf16(const u32x4 *x, int n) {
 // stored.  kGuard = false for passes that lie wholly inside the tile: then
 // the pass is straight-line code, so the compiler keeps every load in
 // flight until its data is needed instead of draining at guard branches.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard, bool kUS = false>
+template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard, bool kUS = false, bool kUL = false>
 __device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const uint64_t *db,
                                              int nd, uint32_t nunits, uint32_t u0) {
   constexpr int kS = Op::kSum ? kMaxRanks : 1;
@@ -337,7 +352,7 @@ __device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const u
     if (kGuard && u >= nunits) u = nunits - 1;
     const uint64_t o = uint64_t(u * 16u);
 #pragma unroll
-    for (int i = 0; i < kS; ++i) x[k][i] = ld16<kNTL>(sa[i] + o);
+    for (int i = 0; i < kS; ++i) x[k][i] = ld16x<kNTL, kUL>(sa[i] + o);
   }
 #pragma unroll
   for (int k = 0; k < kU; ++k) {
@@ -364,7 +379,8 @@ __device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const u
 // kUS: the destinations are off the 16-byte grid (every source on one
 // 16-byte phase, the destinations on another): units follow the sources and
 // every store is a misaligned 16-byte store.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kOne = false, bool kUS = false>
+template <class Op, int kU, bool kNTL, bool kNTS, bool kOne = false, bool kUS = false,
+          bool kUL = false>
 __device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const uint64_t *db,
                                              int nd, uint32_t nunits) {
   constexpr uint32_t kPass = uint32_t(kThreads) * kU;
@@ -381,21 +397,21 @@ __device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const u
         u32x4 x[kU];
 #pragma unroll
         for (int k = 0; k < kU; ++k)
-          x[k] = ld16<kNTL>(sa[0] + uint64_t((u0 + uint32_t(k) * kThreads + tid) * 16u));
+          x[k] = ld16x<kNTL, kUL>(sa[0] + uint64_t((u0 + uint32_t(k) * kThreads + tid) * 16u));
 #pragma unroll
         for (int k = 0; k < kU; ++k)
           st16x<kNTS, kUS>(db[0] + uint64_t((u0 + uint32_t(k) * kThreads + tid) * 16u), x[k]);
       }
       if (u0 < nunits) {
-        pass_aligned<Op, kU, kNTL, kNTS, true, kUS>(sa, ns, db, nd, nunits, u0);
+        pass_aligned<Op, kU, kNTL, kNTS, true, kUS, kUL>(sa, ns, db, nd, nunits, u0);
         drain_vm();
       }
       return;
     }
   }
   for (; u0 + kPass <= nunits; u0 += kPass)
-    pass_aligned<Op, kU, kNTL, kNTS, false, kUS>(sa, ns, db, nd, nunits, u0);
-  if (u0 < nunits) pass_aligned<Op, kU, kNTL, kNTS, true, kUS>(sa, ns, db, nd, nunits, u0);
+    pass_aligned<Op, kU, kNTL, kNTS, false, kUS, kUL>(sa, ns, db, nd, nunits, u0);
+  if (u0 < nunits) pass_aligned<Op, kU, kNTL, kNTS, true, kUS, kUL>(sa, ns, db, nd, nunits, u0);
 }
 
 // ---- LDS-staged body (experimental build) ----------------------------------
@@ -701,7 +717,8 @@ template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true, bo
           bool kWide = false, bool kNTS = kNT, int kLdsRows = 0>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
                                      bool nt_any_phase = false, int64_t wide_max = 0,
-                                     bool shift_stores = false, lds_u32x4 *lds_slice = nullptr) {
+                                     bool shift_stores = false, lds_u32x4 *lds_slice = nullptr,
+                                     bool unaligned_loads = false) {
   if (x1 <= x0) return;
   if (x1 - x0 <= int64_t(kThreads) * Op::kElem) {
     elements<Op>(s, d, x0, x1);
@@ -797,6 +814,16 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
     if (ntl) body_aligned<Op, kU, true, kNTS, kOne>(sa, s.n, db, d.n, nbody);
     else body_aligned<Op, kU, false, kNTS, kOne>(sa, s.n, db, d.n, nbody);
     return;
+  }
+  if constexpr (kRows) {
+    if (unaligned_loads) {
+      // Destination-aligned units whose sources are read with misaligned
+      // 16-byte loads (no lane shuffles, no block past a row; lines at the
+      // ends of a wavefront's range may be read twice).
+      if (ntl) body_aligned<Op, kU, true, kNTS, kOne, false, true>(sa, s.n, db, d.n, nbody);
+      else body_aligned<Op, kU, false, kNTS, kOne, false, true>(sa, s.n, db, d.n, nbody);
+      return;
+    }
   }
   if constexpr (!kRows) {
     // Built without the row bodies (the launch checked that every job is

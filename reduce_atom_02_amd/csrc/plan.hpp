@@ -78,7 +78,8 @@ struct LaunchPlan {
                             // take one wide element pass instead (0: never)
   int32_t shift_stores;     // 1: jobs whose sources share a 16-byte phase off their
                             // destinations' take source-aligned units, misaligned stores
-  int32_t pad_;
+  int32_t unaligned_loads;  // 1: jobs with a source off their destinations' 16-byte phase take
+                            // destination-aligned units, misaligned loads
   int32_t tile_begin[kMaxJobs + 1];
   Job jobs[kMaxJobs];
 };

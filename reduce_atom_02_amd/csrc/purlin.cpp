@@ -640,6 +640,17 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     // on AllGatherV and 4-11% on AllToAllV.
     const int64_t shift_env = env_i64("PURLIN_SHIFT_STORES", -1);
     lp.shift_stores = (shift_env < 0 ? kind != KernelKind::kCopy : shift_env != 0) ? 1 : 0;
+    // Copy broadcasts whose source is off the destinations' phase
+    // (AllGatherV) with 32 - 512 MiB of jobs take destination-aligned units
+    // with misaligned source loads instead of the row body: +2-4% at 64 and
+    // 256 MiB per rank (paired, two runs); at 16 MiB -3%, at 1 GiB even, in
+    // the latency regime slower.  The other copies keep the row body
+    // (AllToAllV 4-9% slower with misaligned loads), and reductions their
+    // misaligned stores.
+    const int64_t ul_env = env_i64("PURLIN_UNALIGNED_LOADS", -1);
+    const bool ul_auto = kind == KernelKind::kCopy && broadcast &&
+                         job_bytes >= (int64_t(32) << 20) && job_bytes <= (int64_t(512) << 20);
+    lp.unaligned_loads = (ul_env < 0 ? ul_auto : ul_env != 0) ? 1 : 0;
     const bool lds = !rows && nt && env_i64("PURLIN_LDS", 0) != 0;
     if (lds) {
       int b = 0;
@@ -654,6 +665,8 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     info.rows = rows ? 1 : 0;
     info.one = one ? 1 : 0;
     info.plain_stores = bcast ? 1 : 0;
+    info.shift_stores = lp.shift_stores;
+    info.unaligned_loads = lp.unaligned_loads;
     info.chunk_bytes = chunk;
     info.tiles = lp.total_tiles;
     info.sync = lp.sync;

@@ -341,3 +341,26 @@ def test_overlap_checks_survive_the_pointer_cache(purlin):
     assert e.value.status == "INVALID_ARG"
     purlin.all_gather([x[:8] for x in ins], [y[:64] for y in outs], [8] * P)
     purlin.check()
+
+
+@pytest.mark.parametrize("name", ["allgather", "alltoall", "reducescatter"])
+def test_tile_forms_at_the_mid_size_broadcast_window(purlin, name):
+    """Odd partition sizes around 40 MiB of jobs: copy broadcasts take
+    destination-aligned units with misaligned loads (32 - 512 MiB of jobs),
+    point-to-point copies the row body, reductions source-aligned units with
+    misaligned stores; element-by-element parity and the form each launch
+    reports."""
+    P = 8
+    print("case tile-forms", name, flush=True)
+    rng = np.random.default_rng([43, len(name)])
+    nparts = P * P if name == "alltoall" else P
+    per = (40 << 20) // 2 // nparts
+    sizes = [per + 2 * k + 1 for k in range(nparts)]
+    counts = pins.counts_for(name, P, sizes)
+    ins, outs = pins.make_case(name, P, counts, "bf16", rng, None, sentinel=0x5E5E)
+    purlin.set_policy(zero_staging="zs")
+    oracle_and_gpu(purlin, name, P, counts, "bf16", ins, outs, None, [3] * P, [0] * P)
+    info = purlin.last_launch()
+    assert info["rows"] == 1, info
+    assert info["unaligned_loads"] == (1 if name == "allgather" else 0), info
+    assert info["shift_stores"] == (1 if name == "reducescatter" else 0), info
