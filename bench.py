@@ -853,8 +853,8 @@ def pipeline_sweep(purlin, T, names, path, dev):
     eight or sixteen workgroups): for each name in `names` at T bytes per
     rank -- a collective, or "onesided", rank 0's T bytes to rank 1 --
     every depth D in 1..8, staging chunk C in 16 KiB .. 1 MiB and
-    workgroups per job (lanes: 8, 16 for the one-sided transfer, 1-8 for a
-    collective), the p50 over 10 cold calls (a 1 GiB fill between calls,
+    workgroups per job (lanes: 8-256 for the one-sided transfer, 1-16 for a
+    collective) and the staged default policy, the p50 over 10 cold calls (a 1 GiB fill between calls,
     outside the events), and the zero-staging kernel at its default policy
     and at several grid sizes.  B_min
     fraction as everywhere: compulsory bytes / (p50 x 8 TB/s); staging's
@@ -895,19 +895,19 @@ def pipeline_sweep(purlin, T, names, path, dev):
                 in_n, out_n, op = SPECS["alltoall"]
                 xi, yo = ins[:2], outs[:2]
                 wgs = (0, 2, 4, 8, 16, 64)
-                lanes = (8, 16)
+                lanes = (8, 16, 64, 128, 256)
             else:
                 s = shapes[name]
                 in_n, out_n, op = SPECS[name]
                 xi = [ins[r][:s["ins"][r]] for r in range(P)]
                 yo = [outs[r][:s["outs"][r]] for r in range(P)]
                 wgs = (0, 32, 64, 128, 256)
-                lanes = (1, 2, 4, 8)
+                lanes = (1, 2, 4, 8, 16)
 
             def fn():
                 purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
 
-            points = [("zs", 0, 0, g) for g in wgs]
+            points = [("zs", 0, 0, g) for g in wgs] + [("staged", 0, 0, 0)]
             points += [("staged", d, c, l) for l in lanes for c in (16 << 10, 64 << 10,
                                                                     256 << 10, 1 << 20)
                        for d in range(1, 9)]

@@ -18,7 +18,7 @@ namespace purlin {
 namespace {
 
 constexpr int64_t kDefaultWatchdogNs = 2000000000;  // 2 s
-constexpr int kMaxLanes = 32;
+constexpr int kMaxLanes = 256;
 // Owner workgroups per lane of a staged reduction (PURLIN_OWNER_TEAM
 // overrides, 1 - kMaxTeam): each combines a slice of every chunk.
 constexpr int kOwnerTeam = 8;
@@ -674,16 +674,8 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     StagedPlan sp{};
     sp.base = lp;
     sp.withhold = pol.test_withhold;
-    // Staged chunks are long: every handoff costs an L2 writeback (release)
-    // and an invalidate (acquire) on the XCDs involved.  About eight chunks
-    // per job, between 64 KiB and 1 MiB.
     int64_t max_job = 0;
     for (const Job &jb : jobs) max_job = std::max(max_job, jb.nbytes);
-    int64_t chunk = pol.chunk_bytes;
-    if (!chunk) {
-      chunk = int64_t(64) << 10;
-      while (chunk < (int64_t(1) << 20) && chunk * 8 < max_job) chunk *= 2;
-    }
     int depth = pol.depth ? pol.depth : 4;
     // roles per lane of each job
     const int owner_team = int(std::min<int64_t>(kMaxTeam, std::max<int64_t>(1, env_i64("PURLIN_OWNER_TEAM", kOwnerTeam))));
@@ -703,12 +695,19 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     }
     if (roles_per_lane > capacity) return PURLIN_ERR_UNSUPPORTED;  // cannot be co-resident
     int lane_cap = pol.wgs_per_rank ? pol.wgs_per_rank : capacity / std::max(1, roles_per_lane);
+    // Staged chunks are long: every handoff costs an L2 writeback (release)
+    // and an invalidate (acquire) on the XCDs involved.  About eight chunks
+    // per job, between 64 KiB and 1 MiB.
+    int64_t chunk = pol.chunk_bytes;
+    if (!chunk) {
+      chunk = int64_t(64) << 10;
+      while (chunk < (int64_t(1) << 20) && chunk * 8 < max_job) chunk *= 2;
+    }
     int64_t ring_bytes = 0, flag_bytes = 0;
     // Lay out tiles, lanes, roles and rings for (chunk, depth, lane_cap).
     auto layout = [&]() {
       sp.base.chunk_bytes = chunk;
       fill_tiles(sp.base, jobs, chunk);
-      sp.depth = depth;
       sp.slot_stride = chunk + 256;
       int max_tiles = 1;
       for (size_t k = 0; k < jobs.size(); ++k)
@@ -716,6 +715,8 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
       int lanes = std::max(1, std::min({lane_cap, kMaxLanes, max_tiles}));
       while (lanes > 1 && lanes * roles_per_lane > capacity) --lanes;
       sp.lanes = lanes;
+      // a default ring is no deeper than the chunks a lane carries
+      sp.depth = pol.depth ? depth : std::min(depth, (max_tiles + lanes - 1) / lanes);
       int role = 0, ring = 0;
       for (size_t k = 0; k < jobs.size(); ++k) {
         sj[k].role_begin = role;
