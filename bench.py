@@ -1071,9 +1071,16 @@ def main():
                      "hbm_frac": round(s["bmin"] / p50 / HBM_PEAK, 4),
                      "bmin_bytes": s["bmin"], "grid": launch[name]["grid"],
                      "chunk_bytes": launch[name]["chunk_bytes"]}
-        k = kern.setdefault(kernel_of(name, launch[name]["rows"], launch[name]["one"],
-                                      launch[name]["plain_stores"]),
-                            {"bytes": 0, "time": 0.0, "launches": 0})
+        kname = kernel_of(name, launch[name]["rows"], launch[name]["one"],
+                          launch[name]["plain_stores"])
+        # HBM bytes per launch from the committed counter summary (when it was
+        # taken on these sources and this workload): dram_frac is the rate HBM
+        # sustained on the bytes actually moved
+        tr = measured_traffic(kname, T, names, args.variant)
+        if tr is not None:
+            per[name]["traffic_bytes"] = tr
+            per[name]["dram_frac"] = round(tr / p50 / HBM_PEAK, 4)
+        k = kern.setdefault(kname, {"bytes": 0, "time": 0.0, "launches": 0})
         k["bytes"] += s["bmin"] * len(ts)
         k["time"] += sum(ts)
         k["launches"] += len(ts)
