@@ -928,6 +928,79 @@ def pipeline_sweep(purlin, T, names, path, dev):
     return rows
 
 
+def paired_bench(purlin, sizes, names, env_b, reps, dev):
+    """Two settings of the library compared on the same buffers: the
+    defaults (A) and the environment overrides `env_b` (B, e.g.
+    {"PURLIN_SHIFT_STORES": "0"}), each collective at each T bytes per rank,
+    `reps` calls per setting alternated call by call (A B, then B A, so
+    neither always runs first), a 1 GiB fill between calls outside the
+    events; one JSON line per (collective, T) with both p50s and the speed
+    ratio A/B of B over A."""
+    import torch
+    import workloads
+    stream = torch.cuda.current_stream()
+    Tmax = max(sizes)
+    shapes_max = collective_shapes(Tmax)
+    n = Tmax // ESZ
+    ins = [workloads.device_values(n, "normal", "bf16", 3, r, dev) for r in range(P)]
+    out_len = max(max(shapes_max[nm]["outs"]) for nm in names)
+    outs = [torch.empty(out_len, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    saved = {k: os.environ.get(k) for k in env_b}
+
+    def setting(b):
+        for k, v in env_b.items():
+            if b:
+                os.environ[k] = v
+            elif saved[k] is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = saved[k]
+
+    rows = []
+    try:
+        for T in sizes:
+            shapes = collective_shapes(T)
+            for name in names:
+                s = shapes[name]
+                in_n, out_n, op = SPECS[name]
+                xi = [ins[r][:s["ins"][r]] for r in range(P)]
+                yo = [outs[r][:s["outs"][r]] for r in range(P)]
+                ev = [[], []]
+                info = [None, None]
+                for b in (0, 1):
+                    setting(b)
+                    purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
+                    info[b] = purlin.last_launch()
+                for it in range(reps):
+                    for b in ((0, 1) if it % 2 == 0 else (1, 0)):
+                        setting(b)
+                        flush.fill_(1.0)
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
+                        e1.record(stream)
+                        ev[b].append((e0, e1))
+                torch.cuda.synchronize()
+                purlin.check(stream)
+                p50 = []
+                for b in (0, 1):
+                    ts = sorted(a.elapsed_time(c) * 1e-3 for a, c in ev[b])
+                    p50.append(ts[len(ts) // 2])
+                row = {"collective": name, "T_bytes": T, "reps": reps, "b_env": env_b,
+                       "a_p50_us": round(p50[0] * 1e6, 2), "b_p50_us": round(p50[1] * 1e6, 2),
+                       "a_hbm_frac": round(s["bmin"] / p50[0] / HBM_PEAK, 4),
+                       "b_hbm_frac": round(s["bmin"] / p50[1] / HBM_PEAK, 4),
+                       "speed_b_over_a": round(p50[0] / p50[1], 4),
+                       "a_grid": info[0]["grid"], "b_grid": info[1]["grid"]}
+                print(json.dumps(row), flush=True)
+                rows.append(row)
+    finally:
+        setting(0)
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -964,6 +1037,11 @@ def main():
     ap.add_argument("--configs", default="",
                     help="write p50 latency of the fp32 AllReduce at 1 MiB per rank and the TP8 "
                          "AllReduce of [t x 7168] bf16 activations to this JSONL file")
+    ap.add_argument("--paired", default="",
+                    help="compare the defaults with environment overrides KEY=VALUE[,KEY=VALUE] "
+                         "on the same buffers, calls alternated, for --only (default all) at "
+                         "each of --sizes (default --size) bytes per rank, --steps calls each")
+    ap.add_argument("--sizes", default="", help="comma-separated T values for --paired")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time only the plain 128-bit streaming copy of --size bytes "
                          "(HBM counter calibration and copy ceiling)")
@@ -999,6 +1077,12 @@ def main():
         return
     if args.configs:
         config_bench(purlin, args.configs, dev)
+        return
+    if args.paired:
+        env_b = dict(kv.split("=", 1) for kv in args.paired.split(","))
+        sizes = [int(v) for v in args.sizes.split(",")] if args.sizes else [T]
+        names = [n for n in SPECS if not args.only or n in args.only.split(",")]
+        paired_bench(purlin, sizes, names, env_b, args.steps, dev)
         return
     if args.pipeline:
         names = args.only.split(",") if args.only else ["alltoall"]
