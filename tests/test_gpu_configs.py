@@ -13,6 +13,11 @@
   [4096 x 7168] with top-8 routing over 256 experts.
 * The benchmark step itself (seven collectives, 1 GiB per rank, default
   policy): the same device-side and sampled checks.
+* Jobs over 4 GiB (P = 2): a 4.5 GiB AllToAllV partition, aligned and six
+  bytes off its destination's phase, compared on the device; a
+  ReduceScatterV whose 4.5 GiB partition starts 10 bytes into each input,
+  sampled, and at every position around the 4 GiB byte mark, against the
+  oracle; zero staging and staged.
 """
 import numpy as np
 import pytest
@@ -218,3 +223,92 @@ def test_alltoall_staged_1gib(purlin, depth):
     purlin.all_to_all(ins, outs, counts)
     purlin.check()
     _device_copy_check("alltoall", counts, ins, outs)
+
+
+# ------------------------------------------------------------ jobs over 4 GiB
+
+BIG = (9 << 29) // 2 + 3      # bf16 elements: 4.5 GiB and 6 bytes in one partition
+
+
+def _big_values(n, rank, dev):
+    """n bf16 N(0,1) values drawn on the device in blocks (bounded temporaries)."""
+    import torch
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    step = 1 << 27
+    for k, a in enumerate(range(0, n, step)):
+        b = min(n, a + step)
+        out[a:b] = workloads.device_values(b - a, "normal", "bf16", 11, rank * 4096 + k, dev)
+    return out
+
+
+def _probe_positions(n, rng, samples=4096):
+    """Sampled positions of an n-element partition, plus every position within
+    16 elements of each 4 GiB byte mark and of both ends (where 32-bit byte
+    offsets would wrap)."""
+    pos = set(int(v) for v in rng.choice(n, size=samples, replace=False))
+    for mark in (0, 1 << 31, n - 16):
+        pos.update(p for p in range(mark - 16, mark + 16) if 0 <= p < n)
+    return np.array(sorted(pos), dtype=np.int64)
+
+
+@pytest.mark.parametrize("variant", ["zs", "staged"])
+@pytest.mark.parametrize("shift", [0, 3])
+def test_copy_job_over_4gib(purlin, variant, shift):
+    """One AllToAllV partition of 4.5 GiB (rank 0 to rank 1, P = 2), landing at
+    element offset `shift` (0: the aligned body; 3: six bytes off the
+    destination's 16-byte phase, the realigning body), and five elements back:
+    each output partition equals the input partition the naming rule maps to
+    it, compared on the device."""
+    import torch
+    dev = torch.device("cuda", 0)
+    print("case copy-over-4GiB", variant, shift, flush=True)
+    counts = [0, BIG, 5, 0]                   # names (0,0) (0,1) (1,0) (1,1)
+    displs = [0, 0, 0, 5] + [0, shift, 0, shift + BIG]
+    ins = [_big_values(BIG, 0, dev), _big_values(5, 1, dev)]
+    outs = [torch.empty(5, dtype=torch.bfloat16, device=dev),
+            torch.empty(shift + BIG, dtype=torch.bfloat16, device=dev)]
+    want = {}
+    for i in range(2):
+        for nm, off, c in oracle.partitions("by_rank_index", i, 2, counts, displs[:4]):
+            want[nm] = (i, off, c)
+    purlin.set_policy(zero_staging=variant)
+    purlin.collective(ins, outs, "by_rank_index", "by_index_rank", "copy", counts, displs)
+    purlin.check()
+    for j in range(2):
+        for nm, off, c in oracle.partitions("by_index_rank", j, 2, counts, displs[4:]):
+            i, soff, _ = want[nm]
+            assert torch.equal(outs[j][off:off + c], ins[i][soff:soff + c]), (variant, shift, nm)
+    del ins, outs
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("variant", ["zs", "staged"])
+def test_sum_job_over_4gib(purlin, variant):
+    """ReduceScatterV over P = 2 whose second partition holds 4.5 GiB and
+    starts 10 bytes into each input (the first holds five elements): the
+    sums at sampled positions, at every position around the 4 GiB byte mark
+    and at both ends, against the oracle's fold of the same input columns."""
+    import torch
+    dev = torch.device("cuda", 0)
+    print("case sum-over-4GiB", variant, flush=True)
+    rng = np.random.default_rng(4242)
+    counts = [5, BIG]
+    displs = [0, 5] + [0, 0]
+    ins = [_big_values(5 + BIG, r, dev) for r in range(2)]
+    outs = [torch.empty(5, dtype=torch.bfloat16, device=dev),
+            torch.empty(BIG, dtype=torch.bfloat16, device=dev)]
+    purlin.set_policy(zero_staging=variant)
+    purlin.collective(ins, outs, "by_index", "by_rank", "sum", counts, displs)
+    purlin.check()
+    for j, (soff, c) in enumerate(((0, 5), (5, BIG))):
+        pos = _probe_positions(c, rng) if c > 4096 else np.arange(c)
+        pt = torch.as_tensor(pos, device=dev)
+        cols = [to_host(ins[i][soff:soff + c][pt], "bf16") for i in range(2)]
+        m = len(pos)
+        want = oracle.collective("whole", "whole", "sum", "bf16", 2, [m], None, cols,
+                                 [np.zeros(m, np.uint16) for _ in range(2)])[0]
+        got = to_host(outs[j][pt], "bf16")
+        inexact = compare("sum-over-4GiB %s rank %d" % (variant, j), got, want, "bf16", "sum")
+        assert inexact == 0
+    del ins, outs
+    torch.cuda.empty_cache()
