@@ -112,6 +112,18 @@ def test_moe_repeated_calls_new_routing(purlin):
         run_case(purlin, 8, 448, [int(v) for v in rng.integers(1, 60, 8)], rng, fanout=2 + seed)
 
 
+def test_moe_with_handshake(purlin):
+    """Dispatch (both forms) and combine with the full entry / exit handshake."""
+    purlin.set_policy(sync=True)
+    try:
+        for seed in range(2):
+            rng = np.random.default_rng([45, seed])
+            run_case(purlin, 8, 448, [int(v) for v in rng.integers(1, 50, 8)], rng, fanout=3)
+        assert purlin.last_launch()["sync"] == 1
+    finally:
+        purlin.set_policy(reset=True)
+
+
 def test_moe_device_side_errors(purlin):
     import torch
     P, H = 2, 8

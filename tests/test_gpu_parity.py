@@ -115,6 +115,23 @@ def test_repeated_calls_and_sync_modes(purlin, sync):
     assert purlin.last_launch()["sync"] == (1 if sync else 0)
 
 
+@pytest.mark.parametrize("variant", ["zs", "staged"])
+@pytest.mark.parametrize("name", NAMES)
+def test_handshake_on_every_shape(purlin, name, variant):
+    """The full per-rank entry / exit handshake (policy sync) on every
+    collective shape, uniform and variable, in both variants, three calls in
+    a row (each launch waits for the previous one's exit counts)."""
+    print("case handshake", name, variant, flush=True)
+    P = 8
+    rng = np.random.default_rng([23, NAMES.index(name), len(variant)])
+    purlin.set_policy(sync=True, zero_staging=variant)
+    for rep, kind in enumerate(("uniform", "v", "gapped")):
+        counts, displs, ins, outs = _case(name, P, "bf16", kind, rng, 700)
+        oracle_and_gpu(purlin, name, P, counts, "bf16", ins, outs, displs)
+        info = purlin.last_launch()
+        assert info["sync"] == 1 and info["zero_staging"] == (1 if variant == "zs" else 0), info
+
+
 def test_zero_counts_launch_nothing(purlin):
     P = 8
     ins = [np.zeros(4, np.uint16) for _ in range(P)]

@@ -82,6 +82,17 @@ def test_ulysses_shifted_buffers(purlin, shift):
     assert purlin.last_launch()["unit"] == (2 if shift == 1 else 8)
 
 
+def test_ulysses_with_handshake(purlin):
+    """Both directions with the full entry / exit handshake."""
+    rng = np.random.default_rng(49)
+    purlin.set_policy(sync=True)
+    try:
+        run(purlin, 8, [40, 0, 33, 51, 7, 29, 45, 12], 24, 128, rng)
+        assert purlin.last_launch()["sync"] == 1
+    finally:
+        purlin.set_policy(reset=True)
+
+
 def test_ulysses_many_tiles_ragged(purlin):
     """Pairs of about 230 KB: several 32 KiB tiles each, ragged last tiles,
     ranks of different lengths and one empty rank."""
