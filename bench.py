@@ -1151,6 +1151,8 @@ def main():
         p50 = ts[len(ts) // 2]
         s = shapes[name]
         per[name] = {"p50_us": round(p50 * 1e6, 2), "mean_us": round(mean * 1e6, 2),
+                     "p10_us": round(ts[len(ts) // 10] * 1e6, 2),
+                     "p90_us": round(ts[min(len(ts) - 1, (9 * len(ts)) // 10)] * 1e6, 2),
                      "algbw_GBps": round(s["T"] / p50 / 1e9, 1),
                      "hbm_frac": round(s["bmin"] / p50 / HBM_PEAK, 4),
                      "bmin_bytes": s["bmin"], "grid": launch[name]["grid"],
@@ -1164,6 +1166,9 @@ def main():
         if tr is not None:
             per[name]["traffic_bytes"] = tr
             per[name]["dram_frac"] = round(tr / p50 / HBM_PEAK, 4)
+            # fewer bytes reached HBM than the collective must move: caches
+            # (L2, the Infinity Cache) served part of it
+            per[name]["cache_assisted"] = tr < 0.99 * s["bmin"]
         k = kern.setdefault(kname, {"bytes": 0, "time": 0.0, "launches": 0})
         k["bytes"] += s["bmin"] * len(ts)
         k["time"] += sum(ts)
