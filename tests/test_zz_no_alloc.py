@@ -107,6 +107,34 @@ def test_noalloc_refuses_a_fixed_plan_too_large(purlin):
     assert all(bool((o == 8.0).all()) for o in outs)
 
 
+def test_noalloc_staged_one_large_job_shrinks(purlin):
+    """A one-sided staged transfer of 48 MiB (P = 2, one partition): the
+    default policy runs many lanes of 1 MiB chunks, more ring than the fixed
+    array holds, so the no-allocation call runs fewer lanes; its output
+    equals purlin_collective's and the source, on two calls in a row (the
+    second smaller)."""
+    import torch
+    for n in ((24 << 20) + 5, (3 << 20) + 1):
+        print("case noalloc staged one job", n, flush=True)
+        counts = [0, n, 0, 0]
+        src = torch.arange(n, dtype=torch.int32, device="cuda").to(torch.int16).view(torch.bfloat16)
+        ins = [src, torch.empty(1, dtype=torch.bfloat16, device="cuda")]
+        got = [torch.empty(1, dtype=torch.bfloat16, device="cuda"),
+               torch.full((n,), 3.0, dtype=torch.bfloat16, device="cuda")]
+        ref = [torch.empty(1, dtype=torch.bfloat16, device="cuda"),
+               torch.full((n,), 7.0, dtype=torch.bfloat16, device="cuda")]
+        purlin.set_policy(zero_staging="staged")
+        purlin.collective(ins, ref, "by_rank_index", "by_index_rank", "copy", counts)
+        grid_ref = purlin.last_launch()["grid"]
+        purlin.collective_noalloc(ins, got, "by_rank_index", "by_index_rank", "copy", counts)
+        grid_fixed = purlin.last_launch()["grid"]
+        purlin.check()
+        assert torch.equal(got[1].view(torch.int16), ref[1].view(torch.int16))
+        assert torch.equal(got[1].view(torch.int16), src.view(torch.int16))
+        if n > (16 << 20):
+            assert grid_fixed < grid_ref, (grid_fixed, grid_ref)
+
+
 def test_noalloc_staged_under_graph_capture(purlin):
     """A staged call captured on a fresh stream: purlin_collective has no
     workspace there and refuses, the no-allocation entry point runs from its
