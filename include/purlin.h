@@ -3,18 +3,19 @@
  *
  * Source of the semantics: "Purlin: Separating Orchestration from the
  * Datapath of Collectives" (arXiv 2609.36954).
- *   - A collective is a naming of an input layout and an output layout plus a
- *     copy or a reduction (abstract).
+ *   - A collective is specified by two layout namings (inputs, outputs) and an
+ *     operation, copy or reduction (abstract).
  *   - Layouts: ReduceScatter combines partition k of every input into y_k at
- *     rank k; AllGather places every y_k, in rank order, at every rank;
+ *     rank k; AllGather gives each rank all of y_0 .. y_{P-1}, ordered by rank;
  *     AllToAll gives rank j partition j of every source (Figure 4 caption).
  *   - AllReduce is ReduceScatter and AllGather composed chunk by chunk
  *     (Figure 6 caption).
  *   - (V) variants have variable partition sizes (Table 2, Figure 16).
  *   - Coordination is derived from the specification by the SNAC protocol
  *     (Stage, Notify, And Consume; abstract), the bytes are moved by the Atom
- *     copy and reduce primitives (abstract), and the zero-staging variant
- *     (Purlin-ZS) omits the staging step (Figure 10 caption).
+ *     copy and reduce primitives (abstract), and in the zero-staging variant
+ *     (Purlin-ZS) consumers read the inputs directly, with no staging step
+ *     (Figure 10 caption).
  *
  * The P "ranks" are P buffer sets in the memory of the one current HIP
  * device: each launch performs the share of every rank.  All pointers in
@@ -100,9 +101,9 @@ typedef enum {
   PURLIN_STAGING_STAGED = 2 /* producers stage chunks in a ring, notify, consumers consume */
 } purlin_staging;
 
-/* Datapath of copy collectives (copy engines: the copy-engine AllGather of the
- * Figure 10 caption, which launches no kernel, and the Figure 3 caption's
- * point that copies need not occupy compute units). */
+/* Datapath of copy collectives (copy engines: the Figure 10 caption's
+ * AllGather on the copy engine, without a kernel of its own, and the Figure 3
+ * caption's point that copies need not occupy compute units). */
 typedef enum {
   PURLIN_ENGINE_AUTO = 0,   /* shader kernels (the Atom) */
   PURLIN_ENGINE_SHADER = 1, /* shader kernels (the Atom) */
@@ -112,7 +113,8 @@ typedef enum {
                                SUM collectives still run on the shader kernels. */
 } purlin_engine;
 
-/* Execution policy ("codesign policies tune execution", Figure 1 caption).
+/* Execution policy (Figure 1 caption: policies chosen with the hardware in
+ * mind decide how a collective runs).
  * A zero field means "automatic".  It never changes a result, only speed. */
 typedef struct {
   int64_t chunk_bytes;   /* bytes per work chunk / staging slot; multiple of 4096 */
@@ -322,9 +324,9 @@ PURLIN_API purlin_status purlin_moe_combine(void *const *y, void *const *out, in
                                             const int64_t *x_rows, hipStream_t stream);
 
 /*
- * Ulysses sequence-parallel AllToAll (Purlin pages, Table 2: the diffusion
- * workload's AllToAll that redistributes sequence and attention-head
- * partitions).  P ranks, `heads` attention heads (a multiple of P), each
+ * Ulysses sequence-parallel AllToAll (Purlin pages, Table 2: in the diffusion
+ * workload an AllToAll moves activations between a sequence-sharded and a
+ * head-sharded layout).  P ranks, `heads` attention heads (a multiple of P), each
  * head `head_bytes` bytes per token (head dimension x element size; even),
  * seq[i] >= 0 tokens on rank i (host array of P), S = sum of seq.  Layouts,
  * row-major, tokens of rank 0 first in the head layout:

@@ -5,8 +5,8 @@ Python binding) imports, links or calls this package; only the tests, the
 smoke check and the benchmark's CPU-baseline leg do.  It shares no code with
 the GPU path: it is numpy and plain Python, written from the definitions in
 "Purlin: Separating Orchestration from the Datapath of Collectives"
-(arXiv 2609.36954): the abstract (a collective is a naming of an input and an
-output layout plus a copy or a reduction), Figure 4 (ReduceScatter,
+(arXiv 2609.36954): the abstract (a collective is given by two layout
+namings, inputs and outputs, and an operation, copy or reduction), Figure 4 (ReduceScatter,
 AllGather and AllToAll layouts), Figure 6 (AllReduce composed of both) and
 Table 2 / Figure 16 (variable-length variants), and ``moe.py``: MoE dispatch
 and combine with the token permutation folded in (Table 2's expert-parallel

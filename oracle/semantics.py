@@ -1,8 +1,9 @@
 """The oracle of Purlin's collective semantics (test infrastructure only).
 
-Purlin specifies a collective as a naming of an input layout, a naming of an
-output layout, and a copy or a reduction (Purlin, abstract).  The layouts
-fix the result without saying how bytes move (Purlin, Figure 4 caption), so
+Purlin specifies a collective by two layout namings, one for the inputs and
+one for the outputs, and an operation, copy or reduction (Purlin, abstract).  The layouts
+determine the result and leave the data movement open (Purlin, Figure 4
+caption), so
 this module computes exactly that definition and models none of the
 orchestration (SNAC) or the datapath (Atom).
 

@@ -2,8 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Purlin names Ulysses sequence parallelism, whose AllToAll redistributes
-sequence and attention-head partitions, among the call sites of its
+Purlin names Ulysses sequence parallelism, whose AllToAll moves data from a
+sequence-sharded to a head-sharded layout and back, among the call sites of its
 collectives (Table 2 of "Purlin: Separating Orchestration from the Datapath
 of Collectives"; the diffusion workload).  The send side is strided: rank
 i's shard of head group j is every (H/P)-th slice of its rows.

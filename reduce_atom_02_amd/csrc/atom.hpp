@@ -1,7 +1,7 @@
 // Atom: the datapath primitives, copy and reduce, for gfx950.
 //
-// Purlin puts "how bytes move on a given GPU generation" in a layer of its
-// own with two primitives, copy and reduce (abstract; Figure 1 caption).
+// Purlin keeps the hardware-specific movement of bytes in a layer of its own
+// with two primitives, copy and reduce (abstract; Figure 1 caption).
 // This is that layer for one CDNA4 GPU, where every byte moves through HBM:
 //
 //  * 16-byte global loads and stores (dwordx4), 64 lanes x 16 B = 1 KiB per

@@ -1,8 +1,8 @@
 // Host planner: derives the jobs of a collective from its specification.
 //
-// Purlin derives coordination from the collective's specification instead
-// of a hand-written communication schedule (abstract; Table 1,
-// "Derivability").  Here that derivation is the naming rule itself: every
+// In Purlin the coordination of a collective follows from its specification,
+// with no communication schedule written by hand (abstract; the
+// derivability column of Table 1).  Here that derivation is the naming rule itself: every
 // output partition takes the input partitions with the same name, in
 // ascending source rank (Figure 4 caption gives the three layouts this
 // reproduces).  Output partitions that take the same source bytes and sit at

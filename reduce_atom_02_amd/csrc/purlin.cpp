@@ -224,7 +224,8 @@ KernelKind kind_of(purlin_op op, purlin_dtype dtype) {
   return dtype == PURLIN_F32 ? KernelKind::kSumF32 : KernelKind::kSumBf16;
 }
 
-// Policy table ("codesign policies tune execution", Figure 1 caption), from
+// Policy table (Figure 1 caption: policies chosen with the hardware in mind
+// decide how a collective runs), from
 // sweeps of grid, chunk and unroll at 1 MiB - 1 GiB per rank on MI355X, the
 // policies alternated call by call on the same buffers.  Large messages
 // want two workgroups per CU (fewer concurrent DRAM streams), smaller ones

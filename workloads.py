@@ -14,8 +14,7 @@ library.  Recipes (all seeded, all synthetic):
 * large device-resident inputs (bandwidth sweeps) are drawn on the GPU by
   torch's seeded generator (``device_values``); tests read back the elements
   they check.
-* Zipf partition sizes (Purlin, Figure 16 caption: Zipf with exponent
-  s = 0.125): partition k weighs ``(pi(k)+1) ** -s`` for a seeded permutation
+* Zipf partition sizes (Purlin, Figure 16 caption: Zipf, s = 0.125): partition k weighs ``(pi(k)+1) ** -s`` for a seeded permutation
   pi of the P ranks; counts are the floors of T * w_k / sum(w), the remainder
   going one element each to the largest fractional parts (ties: lower k).
   Sizes are in elements with no alignment.
