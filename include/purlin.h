@@ -42,7 +42,12 @@
  * Workspace is keyed by the stream handle: a stream destroyed while its work
  * is still running must not be replaced by a new one with the same handle.
  *
- * Thread safety: none; serialize calls from different host threads.
+ * Host threads.  Any thread may call any function: the library serializes
+ * its host bookkeeping (workspace, plan cache, policy) under one lock, and
+ * the launches themselves stay asynchronous.  The policy is process-wide;
+ * purlin_last_launch reports the calling thread's most recent launch.  Do
+ * not call purlin_release while another thread's work may still be using
+ * the workspace it frees.
  */
 #ifndef PURLIN_H_
 #define PURLIN_H_
@@ -135,7 +140,8 @@ typedef struct {
   int64_t src_off, dst_off, len; /* elements */
 } purlin_segment;
 
-/* What the most recent purlin_collective launched (measurement only). */
+/* What the calling thread's most recent successful call launched
+ * (measurement only). */
 typedef struct {
   int32_t grid;          /* workgroups launched */
   int32_t threads;       /* threads per workgroup */
@@ -351,7 +357,8 @@ PURLIN_API purlin_status purlin_ulysses(void *const *in, void *const *out, int P
                                         const int64_t *seq, int64_t heads, int64_t head_bytes,
                                         int to_sequence, hipStream_t stream);
 
-/* Measurement: the launch shape of the most recent successful call. */
+/* Measurement: the launch shape of the calling thread's most recent
+ * successful call. */
 PURLIN_API purlin_status purlin_last_launch(purlin_launch_info *info);
 
 /* Measurement: a plain 128-bit streaming copy of `bytes` bytes (both

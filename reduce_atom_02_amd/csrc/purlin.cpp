@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <memory>
+#include <mutex>
 #include <vector>
 
 #include "collective.hpp"
@@ -62,8 +63,17 @@ purlin_policy &user_policy() {
   return p;
 }
 bool g_user_policy_set = false;
-purlin_launch_info g_last{};
-bool g_have_last = false;
+// What the calling host thread launched last (purlin_last_launch).
+thread_local purlin_launch_info g_last{};
+thread_local bool g_have_last = false;
+
+// One lock over the library's host state (device and stream workspace, the
+// plan cache, the policy, the fixed scratch's addresses): calls from several
+// host threads are serialized here; the launches stay asynchronous.
+std::recursive_mutex &api_mutex() {
+  static std::recursive_mutex m;
+  return m;
+}
 
 int64_t env_i64(const char *name, int64_t dflt) {
   const char *v = std::getenv(name);
@@ -479,6 +489,7 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
                               purlin_dtype dtype, int P, const int64_t *counts,
                               const int64_t *displs, hipStream_t stream, FixedWorkspaceFn fixed_fn) {
   if (!in || !out || !in->bufs || !out->bufs) return PURLIN_ERR_INVALID_ARG;
+  std::lock_guard<std::recursive_mutex> lock(api_mutex());
   const Derived *d = nullptr;
   purlin_status st = derive_cached(in->naming, out->naming, op, dtype, P, counts, displs, &d);
   if (st != PURLIN_OK) return st;
@@ -786,6 +797,7 @@ const char *purlin_strerror(purlin_status s) {
 }
 
 purlin_status purlin_set_policy(const purlin_policy *p) {
+  std::lock_guard<std::recursive_mutex> lock(api_mutex());
   if (!p) {
     g_user_policy_set = false;
     user_policy() = purlin_policy{};
@@ -798,6 +810,7 @@ purlin_status purlin_set_policy(const purlin_policy *p) {
 }
 
 purlin_status purlin_get_policy(purlin_policy *p) {
+  std::lock_guard<std::recursive_mutex> lock(api_mutex());
   if (!p) return PURLIN_ERR_INVALID_ARG;
   *p = effective_policy();
   return PURLIN_OK;
@@ -807,6 +820,7 @@ purlin_status purlin_plan_describe(const purlin_layout *in, const purlin_layout 
                                    purlin_op op, purlin_dtype dtype, int P,
                                    const int64_t *counts, const int64_t *displs,
                                    purlin_segment *segs, int64_t *n_segs) {
+  std::lock_guard<std::recursive_mutex> lock(api_mutex());
   if (!in || !out || !in->bufs || !out->bufs || !n_segs) return PURLIN_ERR_INVALID_ARG;
   const Derived *d = nullptr;
   purlin_status s = derive_cached(in->naming, out->naming, op, dtype, P, counts, displs, &d);
@@ -838,6 +852,7 @@ purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *ou
 purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t row_bytes,
                                   const int32_t *const *idx, const int64_t *counts,
                                   const int64_t *x_rows, int unique, hipStream_t stream) {
+  std::lock_guard<std::recursive_mutex> lock(api_mutex());
   MoePlan m;
   int64_t total = 0, y_total = 0;
   purlin_status st = moe_plan(x, y, P, row_bytes, idx, counts, x_rows, false, &m, &total, &y_total);
@@ -896,6 +911,7 @@ purlin_status purlin_moe_dispatch(void *const *x, void *const *y, int P, int64_t
 purlin_status purlin_moe_combine(void *const *y, void *const *out, int P, int64_t row_bytes,
                                  const int32_t *const *idx, const float *const *w,
                                  const int64_t *counts, const int64_t *x_rows, hipStream_t stream) {
+  std::lock_guard<std::recursive_mutex> lock(api_mutex());
   MoePlan m;
   int64_t total = 0, y_total = 0;
   purlin_status st = moe_plan(y, out, P, row_bytes, idx, counts, x_rows, true, &m, &total, &y_total);
@@ -943,6 +959,7 @@ purlin_status purlin_moe_combine(void *const *y, void *const *out, int P, int64_
 purlin_status purlin_ulysses(void *const *in, void *const *out, int P, const int64_t *seq,
                              int64_t heads, int64_t head_bytes, int to_sequence,
                              hipStream_t stream) {
+  std::lock_guard<std::recursive_mutex> lock(api_mutex());
   StridedPlan sp;
   int unit = 16;
   int64_t total = 0;
@@ -1003,6 +1020,7 @@ purlin_status purlin_ulysses(void *const *in, void *const *out, int P, const int
 
 purlin_status purlin_check(hipStream_t stream) {
   if (hipStreamSynchronize(stream) != hipSuccess) return PURLIN_ERR_HIP;
+  std::lock_guard<std::recursive_mutex> lock(api_mutex());
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return PURLIN_ERR_HIP;
   auto &all = devices();
@@ -1032,6 +1050,7 @@ purlin_status purlin_last_launch(purlin_launch_info *info) {
 }
 
 purlin_status purlin_stream_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream) {
+  std::lock_guard<std::recursive_mutex> lock(api_mutex());
   if (!dst || !src || bytes < 0 || (bytes & 15) || (uintptr_t(dst) & 15) || (uintptr_t(src) & 15))
     return PURLIN_ERR_INVALID_ARG;
   if (bytes == 0) return PURLIN_OK;
@@ -1046,6 +1065,7 @@ purlin_status purlin_stream_copy(void *dst, const void *src, int64_t bytes, hipS
 purlin_status purlin_stream_pattern(const void *const *srcs, int n_src, void *const *dsts,
                                     int n_dst, int64_t bytes, int grid, int64_t tile_bytes,
                                     int unroll, int access, hipStream_t stream) {
+  std::lock_guard<std::recursive_mutex> lock(api_mutex());
   const bool ok_n = (n_src == 0 || n_src == 1 || n_src == 8) && (n_dst == 0 || n_dst == 1 || n_dst == 8) &&
                     (n_src + n_dst) > 0;
   if (!ok_n || (n_src && !srcs) || (n_dst && !dsts) || bytes < 0 || (bytes & 15) || grid < 0 ||
@@ -1068,6 +1088,7 @@ purlin_status purlin_stream_pattern(const void *const *srcs, int n_src, void *co
 }
 
 void purlin_release(void) {
+  std::lock_guard<std::recursive_mutex> lock(api_mutex());
   auto &all = devices();
   int cur = 0;
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;

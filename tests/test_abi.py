@@ -86,6 +86,44 @@ def test_plan_matches_oracle_naming(purlin, P, name, variant):
     assert sorted(got) == expected_segments(name, P, counts, displs)
 
 
+def test_plan_describe_from_many_threads(purlin):
+    """Eight host threads plan 32 different collectives at once, 100 rounds
+    each (the library's plan cache is shared and evicts under them): every
+    plan matches the oracle's naming rule."""
+    import threading
+    rng = np.random.default_rng(97)
+    cases = []
+    for k in range(32):
+        name = list(oracle.COLLECTIVES)[k % len(oracle.COLLECTIVES)]
+        P = int(rng.integers(2, 9))
+        nparts = P * P if name == "alltoall" else P
+        counts = pins.counts_for(name, P, [int(v) for v in rng.integers(0, 9, nparts)])
+        displs = pins.gapped_displs(name, P, counts, rng) if k % 3 == 0 else None
+        cases.append((name, P, counts, displs, expected_segments(name, P, counts, displs)))
+    errors = []
+    start = threading.Barrier(8)
+
+    def work(t):
+        try:
+            start.wait()
+            for rnd in range(100):
+                name, P, counts, displs, want = cases[(t * 5 + rnd) % len(cases)]
+                in_n, out_n, op = oracle.COLLECTIVES[name]
+                got = purlin.plan_describe(in_n, out_n, op, "bf16", counts, bufs(P, A_IN),
+                                           bufs(P, A_OUT), displs)
+                if sorted(got) != want:
+                    errors.append((t, rnd, name, P))
+        except Exception as e:  # reported below, with the thread
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors[:5]
+
+
 def st(purlin, in_n, out_n, op, dtype, counts, P=8, ins=None, outs=None, displs=None):
     return purlin.plan_status(in_n, out_n, op, dtype, counts,
                               ins if ins is not None else bufs(P, A_IN),

@@ -274,6 +274,65 @@ def test_two_streams_interleaved(purlin):
             c.redraw(rng)
 
 
+@pytest.mark.parametrize("variant", ["zs", "staged", "zs_sync"])
+def test_host_threads_on_their_own_streams(purlin, variant):
+    """Four host threads, each enqueueing six collectives on a stream of its
+    own with no synchronization in between: the library serializes its host
+    bookkeeping, every stream has its own workspace, every result matches the
+    oracle, and each thread's purlin_last_launch describes its own calls."""
+    import threading
+    import torch
+    P = 8
+    print("case host threads", variant, flush=True)
+    rng = np.random.default_rng([61, len(variant)])
+    names = ["reducescatter", "alltoall", "allgather", "allreduce"]
+    work_of = []
+    for t in range(4):
+        cases = []
+        for k in range(6):
+            name = names[(t + k) % 4]
+            scale = 20000 if name != "alltoall" else 4000
+            cases.append(Case(name, P, "bf16" if (t + k) % 2 else "f32",
+                              _sizes(name, P, rng, scale), rng))
+        work_of.append(cases)
+    torch.cuda.synchronize()
+    if variant == "staged":
+        purlin.set_policy(zero_staging="staged", chunk_bytes=16384, depth=2)
+    else:
+        purlin.set_policy(zero_staging="zs", sync=variant == "zs_sync")
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    seen = [[] for _ in range(4)]
+    errors = []
+    start = threading.Barrier(4)
+
+    def work(t):
+        try:
+            start.wait()
+            for c in work_of[t]:
+                c.call(purlin, stream=streams[t])
+                seen[t].append(purlin.last_launch()["bytes_min"])
+        except Exception as e:  # reported below, with the thread
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for s_ in streams:
+        purlin.check(s_)
+    for t in range(4):
+        for k, c in enumerate(work_of[t]):
+            c.verify("thread %d call %d" % (t, k))
+    # each thread saw its own launches: the same calls again, one thread
+    for t in range(4):
+        for k, c in enumerate(work_of[t]):
+            c.call(purlin)
+            assert purlin.last_launch()["bytes_min"] == seen[t][k], (t, k)
+    purlin.check()
+
+
 def test_two_streams_moe(purlin):
     """MoE dispatch and combine on two streams at once: one inverse table
     per stream."""
