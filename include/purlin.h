@@ -255,8 +255,22 @@ PURLIN_API purlin_status purlin_check(hipStream_t stream);
 
 /* Replace the policy (NULL restores the defaults).  Environment variables
  * PURLIN_CHUNK_BYTES, PURLIN_DEPTH, PURLIN_WGS_PER_RANK, PURLIN_ZS (0/1),
- * PURLIN_SYNC (0/1) and PURLIN_WATCHDOG_NS override the defaults only.
- * INVALID_ARG for out-of-range fields.  Takes effect on the next call. */
+ * PURLIN_SYNC (0/1), PURLIN_WATCHDOG_NS and PURLIN_ENGINE (purlin_engine)
+ * override the defaults only.  INVALID_ARG for out-of-range fields.  Takes
+ * effect on the next call.
+ *
+ * Datapath switches, read at every call, for measurement (each selects
+ * between forms that give identical results; unset = the measured default):
+ * PURLIN_SHIFT_STORES (0/1: sums whose sources share a 16-byte phase off
+ * their destination's take source-aligned units with misaligned stores),
+ * PURLIN_UNALIGNED_LOADS (0/1: copies off their destination's phase take
+ * destination-aligned units with misaligned loads), PURLIN_BCAST_PLAIN (0/1:
+ * plain stores for large copy broadcasts), PURLIN_NT (0/1: nontemporal
+ * loads and stores), PURLIN_NT_ANY_PHASE (0/1: nontemporal loads also for
+ * sources off their destination's 128-byte phase), PURLIN_UNROLL (0, 1, 2:
+ * units per lane in flight, copies 4 / 8 / 16, sums 1 / 2 / 4), PURLIN_LDS
+ * (0/1: the LDS-staged aligned body), PURLIN_OWNER_TEAM (1-8: owner
+ * workgroups per staged reduction lane). */
 PURLIN_API purlin_status purlin_set_policy(const purlin_policy *p);
 
 /* The policy in force (defaults, environment, then purlin_set_policy). */
