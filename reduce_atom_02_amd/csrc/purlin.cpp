@@ -235,9 +235,9 @@ KernelKind kind_of(purlin_op op, purlin_dtype dtype) {
 }
 
 // Policy table (Figure 1 caption: policies chosen with the hardware in mind
-// decide how a collective runs), from
-// sweeps of grid, chunk and unroll at 1 MiB - 1 GiB per rank on MI355X, the
-// policies alternated call by call on the same buffers.  Large messages
+// decide how a collective runs), from sweeps of grid, chunk and unroll at
+// 1 MiB - 1 GiB per rank on MI355X (256 CUs), the policies alternated call
+// by call on the same buffers.  Large messages
 // want two workgroups per CU (fewer concurrent DRAM streams), smaller ones
 // four (each workgroup has few tiles, so more of them overlap more round
 // trips); the crossover, in bytes of jobs per launch (the per-rank size T
@@ -254,18 +254,18 @@ KernelKind kind_of(purlin_op op, purlin_dtype dtype) {
 //               AllToAllV +4-9% at 64 MiB - 1 GiB per rank).
 // Grids of 1.5 or 2.5 workgroups per CU measured 2-8% slower than either
 // neighbour.  The grid is a whole-device figure (all P ranks share one
-// GPU), so it does not shrink for P < 8.
+// GPU), so it does not shrink for P < 8; it is given in workgroups per CU.
 struct AutoPolicy {
   int grid;
   int64_t chunk;
   int unroll_sel;
 };
 
-AutoPolicy auto_policy(KernelKind kind, bool broadcast, int64_t job_bytes) {
+AutoPolicy auto_policy(KernelKind kind, bool broadcast, int64_t job_bytes, int cus) {
   const int64_t MiB = int64_t(1) << 20;
-  if (kind != KernelKind::kCopy) return {job_bytes >= 16 * MiB ? 512 : 1024, 16 << 10, 0};
-  if (broadcast) return {job_bytes >= 16 * MiB ? 512 : 1024, 16 << 10, 0};
-  return {job_bytes >= 32 * MiB ? 512 : 1024, 32 << 10, 0};
+  if (kind != KernelKind::kCopy) return {(job_bytes >= 16 * MiB ? 2 : 4) * cus, 16 << 10, 0};
+  if (broadcast) return {(job_bytes >= 16 * MiB ? 2 : 4) * cus, 16 << 10, 0};
+  return {(job_bytes >= 32 * MiB ? 2 : 4) * cus, 32 << 10, 0};
 }
 
 // Small messages get smaller chunks, so that the default grid still sees
@@ -560,7 +560,7 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     job_bytes += jb.nbytes;
     broadcast |= jb.dst < 0;
   }
-  const AutoPolicy ap = auto_policy(kind, broadcast, job_bytes);
+  const AutoPolicy ap = auto_policy(kind, broadcast, job_bytes, ds->cus);
   int unroll_sel = unroll_env();
   if (unroll_sel < 0 || unroll_sel > 2) unroll_sel = ap.unroll_sel;
   // Whether some job has a source off its destinations' 16-byte phase and
