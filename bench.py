@@ -505,6 +505,62 @@ def sweep(purlin, T_max, variant, path, dev):
     return rows
 
 
+def policy_sweep(purlin, sizes, names, path, dev, reps=30):
+    """Grid and chunk of the zero-staging kernel swept where the launch
+    dominates less and less (T = 1 MiB .. 32 MiB per rank by default): for
+    each collective and T, workgroups per rank in {auto, 16, 32, 64, 128,
+    256} x chunk in {auto, 4, 8, 16, 32, 64 KiB}, the p50 of `reps` cold
+    calls (a 1 GiB fill between calls, outside the events); one JSONL row per
+    point, with the grid and chunk the launch took."""
+    import torch
+    import workloads
+    stream = torch.cuda.current_stream()
+    Tmax = max(sizes)
+    n = Tmax // ESZ
+    ins = [workloads.device_values(n, "normal", "bf16", 3, r, dev) for r in range(P)]
+    shapes_max = collective_shapes(Tmax)
+    outs = [torch.empty(max(max(shapes_max[nm]["outs"]) for nm in names), dtype=torch.bfloat16,
+                        device=dev) for _ in range(P)]
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    rows = []
+    with open(path, "w") as f:
+        for T in sizes:
+            shapes = collective_shapes(T)
+            for name in names:
+                s = shapes[name]
+                in_n, out_n, op = SPECS[name]
+                xi = [ins[r][:s["ins"][r]] for r in range(P)]
+                yo = [outs[r][:s["outs"][r]] for r in range(P)]
+                for g in (0, 16, 32, 64, 128, 256):
+                    for c in (0, 4 << 10, 8 << 10, 16 << 10, 32 << 10, 64 << 10):
+                        purlin.set_policy(zero_staging="zs", wgs_per_rank=g, chunk_bytes=c)
+                        purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
+                        info = purlin.last_launch()
+                        ev = []
+                        for _ in range(reps):
+                            flush.fill_(1.0)
+                            e0 = torch.cuda.Event(enable_timing=True)
+                            e1 = torch.cuda.Event(enable_timing=True)
+                            e0.record(stream)
+                            purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
+                            e1.record(stream)
+                            ev.append((e0, e1))
+                        torch.cuda.synchronize()
+                        purlin.check(stream)
+                        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+                        p50 = ts[len(ts) // 2]
+                        row = {"collective": name, "T_bytes": T, "wgs_per_rank_policy": g,
+                               "chunk_policy": c, "grid": info["grid"],
+                               "chunk_bytes": info["chunk_bytes"], "p50_us": round(p50 * 1e6, 2),
+                               "hbm_frac": round(s["bmin"] / p50 / HBM_PEAK, 4)}
+                        f.write(json.dumps(row) + "\n")
+                        f.flush()
+                        rows.append(row)
+            print("T=%d KiB done" % (T >> 10), flush=True)
+    purlin.set_policy(reset=True)
+    return rows
+
+
 def config_bench(purlin, path, dev):
     """The AllReduce workloads the latency sweep does not cover, timed like
     its latency regime (20 warm-up calls, 1000 timed calls; device p50
@@ -1041,7 +1097,12 @@ def main():
                     help="compare the defaults with environment overrides KEY=VALUE[,KEY=VALUE] "
                          "on the same buffers, calls alternated, for --only (default all) at "
                          "each of --sizes (default --size) bytes per rank, --steps calls each")
-    ap.add_argument("--sizes", default="", help="comma-separated T values for --paired")
+    ap.add_argument("--sizes", default="",
+                    help="comma-separated T values for --paired and --policy-sweep")
+    ap.add_argument("--policy-sweep", default="",
+                    help="sweep workgroups per rank x chunk of the zero-staging kernel for --only "
+                         "(default all) at --sizes (default 1-32 MiB) bytes per rank, cold p50, "
+                         "every point to this JSONL file")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time only the plain 128-bit streaming copy of --size bytes "
                          "(HBM counter calibration and copy ceiling)")
@@ -1077,6 +1138,12 @@ def main():
         return
     if args.configs:
         config_bench(purlin, args.configs, dev)
+        return
+    if args.policy_sweep:
+        sizes = ([int(v) for v in args.sizes.split(",")] if args.sizes
+                 else [1 << k for k in range(20, 26)])
+        names = [n for n in SPECS if not args.only or n in args.only.split(",")]
+        policy_sweep(purlin, sizes, names, args.policy_sweep, dev)
         return
     if args.paired:
         env_b = dict(kv.split("=", 1) for kv in args.paired.split(","))
