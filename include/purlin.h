@@ -270,7 +270,8 @@ PURLIN_API purlin_status purlin_check(hipStream_t stream);
  * sources off their destination's 128-byte phase), PURLIN_UNROLL (0, 1, 2:
  * units per lane in flight, copies 4 / 8 / 16, sums 1 / 2 / 4), PURLIN_LDS
  * (0/1: the LDS-staged aligned body), PURLIN_OWNER_TEAM (1-8: owner
- * workgroups per staged reduction lane). */
+ * workgroups per staged reduction lane), PURLIN_MID_CHUNKS (0/1: the
+ * mid-size chunk rules of the policy table). */
 PURLIN_API purlin_status purlin_set_policy(const purlin_policy *p);
 
 /* The policy in force (defaults, environment, then purlin_set_policy). */

@@ -581,7 +581,7 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     job_bytes += jb.nbytes;
     broadcast |= jb.dst < 0;
   }
-  const AutoPolicy ap = auto_policy(kind, broadcast, job_bytes, ds->cus);
+  AutoPolicy ap = auto_policy(kind, broadcast, job_bytes, ds->cus);
   int unroll_sel = unroll_env();
   if (unroll_sel < 0 || unroll_sel > 2) unroll_sel = ap.unroll_sel;
   // Whether some job has a source off its destinations' 16-byte phase and
@@ -611,6 +611,18 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
   // compiled code, not the pass).
   const bool small = job_bytes <= (int64_t(512) << 10);
   const bool wide = !staged && rows && (small || kind == KernelKind::kCopy);
+  // Point-to-point copies on the row body (AllToAllV) with 32 - 256 MiB of
+  // jobs run as many workgroups as are resident (five per CU) on 16 KiB
+  // chunks: AllToAllV 21 / 12 / 9 / 4% faster at 4 / 8 / 16 / 32 MiB per
+  // rank than on two per CU and 32 KiB chunks (paired on the same buffers);
+  // the aligned AllToAll gains nothing there and keeps the table's.
+  bool chunk_fixed = false;
+  if (env_i64("PURLIN_MID_CHUNKS", 1) != 0 && kind == KernelKind::kCopy && !broadcast && rows &&
+      job_bytes >= (int64_t(32) << 20) && job_bytes < (int64_t(256) << 20)) {
+    ap.grid = 5 * ds->cus;
+    ap.chunk = 16 << 10;
+    chunk_fixed = true;
+  }
   // Copy broadcasts of 16 MiB of jobs or more store plainly: AllGather 5-8%,
   // AllGatherV 4-8% faster at 64 MiB - 1 GiB per rank than with nontemporal
   // stores (paired on the same buffers, both orders).  Nontemporal stores
@@ -652,7 +664,9 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     const int64_t want_grid = std::min<int64_t>(
         capacity, pol.wgs_per_rank ? int64_t(P) * pol.wgs_per_rank : int64_t(ap.grid));
     const int64_t chunk =
-        pol.chunk_bytes ? pol.chunk_bytes : auto_chunk(kind, broadcast, job_bytes, ap.chunk, want_grid);
+        pol.chunk_bytes ? pol.chunk_bytes
+        : chunk_fixed   ? ap.chunk
+                        : auto_chunk(kind, broadcast, job_bytes, ap.chunk, want_grid);
     lp.chunk_bytes = chunk;
     fill_tiles(lp, jobs, chunk);
     const int grid = int(std::max<int64_t>(1, std::min<int64_t>(lp.total_tiles, want_grid)));
