@@ -616,11 +616,29 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
   // chunks: AllToAllV 21 / 12 / 9 / 4% faster at 4 / 8 / 16 / 32 MiB per
   // rank than on two per CU and 32 KiB chunks (paired on the same buffers);
   // the aligned AllToAll gains nothing there and keeps the table's.
+  // Reductions on the row build (ReduceScatterV) with 16 - 128 MiB of jobs
+  // run three workgroups per CU (as many as are resident) on 8 KiB chunks:
+  // 6-9 / 3 / 2-5% faster at 16 / 32 / 64 MiB per rank (three paired runs
+  // on two boxes), 4-5% slower from 256 MiB.  Copy broadcasts (AllGather(V))
+  // keep four workgroups per CU and 8 KiB chunks up to 32 MiB of jobs:
+  // 4-11% faster at 16-24 MiB per rank (three runs), even at 32.
+  const bool mid_rules = env_i64("PURLIN_MID_CHUNKS", 1) != 0;
+  const int64_t MiB = int64_t(1) << 20;
   bool chunk_fixed = false;
-  if (env_i64("PURLIN_MID_CHUNKS", 1) != 0 && kind == KernelKind::kCopy && !broadcast && rows &&
-      job_bytes >= (int64_t(32) << 20) && job_bytes < (int64_t(256) << 20)) {
+  if (mid_rules && kind == KernelKind::kCopy && !broadcast && rows && job_bytes >= 32 * MiB &&
+      job_bytes < 256 * MiB) {
     ap.grid = 5 * ds->cus;
     ap.chunk = 16 << 10;
+    chunk_fixed = true;
+  } else if (mid_rules && kind != KernelKind::kCopy && rows && job_bytes >= 16 * MiB &&
+             job_bytes < 128 * MiB) {
+    ap.grid = 3 * ds->cus;
+    ap.chunk = 8 << 10;
+    chunk_fixed = true;
+  } else if (mid_rules && kind == KernelKind::kCopy && broadcast && job_bytes >= 16 * MiB &&
+             job_bytes < 32 * MiB) {
+    ap.grid = 4 * ds->cus;
+    ap.chunk = 8 << 10;
     chunk_fixed = true;
   }
   // Copy broadcasts of 16 MiB of jobs or more store plainly: AllGather 5-8%,
