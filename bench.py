@@ -510,8 +510,10 @@ def policy_sweep(purlin, sizes, names, path, dev, reps=30):
     dominates less and less (T = 1 MiB .. 32 MiB per rank by default): for
     each collective and T, workgroups per rank in {auto, 16, 32, 64, 128,
     256} x chunk in {auto, 4, 8, 16, 32, 64 KiB}, the p50 of `reps` cold
-    calls (a 1 GiB fill between calls, outside the events); one JSONL row per
-    point, with the grid and chunk the launch took."""
+    calls (a 1 GiB fill between calls, outside the events); below 1 MiB per
+    rank, the latency sweep's device latency instead (warm, 200 calls queued
+    behind a spin kernel).  One JSONL row per point, with the grid and chunk
+    the launch took."""
     import torch
     import workloads
     stream = torch.cuda.current_stream()
@@ -537,8 +539,14 @@ def policy_sweep(purlin, sizes, names, path, dev, reps=30):
                         purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
                         info = purlin.last_launch()
                         ev = []
-                        for _ in range(reps):
-                            flush.fill_(1.0)
+                        cold = T >= (1 << 20)
+                        n_calls = reps if cold else 200
+                        if not cold:
+                            torch.cuda.synchronize()
+                            torch.cuda._sleep(20_000_000)   # the calls queue up behind it
+                        for _ in range(n_calls):
+                            if cold:
+                                flush.fill_(1.0)
                             e0 = torch.cuda.Event(enable_timing=True)
                             e1 = torch.cuda.Event(enable_timing=True)
                             e0.record(stream)
@@ -990,8 +998,9 @@ def paired_bench(purlin, sizes, names, env_b, reps, dev):
     {"PURLIN_SHIFT_STORES": "0"}), each collective at each T bytes per rank,
     `reps` calls per setting alternated call by call (A B, then B A, so
     neither always runs first), a 1 GiB fill between calls outside the
-    events; one JSON line per (collective, T) with both p50s and the speed
-    ratio A/B of B over A."""
+    events; below 1 MiB per rank warm instead, at least 200 calls each,
+    queued behind a spin kernel (device latency).  One JSON line per
+    (collective, T) with both p50s and the speed ratio A/B of B over A."""
     import torch
     import workloads
     stream = torch.cuda.current_stream()
@@ -1028,10 +1037,18 @@ def paired_bench(purlin, sizes, names, env_b, reps, dev):
                     setting(b)
                     purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
                     info[b] = purlin.last_launch()
-                for it in range(reps):
+                cold = T >= (1 << 20)
+                n_calls = reps if cold else max(reps, 200)
+                for it in range(n_calls):
+                    if not cold and it % 100 == 0:
+                        # below 1 MiB: warm, the calls queued behind a spin
+                        # kernel (device latency, as in the latency sweep)
+                        torch.cuda.synchronize()
+                        torch.cuda._sleep(20_000_000)
                     for b in ((0, 1) if it % 2 == 0 else (1, 0)):
                         setting(b)
-                        flush.fill_(1.0)
+                        if cold:
+                            flush.fill_(1.0)
                         e0 = torch.cuda.Event(enable_timing=True)
                         e1 = torch.cuda.Event(enable_timing=True)
                         e0.record(stream)

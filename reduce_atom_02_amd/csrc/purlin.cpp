@@ -289,7 +289,7 @@ int64_t auto_chunk(KernelKind kind, bool broadcast, int64_t job_bytes, int64_t c
   const int64_t MiB = int64_t(1) << 20;
   const bool mid = env_i64("PURLIN_MID_CHUNKS", 1) != 0;
   if (mid && kind == KernelKind::kCopy && !broadcast && job_bytes < 32 * MiB)
-    return fit_chunk(chunk, job_bytes, grid, 1);
+    return fit_chunk(chunk, job_bytes, grid, 1, job_bytes > MiB / 2 ? 16384 : 4096);
   if (mid && kind == KernelKind::kCopy && broadcast && job_bytes >= 2 * MiB &&
       job_bytes < 16 * MiB)
     return fit_chunk(chunk, job_bytes, grid, 4, 8192);
