@@ -13,6 +13,10 @@
   [4096 x 7168] with top-8 routing over 256 experts.
 * The benchmark step itself (seven collectives, 1 GiB per rank, default
   policy): the same device-side and sampled checks.
+* One size inside each size-dependent rule of the launch policy (grid and
+  chunk: AllToAll(V) at 256 KiB - 8 MiB per rank, AllGather(V) 6 - 24 MiB,
+  ReduceScatterV 24 - 96 MiB, AllReduce 16 - 48 MiB): the same device-side
+  and sampled checks.
 * Jobs over 4 GiB (P = 2): a 4.5 GiB AllToAllV partition, aligned and six
   bytes off its destination's phase, compared on the device; a
   ReduceScatterV whose 4.5 GiB partition starts 10 bytes into each input,
@@ -207,6 +211,39 @@ def test_bench_step_1gib(purlin, variant):
             _device_copy_check(base, s["counts"], xi, yo)
         else:
             _sampled_sum_check(base, s["counts"], xi, yo, rng)
+    del ins, outs
+    torch.cuda.empty_cache()
+
+
+# one size inside each size-dependent rule of the launch policy (grid, chunk)
+REGIMES = [("alltoall", 256 << 10), ("alltoallv", 512 << 10), ("alltoallv", 8 << 20),
+           ("allgather", 24 << 20), ("allgatherv", 6 << 20), ("allgatherv", 24 << 20),
+           ("reducescatterv", 24 << 20), ("reducescatterv", 96 << 20),
+           ("allreduce", 16 << 20), ("allreduce", 48 << 20)]
+
+
+@pytest.mark.parametrize("name,T", REGIMES)
+def test_policy_regimes(purlin, name, T):
+    """The benchmark's collectives at a size inside each rule of the launch
+    policy, default policy: copies compared on the device partition by
+    partition (the naming rule via oracle.partitions), sums on sampled
+    columns against the oracle."""
+    import torch
+    import bench
+    print("case regime", name, T, flush=True)
+    dev = torch.device("cuda", 0)
+    s = bench.collective_shapes(T)[name]
+    rng = np.random.default_rng([77, len(name), T >> 16])
+    ins = [workloads.device_values(s["ins"][r], "normal", "bf16", 5, r, dev) for r in range(P)]
+    outs = [torch.empty(s["outs"][r], dtype=torch.bfloat16, device=dev) for r in range(P)]
+    in_n, out_n, op = bench.SPECS[name]
+    purlin.collective(ins, outs, in_n, out_n, op, s["counts"])
+    purlin.check()
+    base = name.rstrip("v") if name.endswith("v") else name
+    if op == "copy":
+        _device_copy_check(base, s["counts"], ins, outs)
+    else:
+        _sampled_sum_check(base, s["counts"], ins, outs, rng)
     del ins, outs
     torch.cuda.empty_cache()
 
