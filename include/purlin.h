@@ -207,9 +207,14 @@ typedef struct {
  * must stay valid and outputs untouched until the stream reaches that point.
  * The staged variant's workgroups wait for each other; they are numbered so
  * that every job's producers come before its consumers and the jobs before
- * the one being started are wholly resident, so a kernel running beside it
- * on another stream delays it but cannot block it.  A device-side watchdog
- * expiry is reported by purlin_check.
+ * the one being started are wholly resident, so a kernel beside it on
+ * another stream that finishes on its own delays it but cannot block it.
+ * Two staged launches on different streams can block each other when
+ * together they need more workgroups than the device holds and a producer
+ * waits for a slot's credits (a lane with more chunks than ring slots): the
+ * watchdog then ends both with PURLIN_ERR_TIMEOUT.  Keep staged launches on
+ * one stream, or give the policy a depth of at least the chunks per lane.
+ * A device-side watchdog expiry is reported by purlin_check.
  */
 PURLIN_API purlin_status purlin_collective(const purlin_layout *in, const purlin_layout *out,
                                 purlin_op op, purlin_dtype dtype, int P,
