@@ -992,19 +992,22 @@ def pipeline_sweep(purlin, T, names, path, dev):
     return rows
 
 
-def paired_bench(purlin, sizes, names, env_b, reps, dev):
+def paired_bench(purlin, sizes, names, env_b, reps, dev, alloc=0):
     """Two settings of the library compared on the same buffers: the
     defaults (A) and the environment overrides `env_b` (B, e.g.
     {"PURLIN_SHIFT_STORES": "0"}), each collective at each T bytes per rank,
     `reps` calls per setting alternated call by call (A B, then B A, so
     neither always runs first), a 1 GiB fill between calls outside the
     events; below 1 MiB per rank warm instead, at least 200 calls each,
-    queued behind a spin kernel (device latency).  One JSON line per
-    (collective, T) with both p50s and the speed ratio A/B of B over A."""
+    queued behind a spin kernel (device latency).  The buffers are allocated
+    for max(sizes, alloc) bytes per rank and every call uses their prefix
+    (results depend on where the buffers sit, so `alloc` reproduces another
+    run's placement).  One JSON line per (collective, T) with both p50s and
+    the speed ratio A/B of B over A."""
     import torch
     import workloads
     stream = torch.cuda.current_stream()
-    Tmax = max(sizes)
+    Tmax = max(max(sizes), alloc)
     shapes_max = collective_shapes(Tmax)
     n = Tmax // ESZ
     ins = [workloads.device_values(n, "normal", "bf16", 3, r, dev) for r in range(P)]
@@ -1116,6 +1119,9 @@ def main():
                          "each of --sizes (default --size) bytes per rank, --steps calls each")
     ap.add_argument("--sizes", default="",
                     help="comma-separated T values for --paired and --policy-sweep")
+    ap.add_argument("--alloc", type=int, default=0,
+                    help="--paired: allocate the buffers for this many bytes per rank (at least "
+                         "the largest of --sizes)")
     ap.add_argument("--policy-sweep", default="",
                     help="sweep workgroups per rank x chunk of the zero-staging kernel for --only "
                          "(default all) at --sizes (default 1-32 MiB) bytes per rank, cold p50, "
@@ -1166,7 +1172,7 @@ def main():
         env_b = dict(kv.split("=", 1) for kv in args.paired.split(","))
         sizes = [int(v) for v in args.sizes.split(",")] if args.sizes else [T]
         names = [n for n in SPECS if not args.only or n in args.only.split(",")]
-        paired_bench(purlin, sizes, names, env_b, args.steps, dev)
+        paired_bench(purlin, sizes, names, env_b, args.steps, dev, args.alloc)
         return
     if args.pipeline:
         names = args.only.split(",") if args.only else ["alltoall"]

@@ -621,7 +621,11 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
   // 6-9 / 3 / 2-5% faster at 16 / 32 / 64 MiB per rank (three paired runs
   // on two boxes), 4-5% slower from 256 MiB.  Copy broadcasts (AllGather(V))
   // keep four workgroups per CU and 8 KiB chunks up to 32 MiB of jobs:
-  // 4-11% faster at 16-24 MiB per rank (three runs), even at 32.
+  // 4-11% faster at 16-24 MiB per rank (three runs), even at 32.  Each rule
+  // held with the buffers allocated three ways (exactly, and as prefixes of
+  // 256 MiB and 1 GiB allocations).  AllReduce keeps the table's: four
+  // workgroups per CU on 4 KiB chunks at 16-48 MiB per rank measured 7-11%
+  // faster with exactly sized buffers and 6-9% slower with the others.
   const bool mid_rules = env_i64("PURLIN_MID_CHUNKS", 1) != 0;
   const int64_t MiB = int64_t(1) << 20;
   bool chunk_fixed = false;
@@ -639,13 +643,6 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
              job_bytes < 32 * MiB) {
     ap.grid = 4 * ds->cus;
     ap.chunk = 8 << 10;
-    chunk_fixed = true;
-  } else if (mid_rules && kind != KernelKind::kCopy && broadcast && job_bytes >= 16 * MiB &&
-             job_bytes < 64 * MiB) {
-    // AllReduce keeps four workgroups per CU on 4 KiB chunks up to 64 MiB
-    // of jobs: 8-11% faster at 16-32 MiB per rank (paired, two runs)
-    ap.grid = 4 * ds->cus;
-    ap.chunk = 4 << 10;
     chunk_fixed = true;
   }
   // Copy broadcasts of 16 MiB of jobs or more store plainly: AllGather 5-8%,
