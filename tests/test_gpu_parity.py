@@ -381,3 +381,33 @@ def test_tile_forms_at_the_mid_size_broadcast_window(purlin, name):
     assert info["rows"] == 1, info
     assert info["unaligned_loads"] == (1 if name == "allgather" else 0), info
     assert info["shift_stores"] == (1 if name == "reducescatter" else 0), info
+
+
+# every datapath switch the header lists, away from its default
+SWITCHES = [{"PURLIN_SHIFT_STORES": "0"}, {"PURLIN_SHIFT_STORES": "1"},
+            {"PURLIN_UNALIGNED_LOADS": "1"}, {"PURLIN_UNALIGNED_LOADS": "0"},
+            {"PURLIN_BCAST_PLAIN": "0"}, {"PURLIN_NT": "0"}, {"PURLIN_NT_ANY_PHASE": "0"},
+            {"PURLIN_UNROLL": "1"}, {"PURLIN_UNROLL": "2"}, {"PURLIN_LDS": "1"},
+            {"PURLIN_MID_CHUNKS": "0"}, {"PURLIN_OWNER_TEAM": "1"}, {"PURLIN_OWNER_TEAM": "3"}]
+
+
+@pytest.mark.parametrize("switch", SWITCHES, ids=lambda d: ",".join("%s=%s" % kv for kv in d.items()))
+def test_datapath_switches_match_oracle(purlin, switch, monkeypatch):
+    """Each datapath switch only chooses between forms that give the same
+    result: every collective shape, uniform and variable, misaligned, in
+    zero staging (and staged for the owner-team switch), at sizes that span
+    several tiles, matches the oracle with the switch set."""
+    for k, v in switch.items():
+        monkeypatch.setenv(k, v)
+    P = 8
+    staged = "PURLIN_OWNER_TEAM" in switch
+    rng = np.random.default_rng([97, len(str(switch))])
+    for name in NAMES:
+        for kind in ("uniform", "v"):
+            print("case switch", switch, name, kind, flush=True)
+            counts, displs, ins, outs = _case(name, P, "bf16", kind, rng,
+                                              30000 if name != "alltoall" else 6000)
+            shifts = [int(v) for v in rng.integers(0, 8, P)] if kind == "v" else None
+            purlin.set_policy(zero_staging="staged" if staged else "zs",
+                              chunk_bytes=16384 if staged else 0)
+            oracle_and_gpu(purlin, name, P, counts, "bf16", ins, outs, displs, shifts)
