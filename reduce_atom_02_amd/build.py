@@ -56,5 +56,26 @@ def build(verbose=False, extra=(), debug=False):
     return lib
 
 
+def build_all(verbose=False):
+    """Both libraries, compiled concurrently (two hipcc processes)."""
+    import threading
+    out, errs = {}, []
+
+    def one(debug):
+        try:
+            out[debug] = build(verbose=verbose, debug=debug)
+        except Exception as e:  # re-raised below, from the calling thread
+            errs.append(e)
+
+    threads = [threading.Thread(target=one, args=(d,)) for d in (False, True)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    if errs:
+        raise errs[0]
+    return out[False], out[True]
+
+
 if __name__ == "__main__":
     print(build(verbose=True, debug="--debug" in sys.argv))
