@@ -917,7 +917,7 @@ def pipeline_sweep(purlin, T, names, path, dev):
     eight or sixteen workgroups): for each name in `names` at T bytes per
     rank -- a collective, or "onesided", rank 0's T bytes to rank 1 --
     every depth D in 1..8, staging chunk C in 16 KiB .. 1 MiB and
-    workgroups per job (lanes: 8-256 for the one-sided transfer, 1-16 for a
+    workgroups per job (lanes: 8-256 for the one-sided transfer, 1-32 for a
     collective) and the staged default policy, the p50 over 10 cold calls (a 1 GiB fill between calls,
     outside the events), and the zero-staging kernel at its default policy
     and at several grid sizes.  B_min
@@ -966,14 +966,14 @@ def pipeline_sweep(purlin, T, names, path, dev):
                 xi = [ins[r][:s["ins"][r]] for r in range(P)]
                 yo = [outs[r][:s["outs"][r]] for r in range(P)]
                 wgs = (0, 32, 64, 128, 256)
-                lanes = (1, 2, 4, 8, 16)
+                lanes = (1, 2, 4, 8, 16, 32)
 
             def fn():
                 purlin.collective(xi, yo, in_n, out_n, op, s["counts"], stream=stream)
 
             points = [("zs", 0, 0, g) for g in wgs] + [("staged", 0, 0, 0)]
-            points += [("staged", d, c, l) for l in lanes for c in (16 << 10, 64 << 10,
-                                                                    256 << 10, 1 << 20)
+            points += [("staged", d, c, l) for l in lanes
+                       for c in (16 << 10, 32 << 10, 64 << 10, 256 << 10, 1 << 20)
                        for d in range(1, 9)]
             for variant, d, c, g in points:
                 purlin.set_policy(zero_staging=variant, depth=d, chunk_bytes=c, wgs_per_rank=g)

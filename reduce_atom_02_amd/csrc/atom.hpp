@@ -95,6 +95,44 @@ __device__ __forceinline__ void st16x(uint64_t addr, u32x4 v) {
   else st16<kNT>(addr, v);
 }
 
+// Store modes of the tile bodies: plain, nontemporal, or device scope.  A
+// device-scope store (the sc1 cache policy) is written through the XCD's L2
+// and counted as done only once every XCD would read it, so bytes that one
+// workgroup hands to another through HBM are published by a wait for the
+// store counter and a relaxed flag store: no writeback of the L2's dirty
+// lines, which is what a release costs on a multi-XCD gfx950 (measured: a
+// handoff of a 32-256 KiB chunk 1.5-4 times slower with it).  The staged
+// pipeline writes its ring slots this way.
+constexpr int kStorePlain = 0;
+constexpr int kStoreNT = 1;
+constexpr int kStoreDevice = 2;
+
+// The sc1 bit of a buffer instruction's cache-policy operand.
+constexpr int kCpolSc1 = 16;
+
+// Device-scope 16-byte store to base + off (base the same in every lane: it
+// becomes a buffer resource in scalar registers; the range is left open,
+// the caller keeps off inside the buffer).
+__device__ __forceinline__ void st16_device(uint64_t base, uint32_t off, u32x4 v) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), 0, -1, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolSc1);
+}
+
+// 16-byte store of a tile body in store mode kM (an aligned destination).
+template <int kM>
+__device__ __forceinline__ void stm(uint64_t base, uint32_t off, u32x4 v) {
+  if constexpr (kM == kStoreDevice) st16_device(base, off, v);
+  else st16<kM == kStoreNT>(base + off, v);
+}
+
+// Element store (2 or 4 bytes), device scope when kDev.
+template <class T, bool kDev>
+__device__ __forceinline__ void ste(uint64_t addr, T v) {
+  if constexpr (kDev) __hip_atomic_store(gp<T>(addr), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *gp<T>(addr) = v;
+}
+
 // The 16 bytes that start `sh` bytes into the 32-byte pair (lo, hi);
 // sh in [0, 16) is the same for every lane.
 __device__ __forceinline__ u32x4 funnel(u32x4 lo, u32x4 hi, uint32_t sh) {
@@ -177,7 +215,7 @@ struct Dsts {
 // on (at most kThreads - t0 elements).  Every source is loaded before any is
 // added (entries past n repeat source 0, so the loads need no guard), so
 // the loads are in flight together: one memory round trip.
-template <class Op>
+template <class Op, bool kDevStore = false>
 __device__ __forceinline__ void elements(const Srcs &s, const Dsts &d, int64_t y0, int64_t y1,
                                          int t0 = 0) {
   const int64_t n = (y1 - y0) / Op::kElem;
@@ -190,7 +228,7 @@ __device__ __forceinline__ void elements(const Srcs &s, const Dsts &d, int64_t y
     const uint16_t v = *gp<const uint16_t>(s.a[0] + x);
 #pragma unroll
     for (int k = 0; k < kMaxRanks + 1; ++k)
-      if (k < d.n) *gp<uint16_t>(d.b[k] + x) = v;
+      if (k < d.n) ste<uint16_t, kDevStore>(d.b[k] + x, v);
   } else if constexpr (Op::kElem == 4) {
     float v[kMaxRanks];
 #pragma unroll
@@ -201,7 +239,7 @@ __device__ __forceinline__ void elements(const Srcs &s, const Dsts &d, int64_t y
       if (i < s.n) acc = acc + v[i];
 #pragma unroll
     for (int k = 0; k < kMaxRanks + 1; ++k)
-      if (k < d.n) *gp<float>(d.b[k] + x) = acc;
+      if (k < d.n) ste<float, kDevStore>(d.b[k] + x, acc);
   } else {
     uint16_t v[kMaxRanks];
 #pragma unroll
@@ -213,7 +251,7 @@ __device__ __forceinline__ void elements(const Srcs &s, const Dsts &d, int64_t y
     const uint16_t r = uint16_t(bf16_rne(acc));
 #pragma unroll
     for (int k = 0; k < kMaxRanks + 1; ++k)
-      if (k < d.n) *gp<uint16_t>(d.b[k] + x) = r;
+      if (k < d.n) ste<uint16_t, kDevStore>(d.b[k] + x, r);
   }
 }
 
@@ -338,7 +376,7 @@ __device__ __forceinline__ u32x4 fold_bf16(const u32x4 *x, int n) {
 // stored.  kGuard = false for passes that lie wholly inside the tile: then
 // the pass is straight-line code, so the compiler keeps every load in
 // flight until its data is needed instead of draining at guard branches.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard, bool kUS = false, bool kUL = false>
+template <class Op, int kU, bool kNTL, int kNTS, bool kGuard, bool kUS = false, bool kUL = false>
 __device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const uint64_t *db,
                                              int nd, uint32_t nunits, uint32_t u0) {
   constexpr int kS = Op::kSum ? kMaxRanks : 1;
@@ -362,10 +400,13 @@ __device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const u
       if constexpr (!Op::kSum) v = x[k][0];
       else if constexpr (Op::kElem == 4) v = fold_f32(x[k], ns);
       else v = fold_bf16(x[k], ns);
-      const uint64_t o = uint64_t(u * 16u);
 #pragma unroll
-      for (int j = 0; j < kMaxRanks + 1; ++j)
-        if (j < nd) st16x<kNTS, kUS>(db[j] + o, v);
+      for (int j = 0; j < kMaxRanks + 1; ++j) {
+        if (j < nd) {
+          if constexpr (kUS) st16u<kNTS == kStoreNT>(db[j] + uint64_t(u * 16u), v);
+          else stm<kNTS>(db[j], u * 16u, v);
+        }
+      }
     }
   }
 }
@@ -379,10 +420,11 @@ __device__ __forceinline__ void pass_aligned(const uint64_t *sa, int ns, const u
 // kUS: the destinations are off the 16-byte grid (every source on one
 // 16-byte phase, the destinations on another): units follow the sources and
 // every store is a misaligned 16-byte store.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kOne = false, bool kUS = false,
+template <class Op, int kU, bool kNTL, int kNTS, bool kOne = false, bool kUS = false,
           bool kUL = false>
 __device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const uint64_t *db,
                                              int nd, uint32_t nunits) {
+  static_assert(!kUS || kNTS != kStoreDevice, "misaligned stores have no device-scope form");
   constexpr uint32_t kPass = uint32_t(kThreads) * kU;
   uint32_t u0 = 0;
   if constexpr (!Op::kSum && kOne) {
@@ -399,8 +441,11 @@ __device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const u
         for (int k = 0; k < kU; ++k)
           x[k] = ld16x<kNTL, kUL>(sa[0] + uint64_t((u0 + uint32_t(k) * kThreads + tid) * 16u));
 #pragma unroll
-        for (int k = 0; k < kU; ++k)
-          st16x<kNTS, kUS>(db[0] + uint64_t((u0 + uint32_t(k) * kThreads + tid) * 16u), x[k]);
+        for (int k = 0; k < kU; ++k) {
+          const uint32_t o = (u0 + uint32_t(k) * kThreads + tid) * 16u;
+          if constexpr (kUS) st16u<kNTS == kStoreNT>(db[0] + uint64_t(o), x[k]);
+          else stm<kNTS>(db[0], o, x[k]);
+        }
       }
       if (u0 < nunits) {
         pass_aligned<Op, kU, kNTL, kNTS, true, kUS, kUL>(sa, ns, db, nd, nunits, u0);
@@ -425,7 +470,7 @@ __device__ __forceinline__ void body_aligned(const uint64_t *sa, int ns, const u
 // passes.  `slice` is this wavefront's kS * kR KiB of LDS.
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-template <class Op, int kR, int kU, bool kNTL, bool kNTS>
+template <class Op, int kR, int kU, bool kNTL, int kNTS>
 __device__ __forceinline__ void body_lds(const uint64_t *sa, int ns, const uint64_t *db, int nd,
                                          uint32_t nunits, lds_u32x4 *slice) {
   constexpr int kS = Op::kSum ? kMaxRanks : 1;
@@ -461,7 +506,7 @@ __device__ __forceinline__ void body_lds(const uint64_t *sa, int ns, const uint6
       const uint64_t off = (uint64_t(r0 + wave + 4u * uint32_t(k)) * 64u + lane) * 16u;
 #pragma unroll
       for (int j = 0; j < kMaxRanks + 1; ++j)
-        if (j < nd) st16<kNTS>(db[j] + off, v[k]);
+        if (j < nd) stm<kNTS>(db[j], uint32_t(off), v[k]);
     }
   }
   constexpr uint32_t kPass = uint32_t(kThreads) * kU;
@@ -507,7 +552,7 @@ __device__ __forceinline__ u32x4 lane0(u32x4 v) {
 // the same elements at the same places, so the raw blocks are folded first
 // and only the folded block is shifted into place: one shift per unit
 // instead of one per source, and the same rounded values.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kGuard, bool kOne, bool kFold>
+template <class Op, int kU, bool kNTL, int kNTS, bool kGuard, bool kOne, bool kFold>
 __device__ __forceinline__ void pass_rows(const uint64_t *base, const uint32_t *lim, int ns,
                                           const uint64_t *db, int nd, uint32_t nunits,
                                           const uint32_t *sh, uint32_t u0) {
@@ -548,13 +593,13 @@ __device__ __forceinline__ void pass_rows(const uint64_t *base, const uint32_t *
       if (lane == 63u) hi = after;
       const u32x4 v = funnel(f[k], hi, sh[0]);
       if (!kGuard || u < nunits) {
-        const uint64_t o = uint64_t(u) * 16u;
+        const uint32_t o = u * 16u;
         if constexpr (kOne) {
-          st16<kNTS>(db[0] + o, v);
+          stm<kNTS>(db[0], o, v);
         } else {
 #pragma unroll
           for (int j = 0; j < kMaxRanks + 1; ++j)
-            if (j < nd) st16<kNTS>(db[j] + o, v);
+            if (j < nd) stm<kNTS>(db[j], o, v);
         }
       }
     }
@@ -577,13 +622,13 @@ __device__ __forceinline__ void pass_rows(const uint64_t *base, const uint32_t *
       if constexpr (!Op::kSum) v = y[0];
       else if constexpr (Op::kElem == 4) v = fold_f32(y, ns);
       else v = fold_bf16(y, ns);
-      const uint64_t o = uint64_t(u) * 16u;
+      const uint32_t o = u * 16u;
       if constexpr (kOne) {
-        st16<kNTS>(db[0] + o, v);
+        stm<kNTS>(db[0], o, v);
       } else {
 #pragma unroll
         for (int j = 0; j < kMaxRanks + 1; ++j)
-          if (j < nd) st16<kNTS>(db[j] + o, v);
+          if (j < nd) stm<kNTS>(db[j], o, v);
       }
     }
   }
@@ -616,7 +661,7 @@ __device__ __forceinline__ void pass_rows(const uint64_t *base, const uint32_t *
 // sa[i] - sh[i] + 16 b, and a source with sh[i] > 0 needs block nunits too,
 // which holds its last unit's last bytes.  An unguarded pass reads blocks
 // up to u0 + kPass, so it needs u0 + kPass < nunits.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kOne, bool kFoldOk>
+template <class Op, int kU, bool kNTL, int kNTS, bool kOne, bool kFoldOk>
 __device__ __forceinline__ void body_rows(const uint64_t *sa, int ns, const uint64_t *db, int nd,
                                           uint32_t nunits, const uint32_t *sh) {
   constexpr int kS = Op::kSum ? kMaxRanks : 1;
@@ -714,17 +759,19 @@ __device__ __forceinline__ uint64_t line_ref(const Srcs &s, const Dsts &d, bool 
 // or when nt_any_phase asks for it (measured faster for misaligned
 // variable-length partitions too).  A tile spans less than 4 GiB.
 template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true, bool kOne = false,
-          bool kWide = false, bool kNTS = kNT, int kLdsRows = 0>
+          bool kWide = false, int kNTS = kNT, int kLdsRows = 0>
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
                                      bool nt_any_phase = false, int64_t wide_max = 0,
                                      bool shift_stores = false, lds_u32x4 *lds_slice = nullptr,
                                      bool unaligned_loads = false) {
+  constexpr bool kDev = kNTS == kStoreDevice;
+  static_assert(!(kDev && (kWide || kLdsRows > 0)), "device-scope stores: row and aligned bodies only");
   if (x1 <= x0) return;
   if (x1 - x0 <= int64_t(kThreads) * Op::kElem) {
-    elements<Op>(s, d, x0, x1);
+    elements<Op, kDev>(s, d, x0, x1);
     return;
   }
-  if constexpr (kRows) {
+  if constexpr (kRows && !kDev) {
     if (shifted_stores(s, d, shift_stores)) {
       // Every source on one 16-byte phase, the destinations on another:
       // units follow the sources (the loads are the aligned body's, with no
@@ -797,8 +844,8 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
   // 3 without rows (small tiles, the latency regime), so that no wavefront
   // makes two round trips; otherwise to wavefront 0.
   const int t_head = (kRows && any != 0 && nbody <= 2u * uint32_t(kUr) * 64u) ? 128 : 0;
-  elements<Op>(s, d, x0, xh, t_head);
-  elements<Op>(s, d, xb, x1, kThreads - 64);
+  elements<Op, kDev>(s, d, x0, xh, t_head);
+  elements<Op, kDev>(s, d, xb, x1, kThreads - 64);
   if (nbody == 0) return;
 #pragma unroll
   for (int i = 0; i < kMaxRanks; ++i) sa[i] += uint64_t(nh) * 16u;
@@ -830,7 +877,7 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
     // aligned); should a misaligned tile arrive anyway, it is still right,
     // element by element.
     for (int64_t y = xh; y < xb; y += int64_t(kThreads) * Op::kElem)
-      elements<Op>(s, d, y, y + int64_t(kThreads) * Op::kElem < xb ? y + int64_t(kThreads) * Op::kElem : xb);
+      elements<Op, kDev>(s, d, y, y + int64_t(kThreads) * Op::kElem < xb ? y + int64_t(kThreads) * Op::kElem : xb);
     return;
   }
   if (d.n == 1) {

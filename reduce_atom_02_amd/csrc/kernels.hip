@@ -178,6 +178,10 @@ __global__ void __launch_bounds__(kThreads) zs_lds_kernel(const LaunchPlan p) {
 // A ring has `depth` slots; a producer reuses a slot only after its consumers'
 // credits for the previous round arrived.  No workgroup touches another
 // rank's input or output buffer: cross-rank bytes travel through the rings.
+// Producers write slots with device-scope stores, so a ready notify is a
+// drain and a relaxed flag store, and a consumer's acquire is an L2
+// invalidate only; with that, chunks of 32-64 KiB on many lanes are the
+// fastest shape (the ring then stays small).
 struct SlotRef {
   uint64_t data;
   uint64_t *ready;
@@ -235,9 +239,10 @@ __device__ __forceinline__ void write_header(const StagedPlan &sp, uint64_t slot
                                              int chunk) {
   if constexpr (kCheckProtocol) {
     uint64_t *h = slot_header(sp, slot_data);
-    h[0] = tag(e, uint64_t(chunk) + 1u);
-    h[1] = kSlotCanary;
-    __threadfence();  // the header is visible before the release that follows
+    // device scope, like the slot's data, and done before the notify
+    __hip_atomic_store(&h[0], tag(e, uint64_t(chunk) + 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&h[1], kSlotCanary, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
   }
 }
 
@@ -332,17 +337,18 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       d.n = 1;
 #pragma unroll
       for (int q = 0; q < kMaxRanks + 1; ++q) d.b[q] = slot_base(o.data, b0, x0);
-      atom::tile<atom::CopyOp, kU, kNTL>(s, d, x0, x1);
-      // Every wavefront's stores must be acknowledged before thread 0's
-      // release publishes the slot: a workgroup barrier alone does not wait
-      // for other wavefronts' global stores (their head and tail element
-      // passes run on wavefronts 2 and 3), so the release could overtake
-      // them and the owner read a stale line.
+      // the slot is written with device-scope stores
+      atom::tile<atom::CopyOp, kU, kNTL, true, true, false, false, atom::kStoreDevice>(s, d, x0, x1);
+      // Every wavefront's stores must be acknowledged before thread 0
+      // publishes the slot: a workgroup barrier alone does not wait for
+      // other wavefronts' global stores (their head and tail element passes
+      // run on wavefronts 2 and 3), so the notify could overtake them and
+      // the owner read a stale line.
       snac::drain_workgroup();
       if (threadIdx.x == 0) {
         write_header(sp, o.data, e, c);
         const bool withhold = sp.withhold > 0 && ring == 0 && m + 1 == sp.withhold;
-        if (!withhold) snac::store_rel(o.ready, tag(e, round + 1));
+        if (!withhold) snac::publish(o.ready, tag(e, round + 1));
       }
     }
   } else if (kind < sj.n_stage + team) {
@@ -357,9 +363,10 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
       tile_bounds(b0, jb.nbytes, p.chunk_bytes, c, ntl, x0, x1);
       // wait for every staged source chunk, and for the scatter slot's credits
       if (threadIdx.x == 0) {
-        // relaxed polls, then one acquire for all of them: a fence after the
-        // loads that saw the release stores synchronizes with each of them,
-        // and an acquire invalidates the XCD's L2, so one is enough
+        // relaxed polls, then one acquire for all of them: the chunks were
+        // written with device-scope stores and drained before each notify,
+        // and the acquire (an invalidate of the XCD's L2) keeps this
+        // workgroup from reading a stale copy of any of them
         for (int k = 0; k < sj.n_stage && ok; ++k)
           if (!snac::wait_geq<uint64_t, false>(slot_ref(sp, ring0 + k, slot).ready, tag(e, round + 1), p, e))
             ok = 0;
@@ -435,7 +442,8 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
         y0 = x0 + int64_t(a);
         y1 = x0 + int64_t(z);
       }
-      atom::tile<Op, kU, kNTL, false>(s, d, y0, y1);
+      // device-scope stores: the scatter slot (and the owner's output with it)
+      atom::tile<Op, kU, kNTL, false, true, false, false, atom::kStoreDevice>(s, d, y0, y1);
       snac::drain_workgroup();
       if (threadIdx.x == 0) {
         for (int k = 0; k < sj.n_stage; ++k)
@@ -443,7 +451,7 @@ __global__ void __launch_bounds__(kThreads) staged_kernel(const StagedPlan sp) {
         if (sj.n_scatter > 0) {
           // the team's last member writes the scatter slot's header
           if (t + 1 == team) write_header(sp, slot_ref(sp, ring0 + sj.n_stage, slot).data, e, c);
-          snac::store_rel(slot_ref(sp, ring0 + sj.n_stage, slot).ready + t, tag(e, round + 1));
+          snac::publish(slot_ref(sp, ring0 + sj.n_stage, slot).ready + t, tag(e, round + 1));
         }
       }
     }

@@ -745,7 +745,7 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     sp.withhold = pol.test_withhold;
     int64_t max_job = 0;
     for (const Job &jb : jobs) max_job = std::max(max_job, jb.nbytes);
-    int depth = pol.depth ? pol.depth : 4;
+    int depth = pol.depth ? pol.depth : 2;
     // roles per lane of each job
     const int owner_team = int(std::min<int64_t>(kMaxTeam, std::max<int64_t>(1, env_i64("PURLIN_OWNER_TEAM", kOwnerTeam))));
     int roles_per_lane = 0;
@@ -764,13 +764,17 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     }
     if (roles_per_lane > capacity) return PURLIN_ERR_UNSUPPORTED;  // cannot be co-resident
     int lane_cap = pol.wgs_per_rank ? pol.wgs_per_rank : capacity / std::max(1, roles_per_lane);
-    // Staged chunks are long: every handoff costs an L2 writeback (release)
-    // and an invalidate (acquire) on the XCDs involved.  About eight chunks
-    // per job, between 64 KiB and 1 MiB.
+    // Default shape, from the depth x chunk x lanes sweep at 256 MiB per
+    // rank: a ring two slots deep (deeper measured no faster), as many lanes
+    // as fit, and 64 KiB chunks for copies, 256 KiB for reductions (whose
+    // team of owners splits each chunk eight ways); a handoff is a drain and
+    // a flag store (the slots take device-scope stores), so short chunks
+    // pay.  A job shorter than eight chunks takes shorter ones, down to
+    // 16 KiB.
     int64_t chunk = pol.chunk_bytes;
     if (!chunk) {
-      chunk = int64_t(64) << 10;
-      while (chunk < (int64_t(1) << 20) && chunk * 8 < max_job) chunk *= 2;
+      chunk = int64_t(kind == KernelKind::kCopy ? 64 : 256) << 10;
+      while (chunk > (int64_t(16) << 10) && chunk * 8 > max_job) chunk /= 2;
     }
     int64_t ring_bytes = 0, flag_bytes = 0;
     // Lay out tiles, lanes, roles and rings for (chunk, depth, lane_cap).

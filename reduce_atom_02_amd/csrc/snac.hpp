@@ -6,14 +6,22 @@
 // stream has its own, so launches on different streams never share a flag).
 // Costs on a multi-XCD gfx950 shape the protocol:
 //  * an agent-scope acquire invalidates the XCD's L2 and an agent-scope
-//    release writes it back, so neither may sit inside a spin loop;
+//    release writes its dirty lines back, so neither may sit inside a spin
+//    loop, and the release is the dear one;
 //  * a wait therefore polls with relaxed agent-scope loads (which bypass the
 //    non-coherent caches) and issues one acquire fence once the value is
 //    seen, and only when it is about to read data the flag publishes; a
 //    wait for "done reading" (credits, entry) orders later stores only and
 //    takes no acquire;
-//  * a notify that publishes data ("ready") is a release store, so the
-//    chunk written by one workgroup is visible on every XCD;
+//  * a notify that publishes data ("ready") follows data written with
+//    device-scope stores, which are counted as done only once every XCD
+//    would read them: each wavefront waits for its store counter, the
+//    workgroup meets at a barrier, and a relaxed store of the flag then
+//    publishes the chunk (a release store would first write back every
+//    dirty line of the XCD's L2, other workgroups' outputs among them, and
+//    made a handoff of a 32-256 KiB chunk 1.5-4 times slower); the
+//    consumer's acquire fence, a cheap invalidate, keeps it from reading a
+//    stale copy;
 //  * a notify that only says "I have finished reading" (a credit, the exit
 //    count) is a relaxed add issued after every wavefront's loads have
 //    returned their data (s_waitcnt 0, then a barrier): once the data is in
@@ -66,10 +74,18 @@ __device__ __forceinline__ void add_rlx(uint64_t *p, uint64_t v) {
 
 // Every wavefront of the workgroup has its loads back (and its stores
 // acknowledged); call from all threads.  After it, a relaxed notify may say
-// "done reading".
+// "done reading", or publish what the workgroup wrote with device-scope
+// stores (publish()).
 __device__ __forceinline__ void drain_workgroup() {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+}
+
+// Ready notify of data the workgroup wrote with device-scope stores, by one
+// thread after drain_workgroup(): every such store is then visible on every
+// XCD, so the flag needs no release ordering of its own.
+__device__ __forceinline__ void publish(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // This launch's epoch: the stream's epoch word plus one (the block starts

@@ -37,7 +37,11 @@
 // consumers.
 //
 // Memory orders: a notify that publishes data is a release and its wait an
-// acquire, as on the GPU.  The GPU's "done reading" notifies (credits, exit
+// acquire.  On the GPU the producer writes the slot with device-scope
+// stores, waits for all of them to complete and then stores the flag
+// relaxed, which orders the data before the flag the way a release does
+// (without the release's writeback of the L2), and the consumer takes an
+// acquire fence after its wait.  The GPU's "done reading" notifies (credits, exit
 // counts) are relaxed adds issued after the workgroup's loads have returned,
 // and their waits take no acquire; that ordering comes from the hardware (no
 // store issues before the load that saw the flag returned).  C++ gives no
