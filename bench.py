@@ -105,16 +105,18 @@ def measured_traffic(kernel, T, names, variant):
     return None if k is None else int(k["traffic_per_launch"])
 
 
-def kernel_of(name, rows, one, plain=False):
+def kernel_of(name, rows, one, plain=False, device=False):
     """The kernel a collective's launch ran, named as in the rocprofv3
     summaries: the operation, whether it was the build with the realigning
     row bodies (some source off its destinations' 16-byte phase) or the
     aligned-only one, whether it was the build for single-destination jobs
     ("one") or the general one ("general"), and ",plain" for the build with
-    plain body stores (large copy broadcasts)."""
+    plain body stores (large copy broadcasts), ",device" for the one with
+    device-scope stores (broadcasts in their windows)."""
     op = "SumBf16" if SPECS[name][2] == "sum" else "CopyOp"
+    store = ",device" if device else ",plain" if plain else ""
     return "zs_kernel<%s,%s,%s%s>" % (op, "rows" if rows else "aligned",
-                                      "one" if one else "general", ",plain" if plain else "")
+                                      "one" if one else "general", store)
 
 
 def cpu_baseline(T_sample, names, reps=5):
@@ -1248,7 +1250,7 @@ def main():
                      "bmin_bytes": s["bmin"], "grid": launch[name]["grid"],
                      "chunk_bytes": launch[name]["chunk_bytes"]}
         kname = kernel_of(name, launch[name]["rows"], launch[name]["one"],
-                          launch[name]["plain_stores"])
+                          launch[name]["plain_stores"], launch[name]["device_stores"])
         # HBM bytes per launch from the committed counter summary (when it was
         # taken on these sources and this workload): dram_frac is the rate HBM
         # sustained on the bytes actually moved

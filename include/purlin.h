@@ -169,6 +169,8 @@ typedef struct {
   int32_t unaligned_loads; /* zero staging: 1 if jobs with a source off their destinations'
                               phase took destination-aligned units and misaligned loads
                               (copy broadcasts of 32 - 512 MiB of jobs) */
+  int32_t device_stores; /* zero staging: 1 if broadcast jobs were stored at device scope
+                            (written through the L2) */
 } purlin_launch_info;
 
 /*

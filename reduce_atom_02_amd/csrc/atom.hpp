@@ -260,7 +260,7 @@ __device__ __forceinline__ void elements(const Srcs &s, const Dsts &d, int64_t y
 // any is used (indexes past the end are clamped to the last element, so the
 // loads need no branch), so the whole range is one memory round trip.  The
 // caller guarantees 0 < (y1 - y0) / kElem <= kE * kThreads.
-template <class Op, int kE>
+template <class Op, int kE, bool kDevStore = false>
 __device__ __forceinline__ void elements_wide(const Srcs &s, const Dsts &d, int64_t y0, int64_t y1) {
   const int64_t n = (y1 - y0) / Op::kElem;
   const int64_t tid = int64_t(threadIdx.x);
@@ -277,7 +277,7 @@ __device__ __forceinline__ void elements_wide(const Srcs &s, const Dsts &d, int6
       if (i < n) {
 #pragma unroll
         for (int k = 0; k < kMaxRanks + 1; ++k)
-          if (k < d.n) *gp<uint16_t>(d.b[k] + y0 + i * 2) = v[e];
+          if (k < d.n) ste<uint16_t, kDevStore>(d.b[k] + y0 + i * 2, v[e]);
       }
     }
   } else if constexpr (Op::kElem == 4) {
@@ -299,7 +299,7 @@ __device__ __forceinline__ void elements_wide(const Srcs &s, const Dsts &d, int6
       if (i < n) {
 #pragma unroll
         for (int k = 0; k < kMaxRanks + 1; ++k)
-          if (k < d.n) *gp<float>(d.b[k] + y0 + i * 4) = acc;
+          if (k < d.n) ste<float, kDevStore>(d.b[k] + y0 + i * 4, acc);
       }
     }
   } else {
@@ -322,7 +322,7 @@ __device__ __forceinline__ void elements_wide(const Srcs &s, const Dsts &d, int6
       if (i < n) {
 #pragma unroll
         for (int k = 0; k < kMaxRanks + 1; ++k)
-          if (k < d.n) *gp<uint16_t>(d.b[k] + y0 + i * 2) = o;
+          if (k < d.n) ste<uint16_t, kDevStore>(d.b[k] + y0 + i * 2, o);
       }
     }
   }
@@ -765,7 +765,7 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
                                      bool shift_stores = false, lds_u32x4 *lds_slice = nullptr,
                                      bool unaligned_loads = false) {
   constexpr bool kDev = kNTS == kStoreDevice;
-  static_assert(!(kDev && (kWide || kLdsRows > 0)), "device-scope stores: row and aligned bodies only");
+  static_assert(!(kDev && kLdsRows > 0), "the LDS body has no device-scope stores");
   if (x1 <= x0) return;
   if (x1 - x0 <= int64_t(kThreads) * Op::kElem) {
     elements<Op, kDev>(s, d, x0, x1);
@@ -806,7 +806,7 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
     for (int i = 0; i < kMaxRanks; ++i) off |= uint32_t(s.a[i] - d.b[0]) & 15u;
     if (off != 0 && d.n == 1 && x1 - x0 <= wide_max &&
         x1 - x0 <= int64_t(kThreads) * Op::kElem * kWideElems) {
-      elements_wide<Op, kWideElems>(s, d, x0, x1);
+      elements_wide<Op, kWideElems, kDev>(s, d, x0, x1);
       return;
     }
   }

@@ -67,7 +67,7 @@ __device__ __forceinline__ void tile_bounds(uint64_t ref, int64_t n, int64_t C, 
 // kWide: the build for the latency regime, whose small misaligned tiles may
 // take the wide element pass; the others leave that pass out, whose
 // registers would cost a row-body kernel a workgroup per CU.
-template <class Op, int kU, bool kNTL, bool kNTS, bool kRows, bool kOne, bool kWide = false>
+template <class Op, int kU, bool kNTL, int kNTS, bool kRows, bool kOne, bool kWide = false>
 __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
   // With the handshake on, a workgroup whose entry wait failed skips its
   // tiles but still counts itself out, so the stream's epoch advances.
@@ -950,9 +950,18 @@ namespace {
 // without row bodies, and with row bodies for sums; one_build says which
 // launches get one.  The wide builds (latency regime) exist for the row
 // bodies of the default form and unroll, and so do the builds for large copy
-// broadcasts, whose stores are plain (bcast; sums are never asked for one).
+// broadcasts, whose stores are plain (bcast; sums are never asked for one),
+// and the broadcast builds with device-scope stores (dstore: aligned sums,
+// and copies aligned or on the wide row body; dstore_build says which).
 template <class Op, int kU, bool kNT, bool kWideOk = false>
-void *zs_fn(bool rows, bool one, bool wide, bool bcast) {
+void *zs_fn(bool rows, bool one, bool wide, bool bcast, bool dstore) {
+  if constexpr (kNT && kWideOk) {
+    if (dstore && !one) {
+      if (!rows) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, atom::kStoreDevice, false, false>);
+      if constexpr (!Op::kSum)
+        if (wide) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, atom::kStoreDevice, true, false, true>);
+    }
+  }
   if constexpr (kNT) {
     if (one && !rows) return reinterpret_cast<void *>(&zs_kernel<Op, kU, kNT, kNT, false, true>);
     if constexpr (Op::kSum)
@@ -979,18 +988,27 @@ void *st_fn() { return reinterpret_cast<void *>(&staged_kernel<Op, kU, kNT, kNT>
 
 // Unroll depth: 16-byte units each lane keeps in flight per source.
 template <class Op, int kU0, int kU1, int kU2>
-void *pick(bool staged, bool nt, int unroll_sel, bool rows, bool one, bool wide, bool bcast) {
+void *pick(bool staged, bool nt, int unroll_sel, bool rows, bool one, bool wide, bool bcast,
+           bool dstore) {
   if (staged) return nt ? st_fn<Op, kU1, true>() : st_fn<Op, kU1, false>();
   switch (unroll_sel) {
     case 0:
-      return nt ? zs_fn<Op, kU0, true, true>(rows, one, wide, bcast)
-                : zs_fn<Op, kU0, false>(rows, one, false, false);
-    case 2: return nt ? zs_fn<Op, kU2, true>(rows, one, false, false) : zs_fn<Op, kU2, false>(rows, one, false, false);
-    default: return nt ? zs_fn<Op, kU1, true>(rows, one, false, false) : zs_fn<Op, kU1, false>(rows, one, false, false);
+      return nt ? zs_fn<Op, kU0, true, true>(rows, one, wide, bcast, dstore)
+                : zs_fn<Op, kU0, false>(rows, one, false, false, false);
+    case 2:
+      return nt ? zs_fn<Op, kU2, true>(rows, one, false, false, false)
+                : zs_fn<Op, kU2, false>(rows, one, false, false, false);
+    default:
+      return nt ? zs_fn<Op, kU1, true>(rows, one, false, false, false)
+                : zs_fn<Op, kU1, false>(rows, one, false, false, false);
   }
 }
 
 }  // namespace
+
+bool dstore_build(KernelKind kind, bool nt, int unroll_sel, bool rows, bool wide) {
+  return nt && unroll_sel == 0 && (!rows || (kind == KernelKind::kCopy && wide));
+}
 
 bool one_build(KernelKind kind, bool nt, bool rows, bool single_dst) {
   // measured: the single-destination build of the copy with row bodies is
@@ -1006,20 +1024,21 @@ int unroll_of(KernelKind kind, int unroll_sel) {
 }
 
 void *kernel_fn(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows, bool one,
-                bool wide = false, bool bcast = false) {
+                bool wide = false, bool bcast = false, bool dstore = false) {
   switch (kind) {
     case KernelKind::kCopy:
-      return pick<atom::CopyOp, 4, 8, 16>(staged, nt, unroll_sel, rows, one, wide, bcast);
+      return pick<atom::CopyOp, 4, 8, 16>(staged, nt, unroll_sel, rows, one, wide, bcast, dstore);
     case KernelKind::kSumF32:
-      return pick<atom::SumF32, 1, 2, 4>(staged, nt, unroll_sel, rows, one, wide, bcast);
-    default: return pick<atom::SumBf16, 1, 2, 4>(staged, nt, unroll_sel, rows, one, wide, bcast);
+      return pick<atom::SumF32, 1, 2, 4>(staged, nt, unroll_sel, rows, one, wide, bcast, dstore);
+    default:
+      return pick<atom::SumBf16, 1, 2, 4>(staged, nt, unroll_sel, rows, one, wide, bcast, dstore);
   }
 }
 
 hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, bool rows,
-                     bool one, bool wide, bool bcast, int grid, hipStream_t stream) {
+                     bool one, bool wide, bool bcast, bool dstore, int grid, hipStream_t stream) {
   void *args[] = {const_cast<LaunchPlan *>(&p)};
-  return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel, rows, one, wide, bcast), dim3(grid),
+  return hipLaunchKernel(kernel_fn(kind, false, nt, unroll_sel, rows, one, wide, bcast, dstore), dim3(grid),
                          dim3(kThreads), args, 0, stream);
 }
 
@@ -1108,11 +1127,11 @@ hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int gri
 }
 
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
-                               bool one, bool wide, bool bcast, int *blocks) {
+                               bool one, bool wide, bool bcast, bool dstore, int *blocks) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(
       blocks,
       kernel_fn(kind, staged, nt, staged ? 1 : unroll_sel, staged || rows, !staged && one,
-                !staged && wide, !staged && bcast),
+                !staged && wide, !staged && bcast, !staged && dstore),
       kThreads, 0);
 }
 

@@ -17,9 +17,10 @@ enum class KernelKind { kCopy, kSumF32, kSumBf16 };
 // true: the latency-regime build with the wide element pass (row bodies of
 // the default nontemporal form and unroll only; ignored otherwise).  bcast =
 // true: a launch with broadcast jobs, whose body stores are plain (same
-// forms only).
+// forms only).  dstore = true: broadcast jobs stored at device scope (the
+// forms dstore_build accepts).
 hipError_t launch_zs(const LaunchPlan &p, KernelKind kind, bool nt, int unroll_sel, bool rows,
-                     bool one, bool wide, bool bcast, int grid, hipStream_t stream);
+                     bool one, bool wide, bool bcast, bool dstore, int grid, hipStream_t stream);
 hipError_t launch_staged(const StagedPlan &p, KernelKind kind, bool nt, hipStream_t stream);
 // The zero-staging build with the LDS-staged aligned body (launches whose
 // every job is aligned; one: single-destination jobs; bcast: plain stores).
@@ -30,6 +31,10 @@ int unroll_of(KernelKind kind, int unroll_sel);
 // Whether a launch whose jobs all have one destination rank (single_dst) runs
 // the single-destination build (the `one` argument of launch_zs).
 bool one_build(KernelKind kind, bool nt, bool rows, bool single_dst);
+// Whether a broadcast launch of this form has a build with device-scope
+// stores: the default unroll and loads, aligned, or a copy on the wide row
+// body.
+bool dstore_build(KernelKind kind, bool nt, int unroll_sel, bool rows, bool wide);
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,
                               hipStream_t stream);
 // The bare access pattern of a collective (n_src, n_dst in {0, 1, 8}, not
@@ -39,7 +44,7 @@ hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts,
                           int64_t bytes, int grid, int64_t tile_bytes, int unroll, bool ntl,
                           bool nts, hipStream_t stream);
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
-                               bool one, bool wide, bool bcast, int *blocks);
+                               bool one, bool wide, bool bcast, bool dstore, int *blocks);
 
 // MoE dispatch one row at a time (rows: the build with the realigning row
 // bodies), the inverse-map pass, dispatch one token at a time (after the

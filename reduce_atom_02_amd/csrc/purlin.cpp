@@ -50,7 +50,7 @@ struct DeviceState {
   // Outgrown workspace: launches enqueued earlier, or HIP graphs captured
   // earlier, may still use it, so it is freed only by purlin_release.
   std::vector<void *> retired;
-  int occ[3][2][2][3][2][2][2][2] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
+  int occ[3][2][2][3][2][2][2][2][2] = {};  // resident workgroups per CU, by kernel; 0 = not asked yet
 };
 
 std::vector<DeviceState> &devices() {
@@ -202,12 +202,13 @@ purlin_status grow(DeviceState &ds, hipStream_t stream, void **buf, int64_t *hav
 }
 
 int occupancy(DeviceState &s, KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
-              bool one, bool wide, bool bcast) {
+              bool one, bool wide, bool bcast, bool dstore = false) {
   int &o = s.occ[int(kind)][staged ? 1 : 0][nt ? 1 : 0][unroll_sel][rows ? 1 : 0][one ? 1 : 0]
-                [wide ? 1 : 0][bcast ? 1 : 0];
+                [wide ? 1 : 0][bcast ? 1 : 0][dstore ? 1 : 0];
   if (o == 0) {
     int b = 0;
-    if (max_resident_per_cu(kind, staged, nt, unroll_sel, rows, one, wide, bcast, &b) != hipSuccess ||
+    if (max_resident_per_cu(kind, staged, nt, unroll_sel, rows, one, wide, bcast, dstore, &b) !=
+            hipSuccess ||
         b < 1)
       b = 1;
     o = b;
@@ -645,7 +646,8 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     ap.chunk = 8 << 10;
     chunk_fixed = true;
   }
-  // Copy broadcasts of 16 MiB of jobs or more store plainly: AllGather 5-8%,
+  // Copy broadcasts of 16 MiB of jobs or more store plainly (where they do
+  // not store at device scope, below): AllGather 5-8%,
   // AllGatherV 4-8% faster at 64 MiB - 1 GiB per rank than with nontemporal
   // stores (paired on the same buffers, both orders).  Nontemporal stores
   // stay for smaller broadcasts (AllGather 6% faster with them at 4 MiB),
@@ -653,8 +655,24 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
   // 1 GiB) and for single-destination copies (AllToAllV 3-5%).
   const bool bcast = !staged && broadcast && kind == KernelKind::kCopy &&
                      job_bytes >= (int64_t(16) << 20) && env_i64("PURLIN_BCAST_PLAIN", 1) != 0;
+  // Broadcast jobs store at device scope (written through the L2 as they
+  // go, instead of left dirty in it for eviction to write back) in the
+  // windows where that measured faster, paired on the same buffers with
+  // both placements (exactly sized, and prefixes of 1 GiB allocations):
+  //   AllReduce   256 KiB - 128 MiB per rank: 3-8% (16-32 MiB: 5-15%), even
+  //               at 4 MiB and from 256 MiB;
+  //   AllGather   16 - 64 MiB: 1-7%; from 128 MiB 0 to -2.4%, below 16 MiB
+  //               up to -5%;
+  //   AllGatherV  16 MiB - 1 GiB: 1-8% (32 MiB even); below, -3 to -6%.
+  const int64_t dstore_env = env_i64("PURLIN_DEVICE_STORES", -1);
+  const bool dstore_auto =
+      kind != KernelKind::kCopy ? job_bytes >= 256 * 1024 && job_bytes < 256 * MiB
+      : rows                    ? job_bytes >= 16 * MiB
+                                : job_bytes >= 16 * MiB && job_bytes < 128 * MiB;
+  const bool dstore = !staged && broadcast && !one && dstore_build(kind, nt, unroll_sel, rows, wide) &&
+                      (dstore_env < 0 ? dstore_auto : dstore_env != 0);
   const int capacity =
-      ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows, one, wide, bcast);
+      ds->cus * occupancy(*ds, kind, staged, nt, unroll_sel, rows, one, wide, bcast && !dstore, dstore);
 
   // The stream's flag block: for the staged kernel and for the handshake;
   // a zero-staging launch without the handshake touches no flag at all.
@@ -727,13 +745,14 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
       const int g = std::min(grid, ds->cus * b);
       err = launch_zs_lds(lp, kind, single_dst, bcast, g, stream);
     } else {
-      err = launch_zs(lp, kind, nt, unroll_sel, rows, one, wide, bcast, grid, stream);
+      err = launch_zs(lp, kind, nt, unroll_sel, rows, one, wide, bcast && !dstore, dstore, grid, stream);
     }
     info.grid = grid;
     info.zero_staging = 1;
     info.rows = rows ? 1 : 0;
     info.one = one ? 1 : 0;
-    info.plain_stores = bcast ? 1 : 0;
+    info.plain_stores = bcast && !dstore ? 1 : 0;
+    info.device_stores = dstore ? 1 : 0;
     info.shift_stores = lp.shift_stores;
     info.unaligned_loads = lp.unaligned_loads;
     info.chunk_bytes = chunk;

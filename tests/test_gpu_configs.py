@@ -219,7 +219,20 @@ def test_bench_step_1gib(purlin, variant):
 REGIMES = [("alltoall", 256 << 10), ("alltoallv", 512 << 10), ("alltoallv", 8 << 20),
            ("allgather", 24 << 20), ("allgatherv", 6 << 20), ("allgatherv", 24 << 20),
            ("reducescatterv", 24 << 20), ("reducescatterv", 96 << 20),
-           ("allreduce", 16 << 20), ("allreduce", 48 << 20)]
+           ("allreduce", 16 << 20), ("allreduce", 48 << 20),
+           ("allreduce", 128 << 10), ("allreduce", 512 << 10), ("allreduce", 320 << 20),
+           ("allgather", 64 << 20), ("allgather", 160 << 20), ("allgatherv", 96 << 20)]
+
+
+def _expect_device_stores(name, T):
+    """The default policy's windows of broadcast stores at device scope."""
+    if name == "allreduce":
+        return (256 << 10) <= T < (256 << 20)
+    if name == "allgather":
+        return (16 << 20) <= T < (128 << 20)
+    if name == "allgatherv":
+        return T >= (16 << 20)
+    return False
 
 
 @pytest.mark.parametrize("name,T", REGIMES)
@@ -239,6 +252,7 @@ def test_policy_regimes(purlin, name, T):
     in_n, out_n, op = bench.SPECS[name]
     purlin.collective(ins, outs, in_n, out_n, op, s["counts"])
     purlin.check()
+    assert purlin.last_launch()["device_stores"] == int(_expect_device_stores(name, T)), name
     base = name.rstrip("v") if name.endswith("v") else name
     if op == "copy":
         _device_copy_check(base, s["counts"], ins, outs)

@@ -313,12 +313,16 @@ def test_staged_small_misaligned_chunks_repeated(purlin, name):
         oracle_and_gpu(purlin, name, P, counts, "bf16", ins, outs, None, shifts, [rep % 8] * P)
 
 
-@pytest.mark.parametrize("name", ["allgather", "alltoall"])
-def test_store_builds_at_the_broadcast_switch(purlin, name):
-    """Copy broadcasts of 16 MiB of jobs or more run the build with plain
-    stores, single-destination copies the nontemporal one: element-by-element
-    parity just above the switch (AllGather and AllGatherV-like odd sizes),
-    and the build the launch reports."""
+@pytest.mark.parametrize("name,dstores", [("allgather", None), ("allgather", "0"),
+                                          ("alltoall", None)])
+def test_store_builds_at_the_broadcast_switch(purlin, name, dstores, monkeypatch):
+    """Copy broadcasts of 16 MiB of jobs or more on the row body store at
+    device scope (the build with plain stores when that is switched off),
+    single-destination copies nontemporally: element-by-element parity just
+    above the switch (AllGatherV-like odd sizes), and the build the launch
+    reports."""
+    if dstores is not None:
+        monkeypatch.setenv("PURLIN_DEVICE_STORES", dstores)
     P = 8
     print("case store-build", name, flush=True)
     rng = np.random.default_rng([41, len(name)])
@@ -332,10 +336,13 @@ def test_store_builds_at_the_broadcast_switch(purlin, name):
     oracle_and_gpu(purlin, name, P, counts, "bf16", ins, outs, None, [3] * P, [0] * P)
     info = purlin.last_launch()
     if name == "allgather":
-        assert sum(sizes) * 2 >= 16 << 20
-        assert info["plain_stores"] == 1 and info["rows"] == 1, info
+        assert sum(sizes) * 2 >= 16 << 20 and info["rows"] == 1, info
+        if dstores == "0":
+            assert info["plain_stores"] == 1 and info["device_stores"] == 0, info
+        else:
+            assert info["plain_stores"] == 0 and info["device_stores"] == 1, info
     else:
-        assert info["plain_stores"] == 0, info
+        assert info["plain_stores"] == 0 and info["device_stores"] == 0, info
 
 
 def test_overlap_checks_survive_the_pointer_cache(purlin):
@@ -388,7 +395,8 @@ SWITCHES = [{"PURLIN_SHIFT_STORES": "0"}, {"PURLIN_SHIFT_STORES": "1"},
             {"PURLIN_UNALIGNED_LOADS": "1"}, {"PURLIN_UNALIGNED_LOADS": "0"},
             {"PURLIN_BCAST_PLAIN": "0"}, {"PURLIN_NT": "0"}, {"PURLIN_NT_ANY_PHASE": "0"},
             {"PURLIN_UNROLL": "1"}, {"PURLIN_UNROLL": "2"}, {"PURLIN_LDS": "1"},
-            {"PURLIN_MID_CHUNKS": "0"}, {"PURLIN_OWNER_TEAM": "1"}, {"PURLIN_OWNER_TEAM": "3"}]
+            {"PURLIN_MID_CHUNKS": "0"}, {"PURLIN_OWNER_TEAM": "1"}, {"PURLIN_OWNER_TEAM": "3"},
+            {"PURLIN_DEVICE_STORES": "1"}, {"PURLIN_DEVICE_STORES": "0"}]
 
 
 @pytest.mark.parametrize("switch", SWITCHES, ids=lambda d: ",".join("%s=%s" % kv for kv in d.items()))
