@@ -173,16 +173,19 @@ PATTERNS = [
     ("read-only x8", 8, 0, 1, ()),
     ("write-only x8", 0, 8, 1, ()),
 ]
-ACCESS = {(True, True): "nt/nt", (True, False): "nt/plain", (False, True): "plain/nt",
-          (False, False): "plain/plain"}
+# (nontemporal loads, store mode) -> label; "device": stores written through
+# the L2 (device scope), the form the broadcasts take in their windows
+ACCESS = {(True, "nt"): "nt/nt", (True, "plain"): "nt/plain", (False, "nt"): "plain/nt",
+          (False, "plain"): "plain/plain", (True, "device"): "nt/device",
+          (False, "device"): "plain/device"}
 
 
 def ceilings(purlin, T, reps, dev, full=False, path=None):
     """HBM ceiling of each collective's access pattern (purlin_stream_pattern:
     n read streams, m write streams, no planning or flags), the best over a
-    sweep of nontemporal or plain loads x nontemporal or plain stores x tile
-    (16 KiB - 1 MiB) x grid x unroll (full=True: 4 x 4 x 4 grids x 3
-    unrolls; else 4 x 2 x 2 x 1), p50 of `reps` cold calls per point (a 1 GiB
+    sweep of nontemporal or plain loads x nontemporal, plain or device-scope
+    stores x tile (4 KiB - 1 MiB) x grid x unroll (full=True: 6 x 5 x 4
+    grids x 3 unrolls; else 6 x 3 x 2 x 1), p50 of `reps` cold calls per point (a 1 GiB
     fill between calls, outside the events).  Also hipMemcpyAsync device to
     device (torch's copy_) over P*T bytes, as a context figure.  Every point
     goes to `path` (JSONL) when given."""
@@ -209,7 +212,8 @@ def ceilings(purlin, T, reps, dev, full=False, path=None):
         ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
         return ts[len(ts) // 2]
 
-    tiles = (16 << 10, 64 << 10, 256 << 10, 1 << 20) if full else (16 << 10, 256 << 10)
+    tiles = ((4 << 10, 16 << 10, 64 << 10, 256 << 10, 1 << 20) if full
+             else (4 << 10, 16 << 10, 256 << 10))
     grids = (256, 512, 1024, 2048) if full else (512, 1024)
     out = {}
     f = open(path, "w") if path else None
@@ -221,17 +225,18 @@ def ceilings(purlin, T, reps, dev, full=False, path=None):
             s_, d_ = srcs[:nr], dsts[:nw]
         unrolls = ((2, 4, 8) if nr < 8 else (2, 4)) if full else (4,)
         best = None
-        for (ntl, nts) in ACCESS:
-            if nr == 0 and not ntl or nw == 0 and not nts:
+        for (ntl, smode) in ACCESS:
+            if nr == 0 and not ntl or nw == 0 and smode != "nt":
                 continue                       # the unused side: one setting
             for tile in tiles:
                 for g in grids:
                     for u in unrolls:
                         t = p50_of(lambda: purlin.stream_pattern(
                             s_, d_, nbytes, grid=g, tile_bytes=tile, unroll=u, nt_loads=ntl,
-                            nt_stores=nts, stream=stream))
+                            nt_stores=smode == "nt", device_stores=smode == "device",
+                            stream=stream))
                         frac = (nr + nw) * nbytes / t / HBM_PEAK
-                        point = {"pattern": label, "access": ACCESS[(ntl, nts)], "tile": tile,
+                        point = {"pattern": label, "access": ACCESS[(ntl, smode)], "tile": tile,
                                  "grid": g, "unroll": u, "p50_us": round(t * 1e6, 1),
                                  "hbm_frac": round(frac, 4), "bytes": (nr + nw) * nbytes}
                         if f:

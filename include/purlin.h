@@ -395,11 +395,12 @@ PURLIN_API purlin_status purlin_stream_copy(void *dst, const void *src, int64_t 
  * pattern of the unit index; n_dst 0: read-only), all pointers 16-byte
  * aligned and every destination disjoint from every source.  `grid`
  * workgroups (0: four per CU, at most 65536) walk tiles of tile_bytes (0:
- * 16 KiB; a multiple of 16) in grid-stride order, `unroll` 16-byte units
- * per lane in flight (0: 4; else 2, 4 or 8; eight sources take at most 4),
- * with no planning or flags, as
- * the collectives walk theirs.  access bit 0: nontemporal loads, bit 1:
- * nontemporal stores.  INVALID_ARG otherwise.  Asynchronous on `stream`. */
+ * 16 KiB; a multiple of 16, below 4 GiB) in grid-stride order, `unroll`
+ * 16-byte units per lane in flight (0: 4; else 2, 4 or 8; eight sources
+ * take at most 4), with no planning or flags, as the collectives walk
+ * theirs.  access bit 0: nontemporal loads, bit 1: nontemporal stores, bit
+ * 2: device-scope stores (written through the L2; bit 1 is then ignored).
+ * INVALID_ARG otherwise.  Asynchronous on `stream`. */
 PURLIN_API purlin_status purlin_stream_pattern(const void *const *srcs, int n_src,
                                                void *const *dsts, int n_dst, int64_t bytes,
                                                int grid, int64_t tile_bytes, int unroll,

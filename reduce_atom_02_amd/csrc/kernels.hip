@@ -833,18 +833,20 @@ __global__ void __launch_bounds__(kThreads) stream_copy_kernel(atom::u32x4 *dst,
 // read-only), the same offset everywhere, with no planning or flags.  Tiles
 // of `tile16` units are dealt in grid-stride order as the collectives deal
 // theirs; full passes of kU units per lane are unguarded, the tile's last
-// pass is guarded.  kNTL / kNTS: nontemporal loads / stores.
+// pass is guarded.  kNTL: nontemporal loads; kNTS: the store mode (plain,
+// nontemporal or device scope, atom::kStore*).
 struct PatternPtrs {
   const atom::u32x4 *src[kMaxRanks];
   atom::u32x4 *dst[kMaxRanks];
 };
 
 
-// One pass of kU units per lane from unit b (this lane's first); with
-// kGuard, units at or past `end` are neither loaded (clamped) nor stored.
-template <int kR, int kW, int kU, bool kNTL, bool kNTS, bool kGuard>
-__device__ __forceinline__ void pattern_pass(const PatternPtrs &p, int64_t b, int64_t end,
-                                             atom::u32x4 &acc) {
+// One pass of kU units per lane from unit b (this lane's first) of the
+// tile that starts at unit tb; with kGuard, units at or past `end` are
+// neither loaded (clamped) nor stored.
+template <int kR, int kW, int kU, bool kNTL, int kNTS, bool kGuard>
+__device__ __forceinline__ void pattern_pass(const PatternPtrs &p, int64_t tb, int64_t b,
+                                             int64_t end, atom::u32x4 &acc) {
   atom::u32x4 v[kU][kR > 0 ? kR : 1];
 #pragma unroll
   for (int k = 0; k < kU; ++k) {
@@ -868,24 +870,26 @@ __device__ __forceinline__ void pattern_pass(const PatternPtrs &p, int64_t b, in
       acc ^= a;
     } else if (!kGuard || i < end) {
 #pragma unroll
-      for (int w = 0; w < kW; ++w) atom::st16<kNTS>(uint64_t(p.dst[w] + i), a);
+      for (int w = 0; w < kW; ++w)
+        atom::stm<kNTS>(uint64_t(p.dst[w] + tb), uint32_t(i - tb) * 16u, a);
     }
   }
 }
 
-template <int kR, int kW, int kU, bool kNTL, bool kNTS>
+template <int kR, int kW, int kU, bool kNTL, int kNTS>
 __global__ void __launch_bounds__(kThreads) pattern_kernel(PatternPtrs p, int64_t n16, int64_t tile16) {
   constexpr int64_t kPass = int64_t(kThreads) * kU;
   const int64_t ntiles = (n16 + tile16 - 1) / tile16;
   atom::u32x4 acc{0u, 0u, 0u, 0u};
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t end = (t + 1) * tile16 < n16 ? (t + 1) * tile16 : n16;
-    int64_t b = t * tile16;
+    const int64_t tb = t * tile16;
+    int64_t b = tb;
     // full passes: every unit lies inside the tile, no guard
     for (; b + kPass <= end; b += kPass)
-      pattern_pass<kR, kW, kU, kNTL, kNTS, false>(p, b + threadIdx.x, end, acc);
+      pattern_pass<kR, kW, kU, kNTL, kNTS, false>(p, tb, b + threadIdx.x, end, acc);
     if (b < end) {
-      pattern_pass<kR, kW, kU, kNTL, kNTS, true>(p, b + threadIdx.x, end, acc);
+      pattern_pass<kR, kW, kU, kNTL, kNTS, true>(p, tb, b + threadIdx.x, end, acc);
       atom::drain_vm();
     }
   }
@@ -893,36 +897,43 @@ __global__ void __launch_bounds__(kThreads) pattern_kernel(PatternPtrs p, int64_
     if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u) g_pattern_sink = acc;
 }
 
+template <int kR, int kW, int kU, bool kNTL>
+const void *pattern_fn_s(int smode) {
+  if constexpr (kW > 0)
+    if (smode == atom::kStoreDevice)
+      return reinterpret_cast<const void *>(&pattern_kernel<kR, kW, kU, kNTL, atom::kStoreDevice>);
+  return smode == atom::kStorePlain
+             ? reinterpret_cast<const void *>(&pattern_kernel<kR, kW, kU, kNTL, atom::kStorePlain>)
+             : reinterpret_cast<const void *>(&pattern_kernel<kR, kW, kU, kNTL, atom::kStoreNT>);
+}
+
 template <int kR, int kW, int kU>
-const void *pattern_fn_u(bool ntl, bool nts) {
-  if (ntl) return nts ? reinterpret_cast<const void *>(&pattern_kernel<kR, kW, kU, true, true>)
-                      : reinterpret_cast<const void *>(&pattern_kernel<kR, kW, kU, true, false>);
-  return nts ? reinterpret_cast<const void *>(&pattern_kernel<kR, kW, kU, false, true>)
-             : reinterpret_cast<const void *>(&pattern_kernel<kR, kW, kU, false, false>);
+const void *pattern_fn_u(bool ntl, int smode) {
+  return ntl ? pattern_fn_s<kR, kW, kU, true>(smode) : pattern_fn_s<kR, kW, kU, false>(smode);
 }
 
 // Eight sources keep at most four units per lane in flight (eight would
 // hold 256 VGPRs of loads and spill).
 template <int kR, int kW>
-const void *pattern_fn_rw(int unroll, bool ntl, bool nts) {
+const void *pattern_fn_rw(int unroll, bool ntl, int smode) {
   switch (unroll) {
-    case 2: return pattern_fn_u<kR, kW, 2>(ntl, nts);
+    case 2: return pattern_fn_u<kR, kW, 2>(ntl, smode);
     case 8:
-      if constexpr (kR < 8) return pattern_fn_u<kR, kW, 8>(ntl, nts);
-      else return pattern_fn_u<kR, kW, 4>(ntl, nts);
-    default: return pattern_fn_u<kR, kW, 4>(ntl, nts);
+      if constexpr (kR < 8) return pattern_fn_u<kR, kW, 8>(ntl, smode);
+      else return pattern_fn_u<kR, kW, 4>(ntl, smode);
+    default: return pattern_fn_u<kR, kW, 4>(ntl, smode);
   }
 }
 
-const void *pattern_fn(int n_src, int n_dst, int unroll, bool ntl, bool nts) {
-  if (n_src == 0 && n_dst == 1) return pattern_fn_rw<0, 1>(unroll, ntl, nts);
-  if (n_src == 0 && n_dst == 8) return pattern_fn_rw<0, 8>(unroll, ntl, nts);
-  if (n_src == 1 && n_dst == 0) return pattern_fn_rw<1, 0>(unroll, ntl, nts);
-  if (n_src == 8 && n_dst == 0) return pattern_fn_rw<8, 0>(unroll, ntl, nts);
-  if (n_src == 1 && n_dst == 1) return pattern_fn_rw<1, 1>(unroll, ntl, nts);
-  if (n_src == 1 && n_dst == 8) return pattern_fn_rw<1, 8>(unroll, ntl, nts);
-  if (n_src == 8 && n_dst == 1) return pattern_fn_rw<8, 1>(unroll, ntl, nts);
-  if (n_src == 8 && n_dst == 8) return pattern_fn_rw<8, 8>(unroll, ntl, nts);
+const void *pattern_fn(int n_src, int n_dst, int unroll, bool ntl, int smode) {
+  if (n_src == 0 && n_dst == 1) return pattern_fn_rw<0, 1>(unroll, ntl, smode);
+  if (n_src == 0 && n_dst == 8) return pattern_fn_rw<0, 8>(unroll, ntl, smode);
+  if (n_src == 1 && n_dst == 0) return pattern_fn_rw<1, 0>(unroll, ntl, smode);
+  if (n_src == 8 && n_dst == 0) return pattern_fn_rw<8, 0>(unroll, ntl, smode);
+  if (n_src == 1 && n_dst == 1) return pattern_fn_rw<1, 1>(unroll, ntl, smode);
+  if (n_src == 1 && n_dst == 8) return pattern_fn_rw<1, 8>(unroll, ntl, smode);
+  if (n_src == 8 && n_dst == 1) return pattern_fn_rw<8, 1>(unroll, ntl, smode);
+  if (n_src == 8 && n_dst == 8) return pattern_fn_rw<8, 8>(unroll, ntl, smode);
   return nullptr;
 }
 
@@ -930,7 +941,7 @@ const void *pattern_fn(int n_src, int n_dst, int unroll, bool ntl, bool nts) {
 
 hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts, int n_dst,
                           int64_t bytes, int grid, int64_t tile_bytes, int unroll, bool ntl,
-                          bool nts, hipStream_t stream) {
+                          int smode, hipStream_t stream) {
   PatternPtrs p{};
   for (int r = 0; r < kMaxRanks; ++r) {
     p.src[r] = n_src ? static_cast<const atom::u32x4 *>(srcs[r < n_src ? r : 0]) : nullptr;
@@ -938,7 +949,7 @@ hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts,
   }
   int64_t n16 = bytes / 16;
   int64_t tile16 = tile_bytes / 16;
-  const void *fn = pattern_fn(n_src, n_dst, unroll, ntl, nts);
+  const void *fn = pattern_fn(n_src, n_dst, unroll, ntl, smode);
   if (!fn) return hipErrorInvalidValue;
   void *args[] = {&p, &n16, &tile16};
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);

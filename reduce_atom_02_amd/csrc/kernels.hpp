@@ -38,11 +38,12 @@ bool dstore_build(KernelKind kind, bool nt, int unroll_sel, bool rows, bool wide
 hipError_t launch_stream_copy(void *dst, const void *src, int64_t bytes, int grid,
                               hipStream_t stream);
 // The bare access pattern of a collective (n_src, n_dst in {0, 1, 8}, not
-// both 0): `tile_bytes` per tile (a multiple of 16), `unroll` units per lane
-// in flight (2, 4 or 8), nontemporal loads (ntl) and stores (nts).
+// both 0): `tile_bytes` per tile (a multiple of 16, below 4 GiB), `unroll`
+// units per lane in flight (2, 4 or 8), nontemporal loads (ntl), store mode
+// smode (atom::kStorePlain / kStoreNT / kStoreDevice).
 hipError_t launch_pattern(const void *const *srcs, int n_src, void *const *dsts, int n_dst,
                           int64_t bytes, int grid, int64_t tile_bytes, int unroll, bool ntl,
-                          bool nts, hipStream_t stream);
+                          int smode, hipStream_t stream);
 hipError_t max_resident_per_cu(KernelKind kind, bool staged, bool nt, int unroll_sel, bool rows,
                                bool one, bool wide, bool bcast, bool dstore, int *blocks);
 

@@ -646,6 +646,22 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     ap.chunk = 8 << 10;
     chunk_fixed = true;
   }
+  // Aligned copy broadcasts (AllGather) from 64 MiB of jobs run four
+  // workgroups per CU on 4 KiB chunks with device-scope stores (below), from
+  // grid x chunk sweeps at 64 MiB - 1 GiB per rank: +7-8% at 128 MiB -
+  // 1 GiB, +0.7% at 64 MiB, paired against the table's two per CU, 16 KiB
+  // chunks and plain stores on two boxes with both placements (at 32 MiB
+  // -4%).  One workgroup per CU and 32 KiB chunks for AllReduce measured
+  // +1-2% on one box and -3 to -7% on another, so AllReduce keeps the
+  // table's.
+  const bool large_bcast = env_i64("PURLIN_LARGE_BCAST", 1) != 0;
+  const bool large_copy_bcast = large_bcast && broadcast && !rows && kind == KernelKind::kCopy &&
+                                job_bytes >= 64 * MiB && !chunk_fixed;
+  if (large_copy_bcast) {
+    ap.grid = 4 * ds->cus;
+    ap.chunk = 4 << 10;
+    chunk_fixed = true;
+  }
   // Copy broadcasts of 16 MiB of jobs or more store plainly (where they do
   // not store at device scope, below): AllGather 5-8%,
   // AllGatherV 4-8% faster at 64 MiB - 1 GiB per rank than with nontemporal
@@ -661,14 +677,15 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
   // both placements (exactly sized, and prefixes of 1 GiB allocations):
   //   AllReduce   256 KiB - 128 MiB per rank: 3-8% (16-32 MiB: 5-15%), even
   //               at 4 MiB and from 256 MiB;
-  //   AllGather   16 - 64 MiB: 1-7%; from 128 MiB 0 to -2.4%, below 16 MiB
-  //               up to -5%;
+  //   AllGather   16 - 64 MiB: 1-7%; below 16 MiB up to -5%; from 128 MiB
+  //               0 to -2.4% on the table's grid, the gains above on the
+  //               grid and chunk of the large copy broadcasts;
   //   AllGatherV  16 MiB - 1 GiB: 1-8% (32 MiB even); below, -3 to -6%.
   const int64_t dstore_env = env_i64("PURLIN_DEVICE_STORES", -1);
   const bool dstore_auto =
       kind != KernelKind::kCopy ? job_bytes >= 256 * 1024 && job_bytes < 256 * MiB
-      : rows                    ? job_bytes >= 16 * MiB
-                                : job_bytes >= 16 * MiB && job_bytes < 128 * MiB;
+                                : job_bytes >= 16 * MiB &&
+                                      (rows || large_copy_bcast || job_bytes < 128 * MiB);
   const bool dstore = !staged && broadcast && !one && dstore_build(kind, nt, unroll_sel, rows, wide) &&
                       (dstore_env < 0 ? dstore_auto : dstore_env != 0);
   const int capacity =
@@ -1149,8 +1166,8 @@ purlin_status purlin_stream_pattern(const void *const *srcs, int n_src, void *co
   const bool ok_n = (n_src == 0 || n_src == 1 || n_src == 8) && (n_dst == 0 || n_dst == 1 || n_dst == 8) &&
                     (n_src + n_dst) > 0;
   if (!ok_n || (n_src && !srcs) || (n_dst && !dsts) || bytes < 0 || (bytes & 15) || grid < 0 ||
-      grid > 65536 || tile_bytes < 0 || (tile_bytes & 15) ||
-      (unroll != 0 && unroll != 2 && unroll != 4 && unroll != 8) || access < 0 || access > 3)
+      grid > 65536 || tile_bytes < 0 || (tile_bytes & 15) || tile_bytes >= (int64_t(1) << 32) ||
+      (unroll != 0 && unroll != 2 && unroll != 4 && unroll != 8) || access < 0 || access > 7)
     return PURLIN_ERR_INVALID_ARG;
   for (int r = 0; r < n_src; ++r)
     if (!srcs[r] || (uintptr_t(srcs[r]) & 15)) return PURLIN_ERR_INVALID_ARG;
@@ -1162,7 +1179,8 @@ purlin_status purlin_stream_pattern(const void *const *srcs, int n_src, void *co
   if (st != PURLIN_OK) return st;
   return launch_pattern(srcs, n_src, dsts, n_dst, bytes, grid ? grid : ds->cus * 4,
                         tile_bytes ? tile_bytes : int64_t(16) << 10, unroll ? unroll : 4,
-                        (access & 1) != 0, (access & 2) != 0, stream) == hipSuccess
+                        (access & 1) != 0, (access & 4) ? 2 : (access & 2) ? 1 : 0,
+                        stream) == hipSuccess
              ? PURLIN_OK
              : PURLIN_ERR_HIP;
 }

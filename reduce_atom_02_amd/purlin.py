@@ -437,13 +437,14 @@ def stream_copy(dst, src, nbytes, stream=None):
 
 
 def stream_pattern(srcs, dsts, nbytes, grid=0, tile_bytes=0, unroll=0, nt_loads=True,
-                   nt_stores=True, stream=None):
+                   nt_stores=True, stream=None, device_stores=False):
     """Bare read/write pattern of a collective (ceiling measurement): srcs
     and dsts hold 0, 1 or 8 buffers each; grid 0 is four workgroups per CU,
-    tile_bytes 0 is 16 KiB, unroll 0 is 4 units per lane."""
+    tile_bytes 0 is 16 KiB, unroll 0 is 4 units per lane; device_stores
+    writes through the L2 (nt_stores is then ignored)."""
     sa = (ctypes.c_void_p * max(1, len(srcs)))(*[_ptr(x) for x in srcs])
     da = (ctypes.c_void_p * max(1, len(dsts)))(*[_ptr(x) for x in dsts])
-    access = (1 if nt_loads else 0) | (2 if nt_stores else 0)
+    access = (1 if nt_loads else 0) | (2 if nt_stores else 0) | (4 if device_stores else 0)
     _raise(_lib.purlin_stream_pattern(sa, len(srcs), da, len(dsts), int(nbytes), int(grid),
                                       int(tile_bytes), int(unroll), access,
                                       ctypes.c_void_p(_stream(stream))), "purlin_stream_pattern")

@@ -287,6 +287,32 @@ def test_ulysses_argument_checks(purlin):
     assert uly([0, 0], in_=V(0, 0), out_=V(0, 0)) == 0                  # nothing to move
 
 
+def test_stream_pattern_argument_checks(purlin):
+    """The ceiling pattern rejects bad arguments before any HIP call; a
+    zero-byte pattern with valid arguments is a no-op."""
+    import ctypes
+    lib = purlin._lib
+    V = ctypes.c_void_p * 8
+    srcs = V(*[A_IN + r * (1 << 30) for r in range(8)])
+    dsts = V(*[A_OUT + r * (1 << 30) for r in range(8)])
+
+    def pat(n_src=1, n_dst=1, nbytes=0, grid=0, tile=0, unroll=0, access=3):
+        return lib.purlin_stream_pattern(srcs, n_src, dsts, n_dst, nbytes, grid, tile, unroll,
+                                         access, None)
+
+    assert pat(n_src=0, n_dst=0) == 1                # nothing read or written
+    assert pat(n_src=2) == 1                         # 0, 1 or 8 streams only
+    assert pat(nbytes=24) == 1                       # not a multiple of 16
+    assert pat(grid=65537) == 1
+    assert pat(tile=24) == 1
+    assert pat(tile=1 << 32) == 1                    # a tile spans less than 4 GiB
+    assert pat(unroll=3) == 1
+    assert pat(access=8) == 1                        # bits 0-2 only
+    assert pat(access=-1) == 1
+    for access in range(8):                          # every store and load mode
+        assert pat(access=access) == 0
+
+
 @pytest.mark.parametrize("P", [5, 6, 7, 8])
 def test_job_bound_after_the_broadcast_split(purlin, P):
     """A sum of P partitions broadcast to every rank (by_index -> by_index)
