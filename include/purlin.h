@@ -312,11 +312,13 @@ PURLIN_API purlin_status purlin_plan_describe(const purlin_layout *in, const pur
  * library keeps per stream (as purlin_moe_combine); a token twice in one
  * group is then reported.  unique == 0 gathers row by row and allows repeats.
  *
- * Rows are moved as bytes (row_bytes even, buffers 2-byte aligned; 16-byte
- * alignment of every buffer and of row_bytes takes the faster kernels, and
- * is needed for the by-token path).  Ownership as purlin_collective.
+ * Rows are moved as bytes (row_bytes even and at most 1 GiB, buffers 2-byte
+ * aligned; 16-byte alignment of every buffer and of row_bytes takes the
+ * faster kernels, and is needed for the by-token path).  Ownership as
+ * purlin_collective.
  * Synchronous errors: INVALID_ARG for P outside [1, 8], a NULL array or
- * buffer that holds data, a negative count, odd row_bytes, entries for a
+ * buffer that holds data, a negative count, odd row_bytes or one above
+ * 1 GiB, entries for a
  * rank with no rows, an output overlapping an input or another output.
  * Asynchronous: an index outside [0, x_rows[i]) skips its row and makes the
  * next purlin_check return INVALID_ARG.  Asynchronous on `stream`.

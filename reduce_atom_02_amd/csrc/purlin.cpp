@@ -317,8 +317,9 @@ void fill_tiles(LaunchPlan &lp, const std::vector<Job> &jobs, int64_t chunk) {
 purlin_status moe_plan(void *const *rowsrc, void *const *rowdst, int P, int64_t row_bytes,
                        const int32_t *const *idx, const int64_t *counts, const int64_t *x_rows,
                        bool combine, MoePlan *m, int64_t *total_rows, int64_t *y_rows_out) {
+  // a row is one tile, and a tile spans less than 4 GiB (rows up to 1 GiB)
   if (!rowsrc || !rowdst || !idx || !counts || !x_rows || P < 1 || P > kMaxRanks ||
-      row_bytes <= 0 || (row_bytes & 1))
+      row_bytes <= 0 || (row_bytes & 1) || row_bytes > (int64_t(1) << 30))
     return PURLIN_ERR_INVALID_ARG;
   int64_t n_ent[kMaxRanks] = {}, y_rows[kMaxRanks] = {};
   int64_t total = 0, x_total = 0;

@@ -247,6 +247,7 @@ def test_moe_argument_checks(purlin):
     assert disp([1, 1, 1, 1], [4, -4]) == 1                 # negative row count
     assert disp([1, 1, 1, 1], [4, 4], row_bytes=63) == 1    # odd row
     assert disp([1, 1, 1, 1], [4, 4], row_bytes=0) == 1
+    assert disp([1, 1, 1, 1], [4, 4], row_bytes=(1 << 30) + 2) == 1   # a row above 1 GiB
     assert disp([1, 1, 1, 1], [4, 0]) == 1                  # entries for a rank with no rows
     assert disp([1, 1, 1, 1], [4, 4], idx_=V(0x10000, 0)) == 1   # NULL index array with entries
     assert disp([1, 1, 1, 1], [4, 4], y_=V(A_OUT, A_OUT + 64)) == 1  # outputs overlap
