@@ -168,7 +168,7 @@ typedef struct {
                             stores (reductions) */
   int32_t unaligned_loads; /* zero staging: 1 if jobs with a source off their destinations'
                               phase took destination-aligned units and misaligned loads
-                              (copy broadcasts of 32 - 512 MiB of jobs) */
+                              (copy broadcasts of 32 MiB of jobs or more) */
   int32_t device_stores; /* zero staging: 1 if broadcast jobs were stored at device scope
                             (written through the L2) */
 } purlin_launch_info;

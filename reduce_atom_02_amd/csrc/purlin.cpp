@@ -746,15 +746,15 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     const int64_t shift_env = env_i64("PURLIN_SHIFT_STORES", -1);
     lp.shift_stores = (shift_env < 0 ? kind != KernelKind::kCopy : shift_env != 0) ? 1 : 0;
     // Copy broadcasts whose source is off the destinations' phase
-    // (AllGatherV) with 32 - 512 MiB of jobs take destination-aligned units
-    // with misaligned source loads instead of the row body: +2-4% at 64 and
-    // 256 MiB per rank (paired, two runs); at 16 MiB -3%, at 1 GiB even, in
-    // the latency regime slower.  The other copies keep the row body
-    // (AllToAllV 4-9% slower with misaligned loads), and reductions their
-    // misaligned stores.
+    // (AllGatherV) from 32 MiB of jobs take destination-aligned units with
+    // misaligned source loads instead of the row body: +2-4% at 64 and
+    // 256 MiB per rank (paired, two runs), +1.4-2.1% at 768 MiB - 1 GiB with
+    // the device-scope stores they take there (even with plain stores); at
+    // 16 MiB -3%, in the latency regime slower.  The other copies keep the
+    // row body (AllToAllV 4-9% slower with misaligned loads), and
+    // reductions their misaligned stores.
     const int64_t ul_env = env_i64("PURLIN_UNALIGNED_LOADS", -1);
-    const bool ul_auto = kind == KernelKind::kCopy && broadcast &&
-                         job_bytes >= (int64_t(32) << 20) && job_bytes <= (int64_t(512) << 20);
+    const bool ul_auto = kind == KernelKind::kCopy && broadcast && job_bytes >= (int64_t(32) << 20);
     lp.unaligned_loads = (ul_env < 0 ? ul_auto : ul_env != 0) ? 1 : 0;
     const bool lds = !rows && nt && env_i64("PURLIN_LDS", 0) != 0;
     if (lds) {

@@ -370,7 +370,7 @@ def test_overlap_checks_survive_the_pointer_cache(purlin):
 @pytest.mark.parametrize("name", ["allgather", "alltoall", "reducescatter"])
 def test_tile_forms_at_the_mid_size_broadcast_window(purlin, name):
     """Odd partition sizes around 40 MiB of jobs: copy broadcasts take
-    destination-aligned units with misaligned loads (32 - 512 MiB of jobs),
+    destination-aligned units with misaligned loads (from 32 MiB of jobs),
     point-to-point copies the row body, reductions source-aligned units with
     misaligned stores; element-by-element parity and the form each launch
     reports."""
