@@ -163,9 +163,10 @@ typedef struct {
                             at most 128 MiB each way */
   int32_t engine_copies; /* copy-engine transfers enqueued (PURLIN_ENGINE_COPY; grid is then
                             0: no kernel ran), 0 for kernel launches */
-  int32_t shift_stores;  /* zero staging: 1 if jobs whose sources share a 16-byte phase off
-                            their destination's took source-aligned units and misaligned
-                            stores (reductions) */
+  int32_t shift_stores;  /* zero staging: jobs whose sources share a 16-byte phase off
+                            their destination's took source-aligned units (reductions):
+                            1 with misaligned stores, 2 shifted into aligned stores
+                            across carried rows (256 MiB of jobs or more) */
   int32_t unaligned_loads; /* zero staging: 1 if jobs with a source off their destinations'
                               phase took destination-aligned units and misaligned loads
                               (copy broadcasts of 32 MiB of jobs or more) */
@@ -268,8 +269,10 @@ PURLIN_API purlin_status purlin_check(hipStream_t stream);
  *
  * Datapath switches, read at every call, for measurement (each selects
  * between forms that give identical results; unset = the measured default):
- * PURLIN_SHIFT_STORES (0/1: sums whose sources share a 16-byte phase off
- * their destination's take source-aligned units with misaligned stores),
+ * PURLIN_SHIFT_STORES (0/1/2: sums whose sources share a 16-byte phase off
+ * their destination's take the row body / source-aligned units with
+ * misaligned stores / the same units shifted into aligned stores across
+ * rows each wavefront carries),
  * PURLIN_UNALIGNED_LOADS (0/1: copies off their destination's phase take
  * destination-aligned units with misaligned loads), PURLIN_BCAST_PLAIN (0/1:
  * plain stores for large copy broadcasts), PURLIN_NT (0/1: nontemporal
@@ -278,7 +281,10 @@ PURLIN_API purlin_status purlin_check(hipStream_t stream);
  * units per lane in flight, copies 4 / 8 / 16, sums 1 / 2 / 4), PURLIN_LDS
  * (0/1: the LDS-staged aligned body), PURLIN_OWNER_TEAM (1-8: owner
  * workgroups per staged reduction lane), PURLIN_MID_CHUNKS (0/1: the
- * mid-size chunk rules of the policy table). */
+ * mid-size chunk rules of the policy table), PURLIN_DEVICE_STORES (0/1:
+ * broadcast stores at device scope, written through the L2),
+ * PURLIN_LARGE_BCAST (0/1: the grid and chunk of large aligned copy
+ * broadcasts). */
 PURLIN_API purlin_status purlin_set_policy(const purlin_policy *p);
 
 /* The policy in force (defaults, environment, then purlin_set_policy). */

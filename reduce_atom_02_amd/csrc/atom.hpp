@@ -695,6 +695,81 @@ __device__ __forceinline__ void body_rows(const uint64_t *sa, int ns, const uint
     pass_rows<Op, kU, kNTL, kNTS, true, kOne, false>(base, lim, ns, db, nd, nunits, sh, u0);
 }
 
+// Body of a sum tile whose sources share one 16-byte phase and whose
+// destinations (congruent) sit on another, with aligned stores and no
+// block read twice: source-aligned units are loaded and folded, and each
+// destination unit is shifted together from a folded unit and the next
+// (lane shuffle + v_alignbyte).  Each wavefront takes a contiguous block of
+// rows (64 units) and carries a row's folded units until the next row is
+// folded, whose first unit lane 63 needs; the unit after a wavefront's last
+// row is the first of the next wavefront's block, handed over in LDS behind
+// a barrier once per tile.  sa[] / db[]: sources and destinations at the
+// body's first source byte (16-byte aligned sources); n16 source units;
+// sig = (16 - (db - sa)) % 16, the source offset of the first destination
+// unit boundary.  Destination unit k (source bytes 16k + sig ..) is stored
+// for k + 1 < n16; the caller's element passes cover the bytes before unit 0
+// and after unit n16 - 2.  Every wavefront of the workgroup calls it.
+template <class Op, bool kNTL, int kNTS, bool kOne>
+__device__ __forceinline__ void body_carry(const uint64_t *sa, int ns, const uint64_t *db, int nd,
+                                           uint32_t n16, uint32_t sig) {
+  static_assert(Op::kSum, "the carried row body folds sums");
+  __shared__ u32x4 handover[kThreads / 64];
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = uint32_t(__builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)));
+  constexpr uint32_t kWaves = kThreads / 64;
+  const uint32_t nrows = (n16 + 63u) >> 6;
+  const uint32_t per = (nrows + kWaves - 1u) / kWaves;
+  const uint32_t r0 = wave * per < nrows ? wave * per : nrows;
+  const uint32_t r1 = r0 + per < nrows ? r0 + per : nrows;
+  auto fold_row = [&](uint32_t r) -> u32x4 {
+    uint32_t u = (r << 6) + lane;
+    if (u >= n16) u = n16 - 1u;   // past the body: a unit inside it, never stored
+    u32x4 x[kMaxRanks];
+#pragma unroll
+    for (int i = 0; i < kMaxRanks; ++i) x[i] = ld16<kNTL>(sa[i] + uint64_t(u) * 16u);
+    return Op::kElem == 4 ? fold_f32(x, ns) : fold_bf16(x, ns);
+  };
+  auto emit = [&](uint32_t r, u32x4 v) {
+    const uint32_t k = (r << 6) + lane;
+    if (k + 1u < n16) {
+      const uint32_t o = k * 16u + sig;
+      if constexpr (kOne) {
+        stm<kNTS>(db[0], o, v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kMaxRanks + 1; ++j)
+          if (j < nd) stm<kNTS>(db[j], o, v);
+      }
+    }
+  };
+  // the previous tile's last reads of the handover are done
+  __syncthreads();
+  u32x4 cur{0u, 0u, 0u, 0u};
+  if (r0 < r1) {
+    cur = fold_row(r0);
+    if (lane == 0u) handover[wave] = cur;
+    for (uint32_t r = r0; r + 1u < r1; ++r) {
+      const u32x4 nxt = fold_row(r + 1u);
+      // read lane 0 with every lane active (under lane == 63 alone, the
+      // first active lane would be lane 63)
+      const u32x4 first = lane0(nxt);
+      u32x4 hi = next_lane<false>(cur);
+      if (lane == 63u) hi = first;
+      emit(r, funnel(cur, hi, sig));
+      cur = nxt;
+    }
+  }
+  __syncthreads();   // every wavefront's first unit is in LDS
+  if (r0 < r1) {
+    // the unit after this block: the next block's first (a wavefront whose
+    // block is last stores no unit that needs it)
+    const uint32_t w1 = wave + 1u < kWaves ? wave + 1u : wave;
+    u32x4 hi = next_lane<false>(cur);
+    if (lane == 63u) hi = handover[w1];
+    emit(r1 - 1u, funnel(cur, hi, sig));
+  }
+}
+
 // Whether a job's rows are aligned to its sources: a sum with one
 // destination, and some source off the destination's 16-byte phase (the
 // offset between a source and the destination is the same at every byte of
@@ -763,7 +838,7 @@ template <class Op, int kU, bool kNT, bool kFoldOk = true, bool kRows = true, bo
 __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, int64_t x1,
                                      bool nt_any_phase = false, int64_t wide_max = 0,
                                      bool shift_stores = false, lds_u32x4 *lds_slice = nullptr,
-                                     bool unaligned_loads = false) {
+                                     bool unaligned_loads = false, bool carry_rows = false) {
   constexpr bool kDev = kNTS == kStoreDevice;
   static_assert(!(kDev && kLdsRows > 0), "the LDS body has no device-scope stores");
   if (x1 <= x0) return;
@@ -781,13 +856,25 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
           x0 + int64_t((16u - uint32_t((s.a[0] + uint64_t(x0)) & 15u)) & 15u);
       const uint32_t n16 = uint32_t((x1 - xs) >> 4);
       const int64_t xe = xs + int64_t(n16) * 16;
-      elements<Op>(s, d, x0, xs);
-      elements<Op>(s, d, xe, x1, kThreads - 64);
       uint64_t sa[kMaxRanks], db[kMaxRanks + 1];
 #pragma unroll
       for (int i = 0; i < kMaxRanks; ++i) sa[i] = s.a[i] + uint64_t(xs);
 #pragma unroll
       for (int j = 0; j < kMaxRanks + 1; ++j) db[j] = d.b[j] + uint64_t(xs);
+      if constexpr (Op::kSum) {
+        if (carry_rows && n16 >= 2u) {
+          // aligned stores from carried rows: the element passes take the
+          // bytes before the first destination unit and after the last
+          const uint32_t sig = (16u - uint32_t(db[0] & 15u)) & 15u;
+          elements<Op>(s, d, x0, xs + int64_t(sig));
+          elements<Op>(s, d, xs + int64_t(n16 - 1u) * 16 + int64_t(sig), x1, kThreads - 64);
+          if (kNT && nt_any_phase) body_carry<Op, true, kNTS, kOne>(sa, s.n, db, d.n, n16, sig);
+          else body_carry<Op, false, kNTS, kOne>(sa, s.n, db, d.n, n16, sig);
+          return;
+        }
+      }
+      elements<Op>(s, d, x0, xs);
+      elements<Op>(s, d, xe, x1, kThreads - 64);
       if (kNT && nt_any_phase) body_aligned<Op, kU, true, kNTS, kOne, true>(sa, s.n, db, d.n, n16);
       else body_aligned<Op, kU, false, kNTS, kOne, true>(sa, s.n, db, d.n, n16);
       return;

@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(kThreads) zs_kernel(const LaunchPlan p) {
                 t - p.tile_begin[j], p.tile_begin[j + 1] - p.tile_begin[j], x0, x1);
     atom::tile<Op, kU, kNTL, true, kRows, kOne, kWide, kNTS>(s, d, x0, x1, p.nt_any_phase != 0,
                                                   p.wide_max, p.shift_stores != 0, nullptr,
-                                                  p.unaligned_loads != 0);
+                                                  p.unaligned_loads != 0, p.shift_stores == 2);
   }
   if (p.sync) snac::exit_notify(p, e);
 }

@@ -77,7 +77,8 @@ struct LaunchPlan {
   int32_t wide_max;         // tiles up to this many bytes that would take a row body
                             // take one wide element pass instead (0: never)
   int32_t shift_stores;     // 1: jobs whose sources share a 16-byte phase off their
-                            // destinations' take source-aligned units, misaligned stores
+                            // destinations' take source-aligned units, misaligned stores;
+                            // 2: the same units shifted into aligned stores (body_carry)
   int32_t unaligned_loads;  // 1: jobs with a source off their destinations' 16-byte phase take
                             // destination-aligned units, misaligned loads
   int32_t tile_begin[kMaxJobs + 1];

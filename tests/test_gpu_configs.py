@@ -221,7 +221,8 @@ REGIMES = [("alltoall", 256 << 10), ("alltoallv", 512 << 10), ("alltoallv", 8 <<
            ("reducescatterv", 24 << 20), ("reducescatterv", 96 << 20),
            ("allreduce", 16 << 20), ("allreduce", 48 << 20),
            ("allreduce", 128 << 10), ("allreduce", 512 << 10), ("allreduce", 320 << 20),
-           ("allgather", 64 << 20), ("allgather", 160 << 20), ("allgatherv", 96 << 20)]
+           ("allgather", 64 << 20), ("allgather", 160 << 20), ("allgatherv", 96 << 20),
+           ("reducescatterv", 320 << 20)]
 
 
 def _expect_device_stores(name, T):
@@ -256,6 +257,8 @@ def test_policy_regimes(purlin, name, T):
     assert info["device_stores"] == int(_expect_device_stores(name, T)), (name, info)
     if name == "allgather" and T >= (64 << 20):
         assert info["chunk_bytes"] == 4096, info   # the large copy broadcasts' chunk
+    if name == "reducescatterv":                   # misaligned stores, then carried rows
+        assert info["shift_stores"] == (2 if T >= (256 << 20) else 1), info
     base = name.rstrip("v") if name.endswith("v") else name
     if op == "copy":
         _device_copy_check(base, s["counts"], ins, outs)

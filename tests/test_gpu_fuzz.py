@@ -20,7 +20,7 @@ from gpu_util import compare, run_collective, STORE
 pytestmark = pytest.mark.gpu
 
 NAMINGS = ["whole", "by_rank", "by_index", "by_rank_index", "by_index_rank"]
-SWITCHES = [("PURLIN_SHIFT_STORES", "0"), ("PURLIN_UNALIGNED_LOADS", "1"),
+SWITCHES = [("PURLIN_SHIFT_STORES", "0"), ("PURLIN_SHIFT_STORES", "2"), ("PURLIN_UNALIGNED_LOADS", "1"),
             ("PURLIN_BCAST_PLAIN", "0"), ("PURLIN_NT_ANY_PHASE", "0"), ("PURLIN_UNROLL", "1"),
             ("PURLIN_MID_CHUNKS", "0"), ("PURLIN_NT", "0"), ("PURLIN_DEVICE_STORES", "1")]
 

@@ -390,8 +390,28 @@ def test_tile_forms_at_the_mid_size_broadcast_window(purlin, name):
     assert info["shift_stores"] == (1 if name == "reducescatter" else 0), info
 
 
+@pytest.mark.parametrize("chunk", [16384, 65536])
+@pytest.mark.parametrize("name,dtype", [("reducescatter", "bf16"), ("reducescatter", "f32"),
+                                        ("allreduce", "bf16")])
+def test_carried_rows_span_several_rows_per_wavefront(purlin, name, dtype, chunk, monkeypatch):
+    """Sums whose sources share a 16-byte phase off their destinations'
+    (every input shifted by 3 elements, outputs aligned) on the carried-row
+    body, with chunks of 16 and 64 KiB, so that each wavefront carries 4-16
+    rows within a tile and workgroups take several tiles; variable
+    partitions; the oracle element by element (AllReduce: eight
+    destinations per unit)."""
+    monkeypatch.setenv("PURLIN_SHIFT_STORES", "2")
+    P = 8
+    print("case carried-rows", name, dtype, chunk, flush=True)
+    rng = np.random.default_rng([53, len(name), chunk, len(dtype)])
+    counts, displs, ins, outs = _case(name, P, dtype, "v", rng, 90000)
+    purlin.set_policy(chunk_bytes=chunk, zero_staging="zs")
+    oracle_and_gpu(purlin, name, P, counts, dtype, ins, outs, displs, [3] * P, [0] * P)
+    assert purlin.last_launch()["shift_stores"] == 2
+
+
 # every datapath switch the header lists, away from its default
-SWITCHES = [{"PURLIN_SHIFT_STORES": "0"}, {"PURLIN_SHIFT_STORES": "1"},
+SWITCHES = [{"PURLIN_SHIFT_STORES": "0"}, {"PURLIN_SHIFT_STORES": "1"}, {"PURLIN_SHIFT_STORES": "2"},
             {"PURLIN_UNALIGNED_LOADS": "1"}, {"PURLIN_UNALIGNED_LOADS": "0"},
             {"PURLIN_BCAST_PLAIN": "0"}, {"PURLIN_NT": "0"}, {"PURLIN_NT_ANY_PHASE": "0"},
             {"PURLIN_UNROLL": "1"}, {"PURLIN_UNROLL": "2"}, {"PURLIN_LDS": "1"},
