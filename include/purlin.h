@@ -172,6 +172,8 @@ typedef struct {
                               (copy broadcasts of 32 MiB of jobs or more) */
   int32_t device_stores; /* zero staging: 1 if broadcast jobs were stored at device scope
                             (written through the L2) */
+  int32_t unroll;        /* collective kernels: 16-byte units each lane keeps in flight per
+                            source (copies 4 / 8 / 16, sums 1 / 2 / 4); 0 otherwise */
 } purlin_launch_info;
 
 /*

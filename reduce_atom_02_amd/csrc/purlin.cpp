@@ -613,6 +613,14 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
   // compiled code, not the pass).
   const bool small = job_bytes <= (int64_t(512) << 10);
   const bool wide = !staged && rows && (small || kind == KernelKind::kCopy);
+  // Point-to-point copies on the row body (AllToAllV) from 256 MiB of jobs
+  // keep eight units per lane in flight (the build without the wide pass):
+  // +3-9% at 32-512 MiB per rank and +1.1-1.6% at 1 GiB, paired on the
+  // same buffers with both placements (at 16 MiB -1.6%; the aligned
+  // AllToAll 2-6% slower with it).
+  if (!staged && unroll_env() < 0 && kind == KernelKind::kCopy && !broadcast && rows &&
+      job_bytes >= (int64_t(256) << 20))
+    unroll_sel = 1;
   // Point-to-point copies on the row body (AllToAllV) with 32 - 256 MiB of
   // jobs run as many workgroups as are resident (five per CU) on 16 KiB
   // chunks: AllToAllV 21 / 12 / 9 / 4% faster at 4 / 8 / 16 / 32 MiB per
@@ -783,6 +791,7 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     info.device_stores = dstore ? 1 : 0;
     info.shift_stores = lp.shift_stores;
     info.unaligned_loads = lp.unaligned_loads;
+    info.unroll = unroll_of(kind, unroll_sel);
     info.chunk_bytes = chunk;
     info.tiles = lp.total_tiles;
     info.sync = lp.sync;
@@ -874,6 +883,7 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     info.grid = sp.total_roles;
     info.zero_staging = 0;
     info.rows = 1;
+    info.unroll = unroll_of(kind, 1);
     info.depth = sp.depth;
     info.chunk_bytes = sp.base.chunk_bytes;
     info.tiles = sp.base.total_tiles;

@@ -75,7 +75,8 @@ class LaunchInfo(ctypes.Structure):
                 ("sync", ctypes.c_int32), ("rows", ctypes.c_int32), ("unit", ctypes.c_int32),
                 ("one", ctypes.c_int32), ("plain_stores", ctypes.c_int32),
                 ("engine_copies", ctypes.c_int32), ("shift_stores", ctypes.c_int32),
-                ("unaligned_loads", ctypes.c_int32), ("device_stores", ctypes.c_int32)]
+                ("unaligned_loads", ctypes.c_int32), ("device_stores", ctypes.c_int32),
+                ("unroll", ctypes.c_int32)]
 
 
 def _load():
