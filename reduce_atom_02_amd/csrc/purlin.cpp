@@ -650,7 +650,9 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     ap.chunk = 8 << 10;
     chunk_fixed = true;
   } else if (mid_rules && kind == KernelKind::kCopy && broadcast && job_bytes >= 16 * MiB &&
-             job_bytes < 32 * MiB) {
+             (job_bytes < 32 * MiB || (rows && job_bytes < 64 * MiB))) {
+    // (AllGatherV keeps it up to 64 MiB of jobs: +2-5% at 32-48 MiB per
+    // rank, paired with both placements; AllGather gains nothing there)
     ap.grid = 4 * ds->cus;
     ap.chunk = 8 << 10;
     chunk_fixed = true;

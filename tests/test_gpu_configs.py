@@ -222,7 +222,7 @@ REGIMES = [("alltoall", 256 << 10), ("alltoallv", 512 << 10), ("alltoallv", 8 <<
            ("allreduce", 16 << 20), ("allreduce", 48 << 20),
            ("allreduce", 128 << 10), ("allreduce", 512 << 10), ("allreduce", 320 << 20),
            ("allgather", 64 << 20), ("allgather", 160 << 20), ("allgatherv", 96 << 20),
-           ("reducescatterv", 320 << 20), ("alltoallv", 40 << 20)]
+           ("reducescatterv", 320 << 20), ("alltoallv", 40 << 20), ("allgatherv", 40 << 20)]
 
 
 def _expect_device_stores(name, T):
