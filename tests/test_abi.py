@@ -288,6 +288,42 @@ def test_ulysses_argument_checks(purlin):
     assert uly([0, 0], in_=V(0, 0), out_=V(0, 0)) == 0                  # nothing to move
 
 
+def test_binding_structs_match_the_header(purlin, tmp_path):
+    """The binding's ctypes structures have the size and field offsets of
+    the header's structs (compiled with the host compiler), so that no call
+    writes past a structure the binding passes."""
+    import ctypes
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no host compiler")
+    here = os.path.dirname(os.path.abspath(__file__))
+    inc = os.path.join(here, "..", "include")
+    structs = {"purlin_launch_info": purlin.LaunchInfo, "purlin_policy": purlin.Policy,
+               "purlin_layout": purlin.Layout, "purlin_segment": purlin.Segment}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "purlin.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append('  printf("%s size %%zu\\n", sizeof(%s));' % (cname, cname))
+        for f, _ in py._fields_:
+            lines.append('  printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([gcc, "-D__HIP_PLATFORM_AMD__", "-I", inc, "-I", "/opt/rocm/include",
+                    "-o", str(exe), str(src)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                               text=True).stdout.splitlines():
+        a, b, v = line.split()
+        got[(a, b)] = int(v)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
 def test_stream_pattern_argument_checks(purlin):
     """The ceiling pattern rejects bad arguments before any HIP call; a
     zero-byte pattern with valid arguments is a no-op."""
