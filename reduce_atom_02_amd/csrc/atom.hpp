@@ -7,16 +7,23 @@
 //  * 16-byte global loads and stores (dwordx4), 64 lanes x 16 B = 1 KiB per
 //    wavefront instruction, 4 KiB per 256-thread workgroup pass, with kU
 //    independent units per lane in flight;
-//  * units are aligned to the *destination*, so every store is a full
-//    aligned 16-byte store; a source whose address differs from the
-//    destination's modulo 16 is read in aligned 16-byte blocks, and each
-//    lane shifts its block and its neighbour lane's block into place in
-//    registers (lane shuffle + v_alignbyte), never by unaligned or byte-wise
-//    memory accesses; such wavefront rows follow the sources' 128-byte
-//    lines for a sum with one destination, so none of its eight sources'
-//    lines is loaded by two rows (a second nontemporal load of a line
-//    fetches it from HBM again, while split destination lines merge in
-//    L2), and the destinations' lines for copies, which read one stream;
+//  * a tile whose sources sit on its destinations' 16-byte phase moves
+//    aligned units; otherwise it takes one of these forms, chosen per
+//    launch by measurement: the row body (units aligned to the destination,
+//    each source read in aligned 16-byte blocks and shifted into place in
+//    registers with a lane shuffle and v_alignbyte); for sums whose sources
+//    share one phase, source-aligned units with misaligned 16-byte stores,
+//    or the same units folded and shifted into aligned stores across rows
+//    each wavefront carries (body_carry); for copy broadcasts,
+//    destination-aligned units with misaligned 16-byte loads.  Rows follow
+//    the sources' 128-byte lines for a sum with one destination, so none of
+//    its eight sources' lines is loaded by two rows (a second nontemporal
+//    load of a line fetches it from HBM again, while split destination
+//    lines merge in L2), and the destinations' lines for copies, which read
+//    one stream;
+//  * stores are nontemporal, plain, or at device scope (written through the
+//    L2: the staged pipeline's ring slots, and broadcasts where that
+//    measured faster);
 //  * the reduce is a per-lane fold over the sources in ascending rank, in
 //    fp32 (bf16 widened exactly), with one final round to nearest even for
 //    a bf16 output; there is no cross-lane tree, so the summation order is
