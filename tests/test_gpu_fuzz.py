@@ -59,7 +59,7 @@ def _gapped(in_n, out_n, P, counts, rng):
     return side[0] + side[1]
 
 
-def _draw(rng):
+def _draw(rng, scales=(40, 700, 3000, 20000)):
     if rng.random() < 0.6:
         in_n, out_n, op = oracle.COLLECTIVES[list(oracle.COLLECTIVES)[int(rng.integers(0, 4))]]
     else:
@@ -70,7 +70,7 @@ def _draw(rng):
     if oracle.name_count(out_n, P) != nn:
         return None
     dtype = "bf16" if rng.random() < 0.6 else "f32"
-    scale = int(rng.choice([40, 700, 3000, 20000]))
+    scale = int(rng.choice(list(scales)))
     counts = [int(v) for v in rng.integers(0, scale + 1, nn)]
     for _ in range(int(rng.integers(0, 3))):
         counts[int(rng.integers(0, nn))] = 0
@@ -131,3 +131,59 @@ def test_random_collectives_match_oracle(purlin, monkeypatch):
         ran += 1
     print("fuzz: %d cases ran, %d skipped" % (ran, skipped), flush=True)
     assert ran >= 120
+
+
+def test_random_large_collectives_match_oracle(purlin, monkeypatch):
+    """Fewer, larger cases (partitions up to 300 000 elements), with explicit
+    chunks of 16 and 64 KiB among the policies, so that wavefronts take
+    several rows of a tile and workgroups several tiles in every tile form
+    (carried rows, misaligned loads and stores, device-scope stores)."""
+    rng = np.random.default_rng(20261205)
+    ran = skipped = 0
+    for case in range(48):
+        spec = _draw(rng, scales=(60000, 150000, 300000))
+        if spec is None:
+            skipped += 1
+            continue
+        in_n, out_n, op, dtype, P, counts, displs = spec
+        n = len(counts)
+        in_d, out_d = (displs[:n], displs[n:]) if displs is not None else (None, None)
+        in_len = [max([o + c for _, o, c in oracle.partitions(in_n, r, P, counts, in_d)] + [0])
+                  for r in range(P)]
+        out_len = [max([o + c for _, o, c in oracle.partitions(out_n, r, P, counts, out_d)] + [0])
+                   for r in range(P)]
+        ins = [pins._rand_bits(rng, in_len[r], dtype) for r in range(P)]
+        outs = [np.full(out_len[r], 0x3C5A, dtype=STORE[dtype]) for r in range(P)]
+        try:
+            want = oracle.collective(in_n, out_n, op, dtype, P, counts, displs, ins, outs)
+        except oracle.OracleError:
+            skipped += 1
+            continue
+        policy = dict(zero_staging="staged" if rng.random() < 0.2 else "zs",
+                      chunk_bytes=int(rng.choice([0, 16384, 65536])))
+        switch = SWITCHES[int(rng.integers(0, len(SWITCHES)))] if rng.random() < 0.5 else None
+        shifts = [int(v) for v in rng.integers(0, 8, P)]
+        out_shifts = [int(v) for v in rng.integers(0, 8, P)]
+        print("case fuzz-large", case, in_n, out_n, op, dtype, P, sum(counts), displs is not None,
+              policy, switch, flush=True)
+        purlin.set_policy(**policy)
+        if switch:
+            monkeypatch.setenv(*switch)
+        try:
+            got = run_collective(purlin, in_n, out_n, op, dtype, P, counts, displs, ins, outs,
+                                 shifts, out_shifts)
+        except purlin.PurlinError as e:
+            assert e.status == "UNSUPPORTED", (case, e.status)
+            skipped += 1
+            continue
+        finally:
+            if switch:
+                monkeypatch.delenv(switch[0])
+            purlin.set_policy(reset=True)
+        for j in range(P):
+            inexact = compare("fuzz-large case %d rank %d" % (case, j), got[j], want[j], dtype, op)
+            assert inexact == 0, (case, j)
+        ran += 1
+    print("fuzz-large: %d cases ran, %d skipped" % (ran, skipped), flush=True)
+    assert ran >= 20
+
