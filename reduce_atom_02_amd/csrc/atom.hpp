@@ -714,11 +714,15 @@ __device__ __forceinline__ void body_rows(const uint64_t *sa, int ns, const uint
 // body's first source byte (16-byte aligned sources); n16 source units;
 // sig = (16 - (db - sa)) % 16, the source offset of the first destination
 // unit boundary.  Destination unit k (source bytes 16k + sig ..) is stored
-// for k + 1 < n16; the caller's element passes cover the bytes before unit 0
-// and after unit n16 - 2.  Every wavefront of the workgroup calls it.
+// for k + 1 < n16.  The bytes before unit 0 (source bytes [0, sig)) and
+// after unit n16 - 2 (bytes [16 (n16 - 1) + sig, 16 n16)) are written from
+// the folded units 0 and n16 - 1 with 2-byte stores when `edges` is set (a
+// tile whose source range is whole units: no block is then read again);
+// otherwise the caller's element passes cover them.  Every wavefront of the
+// workgroup calls it.
 template <class Op, bool kNTL, int kNTS, bool kOne>
 __device__ __forceinline__ void body_carry(const uint64_t *sa, int ns, const uint64_t *db, int nd,
-                                           uint32_t n16, uint32_t sig) {
+                                           uint32_t n16, uint32_t sig, bool edges) {
   static_assert(Op::kSum, "the carried row body folds sums");
   __shared__ u32x4 handover[kThreads / 64];
   const uint32_t lane = threadIdx.x & 63u;
@@ -735,6 +739,17 @@ __device__ __forceinline__ void body_carry(const uint64_t *sa, int ns, const uin
 #pragma unroll
     for (int i = 0; i < kMaxRanks; ++i) x[i] = ld16<kNTL>(sa[i] + uint64_t(u) * 16u);
     return Op::kElem == 4 ? fold_f32(x, ns) : fold_bf16(x, ns);
+  };
+  // bytes [b0, b1) of a folded unit (2-byte steps) to destination offset
+  // `at` + b of every destination
+  auto bytes_of = [&](u32x4 v, uint32_t b0, uint32_t b1, uint32_t at) {
+    for (uint32_t b = b0; b < b1; b += 2u) {
+      const uint32_t w = b < 4u ? v.x : b < 8u ? v.y : b < 12u ? v.z : v.w;
+      const uint16_t h = uint16_t(w >> ((b & 3u) * 8u));
+#pragma unroll
+      for (int j = 0; j < kMaxRanks + 1; ++j)
+        if (j < (kOne ? 1 : nd)) ste<uint16_t, kNTS == kStoreDevice>(db[j] + at + b, h);
+    }
   };
   auto emit = [&](uint32_t r, u32x4 v) {
     const uint32_t k = (r << 6) + lane;
@@ -755,6 +770,7 @@ __device__ __forceinline__ void body_carry(const uint64_t *sa, int ns, const uin
   if (r0 < r1) {
     cur = fold_row(r0);
     if (lane == 0u) handover[wave] = cur;
+    if (edges && r0 == 0u && lane == 0u) bytes_of(cur, 0u, sig, 0u);   // head
     for (uint32_t r = r0; r + 1u < r1; ++r) {
       const u32x4 nxt = fold_row(r + 1u);
       // read lane 0 with every lane active (under lane == 63 alone, the
@@ -774,6 +790,9 @@ __device__ __forceinline__ void body_carry(const uint64_t *sa, int ns, const uin
     u32x4 hi = next_lane<false>(cur);
     if (lane == 63u) hi = handover[w1];
     emit(r1 - 1u, funnel(cur, hi, sig));
+    // tail: the block holding the last unit writes its bytes past sig
+    if (edges && r1 == nrows && lane == ((n16 - 1u) & 63u))
+      bytes_of(cur, sig, 16u, (n16 - 1u) * 16u);
   }
 }
 
@@ -873,10 +892,15 @@ __device__ __forceinline__ void tile(const Srcs &s, const Dsts &d, int64_t x0, i
           // aligned stores from carried rows: the element passes take the
           // bytes before the first destination unit and after the last
           const uint32_t sig = (16u - uint32_t(db[0] & 15u)) & 15u;
-          elements<Op>(s, d, x0, xs + int64_t(sig));
-          elements<Op>(s, d, xs + int64_t(n16 - 1u) * 16 + int64_t(sig), x1, kThreads - 64);
-          if (kNT && nt_any_phase) body_carry<Op, true, kNTS, kOne>(sa, s.n, db, d.n, n16, sig);
-          else body_carry<Op, false, kNTS, kOne>(sa, s.n, db, d.n, n16, sig);
+          // a tile whose source range is whole units (every tile but a
+          // job's ragged first and last) writes its edges from registers
+          const bool edges = xs == x0 && xe == x1;
+          if (!edges) {
+            elements<Op>(s, d, x0, xs + int64_t(sig));
+            elements<Op>(s, d, xs + int64_t(n16 - 1u) * 16 + int64_t(sig), x1, kThreads - 64);
+          }
+          if (kNT && nt_any_phase) body_carry<Op, true, kNTS, kOne>(sa, s.n, db, d.n, n16, sig, edges);
+          else body_carry<Op, false, kNTS, kOne>(sa, s.n, db, d.n, n16, sig, edges);
           return;
         }
       }

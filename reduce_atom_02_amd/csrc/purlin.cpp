@@ -755,9 +755,9 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     // on AllGatherV and 4-11% on AllToAllV.
     // From 256 MiB of jobs the same units are folded and then shifted into
     // destination-aligned stores across rows each wavefront carries
-    // (body_carry, shift_stores 2): ReduceScatterV +1.5-2.3% at 256 MiB,
-    // +1.9% at 512 MiB and +0.6-1.2% at 1 GiB per rank (paired, runs on
-    // three boxes, both placements), traffic 1.011 x B_min against 1.014;
+    // (body_carry, shift_stores 2): ReduceScatterV +1.5-3.2% at 256 MiB,
+    // +1.9-3.6% at 512 MiB and +0.6-1.3% at 1 GiB per rank (paired, runs on
+    // four boxes, both placements), traffic 1.011 x B_min against 1.014;
     // even at 128 MiB, at 64 MiB -2.7 to +0.6%, at 1-16 MiB -5 to -10%.  PURLIN_SHIFT_STORES: 0 row body, 1
     // misaligned stores, 2 carried rows.
     const int64_t shift_env = env_i64("PURLIN_SHIFT_STORES", -1);
