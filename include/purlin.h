@@ -166,7 +166,7 @@ typedef struct {
   int32_t shift_stores;  /* zero staging: jobs whose sources share a 16-byte phase off
                             their destination's took source-aligned units (reductions):
                             1 with misaligned stores, 2 shifted into aligned stores
-                            across carried rows (256 MiB of jobs or more) */
+                            across carried rows (32 MiB of jobs or more) */
   int32_t unaligned_loads; /* zero staging: 1 if jobs with a source off their destinations'
                               phase took destination-aligned units and misaligned loads
                               (copy broadcasts of 32 MiB of jobs or more) */

@@ -753,15 +753,15 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     // per rank (paired on the same buffers).  Copies keep the row bodies,
     // whose stores are whole lines: misaligned stores measured 2-11% slower
     // on AllGatherV and 4-11% on AllToAllV.
-    // From 256 MiB of jobs the same units are folded and then shifted into
+    // From 32 MiB of jobs the same units are folded and then shifted into
     // destination-aligned stores across rows each wavefront carries
-    // (body_carry, shift_stores 2): ReduceScatterV +1.5-3.2% at 256 MiB,
-    // +1.9-3.6% at 512 MiB and +0.6-1.3% at 1 GiB per rank (paired, runs on
-    // four boxes, both placements), traffic 1.011 x B_min against 1.014;
-    // even at 128 MiB, at 64 MiB -2.7 to +0.6%, at 1-16 MiB -5 to -10%.  PURLIN_SHIFT_STORES: 0 row body, 1
+    // (body_carry, shift_stores 2): ReduceScatterV +0.1-0.7% at 32 MiB,
+    // +1.5-3.9% at 48-512 MiB and +0.6-1.3% at 1 GiB per rank (paired, both
+    // placements), traffic 1.011 x B_min against 1.014; at 16 MiB -0.3 to
+    // +1.3%, at 1-8 MiB 5-12% slower.  PURLIN_SHIFT_STORES: 0 row body, 1
     // misaligned stores, 2 carried rows.
     const int64_t shift_env = env_i64("PURLIN_SHIFT_STORES", -1);
-    const int shift_auto = kind == KernelKind::kCopy ? 0 : job_bytes >= 256 * MiB ? 2 : 1;
+    const int shift_auto = kind == KernelKind::kCopy ? 0 : job_bytes >= 32 * MiB ? 2 : 1;
     lp.shift_stores = shift_env < 0    ? shift_auto
                       : shift_env == 2 ? (kind != KernelKind::kCopy ? 2 : 0)
                                        : (shift_env != 0 ? 1 : 0);

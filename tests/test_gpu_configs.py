@@ -218,7 +218,7 @@ def test_bench_step_1gib(purlin, variant):
 # one size inside each size-dependent rule of the launch policy (grid, chunk)
 REGIMES = [("alltoall", 256 << 10), ("alltoallv", 512 << 10), ("alltoallv", 8 << 20),
            ("allgather", 24 << 20), ("allgatherv", 6 << 20), ("allgatherv", 24 << 20),
-           ("reducescatterv", 24 << 20), ("reducescatterv", 96 << 20),
+           ("reducescatterv", 24 << 20), ("reducescatterv", 32 << 20), ("reducescatterv", 96 << 20),
            ("allreduce", 16 << 20), ("allreduce", 48 << 20),
            ("allreduce", 128 << 10), ("allreduce", 512 << 10), ("allreduce", 320 << 20),
            ("allgather", 64 << 20), ("allgather", 160 << 20), ("allgatherv", 96 << 20),
@@ -258,7 +258,7 @@ def test_policy_regimes(purlin, name, T):
     if name == "allgather" and T >= (64 << 20):
         assert info["chunk_bytes"] == 4096, info   # the large copy broadcasts' chunk
     if name == "reducescatterv":                   # misaligned stores, then carried rows
-        assert info["shift_stores"] == (2 if T >= (256 << 20) else 1), info
+        assert info["shift_stores"] == (2 if T >= (32 << 20) else 1), info
     if name == "alltoallv":                        # eight units per lane from 256 MiB of jobs
         assert info["unroll"] == (8 if P * T >= (256 << 20) else 4), info
     base = name.rstrip("v") if name.endswith("v") else name
