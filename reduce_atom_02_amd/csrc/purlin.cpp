@@ -621,6 +621,14 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
   if (!staged && unroll_env() < 0 && kind == KernelKind::kCopy && !broadcast && rows &&
       job_bytes >= (int64_t(256) << 20))
     unroll_sel = 1;
+  // Aligned single-destination sums (ReduceScatter) with 16 - 256 MiB of
+  // jobs keep two units per lane in flight (sixteen loads): +1.4-3.8% at
+  // 16 - 64 MiB per rank and -0.3 to +1.1% at 96 - 192 MiB (paired, buffers
+  // placed three ways); from 256 MiB 1-3% slower, and AllReduce (broadcast
+  // sums) moved -1.6 to +1.7% from box to box, so it keeps one.
+  if (!staged && unroll_env() < 0 && kind != KernelKind::kCopy && single_dst && !rows &&
+      job_bytes >= (int64_t(16) << 20) && job_bytes < (int64_t(256) << 20))
+    unroll_sel = 1;
   // Point-to-point copies on the row body (AllToAllV) with 32 - 256 MiB of
   // jobs run as many workgroups as are resident (five per CU) on 16 KiB
   // chunks: AllToAllV 21 / 12 / 9 / 4% faster at 4 / 8 / 16 / 32 MiB per

@@ -222,7 +222,8 @@ REGIMES = [("alltoall", 256 << 10), ("alltoallv", 512 << 10), ("alltoallv", 8 <<
            ("allreduce", 16 << 20), ("allreduce", 48 << 20),
            ("allreduce", 128 << 10), ("allreduce", 512 << 10), ("allreduce", 320 << 20),
            ("allgather", 64 << 20), ("allgather", 160 << 20), ("allgatherv", 96 << 20),
-           ("reducescatterv", 320 << 20), ("alltoallv", 40 << 20), ("allgatherv", 40 << 20)]
+           ("reducescatterv", 320 << 20), ("alltoallv", 40 << 20), ("allgatherv", 40 << 20),
+           ("reducescatter", 24 << 20), ("reducescatter", 320 << 20)]
 
 
 def _expect_device_stores(name, T):
@@ -261,6 +262,8 @@ def test_policy_regimes(purlin, name, T):
         assert info["shift_stores"] == (2 if T >= (32 << 20) else 1), info
     if name == "alltoallv":                        # eight units per lane from 256 MiB of jobs
         assert info["unroll"] == (8 if P * T >= (256 << 20) else 4), info
+    if name == "reducescatter":                    # two units per lane at 16 - 256 MiB of jobs
+        assert info["unroll"] == (2 if (16 << 20) <= T < (256 << 20) else 1), info
     base = name.rstrip("v") if name.endswith("v") else name
     if op == "copy":
         _device_copy_check(base, s["counts"], ins, outs)
