@@ -624,8 +624,9 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
   // Aligned single-destination sums (ReduceScatter) with 16 - 256 MiB of
   // jobs keep two units per lane in flight (sixteen loads): +1.4-3.8% at
   // 16 - 64 MiB per rank and -0.3 to +1.1% at 96 - 192 MiB (paired, buffers
-  // placed three ways); from 256 MiB 1-3% slower, and AllReduce (broadcast
-  // sums) moved -1.6 to +1.7% from box to box, so it keeps one.
+  // placed three ways); from 256 MiB 1-3% slower.  AllReduce (broadcast
+  // sums, which would give up their device-scope stores for it) moved -7 to
+  // +2.6% at 16 MiB - 1 GiB per rank with box and placement, so it keeps one.
   if (!staged && unroll_env() < 0 && kind != KernelKind::kCopy && single_dst && !rows &&
       job_bytes >= (int64_t(16) << 20) && job_bytes < (int64_t(256) << 20))
     unroll_sel = 1;
