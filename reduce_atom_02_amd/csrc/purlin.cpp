@@ -766,7 +766,7 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
     // destination-aligned stores across rows each wavefront carries
     // (body_carry, shift_stores 2): ReduceScatterV +0.1-0.7% at 32 MiB,
     // +1.5-3.9% at 48-512 MiB and +0.6-1.3% at 1 GiB per rank (paired, both
-    // placements), traffic 1.011 x B_min against 1.014; at 16 MiB -0.3 to
+    // placements), traffic 1.012 x B_min against 1.014; at 16 MiB -0.3 to
     // +1.3%, at 1-8 MiB 5-12% slower.  PURLIN_SHIFT_STORES: 0 row body, 1
     // misaligned stores, 2 carried rows.
     const int64_t shift_env = env_i64("PURLIN_SHIFT_STORES", -1);
