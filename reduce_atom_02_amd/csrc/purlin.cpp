@@ -674,6 +674,13 @@ purlin_status collective_impl(const purlin_layout *in, const purlin_layout *out,
   // -4%).  One workgroup per CU and 32 KiB chunks for AllReduce measured
   // +1-2% on one box and -3 to -7% on another, so AllReduce keeps the
   // table's.
+  // Aligned point-to-point copies (AllToAll) from 1 GiB of jobs run one
+  // workgroup per CU: +1.6-2.2% at 256 - 512 MiB per rank, +0.2-0.7% at
+  // 128 MiB and 1 GiB (paired, two boxes, both placements); at 64 MiB 3-4.5%
+  // slower, and AllToAllV on the row body 9-17% slower with it.
+  if (mid_rules && kind == KernelKind::kCopy && !broadcast && !rows &&
+      job_bytes >= (int64_t(1) << 30))
+    ap.grid = ds->cus;
   const bool large_bcast = env_i64("PURLIN_LARGE_BCAST", 1) != 0;
   const bool large_copy_bcast = large_bcast && broadcast && !rows && kind == KernelKind::kCopy &&
                                 job_bytes >= 64 * MiB && !chunk_fixed;

@@ -223,7 +223,7 @@ REGIMES = [("alltoall", 256 << 10), ("alltoallv", 512 << 10), ("alltoallv", 8 <<
            ("allreduce", 128 << 10), ("allreduce", 512 << 10), ("allreduce", 320 << 20),
            ("allgather", 64 << 20), ("allgather", 160 << 20), ("allgatherv", 96 << 20),
            ("reducescatterv", 320 << 20), ("alltoallv", 40 << 20), ("allgatherv", 40 << 20),
-           ("reducescatter", 24 << 20), ("reducescatter", 320 << 20)]
+           ("reducescatter", 24 << 20), ("reducescatter", 320 << 20), ("alltoall", 160 << 20)]
 
 
 def _expect_device_stores(name, T):
@@ -264,6 +264,8 @@ def test_policy_regimes(purlin, name, T):
         assert info["unroll"] == (8 if P * T >= (256 << 20) else 4), info
     if name == "reducescatter":                    # two units per lane at 16 - 256 MiB of jobs
         assert info["unroll"] == (2 if (16 << 20) <= T < (256 << 20) else 1), info
+    if name == "alltoall" and P * T >= (1 << 30):  # one workgroup per CU from 1 GiB of jobs
+        assert info["grid"] == torch.cuda.get_device_properties(0).multi_processor_count, info
     base = name.rstrip("v") if name.endswith("v") else name
     if op == "copy":
         _device_copy_check(base, s["counts"], ins, outs)
