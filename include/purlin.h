@@ -283,7 +283,8 @@ PURLIN_API purlin_status purlin_check(hipStream_t stream);
  * units per lane in flight, copies 4 / 8 / 16, sums 1 / 2 / 4), PURLIN_LDS
  * (0/1: the LDS-staged aligned body), PURLIN_OWNER_TEAM (1-8: owner
  * workgroups per staged reduction lane), PURLIN_MID_CHUNKS (0/1: the
- * mid-size chunk rules of the policy table), PURLIN_DEVICE_STORES (0/1:
+ * mid-size grid and chunk rules of the policy table, and AllToAll's one
+ * workgroup per CU from 1 GiB of jobs), PURLIN_DEVICE_STORES (0/1:
  * broadcast stores at device scope, written through the L2),
  * PURLIN_LARGE_BCAST (0/1: the grid and chunk of large aligned copy
  * broadcasts). */
