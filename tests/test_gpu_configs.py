@@ -71,6 +71,23 @@ def test_allreduce_f32_1mib(purlin):
     full_check(purlin, "allreduce", "f32", [n], ins, outs)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_reducescatter_two_units_per_lane(purlin, dtype):
+    """ReduceScatter with 24 MiB per rank (inside the window where aligned
+    single-destination sums keep two units per lane), f32 and bf16, every
+    element against the oracle; the launch reports two units."""
+    T = 24 << 20
+    esz = 4 if dtype == "f32" else 2
+    n = T // esz
+    print("case rs-two-units", dtype, T, flush=True)
+    ins = [workloads.host_values(n, "normal", dtype, 7, r).view(np.uint32 if dtype == "f32" else np.uint16)
+           for r in range(P)]
+    outs = [np.zeros(n // P, np.uint32 if dtype == "f32" else np.uint16) for _ in range(P)]
+    full_check(purlin, "reducescatter", dtype, [n // P] * P, ins, outs)
+    info = purlin.last_launch()
+    assert info["unroll"] == 2 and info["rows"] == 0, info
+
+
 @pytest.mark.parametrize("log2_bytes", range(10, 20))
 def test_reducescatter_and_allgather_bf16_latency_sweep(purlin, log2_bytes):
     T = 1 << log2_bytes
