@@ -100,8 +100,10 @@ def make_case(rng):
 
 
 def test_planner_fuzz_under_sanitizers(driver):
-    rng = np.random.default_rng(20261203)
-    cases = [make_case(rng) for _ in range(3000)]
+    # PURLIN_FUZZ_SEED / PURLIN_FUZZ_CASES: another seed and more cases for a
+    # longer search (defaults: the committed 3000)
+    rng = np.random.default_rng(20261203 + int(os.environ.get("PURLIN_FUZZ_SEED", "0")))
+    cases = [make_case(rng) for _ in range(int(os.environ.get("PURLIN_FUZZ_CASES", "3000")))]
     # the seven collectives at P = 8 with misaligned outputs, and the case that
     # overflows the launch plan (by_index -> by_index sum, outputs off phase)
     for name, (i_, o_, op_) in oracle.COLLECTIVES.items():
